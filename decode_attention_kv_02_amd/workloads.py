@@ -1,0 +1,152 @@
+"""Seeded synthetic decode-attention inputs, shared by the tests and the benchmark.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic, so both the CPU oracle and the HIP path consume exactly
+the tensors made here.
+
+Recipe (one per workload):
+  * ``torch.Generator('cpu').manual_seed(seed_base + t)`` with t = 1 for q,
+    2 for K, 3 for V; the workload presets use ``seed_base = 1000 * index``.
+  * Values are float32 N(0, 1) rounded to float16 (round-to-nearest-even).
+  * K and V are drawn slot by slot, each slot as one ``[n_kv, L_s, D]`` block,
+    and packed back to back (ragged, no padding): slot s starts at element
+    ``sum_{t<s} n_kv * L_t * D``.
+  * Block-int8 V: the float32 N(0, 1) draw is quantised per block of 32
+    consecutive dims: ``scale = fp16(max|v| / 127)``,
+    ``code = clamp(round_half_even(v / scale), -127, 127)``; an all-zero block
+    gets scale 0 and codes 0.  Scales are laid out ``[slot][n_kv][L_s][D/32]``.
+  * q is ``[n_slots, n_q, D]`` and the softmax scale is ``1/sqrt(D)`` in float32.
+
+The presets are gemma-style decode shapes (16 query heads over 8 KV heads at
+head_dim 256, contexts from 1K to 131K, several decode slots) as the pages
+describe them (hf2q gemma4 batched_body.rs; tessl nn.rs decode tuning tables).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+QUANT_BLOCK = 32
+
+
+@dataclasses.dataclass(frozen=True)
+class WorkloadConfig:
+    index: int
+    name: str
+    description: str
+    seq_lens: Tuple[int, ...]
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    v_int8: bool
+    windows: Tuple[int, ...] = (0,)
+
+    @property
+    def n_slots(self) -> int:
+        return len(self.seq_lens)
+
+    @property
+    def seed_base(self) -> int:
+        return 1000 * self.index
+
+
+WORKLOADS = (
+    WorkloadConfig(0, "single_d64_L256",
+                   "1 slot, 1 q / 1 kv head, head_dim 64, KV length 256, fp16 K/V",
+                   (256,), 1, 1, 64, False),
+    WorkloadConfig(1, "gqa_d256_L4096",
+                   "1 slot, 16 q / 8 kv heads, head_dim 256, KV length 4096, fp16 K/V",
+                   (4096,), 16, 8, 256, False),
+    WorkloadConfig(2, "ragged_4slot_d256",
+                   "4 slots, KV lengths 1024/8192/32768/2000, 16 q / 8 kv, head_dim 256, fp16 K/V",
+                   (1024, 8192, 32768, 2000), 16, 8, 256, False),
+    WorkloadConfig(3, "hybrid_int8v_8x32768",
+                   "8 slots x 32768, 16 q / 8 kv, head_dim 256, fp16 K, int8 V (blocks of 32, fp16 scales)",
+                   (32768,) * 8, 16, 8, 256, True),
+    WorkloadConfig(4, "long_131072_window1024",
+                   "1 slot x 131072, 16 q / 8 kv, head_dim 256, fp16 K/V; full and last-1024 window",
+                   (131072,), 16, 8, 256, False, (0, 1024)),
+)
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    """Host (CPU) tensors of one decode-attention call."""
+    q: torch.Tensor                    # float16 [n_slots, n_q, D]
+    k: torch.Tensor                    # float16 packed [sum_s n_kv*L_s*D]
+    v: torch.Tensor                    # float16 or int8, same layout as k
+    v_scales: Optional[torch.Tensor]   # float16 [sum_s n_kv*L_s*D/32] or None
+    seq_lens: Tuple[int, ...]
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    scale: float
+
+    @property
+    def n_slots(self) -> int:
+        return len(self.seq_lens)
+
+    @property
+    def v_int8(self) -> bool:
+        return self.v_scales is not None
+
+
+def quantize_int8_blocks(v32: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Symmetric int8 per block of 32 along the last dim (input generation only)."""
+    d = v32.shape[-1]
+    if d % QUANT_BLOCK:
+        raise ValueError("head_dim must be a multiple of 32 for block-int8 V")
+    blocks = v32.reshape(*v32.shape[:-1], d // QUANT_BLOCK, QUANT_BLOCK)
+    amax = blocks.abs().amax(dim=-1)
+    scale16 = (amax / 127.0).to(torch.float16)
+    scale32 = scale16.to(torch.float32).unsqueeze(-1)
+    safe = torch.where(scale32 == 0, torch.ones_like(scale32), scale32)
+    codes = torch.round(blocks / safe).clamp_(-127, 127)
+    codes = torch.where(scale32 == 0, torch.zeros_like(codes), codes)
+    return codes.to(torch.int8).reshape(v32.shape), scale16
+
+
+def make_inputs(seq_lens: Sequence[int], n_q_heads: int, n_kv_heads: int, head_dim: int,
+                v_int8: bool, seed_base: int, scale: Optional[float] = None) -> DecodeInputs:
+    seq_lens = tuple(int(x) for x in seq_lens)
+    n_slots = len(seq_lens)
+    total_rows = sum(seq_lens) * n_kv_heads
+    gq = torch.Generator("cpu").manual_seed(seed_base + 1)
+    gk = torch.Generator("cpu").manual_seed(seed_base + 2)
+    gv = torch.Generator("cpu").manual_seed(seed_base + 3)
+
+    q = torch.randn((n_slots, n_q_heads, head_dim), generator=gq, dtype=torch.float32).to(torch.float16)
+    k = torch.empty(total_rows * head_dim, dtype=torch.float16)
+    if v_int8:
+        v = torch.empty(total_rows * head_dim, dtype=torch.int8)
+        vs = torch.empty(total_rows * head_dim // QUANT_BLOCK, dtype=torch.float16)
+    else:
+        v = torch.empty(total_rows * head_dim, dtype=torch.float16)
+        vs = None
+    off = 0
+    for L in seq_lens:
+        n = n_kv_heads * L * head_dim
+        if n:
+            kb = torch.randn((n_kv_heads, L, head_dim), generator=gk, dtype=torch.float32)
+            k[off:off + n] = kb.reshape(-1).to(torch.float16)
+            del kb
+            vb = torch.randn((n_kv_heads, L, head_dim), generator=gv, dtype=torch.float32)
+            if v_int8:
+                codes, sc = quantize_int8_blocks(vb)
+                v[off:off + n] = codes.reshape(-1)
+                vs[off // QUANT_BLOCK:(off + n) // QUANT_BLOCK] = sc.reshape(-1)
+            else:
+                v[off:off + n] = vb.reshape(-1).to(torch.float16)
+            del vb
+        off += n
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(head_dim), dtype=torch.float32))
+    return DecodeInputs(q, k, v, vs, seq_lens, n_q_heads, n_kv_heads, head_dim, scale)
+
+
+def workload_inputs(cfg: WorkloadConfig) -> DecodeInputs:
+    return make_inputs(cfg.seq_lens, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
+                       cfg.v_int8, cfg.seed_base)

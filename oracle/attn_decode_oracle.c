@@ -1,0 +1,235 @@
+/*
+ * attn_decode_oracle.c -- CPU fp64 oracle for single-query (decode) attention
+ * over a grouped-query KV cache with an F16 K cache and either an F16 V cache
+ * or a block-int8 V cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference that the
+ * HIP path is compared against.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it.  It shares no code, header,
+ * constant or helper with the HIP library, and the HIP library never calls it.
+ *
+ * What it computes is the plain definition of the result that the pages'
+ * split-KV decode kernels reach up to rounding order:
+ *
+ *   for each slot s, query head h, dim d:
+ *     G    = n_q / n_kv,  kvh = floor(h / G)
+ *          (mlx-native flash_attn_vec_hybrid.metal, flash_attn_vec_hybrid_impl:
+ *           "GQA: map query head to KV head")
+ *     lo   = (W > 0 && L_s > W) ? L_s - W : 0,  hi = L_s
+ *          (same kernel, the sliding-window start; tessl nn.rs,
+ *           flash_attn_decode: window 0 selects the global rule)
+ *     x_j  = scale * sum_d q[s,h,d] * K[s,kvh,j,d]          for j in [lo, hi)
+ *          (same kernel, "Q * K^T" block: the dot is formed first and the
+ *           scale is applied to the finished dot)
+ *     out  = sum_j exp(x_j - m) V[s,kvh,j,:] / sum_j exp(x_j - m),  m = max x_j
+ *          (same kernel, "Online softmax" and the final 1/S normalisation;
+ *           an empty range writes zeros because S == 0 gives inv_S = 0)
+ *
+ * The softmax is evaluated in two exact passes (max, then weights) rather than
+ * online; the online form and the split over KV chunks only change rounding.
+ *
+ * V dequantisation (block-int8 regime): a V element is int8 code times the
+ * fp16 scale of its block of 32 consecutive dims along head_dim.  The oracle
+ * reads the stored codes and scales and never re-quantises.  The block size
+ * and scale type are this build's V format (the pages' own hybrid V is a
+ * codebook format; see the reading recorded in the design notes).
+ *
+ * Cache layout (packed ragged slots): slot s's K occupies n_kv * L_s * D
+ * elements starting at element offset sum_{t<s} n_kv * L_t * D, laid out
+ * [kv_head][pos][dim]; V codes are packed identically; V scales are laid out
+ * [kv_head][pos][D/32] per slot, packed the same way.
+ *
+ * All arithmetic is IEEE double.  fp16 -> double is exact (decoded from the
+ * bit pattern below).  Built without fast-math and without FP contraction.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* IEEE-754 binary16 -> double, exact.  1 sign bit, 5 exponent bits (bias 15),
+ * 10 fraction bits; exponent 0 is the subnormal range (no implicit 1, scale
+ * 2^-24), exponent 31 is inf / NaN. */
+double oracle_half_to_double(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int expo = (h >> 10) & 0x1f;
+    const int frac = h & 0x3ff;
+    double mag;
+    if (expo == 0) {
+        mag = ldexp((double)frac, -24);
+    } else if (expo == 31) {
+        mag = frac ? NAN : INFINITY;
+    } else {
+        mag = ldexp((double)(1024 + frac), expo - 25);
+    }
+    return sign ? -mag : mag;
+}
+
+typedef struct {
+    const uint16_t *q;
+    const uint16_t *k;
+    const void *v;
+    const uint16_t *v_scales; /* NULL => V is fp16 */
+    const int32_t *seq_lens;
+    const int64_t *slot_first_pos; /* sum of L_t for t < s */
+    int32_t window;
+    double *out;
+    int32_t n_slots, n_q, n_kv, d;
+    double scale;
+    const int32_t *rows; /* NULL => every (s, h) row in order */
+    int64_t n_rows;
+    int n_threads;
+    int thread_id;
+    int status;
+} oracle_job;
+
+/* One output row (slot s, query head h) by the plain definition. */
+static int oracle_row(const oracle_job *jb, int64_t row, double *dst)
+{
+    const int32_t s = (int32_t)(row / jb->n_q);
+    const int32_t h = (int32_t)(row % jb->n_q);
+    const int32_t D = jb->d;
+    const int32_t G = jb->n_q / jb->n_kv;
+    const int32_t kvh = h / G;
+    const int32_t L = jb->seq_lens[s];
+    const int32_t W = jb->window;
+    const int32_t lo = (W > 0 && L > W) ? L - W : 0;
+    const int32_t hi = L;
+
+    /* element index of row (s, kvh, pos 0) in the packed K / V-code arrays */
+    const int64_t kv_row0 = (int64_t)jb->n_kv * jb->slot_first_pos[s] + (int64_t)kvh * L;
+    const uint16_t *qrow = jb->q + ((int64_t)s * jb->n_q + h) * D;
+
+    int d;
+    for (d = 0; d < D; ++d) dst[d] = 0.0;
+    if (hi <= lo) return 0; /* empty range: zeros */
+
+    double *x = (double *)malloc(sizeof(double) * (size_t)(hi - lo));
+    double *qd = (double *)malloc(sizeof(double) * (size_t)D);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!x || !qd || !acc) {
+        free(x); free(qd); free(acc);
+        return -1;
+    }
+    for (d = 0; d < D; ++d) { qd[d] = oracle_half_to_double(qrow[d]); acc[d] = 0.0; }
+
+    /* pass 1: logits and their maximum */
+    double m = -INFINITY;
+    int32_t j;
+    for (j = lo; j < hi; ++j) {
+        const uint16_t *krow = jb->k + (kv_row0 + j) * D;
+        double dot = 0.0;
+        for (d = 0; d < D; ++d) dot += qd[d] * oracle_half_to_double(krow[d]);
+        x[j - lo] = jb->scale * dot;
+        if (x[j - lo] > m) m = x[j - lo];
+    }
+
+    /* pass 2: weights, their sum, and the weighted sum of dequantised V */
+    double Z = 0.0;
+    for (j = lo; j < hi; ++j) {
+        const double w = exp(x[j - lo] - m);
+        Z += w;
+        if (jb->v_scales == NULL) {
+            const uint16_t *vrow = (const uint16_t *)jb->v + (kv_row0 + j) * D;
+            for (d = 0; d < D; ++d) acc[d] += w * oracle_half_to_double(vrow[d]);
+        } else {
+            const int8_t *vrow = (const int8_t *)jb->v + (kv_row0 + j) * D;
+            const uint16_t *srow = jb->v_scales + (kv_row0 + j) * (D / 32);
+            for (d = 0; d < D; ++d) {
+                const double vdq = (double)vrow[d] * oracle_half_to_double(srow[d / 32]);
+                acc[d] += w * vdq;
+            }
+        }
+    }
+    for (d = 0; d < D; ++d) dst[d] = acc[d] / Z;
+
+    free(x); free(qd); free(acc);
+    return 0;
+}
+
+static void *oracle_worker(void *arg)
+{
+    oracle_job *jb = (oracle_job *)arg;
+    int64_t i;
+    for (i = jb->thread_id; i < jb->n_rows; i += jb->n_threads) {
+        const int64_t row = jb->rows ? (int64_t)jb->rows[i] : i;
+        if (oracle_row(jb, row, jb->out + i * jb->d) != 0) {
+            jb->status = -2;
+            break;
+        }
+    }
+    return NULL;
+}
+
+/*
+ * oracle_attn_decode_f64
+ *   q         fp16 bits [n_slots][n_q][D]
+ *   k         fp16 bits, packed ragged [slot][n_kv][L_s][D]
+ *   v         fp16 bits (v_scales == NULL) or int8 codes, same layout as k
+ *   v_scales  fp16 bits [slot][n_kv][L_s][D/32], or NULL
+ *   seq_lens  [n_slots], each >= 0
+ *   window    0 = full attention, W > 0 = last W positions
+ *   out       double [n_rows][D] where row i is rows[i] (= s * n_q + h),
+ *             or [n_slots][n_q][D] when rows == NULL
+ *   n_threads worker threads (>= 1)
+ * Returns 0, -1 for invalid arguments, -2 for allocation failure.
+ */
+int oracle_attn_decode_f64(const uint16_t *q, const uint16_t *k, const void *v,
+                           const uint16_t *v_scales, const int32_t *seq_lens,
+                           int32_t window, double *out, int32_t n_slots,
+                           int32_t n_q, int32_t n_kv, int32_t head_dim, float scale,
+                           const int32_t *rows, int64_t n_rows, int32_t n_threads)
+{
+    int32_t s;
+    int t;
+    if (n_slots < 0 || n_q <= 0 || n_kv <= 0 || head_dim <= 0 || window < 0) return -1;
+    if (n_q % n_kv != 0) return -1;
+    if (v_scales != NULL && head_dim % 32 != 0) return -1;
+    if (n_threads < 1) n_threads = 1;
+    if (rows == NULL) n_rows = (int64_t)n_slots * n_q;
+    if (n_rows == 0) return 0;
+    for (s = 0; s < n_slots; ++s)
+        if (seq_lens[s] < 0) return -1;
+    if (rows != NULL) {
+        int64_t i;
+        for (i = 0; i < n_rows; ++i)
+            if (rows[i] < 0 || rows[i] >= (int64_t)n_slots * n_q) return -1;
+    }
+
+    int64_t *first = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_slots + 1));
+    oracle_job *jobs = (oracle_job *)malloc(sizeof(oracle_job) * (size_t)n_threads);
+    pthread_t *tids = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+    if (!first || !jobs || !tids) {
+        free(first); free(jobs); free(tids);
+        return -2;
+    }
+    first[0] = 0;
+    for (s = 0; s < n_slots; ++s) first[s + 1] = first[s] + seq_lens[s];
+
+    for (t = 0; t < n_threads; ++t) {
+        oracle_job *jb = &jobs[t];
+        jb->q = q; jb->k = k; jb->v = v; jb->v_scales = v_scales;
+        jb->seq_lens = seq_lens; jb->slot_first_pos = first; jb->window = window;
+        jb->out = out; jb->n_slots = n_slots; jb->n_q = n_q; jb->n_kv = n_kv;
+        jb->d = head_dim; jb->scale = (double)scale; jb->rows = rows;
+        jb->n_rows = n_rows; jb->n_threads = n_threads; jb->thread_id = t;
+        jb->status = 0;
+    }
+    int started = 0;
+    for (t = 1; t < n_threads; ++t) {
+        if (pthread_create(&tids[t], NULL, oracle_worker, &jobs[t]) != 0) break;
+        started = t;
+    }
+    /* threads that failed to start: run their share here */
+    for (t = started + 1; t < n_threads; ++t) oracle_worker(&jobs[t]);
+    oracle_worker(&jobs[0]);
+    for (t = 1; t <= started; ++t) pthread_join(tids[t], NULL);
+
+    int status = 0;
+    for (t = 0; t < n_threads; ++t)
+        if (jobs[t].status != 0) status = jobs[t].status;
+    free(first); free(jobs); free(tids);
+    return status;
+}

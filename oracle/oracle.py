@@ -1,0 +1,133 @@
+"""ctypes front end of the C fp64 oracle (test infrastructure only).
+
+``oracle_attn_decode`` computes, for each (slot, query head) row, the plain
+softmax attention of one fp16 query over that slot's packed KV cache:
+
+    out[s, h, :] = sum_j softmax_j(scale * q[s,h,:] . K[s,kvh,j,:]) * V[s,kvh,j,:]
+
+with ``kvh = h // (n_q // n_kv)`` and ``j`` over the last ``window`` positions
+(all positions when ``window`` is 0 or at least ``L_s``).  See the C source
+for the citations of each step on the pages (mlx-native
+flash_attn_vec_hybrid.metal; tessl nn.rs, flash_attn_decode).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_decode_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_attn_decode.so")
+
+_lock = threading.Lock()
+_lib = None
+
+
+def oracle_library_path() -> str:
+    return _LIB
+
+
+def build_oracle(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE double: no fast-math, no contraction)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = [
+        "gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
+        "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+        _SRC, "-o", tmp, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build_oracle()
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_half_to_double.restype = ctypes.c_double
+        lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_attn_decode_f64.restype = ctypes.c_int
+        lib.oracle_attn_decode_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+        ]
+        _lib = lib
+        return lib
+
+
+def half_to_double(bits: int) -> float:
+    """The oracle's own fp16 bit-pattern decoder (exposed so it can be pinned)."""
+    return _load().oracle_half_to_double(int(bits) & 0xFFFF)
+
+
+def _as_c(arr: np.ndarray, dtype) -> np.ndarray:
+    arr = np.asarray(arr)
+    if arr.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {arr.dtype}")
+    return np.ascontiguousarray(arr)
+
+
+def _ptr(arr):
+    return None if arr is None else arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def oracle_attn_decode(q, k, v, v_scales, seq_lens, window, n_q, n_kv, head_dim,
+                       scale, rows=None, threads=None) -> np.ndarray:
+    """Plain fp64 decode attention.
+
+    q: float16 [n_slots, n_q, D]; k: float16 packed [sum_s n_kv*L_s*D];
+    v: float16 (``v_scales is None``) or int8, same layout as k;
+    v_scales: float16 [sum_s n_kv*L_s*D/32] or None; seq_lens: ints.
+    rows: optional iterable of flat row ids ``s*n_q + h``.
+    Returns float64 ``[n_slots, n_q, D]``, or ``[len(rows), D]`` when rows is given.
+    """
+    lib = _load()
+    seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    n_slots = int(seq.shape[0])
+    q16 = _as_c(q, np.float16)
+    if q16.size != n_slots * n_q * head_dim:
+        raise ValueError("q has the wrong number of elements")
+    total = int(seq.astype(np.int64).sum()) * n_kv * head_dim
+    k16 = _as_c(k, np.float16).reshape(-1)
+    if k16.size != total:
+        raise ValueError("k has the wrong number of elements")
+    if v_scales is None:
+        vv = _as_c(v, np.float16).reshape(-1)
+        sc = None
+    else:
+        vv = _as_c(v, np.int8).reshape(-1)
+        sc = _as_c(v_scales, np.float16).reshape(-1)
+        if sc.size != total // 32:
+            raise ValueError("v_scales has the wrong number of elements")
+    if vv.size != total:
+        raise ValueError("v has the wrong number of elements")
+    if rows is None:
+        rows_arr = None
+        n_rows = n_slots * n_q
+        out = np.zeros((n_slots, n_q, head_dim), dtype=np.float64)
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(list(rows), dtype=np.int32))
+        n_rows = int(rows_arr.shape[0])
+        out = np.zeros((n_rows, head_dim), dtype=np.float64)
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+    rc = lib.oracle_attn_decode_f64(
+        _ptr(q16), _ptr(k16), _ptr(vv), _ptr(sc), _ptr(seq), int(window), _ptr(out),
+        n_slots, int(n_q), int(n_kv), int(head_dim), float(scale),
+        _ptr(rows_arr), n_rows, int(threads),
+    )
+    if rc != 0:
+        raise ValueError(f"oracle_attn_decode_f64 returned {rc}")
+    return out
