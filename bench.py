@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark: effective KV GB/s (fraction of HBM peak) and us/call.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--quick]
+
+A step is one ``attn_decode`` call (partial kernel + combine kernel) over the
+whole batch of the workload, with every input already resident in HBM.  The
+headline workload is the hybrid KV regime at 8 slots x 32768 positions (fp16
+K, int8 V in blocks of 32 with fp16 scales, 16 q / 8 kv heads, head_dim 256):
+1.64 GB of KV per call, far above the 256 MB Infinity Cache, so back-to-back
+steps stream from HBM.  The K steps are bracketed by device synchronisation;
+``value`` = algorithmic KV bytes per step / wall time per step.
+
+Algorithmic bytes (what the method must move) = every K, V and V-scale byte of
+each slot's attended range, read once:
+    sum_s n_s * n_kv * (2*D + bytes_V),  bytes_V = 2*D (fp16) or D + 2*D/32 (int8).
+
+One JSON line is printed.  Besides the contract fields it carries
+  * ``roofline``: the partial kernel's algorithmic bytes / its average launch
+    duration (HIP events recorded by the library around the partial launch, on
+    the call's stream, inside the timed region) against the 8 TB/s HBM peak,
+    and ``traffic`` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary
+    when that summary was taken on the current kernel source, else null;
+  * ``cpu_baseline``: the CPU fp64 oracle timed on a bounded sample of the same
+    workload on this host's cores;
+  * ``per_config``: every workload preset, cold (a 1 GiB cache-flush write
+    before each timed call) and warm (back-to-back calls).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import statistics
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_kv_02_amd", "csrc", "attn_decode_kernels.hpp")
+TRAFFIC_SUMMARY_DIR = os.path.join(ROOT, "profiles")
+METRIC = "decode-attention effective KV GB/s (% of HBM peak) + µs/call per config"
+HEADLINE = "hybrid_int8v_8x32768"
+
+
+def attended(L: int, window: int) -> int:
+    return L - (L - window if (window > 0 and L > window) else 0)
+
+
+def kv_bytes(seq_lens, window, n_kv, d, v_int8) -> int:
+    per_row = 2 * d + (d + 2 * (d // 32) if v_int8 else 2 * d)
+    return sum(attended(L, window) for L in seq_lens) * n_kv * per_row
+
+
+def kernel_source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str, window: int):
+    """HBM bytes per partial-kernel launch from the committed PMC summary, or None."""
+    path = os.path.join(TRAFFIC_SUMMARY_DIR, f"traffic_{workload}_w{window}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        if m:
+            vals[m.group(1)] = m.group(2)
+    if vals.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--quick", action="store_true", help="headline workload only (no per_config, no cpu_baseline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--reps", type=int, default=50, help="timed reps per preset for per_config")
+    ap.add_argument("--chunk", type=int, default=0, help="forced chunk size (tuning only)")
+    return ap.parse_args(argv)
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by slot, KV head or sequence chunk across GPUs by design, "
+              "but no multi-GPU run exists)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from decode_attention_kv_02_amd import binding
+    from decode_attention_kv_02_amd.workloads import WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    by_name = {w.name: w for w in WORKLOADS}
+    if args.workload not in by_name:
+        print(f"unknown workload {args.workload}; choose from {sorted(by_name)}", file=sys.stderr)
+        return 2
+    cfg = by_name[args.workload]
+    window = cfg.windows[0]
+
+    def upload(inp):
+        return (inp.q.to(dev), inp.k.to(dev), inp.v.to(dev),
+                None if inp.v_scales is None else inp.v_scales.to(dev))
+
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)  # materialise the underlying hipEvent_t
+        return e
+
+    def call(inp, tens, out, W, ev0=None, ev1=None):
+        q, k, v, vs = tens
+        binding.attn_decode_ex(q, k, v, vs, inp.seq_lens, W, out, inp.n_slots, inp.n_q_heads,
+                               inp.n_kv_heads, inp.head_dim, inp.scale, stream=stream,
+                               chunk=args.chunk,
+                               ev_partial_begin=ev0.cuda_event if ev0 is not None else None,
+                               ev_partial_end=ev1.cuda_event if ev1 is not None else None)
+
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    inp = workload_inputs(cfg)
+    tens = upload(inp)
+    out = torch.empty((inp.n_slots, inp.n_q_heads, inp.head_dim), dtype=torch.float32, device=dev)
+    nbytes = kv_bytes(inp.seq_lens, window, inp.n_kv_heads, inp.head_dim, inp.v_int8)
+
+    for _ in range(args.warmup):
+        call(inp, tens, out, window)
+    torch.cuda.synchronize()
+
+    evs = [(new_event(), new_event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        call(inp, tens, out, window, e0, e1)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    partial_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    partial_avg_s = statistics.fmean(partial_ms) * 1e-3
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / partial_avg_s / 1e9
+    assert torch.isfinite(out).all().item(), "non-finite output"
+
+    traffic = read_traffic(cfg.name, window)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "n_slots": inp.n_slots,
+            "seq_lens": list(inp.seq_lens),
+            "n_q_heads": inp.n_q_heads,
+            "n_kv_heads": inp.n_kv_heads,
+            "head_dim": inp.head_dim,
+            "window": window,
+            "k_format": "fp16",
+            "v_format": "int8 codes, fp16 scale per 32 dims" if inp.v_int8 else "fp16",
+            "kv_bytes_per_call": nbytes,
+            "us_per_call": round(ms_per_step * 1e3, 2),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "chunk_override": args.chunk,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "attn_partial_kernel",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(partial_avg_s * 1e6, 2),
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+    }
+
+    # ---- every preset: cold (flushed) and warm
+    if not args.quick:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        per = []
+        for w in WORKLOADS:
+            if w.name != cfg.name:
+                print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+                pin = workload_inputs(w)
+                ptens = upload(pin)
+                del pin.k, pin.v
+            else:
+                pin, ptens = inp, tens
+            pout = torch.empty((pin.n_slots, pin.n_q_heads, pin.head_dim), dtype=torch.float32, device=dev)
+            for W in w.windows:
+                nb = kv_bytes(pin.seq_lens, W, pin.n_kv_heads, pin.head_dim, pin.v_int8)
+                for _ in range(3):
+                    call(pin, ptens, pout, W)
+                cold = []
+                pk = []
+                for _ in range(args.reps):
+                    flush.fill_(1.0)
+                    a, b, c0, c1 = new_event(), new_event(), new_event(), new_event()
+                    a.record(stream)
+                    call(pin, ptens, pout, W, c0, c1)
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    cold.append(a.elapsed_time(b) * 1e3)
+                    pk.append(c0.elapsed_time(c1) * 1e3)
+                warm_n = max(args.reps, 20)
+                torch.cuda.synchronize()
+                a, b = new_event(), new_event()
+                a.record(stream)
+                for _ in range(warm_n):
+                    call(pin, ptens, pout, W)
+                b.record(stream)
+                torch.cuda.synchronize()
+                warm = a.elapsed_time(b) * 1e3 / warm_n
+                med = statistics.median(cold)
+                per.append({
+                    "workload": w.name, "window": W, "kv_bytes": nb,
+                    "cold_us_median": round(med, 2),
+                    "cold_us_p10": round(float(np.percentile(cold, 10)), 2),
+                    "cold_us_p90": round(float(np.percentile(cold, 90)), 2),
+                    "cold_gbs": round(nb / (med * 1e-6) / 1e9, 1),
+                    "cold_hbm_frac": round(nb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "partial_kernel_us_median": round(statistics.median(pk), 2),
+                    "warm_us_per_call": round(warm, 2),
+                    "warm_gbs": round(nb / (warm * 1e-6) / 1e9, 1),
+                })
+                print(f"[bench] {w.name} W={W}: cold {med:.2f} us ({per[-1]['cold_gbs']} GB/s), "
+                      f"warm {warm:.2f} us", file=sys.stderr, flush=True)
+            if w.name != cfg.name:
+                del ptens
+                torch.cuda.empty_cache()
+        result["per_config"] = per
+
+    # ---- CPU fp64 oracle on a bounded sample of the headline workload
+    if not args.quick and not args.no_cpu_baseline:
+        from oracle import oracle_attn_decode
+        threads = len(os.sched_getaffinity(0))
+        n_sample_slots = min(inp.n_slots, 4)
+        rows = list(range(n_sample_slots * inp.n_q_heads))
+        print(f"[bench] cpu oracle on {len(rows)} rows with {threads} threads", file=sys.stderr, flush=True)
+        qn, kn, vn = inp.q.numpy(), inp.k.numpy(), inp.v.numpy()
+        sn = None if inp.v_scales is None else inp.v_scales.numpy()
+        t0 = time.perf_counter()
+        oracle_attn_decode(qn, kn, vn, sn, inp.seq_lens, window, inp.n_q_heads, inp.n_kv_heads,
+                           inp.head_dim, inp.scale, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        sb = kv_bytes(inp.seq_lens[:n_sample_slots], window, inp.n_kv_heads, inp.head_dim, inp.v_int8)
+        result["cpu_baseline"] = {
+            "value": round(sb / dt / 1e9, 3),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {n_sample_slots} of {inp.n_slots} slots of {cfg.name} "
+                      f"({len(rows)} query rows, {sb} KV bytes), one pass, {dt:.2f} s wall",
+        }
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

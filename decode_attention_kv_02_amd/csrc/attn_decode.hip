@@ -1,0 +1,315 @@
+// attn_decode.hip -- C ABI, validation, workspace and launches of the
+// split-KV decode-attention library (see include/attn_decode.h).
+//
+// Host-side validation rejects every bad shape, pointer, alignment and
+// overlap before anything is enqueued, so the kernels only guard their own
+// tails (the convention of tessl nn.rs: the wrappers reject out-of-bounds
+// work on the host; flash_attn_decode validates dims, head_dim and capacity
+// before encoding).  The slot table travels by value in the kernel arguments:
+// no host-to-device copy, nothing to keep alive, nothing to synchronise.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/attn_decode.h"
+#include "attn_decode_kernels.hpp"
+#include "planner.hpp"
+
+using namespace attn_decode_impl;
+
+static_assert(ATTN_DECODE_MAX_SLOTS_PER_LAUNCH == kMaxSlotsPerLaunch, "slot table size");
+static_assert(ATTN_DECODE_MAX_CHUNKS == kMaxChunks, "chunk bound");
+static_assert(kCombineMaxChunks >= kMaxChunks, "combine LDS holds every chunk weight");
+static_assert(sizeof(LaunchArgs) <= 4096, "kernel arguments stay within 4 KiB");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+// ------------------------------------------------------------ workspace cache
+
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void *>, Workspace> g_ws;  // keyed by (device, stream)
+
+int acquire_workspace(int device, hipStream_t stream, size_t need, void **out) {
+    *out = nullptr;
+    if (need == 0) return ATTN_DECODE_OK;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &ws = g_ws[std::make_pair(device, (void *)stream)];
+    if (ws.bytes >= need) {
+        *out = ws.ptr;
+        return ATTN_DECODE_OK;
+    }
+    if (ws.ptr != nullptr) {
+        // earlier work of this stream may still read the old buffer
+        hipError_t e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+        e = hipFree(ws.ptr);
+        ws.ptr = nullptr;
+        ws.bytes = 0;
+        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipFree: ") + hipGetErrorString(e));
+    }
+    size_t bytes = need + need / 4;
+    bytes = (bytes + 0xFFFF) & ~size_t(0xFFFF);
+    void *p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ATTN_DECODE_ENOMEM, "workspace hipMalloc of " + std::to_string(bytes) + " bytes: " + hipGetErrorString(e));
+    }
+    ws.ptr = p;
+    ws.bytes = bytes;
+    *out = p;
+    return ATTN_DECODE_OK;
+}
+
+// ------------------------------------------------------------ kernel tables
+
+typedef void (*partial_fn)(const LaunchArgs);
+typedef void (*combine_fn)(const LaunchArgs);
+
+template <int D>
+partial_fn partial_for(int GB, bool v_int8) {
+    if (v_int8) {
+        switch (GB) {
+            case 1: return attn_partial_kernel<D, 1, true>;
+            case 2: return attn_partial_kernel<D, 2, true>;
+            case 4: return attn_partial_kernel<D, 4, true>;
+        }
+    } else {
+        switch (GB) {
+            case 1: return attn_partial_kernel<D, 1, false>;
+            case 2: return attn_partial_kernel<D, 2, false>;
+            case 4: return attn_partial_kernel<D, 4, false>;
+        }
+    }
+    return nullptr;
+}
+
+partial_fn select_partial(int D, int GB, bool v_int8) {
+    switch (D) {
+        case 64: return partial_for<64>(GB, v_int8);
+        case 128: return partial_for<128>(GB, v_int8);
+        case 256: return partial_for<256>(GB, v_int8);
+        case 512: return partial_for<512>(GB, v_int8);
+    }
+    return nullptr;
+}
+
+combine_fn select_combine(int D) {
+    switch (D) {
+        case 64: return attn_combine_kernel<64>;
+        case 128: return attn_combine_kernel<128>;
+        case 256: return attn_combine_kernel<256>;
+        case 512: return attn_combine_kernel<512>;
+    }
+    return nullptr;
+}
+
+// ------------------------------------------------------------ validation helpers
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+int run(const void *q, const void *k_cache, const void *v_cache, const void *v_scales,
+        const int32_t *seq_lens, int32_t window, float *out, int32_t n_slots, int32_t n_q,
+        int32_t n_kv, int32_t D, float scale, void *stream_ptr, const attn_decode_options *opts) {
+    g_last_error.clear();
+    const bool v_int8 = v_scales != nullptr;
+    const int32_t chunk = opts ? opts->chunk : 0;
+
+    std::string err = check_shapes(seq_lens, n_slots, window, n_q, n_kv, D, v_int8, chunk);
+    if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
+    if (!std::isfinite(scale)) return fail(ATTN_DECODE_EINVAL, "scale must be finite");
+    if (n_slots == 0) return ATTN_DECODE_OK;
+
+    // sizes (64-bit, overflow-checked)
+    uint64_t total_pos = 0;
+    for (int32_t s = 0; s < n_slots; ++s) total_pos += (uint64_t)seq_lens[s];
+    const uint64_t kv_elems = total_pos * (uint64_t)n_kv * (uint64_t)D;
+    if (total_pos > (uint64_t(1) << 40) || kv_elems > (uint64_t(1) << 46))
+        return fail(ATTN_DECODE_EINVAL, "KV cache too large");
+    const uint64_t q_bytes = (uint64_t)n_slots * n_q * D * 2;
+    const uint64_t out_bytes = (uint64_t)n_slots * n_q * D * 4;
+    const uint64_t k_bytes = kv_elems * 2;
+    const uint64_t v_bytes = kv_elems * (v_int8 ? 1 : 2);
+    const uint64_t s_bytes = v_int8 ? kv_elems / kQuantBlock * 2 : 0;
+
+    if (q == nullptr) return fail(ATTN_DECODE_EINVAL, "q is NULL");
+    if (out == nullptr) return fail(ATTN_DECODE_EINVAL, "out is NULL");
+    if (kv_elems > 0 && (k_cache == nullptr || v_cache == nullptr))
+        return fail(ATTN_DECODE_EINVAL, "k_cache / v_cache is NULL");
+    if (!aligned(q, 16) || !aligned(out, 16)) return fail(ATTN_DECODE_EINVAL, "q and out must be 16-byte aligned");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return fail(ATTN_DECODE_EINVAL, "k_cache and v_cache must be 16-byte aligned");
+    if (v_int8 && !aligned(v_scales, 2)) return fail(ATTN_DECODE_EINVAL, "v_scales must be 2-byte aligned");
+    if (overlaps(out, out_bytes, q, q_bytes) || overlaps(out, out_bytes, k_cache, k_bytes) ||
+        overlaps(out, out_bytes, v_cache, v_bytes) || overlaps(out, out_bytes, v_scales, s_bytes))
+        return fail(ATTN_DECODE_EINVAL, "out overlaps an input");
+
+    CallPlan plan;
+    err = make_plan(seq_lens, n_slots, window, n_q, n_kv, D, chunk, plan);
+    if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
+
+    const partial_fn pk = select_partial(D, plan.GB, v_int8);
+    const combine_fn ck = select_combine(D);
+    if (pk == nullptr || ck == nullptr) return fail(ATTN_DECODE_EINVAL, "no kernel for this shape");
+
+    // ---- HIP from here on
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    void *ws = nullptr;
+    int rc = acquire_workspace(device, stream, (size_t)plan.workspace_bytes, &ws);
+    if (rc != ATTN_DECODE_OK) return rc;
+    float *ws_o = static_cast<float *>(ws);
+    float *ws_ml = ws_o ? ws_o + plan.part_rows * D : nullptr;
+
+    const double scale_log2 = (double)scale * 1.4426950408889634074;  // scale * log2(e)
+
+    LaunchArgs args;
+    std::memset(&args, 0, sizeof(args));
+    args.q = static_cast<const uint16_t *>(q);
+    args.k = static_cast<const uint16_t *>(k_cache);
+    args.v = v_cache;
+    args.vs = static_cast<const uint16_t *>(v_scales);
+    args.out = out;
+    args.ws_o = ws_o;
+    args.ws_ml = ws_ml;
+    args.n_q = n_q;
+    args.G = plan.G;
+    args.n_sub = plan.n_sub;
+    args.scale_log2 = (float)scale_log2;
+
+    auto fill = [&](const LaunchGroup &lg) {
+        args.n_slots = lg.slot_end - lg.slot_begin;
+        args.slot0 = lg.slot_begin;
+        int32_t item = 0, comb = 0;
+        for (int s = lg.slot_begin; s < lg.slot_end; ++s) {
+            const SlotPlan &sp = plan.slots[s];
+            SlotDesc &sd = args.slot[s - lg.slot_begin];
+            sd.kv_row0 = sp.kv_row0;
+            sd.part_row0 = sp.part_row0;
+            sd.L = sp.L;
+            sd.lo = sp.lo;
+            sd.chunk = sp.chunk;
+            sd.n_chunks = sp.n_chunks;
+            sd.item_begin = item;
+            sd.comb_begin = comb;
+            item += n_kv * plan.n_sub * sp.n_chunks;
+            if (sp.n_chunks > 1) comb += n_q;
+        }
+        args.n_items = item;
+        args.n_comb = comb;
+    };
+
+    if (opts && opts->ev_partial_begin) {
+        e = hipEventRecord(reinterpret_cast<hipEvent_t>(opts->ev_partial_begin), stream);
+        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipEventRecord: ") + hipGetErrorString(e));
+    }
+    for (const LaunchGroup &lg : plan.groups) {
+        fill(lg);
+        hipLaunchKernelGGL(pk, dim3((unsigned)lg.items), dim3(kThreads), 0, stream, args);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
+    }
+    if (opts && opts->ev_partial_end) {
+        e = hipEventRecord(reinterpret_cast<hipEvent_t>(opts->ev_partial_end), stream);
+        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipEventRecord: ") + hipGetErrorString(e));
+    }
+    for (const LaunchGroup &lg : plan.groups) {
+        if (lg.combine_rows == 0) continue;
+        fill(lg);
+        hipLaunchKernelGGL(ck, dim3((unsigned)lg.combine_rows), dim3(kThreads), 0, stream, args);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("combine kernel launch: ") + hipGetErrorString(e));
+    }
+    return ATTN_DECODE_OK;
+}
+
+}  // namespace
+
+// ============================================================ C ABI
+
+extern "C" int attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                           const void *v_scales, const int32_t *seq_lens, int32_t window,
+                           float *out, int32_t n_slots, int32_t n_q_heads, int32_t n_kv_heads,
+                           int32_t head_dim, float scale, void *stream) {
+    return run(q, k_cache, v_cache, v_scales, seq_lens, window, out, n_slots, n_q_heads,
+               n_kv_heads, head_dim, scale, stream, nullptr);
+}
+
+extern "C" int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
+                              const void *v_scales, const int32_t *seq_lens, int32_t window,
+                              float *out, int32_t n_slots, int32_t n_q_heads, int32_t n_kv_heads,
+                              int32_t head_dim, float scale, void *stream,
+                              const attn_decode_options *opts) {
+    return run(q, k_cache, v_cache, v_scales, seq_lens, window, out, n_slots, n_q_heads,
+               n_kv_heads, head_dim, scale, stream, opts);
+}
+
+extern "C" int attn_decode_plan(const int32_t *seq_lens, int32_t n_slots, int32_t window,
+                                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                int32_t v_int8, int32_t chunk, int32_t *chunk_keys,
+                                int32_t *n_chunks, int64_t *workspace_bytes,
+                                int64_t *n_partial_workgroups) {
+    g_last_error.clear();
+    std::string err = check_shapes(seq_lens, n_slots, window, n_q_heads, n_kv_heads, head_dim,
+                                   v_int8 != 0, chunk);
+    if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
+    CallPlan plan;
+    err = make_plan(seq_lens, n_slots, window, n_q_heads, n_kv_heads, head_dim, chunk, plan);
+    if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
+    for (int32_t s = 0; s < n_slots; ++s) {
+        if (chunk_keys) chunk_keys[s] = plan.slots[s].chunk;
+        if (n_chunks) n_chunks[s] = plan.slots[s].n_chunks;
+    }
+    if (workspace_bytes) *workspace_bytes = plan.workspace_bytes;
+    if (n_partial_workgroups) *n_partial_workgroups = plan.total_items;
+    return ATTN_DECODE_OK;
+}
+
+extern "C" const char *attn_decode_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int attn_decode_release(void) {
+    g_last_error.clear();
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    int rc = ATTN_DECODE_OK;
+    int cur = 0;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (auto &kv : g_ws) {
+        Workspace &ws = kv.second;
+        if (ws.ptr == nullptr) continue;
+        hipError_t e = hipSetDevice(kv.first.first);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e == hipSuccess) e = hipFree(ws.ptr);
+        if (e != hipSuccess) rc = fail(ATTN_DECODE_EHIP, std::string("release: ") + hipGetErrorString(e));
+        ws.ptr = nullptr;
+        ws.bytes = 0;
+    }
+    g_ws.clear();
+    if (have_cur) (void)hipSetDevice(cur);
+    return rc;
+}

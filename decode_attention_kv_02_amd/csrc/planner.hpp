@@ -1,0 +1,157 @@
+// planner.hpp -- host-side split-KV planner of the decode-attention library.
+//
+// Pure C++ (no HIP): validates shapes and turns per-slot KV lengths into the
+// flat work list the partial kernel runs over.  The pages split the KV range
+// of each query row over workgroups and merge the pieces by log-sum-exp
+// (mlx-native flash_attn_vec_hybrid.metal, the NWG split-K of
+// flash_attn_vec_hybrid_impl; tessl nn.rs, flash_attn_decode and the
+// DecodeChunk table); mlx-native's GQA-grouped batched kernel lets every slot
+// run its own split (FlashAttnHybridSlotBucket).  Here the split of a slot is a
+// function of that slot's attended length alone, so batching slots never
+// changes any slot's result, and every workgroup of a launch does one chunk of
+// at most `chunk` positions (a flat list instead of a padded grid).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace attn_decode_impl {
+
+constexpr int kMaxSlotsPerLaunch = 64;   // slot table passed by value in the kernel arguments
+constexpr int kMaxChunks = 4096;         // per slot; bounds the combine kernel's LDS weights
+constexpr int kChunkQuantum = 64;        // chunk sizes are multiples of this (one WG iteration at D=256)
+constexpr int kChunkMin = 64;
+constexpr int kChunkMax = 1024;
+constexpr int kTargetChunks = 64;        // chunks per (slot, kv head) the planner aims for
+constexpr int64_t kMaxItemsPerLaunch = int64_t(1) << 24;  // 2^24 workgroups x 256 threads < 2^32
+constexpr int kQuantBlock = 32;          // int8 V: dims per fp16 scale
+
+struct SlotPlan {
+    int32_t L = 0;          // slot KV length
+    int32_t lo = 0;         // first attended position
+    int32_t n = 0;          // attended positions (L - lo)
+    int32_t chunk = 0;      // positions per chunk
+    int32_t n_chunks = 1;   // >= 1 (an empty slot has one empty chunk)
+    int64_t kv_row0 = 0;    // n_kv * sum_{t<s} L_t : row of (slot, kv head 0, pos 0)
+    int64_t part_row0 = -1; // first partial row when n_chunks > 1, else -1
+};
+
+struct LaunchGroup {
+    int slot_begin = 0, slot_end = 0;  // [begin, end) global slot indices
+    int64_t items = 0;                 // partial-kernel workgroups
+    int64_t combine_rows = 0;          // combine-kernel workgroups
+};
+
+struct CallPlan {
+    int G = 1;           // query heads per KV head
+    int GB = 1;          // query heads per workgroup (1, 2 or 4; divides G)
+    int n_sub = 1;       // G / GB workgroups share one (slot, kv head, chunk)
+    std::vector<SlotPlan> slots;
+    std::vector<LaunchGroup> groups;
+    int64_t part_rows = 0;         // partial rows (each head_dim floats + 2 stats)
+    int64_t workspace_bytes = 0;
+    int64_t total_items = 0;
+};
+
+inline bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Positions per chunk for a slot attending n positions (n >= 1).
+inline int64_t chunk_for(int64_t n, int32_t forced) {
+    int64_t c;
+    if (forced > 0) {
+        c = forced;
+    } else {
+        c = ceil_div(n, kTargetChunks);
+        c = ceil_div(c, kChunkQuantum) * kChunkQuantum;
+        if (c < kChunkMin) c = kChunkMin;
+        if (c > kChunkMax) c = kChunkMax;
+    }
+    const int64_t floor_c = ceil_div(n, kMaxChunks);
+    if (c < floor_c) c = forced > 0 ? floor_c : ceil_div(floor_c, kChunkQuantum) * kChunkQuantum;
+    return c;
+}
+
+// Shape checks shared by every entry point.  Returns "" when valid.
+inline std::string check_shapes(const int32_t *seq_lens, int32_t n_slots, int32_t window,
+                                int32_t n_q, int32_t n_kv, int32_t head_dim, bool v_int8,
+                                int32_t chunk) {
+    if (n_slots < 0) return "n_slots must be >= 0";
+    if (n_slots > 0 && seq_lens == nullptr) return "seq_lens is NULL";
+    if (n_q <= 0 || n_kv <= 0) return "n_q_heads and n_kv_heads must be positive";
+    if (n_q % n_kv != 0) return "n_q_heads must be a multiple of n_kv_heads";
+    if (!supported_head_dim(head_dim)) return "head_dim must be 64, 128, 256 or 512";
+    if (v_int8 && head_dim % kQuantBlock != 0) return "int8 V needs head_dim % 32 == 0";
+    if (window < 0) return "window must be >= 0";
+    if (chunk < 0) return "chunk override must be >= 0";
+    for (int32_t s = 0; s < n_slots; ++s)
+        if (seq_lens[s] < 0) return "seq_lens[" + std::to_string(s) + "] is negative";
+    return "";
+}
+
+inline int heads_per_workgroup(int G) {
+    if (G % 4 == 0) return 4;
+    if (G % 2 == 0) return 2;
+    return 1;
+}
+
+// Builds the plan; returns "" on success or an error message.
+inline std::string make_plan(const int32_t *seq_lens, int32_t n_slots, int32_t window,
+                             int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t chunk,
+                             CallPlan &plan) {
+    plan = CallPlan();
+    plan.G = n_q / n_kv;
+    plan.GB = heads_per_workgroup(plan.G);
+    plan.n_sub = plan.G / plan.GB;
+    plan.slots.resize(n_slots);
+    int64_t rows = 0;   // running sum of L_t (positions)
+    int64_t part = 0;
+    for (int32_t s = 0; s < n_slots; ++s) {
+        SlotPlan &sp = plan.slots[s];
+        sp.L = seq_lens[s];
+        sp.lo = (window > 0 && sp.L > window) ? sp.L - window : 0;
+        sp.n = sp.L - sp.lo;
+        sp.kv_row0 = rows * n_kv;
+        rows += sp.L;
+        if (sp.n == 0) {
+            sp.chunk = 0;
+            sp.n_chunks = 1;
+        } else {
+            const int64_t c = chunk_for(sp.n, chunk);
+            sp.chunk = (int32_t)(c > sp.n ? sp.n : c);
+            sp.n_chunks = (int32_t)ceil_div(sp.n, sp.chunk);
+        }
+        if (sp.n_chunks > 1) {
+            sp.part_row0 = part;
+            part += (int64_t)n_q * sp.n_chunks;
+        }
+    }
+    plan.part_rows = part;
+    plan.workspace_bytes = part * (int64_t)(head_dim + 2) * (int64_t)sizeof(float);
+
+    // launch groups: at most kMaxSlotsPerLaunch slots and kMaxItemsPerLaunch workgroups
+    LaunchGroup g;
+    g.slot_begin = 0;
+    for (int32_t s = 0; s < n_slots; ++s) {
+        const SlotPlan &sp = plan.slots[s];
+        const int64_t items = (int64_t)n_kv * plan.n_sub * sp.n_chunks;
+        if (items > kMaxItemsPerLaunch) return "too many workgroups for one slot (n_kv_heads too large)";
+        const bool full = (s - g.slot_begin) >= kMaxSlotsPerLaunch || g.items + items > kMaxItemsPerLaunch;
+        if (full) {
+            g.slot_end = s;
+            plan.groups.push_back(g);
+            g = LaunchGroup();
+            g.slot_begin = s;
+        }
+        g.items += items;
+        if (sp.n_chunks > 1) g.combine_rows += n_q;
+    }
+    g.slot_end = n_slots;
+    if (n_slots > 0) plan.groups.push_back(g);
+    for (const LaunchGroup &lg : plan.groups) plan.total_items += lg.items;
+    return "";
+}
+
+}  // namespace attn_decode_impl

@@ -1,0 +1,140 @@
+/*
+ * attn_decode.h -- C ABI of the MI355X (gfx950) split-KV decode-attention library.
+ *
+ * One call computes, for every decode slot s and query head h,
+ *
+ *     out[s,h,:] = sum_j softmax_j(scale * q[s,h,:] . K[s,kvh,j,:]) * V[s,kvh,j,:]
+ *
+ * with kvh = h / (n_q_heads / n_kv_heads) (consecutive query heads share a KV
+ * head), and j over the attended range [lo_s, L_s): lo_s = L_s - window when
+ * window > 0 and L_s > window, else 0.  This is the operation of the pages'
+ * decode flash-attention kernels: mlx-native 0.21.1 flash_attn_vec_hybrid.metal
+ * (flash_attn_vec_hybrid_impl and its batched and GQA-grouped forms: GQA map,
+ * sliding-window start, QK dot then scale, online softmax, split-K partials
+ * merged by log-sum-exp, S == 0 writing zeros) and tessl 0.2.0 nn.rs
+ * (flash_attn_decode: FlashDecoding split over the KV sequence, window 0 =
+ * global attention, host-side validation before any dispatch).
+ *
+ * The K cache is fp16.  The V cache is fp16, or ("hybrid" regime) symmetric
+ * int8 codes in blocks of 32 consecutive dims along head_dim with one fp16
+ * scale per block: V = code * scale, exact in fp32.
+ *
+ * Memory layout (all device memory unless stated otherwise, caller-owned):
+ *   q        fp16  [n_slots][n_q_heads][head_dim], 16-byte aligned
+ *   k_cache  fp16  packed ragged slots: slot s is a [n_kv_heads][L_s][head_dim]
+ *                  block starting at element sum_{t<s} n_kv_heads*L_t*head_dim;
+ *                  16-byte aligned
+ *   v_cache  fp16 (v_scales == NULL) or int8 codes, same layout as k_cache;
+ *                  16-byte aligned
+ *   v_scales fp16  [slot][n_kv_heads][L_s][head_dim/32], packed like k_cache;
+ *                  NULL selects fp16 V; 2-byte aligned
+ *   seq_lens HOST  int32 [n_slots], each L_s >= 0
+ *   out      fp32  [n_slots][n_q_heads][head_dim], 16-byte aligned; must not
+ *                  overlap q, k_cache, v_cache or v_scales
+ *
+ * Execution: every entry point that takes a stream is asynchronous on it
+ * (a hipStream_t passed as void*; NULL = the null stream of the current
+ * device).  It enqueues one partial kernel per launch group (up to 64 slots)
+ * and one combine kernel per group that has a slot split over several KV
+ * chunks; it never synchronises the host and never reads device memory from
+ * the host.  Inputs must stay alive and unmodified until the work completes.
+ *
+ * Workspace: the library keeps one growable partials buffer per (device,
+ * stream).  It is never zeroed (every element the combine reads is written by
+ * the same call's partial kernel).  Growing it synchronises that stream once.
+ * Calls on different streams use different buffers; calls that overlap on
+ * the same stream are ordered by the stream.  attn_decode_release frees them.
+ *
+ * Determinism: the KV split of a slot depends only on that slot's own
+ * attended length, head_dim, the V format and the chunk override, so a
+ * batched call returns bitwise the same rows as one call per slot, and
+ * repeated calls are bitwise identical.
+ *
+ * Errors: every int-returning entry point returns ATTN_DECODE_OK (0) or a
+ * negative code; attn_decode_last_error() then describes the failure (per
+ * host thread).  Argument errors are detected before anything is enqueued,
+ * so a failed call leaves the stream untouched.
+ */
+#ifndef ATTN_DECODE_H
+#define ATTN_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_DECODE_OK 0
+#define ATTN_DECODE_EINVAL (-1) /* invalid argument: shape, pointer, alignment, overlap */
+#define ATTN_DECODE_ENOMEM (-2) /* workspace allocation failed */
+#define ATTN_DECODE_EHIP (-3)   /* a HIP runtime call or kernel launch failed */
+
+/* Largest number of slots one partial/combine launch covers; more slots are
+ * split into several launch groups inside one call. */
+#define ATTN_DECODE_MAX_SLOTS_PER_LAUNCH 64
+/* Upper bound of KV chunks per slot; the planner widens chunks to stay below. */
+#define ATTN_DECODE_MAX_CHUNKS 4096
+
+/*
+ * attn_decode -- decode attention for n_slots slots in one call.
+ *
+ * head_dim must be 64, 128, 256 or 512; n_q_heads a positive multiple of
+ * n_kv_heads; window >= 0 (0 = full attention, window >= L_s also means full);
+ * scale finite (e.g. 1/sqrt(head_dim)).  A slot with L_s = 0 gets zeros.
+ * n_slots = 0 is a no-op that returns 0.  Pointers may be NULL only for
+ * arrays with no elements (k_cache/v_cache when every L_s is 0).
+ */
+int attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                const void *v_scales, const int32_t *seq_lens, int32_t window,
+                float *out, int32_t n_slots, int32_t n_q_heads, int32_t n_kv_heads,
+                int32_t head_dim, float scale, void *stream);
+
+/* Options of attn_decode_ex.  Zero-initialise and set what is needed. */
+typedef struct attn_decode_options {
+    /* KV positions per chunk: 0 = the planner's choice; otherwise a positive
+     * value forcing that chunk size for every slot (still widened to keep at
+     * most ATTN_DECODE_MAX_CHUNKS chunks per slot).  Used by tuning sweeps
+     * and by the chunking-invariance tests (cf. tessl nn.rs,
+     * flash_attn_decode_with_chunk). */
+    int32_t chunk;
+    int32_t reserved0;
+    /* hipEvent_t handles (as void*) recorded on the stream immediately before
+     * the first partial-kernel launch and immediately after the last one, or
+     * NULL.  They bracket the partial (KV-streaming) kernels alone. */
+    void *ev_partial_begin;
+    void *ev_partial_end;
+} attn_decode_options;
+
+/* attn_decode with options; opts == NULL behaves exactly like attn_decode. */
+int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
+                   const void *v_scales, const int32_t *seq_lens, int32_t window,
+                   float *out, int32_t n_slots, int32_t n_q_heads, int32_t n_kv_heads,
+                   int32_t head_dim, float scale, void *stream,
+                   const attn_decode_options *opts);
+
+/*
+ * attn_decode_plan -- the host planner alone (no HIP call, usable without a
+ * GPU).  For the given shapes it writes, per slot, the KV positions per chunk
+ * and the number of chunks (arrays of n_slots, may be NULL), the workspace
+ * bytes the call needs and the number of partial-kernel workgroups it
+ * launches (may be NULL).  v_int8 != 0 selects the int8 V format.
+ * Returns 0 or ATTN_DECODE_EINVAL for shapes attn_decode would reject.
+ */
+int attn_decode_plan(const int32_t *seq_lens, int32_t n_slots, int32_t window,
+                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                     int32_t v_int8, int32_t chunk, int32_t *chunk_keys,
+                     int32_t *n_chunks, int64_t *workspace_bytes,
+                     int64_t *n_partial_workgroups);
+
+/* Message describing the last non-zero return on this host thread ("" if none). */
+const char *attn_decode_last_error(void);
+
+/* Free every workspace the library holds, after synchronising each device
+ * that owns one.  Later calls allocate again.  Returns 0 or ATTN_DECODE_EHIP. */
+int attn_decode_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_DECODE_H */

@@ -1,0 +1,160 @@
+"""C-ABI checks that need no GPU: symbols, the host planner, argument validation.
+
+Validation runs before any HIP call (the tessl nn.rs convention: wrappers
+reject bad work on the host before encoding), so invalid calls can be made
+here with dummy pointers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from decode_attention_kv_02_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_decode\w*)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared_functions() == sorted(binding.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
+                        capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_decode\w*)", nm))
+    assert exported == set(_declared_functions())
+
+
+def test_last_error_starts_empty_and_release_is_safe_without_work():
+    assert binding.last_error() == ""
+    binding.attn_decode_release()
+
+
+# ------------------------------------------------------------------ planner
+
+def _lo(L, W):
+    return L - W if (W > 0 and L > W) else 0
+
+
+@pytest.mark.parametrize("seq,W", [
+    ([256], 0), ([4096], 0), ([1024, 8192, 32768, 2000], 0), ([32768] * 8, 0),
+    ([131072], 0), ([131072], 1024), ([0, 1, 63, 64, 65, 1000], 0), ([5000, 3], 100),
+    ([2 ** 30], 0),
+])
+def test_plan_chunks_cover_each_attended_range(seq, W):
+    p = binding.attn_decode_plan(seq, W, 16, 8, 256)
+    for L, c, n in zip(seq, p["chunk"], p["n_chunks"]):
+        span = L - _lo(L, W)
+        assert 1 <= n <= 4096
+        if span == 0:
+            assert n == 1
+        else:
+            assert 1 <= c <= span
+            assert (n - 1) * c < span <= n * c  # chunks tile [lo, L), only the last is short
+    assert p["partial_workgroups"] == sum(p["n_chunks"]) * 8
+    rows = sum(16 * n for n in p["n_chunks"] if n > 1)
+    assert p["workspace_bytes"] == rows * (256 + 2) * 4
+
+
+def test_plan_of_a_slot_does_not_depend_on_its_batch():
+    seq = [1024, 8192, 32768, 2000, 0, 77]
+    batched = binding.attn_decode_plan(seq, 0, 16, 8, 256)
+    for i, L in enumerate(seq):
+        solo = binding.attn_decode_plan([L], 0, 16, 8, 256)
+        assert solo["chunk"][0] == batched["chunk"][i]
+        assert solo["n_chunks"][0] == batched["n_chunks"][i]
+
+
+def test_forced_chunk_is_used_and_still_bounded():
+    p = binding.attn_decode_plan([1000, 10], 0, 4, 2, 128, chunk=7)
+    assert p["chunk"] == [7, 7] and p["n_chunks"] == [143, 2]
+    p = binding.attn_decode_plan([1000], 0, 4, 2, 128, chunk=5000)
+    assert p["chunk"] == [1000] and p["n_chunks"] == [1]
+    p = binding.attn_decode_plan([100000], 0, 4, 2, 128, chunk=1)
+    assert p["n_chunks"][0] <= 4096
+
+
+def test_gqa_blocks_multiply_workgroups_for_large_groups():
+    # G = 8 runs as two blocks of 4 heads; G = 3 as three single heads
+    assert binding.attn_decode_plan([640], 0, 16, 2, 128)["partial_workgroups"] == 2 * 2 * 10
+    assert binding.attn_decode_plan([640], 0, 6, 2, 128)["partial_workgroups"] == 2 * 3 * 10
+
+
+@pytest.mark.parametrize("args,frag", [
+    (dict(n_q=3, n_kv=2), "multiple"),
+    (dict(D=96), "head_dim"),
+    (dict(W=-1), "window"),
+    (dict(seq=[4, -1]), "negative"),
+    (dict(n_q=0), "positive"),
+])
+def test_plan_rejects_invalid_shapes(args, frag):
+    a = dict(seq=[4], W=0, n_q=2, n_kv=1, D=64)
+    a.update(args)
+    with pytest.raises(binding.AttnDecodeError) as ei:
+        binding.attn_decode_plan(a["seq"], a["W"], a["n_q"], a["n_kv"], a["D"])
+    assert ei.value.code == binding.ATTN_DECODE_EINVAL and frag in ei.value.message
+
+
+# ------------------------------------------------------------------ attn_decode validation
+
+# Fake, well-aligned, disjoint "device" addresses: validation fails before any use.
+Q, K, V, S, OUT = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def _call(**kw):
+    a = dict(q=Q, k=K, v=V, vs=None, seq=[8], W=0, out=OUT, n_q=2, n_kv=1, D=64, scale=0.125)
+    a.update(kw)
+    rc = binding.attn_decode_raw(a["q"], a["k"], a["v"], a["vs"], a["seq"], a["W"], a["out"],
+                                 len(a["seq"]), a["n_q"], a["n_kv"], a["D"], a["scale"], None)
+    return rc, binding.last_error()
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(n_q=3, n_kv=2), "multiple"),
+    (dict(D=100), "head_dim"),
+    (dict(W=-2), "window"),
+    (dict(seq=[3, -4]), "negative"),
+    (dict(scale=float("nan")), "finite"),
+    (dict(scale=float("inf")), "finite"),
+    (dict(q=0), "q is NULL"),
+    (dict(out=0), "out is NULL"),
+    (dict(k=0), "NULL"),
+    (dict(q=Q + 8), "aligned"),
+    (dict(out=OUT + 4), "aligned"),
+    (dict(v=V + 2), "aligned"),
+    (dict(vs=S + 1), "aligned"),
+    (dict(out=Q), "overlaps"),
+    (dict(out=K + 64), "overlaps"),
+    (dict(out=V - 16), "overlaps"),
+    (dict(vs=OUT + 32), "overlaps"),
+])
+def test_invalid_calls_return_einval_before_any_gpu_work(kw, frag):
+    rc, msg = _call(**kw)
+    assert rc == binding.ATTN_DECODE_EINVAL
+    assert frag in msg
+
+
+def test_zero_slots_is_a_noop():
+    rc = binding.attn_decode_raw(None, None, None, None, [], 0, None, 0, 1, 1, 64, 1.0, None)
+    assert rc == binding.ATTN_DECODE_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros((1, 1, 64), dtype=torch.float16)
+    k = torch.zeros(64, dtype=torch.float16)
+    out = torch.zeros((1, 1, 64), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        binding.attn_decode(q, k, k, None, [1], 0, out, 1, 1, 1, 64, 0.125)

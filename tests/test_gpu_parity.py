@@ -1,0 +1,194 @@
+"""Parity of the HIP path (through the C ABI) with the CPU fp64 oracle.
+
+Bar: max-abs <= 2e-3 and relative-L2 <= 1e-3 over each output tensor (fp32
+GPU output vs the fp64 oracle), plus exact structural contracts: batched ==
+per-slot bitwise, run-to-run bitwise determinism, immunity to a recycled
+(unzeroed, NaN-poisoned) workspace (the contract behind tessl nn.rs's
+unzeroed decode scratch), and exact single-key results.
+
+Inputs are the seeded workloads of ``decode_attention_kv_02_amd.workloads``.
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_kv_02_amd import binding
+from decode_attention_kv_02_amd.workloads import WORKLOADS, make_inputs, workload_inputs
+
+from gpu_util import assert_parity, run_gpu, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _report(name, err):
+    print(f"[parity] {name}: max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}", flush=True)
+
+
+# ------------------------------------------------------------------ the five workloads
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_workload_full_output(idx):
+    cfg = WORKLOADS[idx]
+    inp = workload_inputs(cfg)
+    for W in cfg.windows:
+        got = run_gpu(inp, W).cpu().numpy()
+        ref = run_oracle(inp, W)
+        _report(f"{cfg.name} W={W}", assert_parity(got, ref, cfg.name))
+
+
+def test_workload_hybrid_int8_sampled_rows():
+    cfg = WORKLOADS[3]
+    inp = workload_inputs(cfg)
+    got = run_gpu(inp, 0).cpu().numpy().reshape(-1, cfg.head_dim)
+    assert np.all(np.isfinite(got))
+    # every slot, first and last head of each KV-head pair boundary
+    rows = [s * cfg.n_q_heads + h for s in range(cfg.n_slots) for h in (0, 1, 7, 14, 15)]
+    ref = run_oracle(inp, 0, rows=rows)
+    _report(cfg.name + " (sampled rows)", assert_parity(got[rows], ref, cfg.name))
+
+
+def test_workload_long_context_full_and_window():
+    cfg = WORKLOADS[4]
+    inp = workload_inputs(cfg)
+    dev = to_device(inp)
+    for W in cfg.windows:
+        got = run_gpu(inp, W, dev_tensors=dev).cpu().numpy()
+        ref = run_oracle(inp, W)
+        _report(f"{cfg.name} W={W}", assert_parity(got, ref, cfg.name))
+
+
+# ------------------------------------------------------------------ edge cases
+
+EDGE = [
+    # seq_lens, n_q, n_kv, D, v_int8, window
+    ((1,), 1, 1, 64, False, 0),
+    ((0, 5, 0, 64, 65, 127, 128, 129, 1000), 4, 2, 128, False, 0),
+    ((300, 1), 8, 8, 256, True, 0),
+    ((777,), 16, 2, 256, False, 0),
+    ((513, 2), 6, 2, 512, False, 0),
+    ((4000, 10, 2500), 16, 8, 256, True, 100),
+    ((2049,), 4, 1, 64, True, 2048),
+    ((3000,), 2, 1, 512, True, 1),
+    ((1500, 1500), 32, 8, 128, False, 999),
+    ((0, 0), 2, 2, 256, False, 0),
+    ((63, 64, 65, 4095, 4096, 4097), 16, 8, 256, False, 0),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"e{i}" for i in range(len(EDGE))])
+def test_edge_cases(case):
+    seq, nq, nkv, d, i8, W = case
+    inp = make_inputs(seq, nq, nkv, d, i8, seed_base=5000 + 17 * EDGE.index(case))
+    got = run_gpu(inp, W).cpu().numpy()
+    ref = run_oracle(inp, W)
+    _report(f"edge {case}", assert_parity(got, ref, str(case)))
+    for s, L in enumerate(seq):
+        if L == 0:
+            assert np.all(got[s] == 0.0)
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 16, 64, 200, 5000])
+@pytest.mark.parametrize("i8", [False, True])
+def test_chunking_changes_only_rounding(chunk, i8):
+    seq = (3001, 700, 1)
+    inp = make_inputs(seq, 8, 4, 256, i8, seed_base=7100)
+    ref = run_oracle(inp, 0)
+    got = run_gpu(inp, 0, chunk=chunk).cpu().numpy()
+    _report(f"chunk {chunk} int8={i8}", assert_parity(got, ref, f"chunk={chunk}"))
+
+
+def test_single_key_is_exact():
+    for i8 in (False, True):
+        inp = make_inputs((1, 1), 4, 2, 256, i8, seed_base=7200)
+        got = run_gpu(inp, 0).cpu().numpy()
+        ref = run_oracle(inp, 0)
+        assert np.array_equal(got.astype(np.float64), ref), f"int8={i8}"
+
+
+def test_large_logits_stay_stable():
+    inp = make_inputs((2500, 333), 16, 8, 256, False, seed_base=7300)
+    inp.q.mul_(12.0)   # logits of several hundred: exp must not overflow
+    got = run_gpu(inp, 0).cpu().numpy()
+    ref = run_oracle(inp, 0)
+    _report("large logits", assert_parity(got, ref, "large logits"))
+
+
+def test_many_slots_span_several_launch_groups():
+    rng = np.random.default_rng(7400)
+    seq = tuple(int(x) for x in rng.integers(0, 400, size=150))
+    inp = make_inputs(seq, 4, 2, 128, True, seed_base=7400)
+    got = run_gpu(inp, 0).cpu().numpy()
+    ref = run_oracle(inp, 0)
+    _report("150 slots", assert_parity(got, ref, "150 slots"))
+
+
+# ------------------------------------------------------------------ structural contracts
+
+def _slot_inputs(inp, s):
+    d, nkv = inp.head_dim, inp.n_kv_heads
+    off = sum(inp.seq_lens[:s]) * nkv * d
+    n = inp.seq_lens[s] * nkv * d
+    vs = None if inp.v_scales is None else inp.v_scales[off // 32:(off + n) // 32].clone()
+    return type(inp)(inp.q[s:s + 1].clone(), inp.k[off:off + n].clone(), inp.v[off:off + n].clone(),
+                     vs, (inp.seq_lens[s],), inp.n_q_heads, nkv, d, inp.scale)
+
+
+@pytest.mark.parametrize("i8", [False, True])
+def test_batched_equals_per_slot_bitwise(i8):
+    seq = (1024, 8192, 0, 2000, 1, 333)
+    inp = make_inputs(seq, 16, 8, 256, i8, seed_base=7500)
+    for W in (0, 700):
+        batched = run_gpu(inp, W)
+        for s in range(len(seq)):
+            solo = run_gpu(_slot_inputs(inp, s), W)
+            assert torch.equal(batched[s:s + 1], solo), (W, s)
+
+
+def test_run_to_run_bitwise_determinism():
+    inp = make_inputs((5000, 1234, 77), 16, 8, 256, True, seed_base=7600)
+    dev = to_device(inp)
+    a = run_gpu(inp, 0, dev_tensors=dev)
+    b = run_gpu(inp, 0, dev_tensors=dev)
+    assert torch.equal(a, b)
+
+
+def test_recycled_workspace_is_never_read_stale():
+    # A long call with a NaN query leaves NaN partials all over the workspace;
+    # shorter and longer calls afterwards must not read any of them.
+    long_nan = make_inputs((20000, 9000), 16, 8, 256, False, seed_base=7700)
+    long_nan.q[:] = float("nan")
+    run_gpu(long_nan, 0)
+    for seq, seed in (((3000,), 7701), ((600, 20000), 7702), ((9000, 100, 5), 7703)):
+        inp = make_inputs(seq, 16, 8, 256, False, seed_base=seed)
+        got = run_gpu(inp, 0).cpu().numpy()
+        ref = run_oracle(inp, 0)
+        assert_parity(got, ref, f"after NaN workspace {seq}")
+        run_gpu(long_nan, 0)
+
+
+def test_side_stream():
+    inp = make_inputs((4096, 100), 16, 8, 256, False, seed_base=7800)
+    dev = to_device(inp)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        got = run_gpu(inp, 0, dev_tensors=dev, stream=s)
+    ref = run_oracle(inp, 0)
+    assert_parity(got.cpu().numpy(), ref, "side stream")
+
+
+def test_binding_rejects_wrong_dtype_on_gpu():
+    inp = make_inputs((10,), 2, 1, 64, False, seed_base=7900)
+    q, k, v, _ = to_device(inp)
+    out = torch.empty((1, 2, 64), dtype=torch.float16, device=q.device)
+    with pytest.raises(TypeError):
+        binding.attn_decode(q, k, v, None, (10,), 0, out, 1, 2, 1, 64, inp.scale)
