@@ -23,7 +23,7 @@ One JSON line is printed.  Besides the contract fields it carries
     when that summary was taken on the current kernel source, else null;
   * ``cpu_baseline``: the CPU fp64 oracle timed on a bounded sample of the same
     workload on this host's cores;
-  * ``per_config``: every workload preset, cold (a 1 GiB cache-flush write
+  * ``per_config``: every workload preset, cold (a 1 GiB cache-flush read
     before each timed call) and warm (back-to-back calls).
 """
 from __future__ import annotations
@@ -88,7 +88,23 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reps", type=int, default=50, help="timed reps per preset for per_config")
     ap.add_argument("--chunk", type=int, default=0, help="forced chunk size (tuning only)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (5 times), to scale "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     return ap.parse_args(argv)
+
+
+def calibrate_copy(nbytes: int) -> int:
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "copies": 5}), flush=True)
+    return 0
 
 
 def main(argv=None) -> int:
@@ -98,6 +114,9 @@ def main(argv=None) -> int:
               "(the path shards by slot, KV head or sequence chunk across GPUs by design, "
               "but no multi-GPU run exists)", file=sys.stderr)
         return 2
+
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy)
 
     import numpy as np
     import torch
@@ -206,7 +225,7 @@ def main(argv=None) -> int:
 
     # ---- every preset: cold (flushed) and warm
     if not args.quick:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         per = []
         for w in WORKLOADS:
             if w.name != cfg.name:
@@ -224,7 +243,7 @@ def main(argv=None) -> int:
                 cold = []
                 pk = []
                 for _ in range(args.reps):
-                    flush.fill_(1.0)
+                    flush.sum()  # read 1 GiB: evicts the inputs, leaves no dirty lines
                     a, b, c0, c1 = new_event(), new_event(), new_event(), new_event()
                     a.record(stream)
                     call(pin, ptens, pout, W, c0, c1)
@@ -264,7 +283,7 @@ def main(argv=None) -> int:
     if not args.quick and not args.no_cpu_baseline:
         from oracle import oracle_attn_decode
         threads = len(os.sched_getaffinity(0))
-        n_sample_slots = min(inp.n_slots, 4)
+        n_sample_slots = inp.n_slots
         rows = list(range(n_sample_slots * inp.n_q_heads))
         print(f"[bench] cpu oracle on {len(rows)} rows with {threads} threads", file=sys.stderr, flush=True)
         qn, kn, vn = inp.q.numpy(), inp.k.numpy(), inp.v.numpy()
@@ -279,7 +298,7 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "cores": threads,
             "kind": "oracle",
-            "sample": f"first {n_sample_slots} of {inp.n_slots} slots of {cfg.name} "
+            "sample": f"all {n_sample_slots} slots of {cfg.name} "
                       f"({len(rows)} query rows, {sb} KV bytes), one pass, {dt:.2f} s wall",
         }
 

@@ -44,7 +44,7 @@ class AttnDecodeError(RuntimeError):
 class _Options(ctypes.Structure):
     _fields_ = [
         ("chunk", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("merge_mode", ctypes.c_int32),
         ("ev_partial_begin", ctypes.c_void_p),
         ("ev_partial_end", ctypes.c_void_p),
     ]
@@ -163,13 +163,14 @@ def attn_decode(q, k_cache, v_cache, v_scales, seq_lens, window: int, out,
 
 def attn_decode_ex(q, k_cache, v_cache, v_scales, seq_lens, window: int, out,
                    n_slots: Optional[int], n_q_heads: int, n_kv_heads: int, head_dim: int,
-                   scale: float, stream=None, chunk: int = 0,
+                   scale: float, stream=None, chunk: int = 0, merge_mode: int = 0,
                    ev_partial_begin: Optional[int] = None, ev_partial_end: Optional[int] = None) -> None:
-    """attn_decode with a forced chunk size and/or raw hipEvent_t handles around the partial kernel."""
+    """attn_decode with a forced chunk size, a merge mode (0 automatic, 1 combine kernel,
+    2 in-kernel merge) and/or raw hipEvent_t handles around the partial kernel."""
     lib = load_library()
     seq_arr, n_slots, dev, (pq, pk, pv, ps, po) = _marshal(
         q, k_cache, v_cache, v_scales, seq_lens, out, n_slots, n_q_heads, n_kv_heads, head_dim)
-    opts = _Options(int(chunk), 0, ev_partial_begin or None, ev_partial_end or None)
+    opts = _Options(int(chunk), int(merge_mode), ev_partial_begin or None, ev_partial_end or None)
     rc = lib.attn_decode_ex(pq, pk, pv, ps, seq_arr, int(window), po, int(n_slots), int(n_q_heads),
                             int(n_kv_heads), int(head_dim), float(scale), _stream_handle(stream, dev),
                             ctypes.byref(opts))

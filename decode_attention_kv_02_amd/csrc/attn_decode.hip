@@ -11,6 +11,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -18,14 +19,15 @@
 #include <utility>
 
 #include "../../include/attn_decode.h"
-#include "attn_decode_kernels.hpp"
 #include "planner.hpp"
+#include "attn_decode_kernels.hpp"
 
 using namespace attn_decode_impl;
 
 static_assert(ATTN_DECODE_MAX_SLOTS_PER_LAUNCH == kMaxSlotsPerLaunch, "slot table size");
 static_assert(ATTN_DECODE_MAX_CHUNKS == kMaxChunks, "chunk bound");
 static_assert(kCombineMaxChunks >= kMaxChunks, "combine LDS holds every chunk weight");
+static_assert(kFusedMaxChunks <= kMaxChunks, "in-kernel merge bound");
 static_assert(sizeof(LaunchArgs) <= 4096, "kernel arguments stay within 4 KiB");
 
 namespace {
@@ -42,40 +44,59 @@ int fail(int code, const std::string &msg) {
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
+    int64_t counter_cap = 0;   // counters at the front; zero between calls
 };
 
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void *>, Workspace> g_ws;  // keyed by (device, stream)
 
-int acquire_workspace(int device, hipStream_t stream, size_t need, void **out) {
-    *out = nullptr;
-    if (need == 0) return ATTN_DECODE_OK;
+// Returns the counters (all zero) and the partials area of the (device, stream)
+// workspace, growing it when the call needs more of either.
+int acquire_workspace(int device, hipStream_t stream, int64_t n_counters, int64_t data_bytes,
+                      uint32_t **counters, float **data) {
+    *counters = nullptr;
+    *data = nullptr;
+    if (n_counters == 0 && data_bytes == 0) return ATTN_DECODE_OK;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &ws = g_ws[std::make_pair(device, (void *)stream)];
-    if (ws.bytes >= need) {
-        *out = ws.ptr;
-        return ATTN_DECODE_OK;
+    const int64_t have_data = (int64_t)ws.bytes - counter_region_bytes(ws.counter_cap);
+    if (ws.ptr == nullptr || ws.counter_cap < n_counters || have_data < data_bytes) {
+        if (ws.ptr != nullptr) {
+            // earlier work of this stream may still use the old buffer
+            hipError_t e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+            e = hipFree(ws.ptr);
+            ws.ptr = nullptr;
+            ws.bytes = 0;
+            ws.counter_cap = 0;
+            if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipFree: ") + hipGetErrorString(e));
+        }
+        const int64_t cap = std::max<int64_t>(n_counters + n_counters / 4, 4096);
+        int64_t want = data_bytes + data_bytes / 4;
+        want = (want + 0xFFFF) & ~int64_t(0xFFFF);
+        const size_t bytes = (size_t)(counter_region_bytes(cap) + want);
+        void *p = nullptr;
+        hipError_t e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(ATTN_DECODE_ENOMEM, "workspace hipMalloc of " + std::to_string(bytes) + " bytes: " + hipGetErrorString(e));
+        }
+        // counters start at zero (a fill kernel, no memset node); every call
+        // leaves the counters it used at zero again
+        const int64_t words = counter_region_bytes(cap) / 4;
+        hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<uint32_t *>(p), words, 0u);
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return fail(ATTN_DECODE_EHIP, std::string("counter fill launch: ") + hipGetErrorString(e));
+        }
+        ws.ptr = p;
+        ws.bytes = bytes;
+        ws.counter_cap = cap;
     }
-    if (ws.ptr != nullptr) {
-        // earlier work of this stream may still read the old buffer
-        hipError_t e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
-        e = hipFree(ws.ptr);
-        ws.ptr = nullptr;
-        ws.bytes = 0;
-        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipFree: ") + hipGetErrorString(e));
-    }
-    size_t bytes = need + need / 4;
-    bytes = (bytes + 0xFFFF) & ~size_t(0xFFFF);
-    void *p = nullptr;
-    hipError_t e = hipMalloc(&p, bytes);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(ATTN_DECODE_ENOMEM, "workspace hipMalloc of " + std::to_string(bytes) + " bytes: " + hipGetErrorString(e));
-    }
-    ws.ptr = p;
-    ws.bytes = bytes;
-    *out = p;
+    *counters = static_cast<uint32_t *>(ws.ptr);
+    *data = reinterpret_cast<float *>(static_cast<char *>(ws.ptr) + counter_region_bytes(ws.counter_cap));
     return ATTN_DECODE_OK;
 }
 
@@ -138,8 +159,9 @@ int run(const void *q, const void *k_cache, const void *v_cache, const void *v_s
     g_last_error.clear();
     const bool v_int8 = v_scales != nullptr;
     const int32_t chunk = opts ? opts->chunk : 0;
+    const int32_t merge_mode = opts ? opts->merge_mode : 0;
 
-    std::string err = check_shapes(seq_lens, n_slots, window, n_q, n_kv, D, v_int8, chunk);
+    std::string err = check_shapes(seq_lens, n_slots, window, n_q, n_kv, D, v_int8, chunk, merge_mode);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
     if (!std::isfinite(scale)) return fail(ATTN_DECODE_EINVAL, "scale must be finite");
     if (n_slots == 0) return ATTN_DECODE_OK;
@@ -169,7 +191,7 @@ int run(const void *q, const void *k_cache, const void *v_cache, const void *v_s
         return fail(ATTN_DECODE_EINVAL, "out overlaps an input");
 
     CallPlan plan;
-    err = make_plan(seq_lens, n_slots, window, n_q, n_kv, D, chunk, plan);
+    err = make_plan(seq_lens, n_slots, window, n_q, n_kv, D, chunk, merge_mode, plan);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
 
     const partial_fn pk = select_partial(D, plan.GB, v_int8);
@@ -181,10 +203,11 @@ int run(const void *q, const void *k_cache, const void *v_cache, const void *v_s
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
-    void *ws = nullptr;
-    int rc = acquire_workspace(device, stream, (size_t)plan.workspace_bytes, &ws);
+    uint32_t *counters = nullptr;
+    float *ws_o = nullptr;
+    const int64_t data_bytes = plan.part_rows * (int64_t)(D + 2) * (int64_t)sizeof(float);
+    int rc = acquire_workspace(device, stream, plan.n_counters, data_bytes, &counters, &ws_o);
     if (rc != ATTN_DECODE_OK) return rc;
-    float *ws_o = static_cast<float *>(ws);
     float *ws_ml = ws_o ? ws_o + plan.part_rows * D : nullptr;
 
     const double scale_log2 = (double)scale * 1.4426950408889634074;  // scale * log2(e)
@@ -198,6 +221,8 @@ int run(const void *q, const void *k_cache, const void *v_cache, const void *v_s
     args.out = out;
     args.ws_o = ws_o;
     args.ws_ml = ws_ml;
+    args.counters = counters;
+    args.fuse_limit = plan.fuse_limit;
     args.n_q = n_q;
     args.G = plan.G;
     args.n_sub = plan.n_sub;
@@ -218,11 +243,11 @@ int run(const void *q, const void *k_cache, const void *v_cache, const void *v_s
             sd.n_chunks = sp.n_chunks;
             sd.item_begin = item;
             sd.comb_begin = comb;
+            sd.cnt_base = sp.cnt_base;
             item += n_kv * plan.n_sub * sp.n_chunks;
-            if (sp.n_chunks > 1) comb += n_q;
+            if (sp.n_chunks > 1 && !sp.fused) comb += n_q;
         }
         args.n_items = item;
-        args.n_comb = comb;
     };
 
     if (opts && opts->ev_partial_begin) {
@@ -242,7 +267,7 @@ int run(const void *q, const void *k_cache, const void *v_cache, const void *v_s
     for (const LaunchGroup &lg : plan.groups) {
         if (lg.combine_rows == 0) continue;
         fill(lg);
-        hipLaunchKernelGGL(ck, dim3((unsigned)lg.combine_rows), dim3(kThreads), 0, stream, args);
+        hipLaunchKernelGGL(ck, dim3((unsigned)(lg.combine_rows * (D / kCombineDims))), dim3(kThreads), 0, stream, args);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("combine kernel launch: ") + hipGetErrorString(e));
     }
@@ -280,7 +305,7 @@ extern "C" int attn_decode_plan(const int32_t *seq_lens, int32_t n_slots, int32_
                                    v_int8 != 0, chunk);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
     CallPlan plan;
-    err = make_plan(seq_lens, n_slots, window, n_q_heads, n_kv_heads, head_dim, chunk, plan);
+    err = make_plan(seq_lens, n_slots, window, n_q_heads, n_kv_heads, head_dim, chunk, kMergeAuto, plan);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
     for (int32_t s = 0; s < n_slots; ++s) {
         if (chunk_keys) chunk_keys[s] = plan.slots[s].chunk;

@@ -10,7 +10,7 @@
 //    shares the K and V rows the workgroup streams, so each byte of the chunk
 //    is read from HBM once for all of them (the GQA grouping of mlx-native's
 //    flash_attn_vec_hybrid_batched_gqa_impl; tessl's DecodeHeadBlock::Group).
-//    A row is read by R = head_dim/16 lanes with 16-byte loads (a wave loads
+//    A row is read by R = head_dim/16 lanes with 16-byte non-temporal loads (a wave loads
 //    64/R consecutive rows per instruction, fully coalesced); the QK dot uses
 //    v_dot2_f32_f16 on the fp16 pairs and an all-reduce over the R lanes made
 //    of DPP row ops (quad_perm, row_half_mirror, row_mirror) plus one swizzle
@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "planner.hpp"  // kFusedMaxChunks, shared with the host planner
+
 namespace attn_decode_impl {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -46,7 +48,9 @@ struct SlotDesc {
     int32_t chunk;      // positions per chunk
     int32_t n_chunks;   // chunks of the slot
     int32_t item_begin; // first partial workgroup of the slot in this launch
-    int32_t comb_begin; // first combine workgroup of the slot in this launch
+    int32_t comb_begin; // first combine-kernel row of the slot in this launch
+    int32_t cnt_base;   // first arrival counter of the slot (in-kernel merge)
+    int32_t pad0;
 };
 
 struct LaunchArgs {
@@ -57,6 +61,7 @@ struct LaunchArgs {
     float *out;             // fp32 [n_slots_total][n_q][D]
     float *ws_o;            // partial O rows [part_rows][D]
     float *ws_ml;           // partial (M, S) [part_rows][2]
+    uint32_t *counters;     // arrival counters of in-kernel merges, zero between calls
     int32_t n_slots;        // slots in this launch
     int32_t slot0;          // global index of the launch's first slot
     int32_t n_q;
@@ -64,7 +69,7 @@ struct LaunchArgs {
     int32_t n_sub;          // G / GB
     float scale_log2;       // scale * log2(e)
     int32_t n_items;
-    int32_t n_comb;
+    int32_t fuse_limit;     // slots with 2..fuse_limit chunks merge inside the partial kernel
     SlotDesc slot[64];
 };
 
@@ -92,7 +97,27 @@ __device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x)));
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, shfl_xor_f32(x, off));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x += shfl_xor_f32(x, off);
+    return x;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load: each KV byte is used once, so it is marked non-temporal.
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
@@ -109,6 +134,98 @@ __device__ __forceinline__ int upper_index(int n, int x, F key) {
     return lo;
 }
 
+// ---------------------------------------------------------------- chunk merge
+
+// Log-sum-exp merge of the nc chunk partials of GB consecutive query heads
+// (h0 .. h0+GB-1 of the slot whose partial rows start at part_row0) into
+// out_rows ([GB][D] fp32), by one 256-thread workgroup:
+//   M* = max_c M_c,  w_c = 2^(M_c - M*),  S* = sum_c w_c S_c,
+//   out = sum_c w_c O_c / S*   (S* == 0 gives zeros).
+// The chunks are visited in a fixed order, so the result does not depend on
+// which workgroup runs the merge.
+template <int D, int GB>
+__device__ __forceinline__ void merge_chunks(const LaunchArgs &args, int64_t part_row0, int nc, int h0,
+                                             float *out_rows) {
+    constexpr int COLS = GB * D / 4;                            // float4 columns of the GB rows
+    constexpr int CG = COLS >= kThreads ? 1 : kThreads / COLS;  // chunk groups
+    __shared__ float s_wt[GB][kFusedMaxChunks];
+    __shared__ float s_lsum[GB];
+    __shared__ float4 s_acc[CG > 1 ? CG : 1][CG > 1 ? COLS : 1];
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+
+    if (w < GB) {   // wave g prepares the chunk weights of head g
+        const float *ml = args.ws_ml + (part_row0 + (int64_t)(h0 + w) * nc) * 2;
+        float mx = -INFINITY;
+        for (int cc = lane; cc < nc; cc += 64) mx = fmaxf(mx, ml[2 * cc]);
+        mx = wave_max(mx);
+        const float ms = (mx == -INFINITY) ? 0.f : mx;
+        float ls = 0.f;
+        for (int cc = lane; cc < nc; cc += 64) {
+            const float wc = fast_exp2(ml[2 * cc] - ms);
+            s_wt[w][cc] = wc;
+            ls += wc * ml[2 * cc + 1];
+        }
+        ls = wave_sum(ls);
+        if (lane == 0) s_lsum[w] = ls;
+    }
+    __syncthreads();
+
+    for (int col0 = 0; col0 < COLS; col0 += (CG > 1 ? COLS : kThreads)) {
+        const int t = tid % (CG > 1 ? COLS : kThreads);
+        const int cg = CG > 1 ? tid / COLS : 0;
+        const int col = col0 + t;
+        const int g = col / (D / 4);
+        const int d0 = (col - g * (D / 4)) * 4;
+        const float *src = args.ws_o + (part_row0 + (int64_t)(h0 + g) * nc) * D + d0;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        int cc = cg;
+        for (; cc + 3 * CG < nc; cc += 4 * CG) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *(const float4 *)(src + (int64_t)(cc + u * CG) * D);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float wc = s_wt[g][cc + u * CG];
+                acc.x = fmaf(wc, v[u].x, acc.x);
+                acc.y = fmaf(wc, v[u].y, acc.y);
+                acc.z = fmaf(wc, v[u].z, acc.z);
+                acc.w = fmaf(wc, v[u].w, acc.w);
+            }
+        }
+        for (; cc < nc; cc += CG) {
+            const float4 v = *(const float4 *)(src + (int64_t)cc * D);
+            const float wc = s_wt[g][cc];
+            acc.x = fmaf(wc, v.x, acc.x);
+            acc.y = fmaf(wc, v.y, acc.y);
+            acc.z = fmaf(wc, v.z, acc.z);
+            acc.w = fmaf(wc, v.w, acc.w);
+        }
+        if constexpr (CG > 1) {
+            s_acc[cg][t] = acc;
+            __syncthreads();
+            if (tid < COLS) {
+                acc = s_acc[0][tid];
+#pragma unroll
+                for (int k = 1; k < CG; ++k) {
+                    const float4 u = s_acc[k][tid];
+                    acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
+                }
+            }
+        }
+        if (CG == 1 || tid < COLS) {
+            const float ls = s_lsum[g];
+            float4 r;
+            r.x = (ls == 0.f) ? 0.f : acc.x / ls;
+            r.y = (ls == 0.f) ? 0.f : acc.y / ls;
+            r.z = (ls == 0.f) ? 0.f : acc.z / ls;
+            r.w = (ls == 0.f) ? 0.f : acc.w / ls;
+            *(float4 *)(out_rows + g * D + d0) = r;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- partial kernel
 
 template <int D>
@@ -118,6 +235,15 @@ struct Geometry {
     static constexpr int U = (D == 512) ? 4 : (16 / P);     // loads per wave iteration
     static constexpr int RW = P * U;                        // rows per wave iteration
     static constexpr int HALF = D / 2;
+};
+
+// Registers of one wave iteration: U K rows (two 16-byte halves per lane) and
+// U V rows (fp16: two halves; int8: one 16-byte code load and one scale).
+template <int U>
+struct Frag {
+    uint4 ka[U], kb[U];
+    uint4 va[U], vb[U];
+    uint16_t vsc[U];
 };
 
 template <int D, int GB, bool VINT8>
@@ -168,31 +294,29 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     const float sl2 = args.scale_log2;
     const uint16_t *kbase = args.k + rowbase * D;
 
-    for (int wb = cbeg + w * RW; wb < cend; wb += kWaves * RW) {
-        // ---- issue every load of the iteration
-        uint4 ka[U], kb[U];
-        uint4 va[U], vb[U];      // fp16 V: two 16-byte halves; int8 V: codes in va
-        uint16_t vsc[U];
-        int rowv[U];
+    // Rows [wb, wb + RW) of one wave iteration: lane group rg reads row wb + u*P + rg.
+    // Rows past the chunk end are clamped to its last row (in bounds) and masked.
+    auto load = [&](int wb, Frag<U> &f) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int row = wb + u * P + rg;
-            rowv[u] = row;
             const int rc = row < cend ? row : cend - 1;
             const uint16_t *kp = kbase + (int64_t)rc * D;
-            ka[u] = *(const uint4 *)(kp + sl * 8);
-            kb[u] = *(const uint4 *)(kp + HALF + sl * 8);
+            f.ka[u] = load_stream16(kp + sl * 8);
+            f.kb[u] = load_stream16(kp + HALF + sl * 8);
             if constexpr (VINT8) {
                 const int8_t *vp = (const int8_t *)args.v + (rowbase + rc) * D;
-                va[u] = *(const uint4 *)(vp + sl * 16);
-                vsc[u] = args.vs[(rowbase + rc) * (D / 32) + (sl >> 1)];
+                f.va[u] = load_stream16(vp + sl * 16);
+                f.vsc[u] = args.vs[(rowbase + rc) * (D / 32) + (sl >> 1)];
             } else {
                 const uint16_t *vp = (const uint16_t *)args.v + (rowbase + rc) * D;
-                va[u] = *(const uint4 *)(vp + sl * 8);
-                vb[u] = *(const uint4 *)(vp + HALF + sl * 8);
+                f.va[u] = load_stream16(vp + sl * 8);
+                f.vb[u] = load_stream16(vp + HALF + sl * 8);
             }
         }
+    };
 
+    auto consume = [&](int wb, const Frag<U> &f) {
         // ---- logits (log2 domain)
         float s[U][GB];
 #pragma unroll
@@ -200,43 +324,21 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
 #pragma unroll
             for (int g = 0; g < GB; ++g) {
                 float acc = 0.f;
-                acc = __builtin_amdgcn_fdot2(as_h2(ka[u].x), qv[g][0], acc, false);
-                acc = __builtin_amdgcn_fdot2(as_h2(ka[u].y), qv[g][1], acc, false);
-                acc = __builtin_amdgcn_fdot2(as_h2(ka[u].z), qv[g][2], acc, false);
-                acc = __builtin_amdgcn_fdot2(as_h2(ka[u].w), qv[g][3], acc, false);
-                acc = __builtin_amdgcn_fdot2(as_h2(kb[u].x), qv[g][4], acc, false);
-                acc = __builtin_amdgcn_fdot2(as_h2(kb[u].y), qv[g][5], acc, false);
-                acc = __builtin_amdgcn_fdot2(as_h2(kb[u].z), qv[g][6], acc, false);
-                acc = __builtin_amdgcn_fdot2(as_h2(kb[u].w), qv[g][7], acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(f.ka[u].x), qv[g][0], acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(f.ka[u].y), qv[g][1], acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(f.ka[u].z), qv[g][2], acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(f.ka[u].w), qv[g][3], acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(f.kb[u].x), qv[g][4], acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(f.kb[u].y), qv[g][5], acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(f.kb[u].z), qv[g][6], acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(f.kb[u].w), qv[g][7], acc, false);
                 acc = group_sum<R>(acc);
-                s[u][g] = rowv[u] < cend ? acc * sl2 : -INFINITY;
+                s[u][g] = (wb + u * P + rg) < cend ? acc * sl2 : -INFINITY;
             }
         }
 
-        // ---- V rows as fp32 (shared by the GB heads)
-        float vf[U][16];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if constexpr (VINT8) {
-                const uint32_t wd[4] = {va[u].x, va[u].y, va[u].z, va[u].w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    vf[u][4 * j + 0] = (float)(int8_t)(wd[j]);
-                    vf[u][4 * j + 1] = (float)(int8_t)(wd[j] >> 8);
-                    vf[u][4 * j + 2] = (float)(int8_t)(wd[j] >> 16);
-                    vf[u][4 * j + 3] = (float)(int8_t)(wd[j] >> 24);
-                }
-            } else {
-                const uint32_t wd[8] = {va[u].x, va[u].y, va[u].z, va[u].w, vb[u].x, vb[u].y, vb[u].z, vb[u].w};
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    vf[u][2 * j + 0] = h2f((uint16_t)(wd[j] & 0xFFFF));
-                    vf[u][2 * j + 1] = h2f((uint16_t)(wd[j] >> 16));
-                }
-            }
-        }
-
-        // ---- online softmax + V accumulation, per head
+        // ---- online softmax: new running max, rescale, weights of the U rows
+        float p[U][GB];
 #pragma unroll
         for (int g = 0; g < GB; ++g) {
             float mx = m[g];
@@ -244,25 +346,66 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
             for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u][g]);
             const float ms = (mx == -INFINITY) ? 0.f : mx;
             const float alpha = fast_exp2(m[g] - ms);
-            float p[U];
             float psum = 0.f;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                p[u] = fast_exp2(s[u][g] - ms);
-                psum += p[u];
+                p[u][g] = fast_exp2(s[u][g] - ms);
+                psum += p[u][g];
             }
             l[g] = l[g] * alpha + psum;
             m[g] = mx;
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[g][i] *= alpha;
+        }
+
+        // ---- V accumulation: each row is converted to fp32 once and used by the GB heads
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float wgt = p[u];
-                if constexpr (VINT8) wgt *= h2f(vsc[u]);
+        for (int u = 0; u < U; ++u) {
+            float vf[16];
+            if constexpr (VINT8) {
+                const uint32_t wd[4] = {f.va[u].x, f.va[u].y, f.va[u].z, f.va[u].w};
 #pragma unroll
-                for (int i = 0; i < 16; ++i) o[g][i] = fmaf(wgt, vf[u][i], o[g][i]);
+                for (int j = 0; j < 4; ++j) {
+                    vf[4 * j + 0] = (float)(int8_t)(wd[j]);
+                    vf[4 * j + 1] = (float)(int8_t)(wd[j] >> 8);
+                    vf[4 * j + 2] = (float)(int8_t)(wd[j] >> 16);
+                    vf[4 * j + 3] = (float)(int8_t)(wd[j] >> 24);
+                }
+            } else {
+                const uint32_t wd[8] = {f.va[u].x, f.va[u].y, f.va[u].z, f.va[u].w,
+                                        f.vb[u].x, f.vb[u].y, f.vb[u].z, f.vb[u].w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    vf[2 * j + 0] = h2f((uint16_t)(wd[j] & 0xFFFF));
+                    vf[2 * j + 1] = h2f((uint16_t)(wd[j] >> 16));
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < GB; ++g) {
+                float wgt = p[u][g];
+                if constexpr (VINT8) wgt *= h2f(f.vsc[u]);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[g][i] = fmaf(wgt, vf[i], o[g][i]);
             }
         }
+    };
+
+    // Two register buffers: the loads of the next iteration are in flight
+    // while the current one is computed.
+    constexpr int STEP = kWaves * RW;
+    Frag<U> fa, fb;
+    int wb = cbeg + w * RW;
+    if (wb < cend) load(wb, fa);
+    while (wb < cend) {
+        int wn = wb + STEP;
+        if (wn < cend) load(wn, fb);
+        consume(wb, fa);
+        wb = wn;
+        if (wb >= cend) break;
+        wn = wb + STEP;
+        if (wn < cend) load(wn, fa);
+        consume(wb, fb);
+        wb = wn;
     }
 
     // ---- merge the P lane groups of the wave (lanes lane ^ off share the dims)
@@ -311,6 +454,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     __syncthreads();
 
     const bool single = sd.n_chunks == 1;
+    const bool fused = !single && sd.n_chunks <= args.fuse_limit;
     for (int idx = tid; idx < GB * D; idx += kThreads) {
         const int g = idx / D;
         const int d = idx - g * D;
@@ -329,37 +473,67 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
             args.out[(slot_g * args.n_q + h0 + g) * D + d] = (lsum == 0.f) ? 0.f : acc / lsum;
         } else {
             const int64_t prow = sd.part_row0 + (int64_t)(h0 + g) * sd.n_chunks + c;
-            args.ws_o[prow * D + d] = acc;
-            if (d == 0) {
-                args.ws_ml[prow * 2 + 0] = mx;
-                args.ws_ml[prow * 2 + 1] = lsum;
+            if (fused) {
+                // agent-scope stores (sc1): coherent across XCDs without an L2 write-back
+                __hip_atomic_store(args.ws_o + prow * D + d, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (d == 0) {
+                    __hip_atomic_store(args.ws_ml + prow * 2 + 0, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(args.ws_ml + prow * 2 + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            } else {
+                args.ws_o[prow * D + d] = acc;
+                if (d == 0) {
+                    args.ws_ml[prow * 2 + 0] = mx;
+                    args.ws_ml[prow * 2 + 1] = lsum;
+                }
             }
         }
     }
+    if (!fused) return;
+
+    // ---- in-kernel merge: the last chunk of this (slot, kv head, head block) to finish merges all
+    // Every wave waits until its partial stores have completed (they are
+    // agent-scope stores, so completion means visible to every XCD), then one
+    // thread takes a ticket.  The workgroup holding the last ticket acquires at
+    // agent scope and reads every chunk's partial back.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __shared__ int s_last;
+    uint32_t *counter = args.counters + sd.cnt_base + kvh * args.n_sub + sub;
+    if (tid == 0)
+        s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (uint32_t)(sd.n_chunks - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    merge_chunks<D, GB>(args, sd.part_row0, sd.n_chunks, h0, args.out + (slot_g * args.n_q + h0) * D);
+    // the counter is zero again for the next call on this stream
+    if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- combine kernel
 
 constexpr int kCombineMaxChunks = 4096;
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, shfl_xor_f32(x, off));
-    return x;
-}
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x += shfl_xor_f32(x, off);
-    return x;
-}
+// Dims of one output row merged by one combine workgroup.
+constexpr int kCombineDims = 64;
 
+// One workgroup per (slot, query head, 64-dim slice).  16 groups of 16
+// threads split the chunks; each thread owns 4 dims (16-byte loads of the
+// partial rows, coalesced over the 16 threads) and sums its share of the
+// chunks; the 16 group sums are added in LDS in a fixed order.
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const LaunchArgs args) {
+    constexpr int SLICES = D / kCombineDims;
+    constexpr int TPR = kCombineDims / 4;       // threads per chunk row of the slice
+    constexpr int CG = kThreads / TPR;          // chunk groups
     __shared__ float s_w[kCombineMaxChunks];
+    __shared__ float4 s_acc[CG][TPR];
     __shared__ float s_red[kWaves];
 
-    const int row = blockIdx.x;
+    const int row = blockIdx.x / SLICES;
+    const int slice = blockIdx.x - row * SLICES;
     const int si = upper_index(args.n_slots, row, [&](int i) { return args.slot[i].comb_begin; });
     const SlotDesc sd = args.slot[si];
     const int h = row - sd.comb_begin;
@@ -395,13 +569,55 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const LaunchArgs
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) lsum += s_red[ww];
 
-    float *dst = args.out + (slot_g * args.n_q + h) * D;
-    for (int d = tid; d < D; d += kThreads) {
-        float acc = 0.f;
-        const float *src = args.ws_o + base * D + d;
-        for (int c = 0; c < nc; ++c) acc = fmaf(s_w[c], src[(int64_t)c * D], acc);
-        dst[d] = (lsum == 0.f) ? 0.f : acc / lsum;
+    // weighted sum of the partial O rows over this thread's chunks
+    const int cg = tid / TPR;
+    const int j = tid - cg * TPR;
+    const int d0 = slice * kCombineDims + 4 * j;
+    const float *src = args.ws_o + base * D + d0;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int c = cg;
+    for (; c + 3 * CG < nc; c += 4 * CG) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *(const float4 *)(src + (int64_t)(c + u * CG) * D);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float wc = s_w[c + u * CG];
+            acc.x = fmaf(wc, v[u].x, acc.x);
+            acc.y = fmaf(wc, v[u].y, acc.y);
+            acc.z = fmaf(wc, v[u].z, acc.z);
+            acc.w = fmaf(wc, v[u].w, acc.w);
+        }
     }
+    for (; c < nc; c += CG) {
+        const float4 v = *(const float4 *)(src + (int64_t)c * D);
+        const float wc = s_w[c];
+        acc.x = fmaf(wc, v.x, acc.x);
+        acc.y = fmaf(wc, v.y, acc.y);
+        acc.z = fmaf(wc, v.z, acc.z);
+        acc.w = fmaf(wc, v.w, acc.w);
+    }
+    s_acc[cg][j] = acc;
+    __syncthreads();
+    if (tid < TPR) {
+        float4 t = s_acc[0][tid];
+#pragma unroll
+        for (int g = 1; g < CG; ++g) {
+            const float4 u = s_acc[g][tid];
+            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+        }
+        float4 r;
+        r.x = (lsum == 0.f) ? 0.f : t.x / lsum;
+        r.y = (lsum == 0.f) ? 0.f : t.y / lsum;
+        r.z = (lsum == 0.f) ? 0.f : t.z / lsum;
+        r.w = (lsum == 0.f) ? 0.f : t.w / lsum;
+        *(float4 *)(args.out + (slot_g * args.n_q + h) * D + slice * kCombineDims + 4 * tid) = r;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t value) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = value;
 }
 
 }  // namespace attn_decode_impl

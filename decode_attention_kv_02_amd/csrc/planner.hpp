@@ -12,6 +12,7 @@
 // at most `chunk` positions (a flat list instead of a padded grid).
 #pragma once
 
+#include <climits>
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -20,10 +21,9 @@ namespace attn_decode_impl {
 
 constexpr int kMaxSlotsPerLaunch = 64;   // slot table passed by value in the kernel arguments
 constexpr int kMaxChunks = 4096;         // per slot; bounds the combine kernel's LDS weights
-constexpr int kChunkQuantum = 64;        // chunk sizes are multiples of this (one WG iteration at D=256)
+constexpr int kChunkQuantum = 64;        // chunk sizes are multiples of this (one workgroup iteration at D=256)
 constexpr int kChunkMin = 64;
-constexpr int kChunkMax = 1024;
-constexpr int kTargetChunks = 64;        // chunks per (slot, kv head) the planner aims for
+constexpr int kChunkMax = 2048;
 constexpr int64_t kMaxItemsPerLaunch = int64_t(1) << 24;  // 2^24 workgroups x 256 threads < 2^32
 constexpr int kQuantBlock = 32;          // int8 V: dims per fp16 scale
 
@@ -35,6 +35,8 @@ struct SlotPlan {
     int32_t n_chunks = 1;   // >= 1 (an empty slot has one empty chunk)
     int64_t kv_row0 = 0;    // n_kv * sum_{t<s} L_t : row of (slot, kv head 0, pos 0)
     int64_t part_row0 = -1; // first partial row when n_chunks > 1, else -1
+    bool fused = false;     // 2..fuse_limit chunks: merged inside the partial kernel
+    int32_t cnt_base = 0;   // first arrival counter when fused
 };
 
 struct LaunchGroup {
@@ -50,21 +52,54 @@ struct CallPlan {
     std::vector<SlotPlan> slots;
     std::vector<LaunchGroup> groups;
     int64_t part_rows = 0;         // partial rows (each head_dim floats + 2 stats)
-    int64_t workspace_bytes = 0;
+    int64_t n_counters = 0;        // arrival counters (one per kv head and head block of fused slots)
+    int fuse_limit = 1;            // largest chunk count merged inside the partial kernel
+    int64_t workspace_bytes = 0;   // counter region (256-byte aligned) + partial rows
     int64_t total_items = 0;
 };
+
+// With the in-kernel merge, slots split into at most this many chunks are
+// merged by the last of their workgroups to finish (its LDS holds one weight
+// per chunk); longer slots still go to the combine kernel.
+constexpr int kFusedMaxChunks = 256;
+
+// kMergeAuto currently selects the combine kernel: on MI355X the in-kernel
+// merge measured slower on every preset (each workgroup must wait for its
+// write-through partial stores before it may take a ticket, and the last one
+// merges alone), e.g. 276 vs 252 us for 8 x 32768 int8-V slots.
+enum MergeMode { kMergeAuto = 0, kMergeCombineKernel = 1, kMergeInKernel = 2 };
+
+// Counters sit at the front of the workspace in a 256-byte aligned region.
+inline int64_t counter_region_bytes(int64_t n_counters) { return (n_counters * 4 + 255) / 256 * 256; }
 
 inline bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Positions per chunk for a slot attending n positions (n >= 1).
+// Chunks per (slot, kv head) the planner aims for, by attended length.  Short
+// slots are split finely so that a lone slot still fills the GPU; long slots
+// get long chunks, because every workgroup pays a fixed cost (first-load
+// latency, the lane/wave merge, a partial row per head) and the combine reads
+// one partial row per chunk.  Measured on MI355X with forced chunk sizes
+// (warm, back-to-back calls): 1 x 4096 and a 1024-position window run fastest
+// at 64 positions per chunk, 1 x 131072 at 2048, 8 x 32768 int8-V at 2048
+// (1024 is 2% slower there but twice as fast for a lone 32768 slot, so 32768
+// gets 1024).  The pages make the same trade (tessl nn.rs DecodeChunk: grid
+// parallelism against the number of partials the reduce pass combines).
+inline int64_t target_chunks(int64_t n) {
+    if (n <= 8192) return 64;
+    if (n <= 65536) return 32;
+    return 16;
+}
+
+// Positions per chunk for a slot attending n positions (n >= 1).  Depends on
+// the slot's own length only, so a slot is split the same way in every batch.
 inline int64_t chunk_for(int64_t n, int32_t forced) {
     int64_t c;
     if (forced > 0) {
         c = forced;
     } else {
-        c = ceil_div(n, kTargetChunks);
+        c = ceil_div(n, target_chunks(n));
         c = ceil_div(c, kChunkQuantum) * kChunkQuantum;
         if (c < kChunkMin) c = kChunkMin;
         if (c > kChunkMax) c = kChunkMax;
@@ -77,8 +112,10 @@ inline int64_t chunk_for(int64_t n, int32_t forced) {
 // Shape checks shared by every entry point.  Returns "" when valid.
 inline std::string check_shapes(const int32_t *seq_lens, int32_t n_slots, int32_t window,
                                 int32_t n_q, int32_t n_kv, int32_t head_dim, bool v_int8,
-                                int32_t chunk) {
+                                int32_t chunk, int32_t merge_mode = 0) {
     if (n_slots < 0) return "n_slots must be >= 0";
+    if (merge_mode != kMergeAuto && merge_mode != kMergeCombineKernel && merge_mode != kMergeInKernel)
+        return "unknown merge_mode";
     if (n_slots > 0 && seq_lens == nullptr) return "seq_lens is NULL";
     if (n_q <= 0 || n_kv <= 0) return "n_q_heads and n_kv_heads must be positive";
     if (n_q % n_kv != 0) return "n_q_heads must be a multiple of n_kv_heads";
@@ -100,8 +137,9 @@ inline int heads_per_workgroup(int G) {
 // Builds the plan; returns "" on success or an error message.
 inline std::string make_plan(const int32_t *seq_lens, int32_t n_slots, int32_t window,
                              int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t chunk,
-                             CallPlan &plan) {
+                             int32_t merge_mode, CallPlan &plan) {
     plan = CallPlan();
+    plan.fuse_limit = merge_mode == kMergeInKernel ? kFusedMaxChunks : 1;
     plan.G = n_q / n_kv;
     plan.GB = heads_per_workgroup(plan.G);
     plan.n_sub = plan.G / plan.GB;
@@ -126,10 +164,17 @@ inline std::string make_plan(const int32_t *seq_lens, int32_t n_slots, int32_t w
         if (sp.n_chunks > 1) {
             sp.part_row0 = part;
             part += (int64_t)n_q * sp.n_chunks;
+            sp.fused = sp.n_chunks <= plan.fuse_limit;
+            if (sp.fused) {
+                if (plan.n_counters + (int64_t)n_kv * plan.n_sub > INT32_MAX) return "too many split slots";
+                sp.cnt_base = (int32_t)plan.n_counters;
+                plan.n_counters += (int64_t)n_kv * plan.n_sub;
+            }
         }
     }
     plan.part_rows = part;
-    plan.workspace_bytes = part * (int64_t)(head_dim + 2) * (int64_t)sizeof(float);
+    plan.workspace_bytes = counter_region_bytes(plan.n_counters) +
+                           part * (int64_t)(head_dim + 2) * (int64_t)sizeof(float);
 
     // launch groups: at most kMaxSlotsPerLaunch slots and kMaxItemsPerLaunch workgroups
     LaunchGroup g;
@@ -146,7 +191,7 @@ inline std::string make_plan(const int32_t *seq_lens, int32_t n_slots, int32_t w
             g.slot_begin = s;
         }
         g.items += items;
-        if (sp.n_chunks > 1) g.combine_rows += n_q;
+        if (sp.n_chunks > 1 && !sp.fused) g.combine_rows += n_q;
     }
     g.slot_end = n_slots;
     if (n_slots > 0) plan.groups.push_back(g);

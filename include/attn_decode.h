@@ -34,16 +34,21 @@
  *
  * Execution: every entry point that takes a stream is asynchronous on it
  * (a hipStream_t passed as void*; NULL = the null stream of the current
- * device).  It enqueues one partial kernel per launch group (up to 64 slots)
- * and one combine kernel per group that has a slot split over several KV
- * chunks; it never synchronises the host and never reads device memory from
- * the host.  Inputs must stay alive and unmodified until the work completes.
+ * device).  A call enqueues one partial kernel per launch group of up to 64
+ * slots (normally one group) and, when some slot is split into several KV
+ * chunks, one log-sum-exp combine kernel per such group.  It never
+ * synchronises the host and never reads device memory from the host.  Inputs
+ * must stay alive and unmodified until the work completes.
  *
- * Workspace: the library keeps one growable partials buffer per (device,
- * stream).  It is never zeroed (every element the combine reads is written by
- * the same call's partial kernel).  Growing it synchronises that stream once.
- * Calls on different streams use different buffers; calls that overlap on
- * the same stream are ordered by the stream.  attn_decode_release frees them.
+ * Workspace: the library keeps one growable buffer per (device, stream): a
+ * block of arrival counters used by the in-kernel merge mode (zeroed by a fill
+ * kernel when the buffer is allocated; every call returns the counters it
+ * uses to zero) followed by the per-chunk partials, which are never zeroed
+ * (every partial a merge reads was written by the same call).  Allocating or growing it calls hipMalloc
+ * and synchronises that stream once, so a call that needs a bigger workspace
+ * cannot be captured into a HIP graph; a call that fits the existing one only
+ * enqueues kernels.  Calls on different streams use different buffers; calls
+ * on the same stream are ordered by it.  attn_decode_release frees them.
  *
  * Determinism: the KV split of a slot depends only on that slot's own
  * attended length, head_dim, the V format and the chunk override, so a
@@ -69,8 +74,8 @@ extern "C" {
 #define ATTN_DECODE_ENOMEM (-2) /* workspace allocation failed */
 #define ATTN_DECODE_EHIP (-3)   /* a HIP runtime call or kernel launch failed */
 
-/* Largest number of slots one partial/combine launch covers; more slots are
- * split into several launch groups inside one call. */
+/* Largest number of slots one kernel launch covers; more slots are split
+ * into several launch groups inside one call. */
 #define ATTN_DECODE_MAX_SLOTS_PER_LAUNCH 64
 /* Upper bound of KV chunks per slot; the planner widens chunks to stay below. */
 #define ATTN_DECODE_MAX_CHUNKS 4096
@@ -97,10 +102,18 @@ typedef struct attn_decode_options {
      * and by the chunking-invariance tests (cf. tessl nn.rs,
      * flash_attn_decode_with_chunk). */
     int32_t chunk;
-    int32_t reserved0;
+    /* How a slot split over several chunks is merged: 0 = automatic (today
+     * the combine kernel, the faster of the two on MI355X), 1 = the separate
+     * combine kernel, 2 = in-kernel: slots with at most 256 chunks are merged
+     * inside the partial kernel by the last workgroup of each (slot, KV head)
+     * to finish (one launch per call), longer ones by the combine kernel.
+     * Results of the modes differ only in rounding; within one mode batched
+     * equals per-slot bitwise. */
+    int32_t merge_mode;
     /* hipEvent_t handles (as void*) recorded on the stream immediately before
      * the first partial-kernel launch and immediately after the last one, or
-     * NULL.  They bracket the partial (KV-streaming) kernels alone. */
+     * NULL.  They bracket the partial (KV-streaming) kernels, including the
+     * in-kernel merges, and exclude the combine kernel. */
     void *ev_partial_begin;
     void *ev_partial_end;
 } attn_decode_options;

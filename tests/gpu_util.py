@@ -17,13 +17,14 @@ def to_device(inp, dev="cuda:0"):
             None if inp.v_scales is None else inp.v_scales.to(d))
 
 
-def run_gpu(inp, window, chunk=0, dev_tensors=None, stream=None, poison=True):
+def run_gpu(inp, window, chunk=0, dev_tensors=None, stream=None, poison=True, merge_mode=0):
     q, k, v, vs = dev_tensors if dev_tensors is not None else to_device(inp)
     out = torch.empty((inp.n_slots, inp.n_q_heads, inp.head_dim), dtype=torch.float32, device=q.device)
     if poison:
         out.fill_(float("nan"))
     binding.attn_decode_ex(q, k, v, vs, inp.seq_lens, window, out, inp.n_slots, inp.n_q_heads,
-                           inp.n_kv_heads, inp.head_dim, inp.scale, stream=stream, chunk=chunk)
+                           inp.n_kv_heads, inp.head_dim, inp.scale, stream=stream, chunk=chunk,
+                           merge_mode=merge_mode)
     torch.cuda.synchronize()
     return out
 

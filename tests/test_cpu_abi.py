@@ -65,6 +65,7 @@ def test_plan_chunks_cover_each_attended_range(seq, W):
             assert (n - 1) * c < span <= n * c  # chunks tile [lo, L), only the last is short
     assert p["partial_workgroups"] == sum(p["n_chunks"]) * 8
     rows = sum(16 * n for n in p["n_chunks"] if n > 1)
+    # the planner query reports the automatic merge mode: combine kernel, no counters
     assert p["workspace_bytes"] == rows * (256 + 2) * 4
 
 

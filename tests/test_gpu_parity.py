@@ -96,14 +96,26 @@ def test_edge_cases(case):
             assert np.all(got[s] == 0.0)
 
 
+@pytest.mark.parametrize("merge_mode", [0, 2])
 @pytest.mark.parametrize("chunk", [1, 3, 16, 64, 200, 5000])
 @pytest.mark.parametrize("i8", [False, True])
-def test_chunking_changes_only_rounding(chunk, i8):
+def test_chunking_changes_only_rounding(chunk, i8, merge_mode):
+    # chunk 3 splits the slots into 1001 / 234 / 1 chunks: in the in-kernel merge
+    # mode the first still goes through the combine kernel, the second does not
     seq = (3001, 700, 1)
     inp = make_inputs(seq, 8, 4, 256, i8, seed_base=7100)
     ref = run_oracle(inp, 0)
-    got = run_gpu(inp, 0, chunk=chunk).cpu().numpy()
-    _report(f"chunk {chunk} int8={i8}", assert_parity(got, ref, f"chunk={chunk}"))
+    got = run_gpu(inp, 0, chunk=chunk, merge_mode=merge_mode).cpu().numpy()
+    _report(f"chunk {chunk} int8={i8} merge={merge_mode}", assert_parity(got, ref, f"chunk={chunk}"))
+
+
+@pytest.mark.parametrize("D,nq,nkv", [(64, 4, 1), (128, 8, 2), (256, 16, 2), (512, 4, 4), (512, 16, 4)])
+def test_in_kernel_merge_every_geometry(D, nq, nkv):
+    # every (head_dim, heads per workgroup) layout of the in-kernel merge, at 256 chunks
+    inp = make_inputs((256 * 5 + 3, 70), nq, nkv, D, D % 32 == 0 and nq == 16, seed_base=7150 + D + nq)
+    ref = run_oracle(inp, 0)
+    got = run_gpu(inp, 0, chunk=5, merge_mode=2).cpu().numpy()
+    _report(f"merge geometry D={D} G={nq // nkv}", assert_parity(got, ref, f"D={D}"))
 
 
 def test_single_key_is_exact():
@@ -143,36 +155,39 @@ def _slot_inputs(inp, s):
 
 
 @pytest.mark.parametrize("i8", [False, True])
-def test_batched_equals_per_slot_bitwise(i8):
-    seq = (1024, 8192, 0, 2000, 1, 333)
+@pytest.mark.parametrize("merge_mode", [0, 2])
+def test_batched_equals_per_slot_bitwise(i8, merge_mode):
+    seq = (1024, 8192, 0, 2000, 1, 333, 40000)
     inp = make_inputs(seq, 16, 8, 256, i8, seed_base=7500)
     for W in (0, 700):
-        batched = run_gpu(inp, W)
+        batched = run_gpu(inp, W, merge_mode=merge_mode)
         for s in range(len(seq)):
-            solo = run_gpu(_slot_inputs(inp, s), W)
+            solo = run_gpu(_slot_inputs(inp, s), W, merge_mode=merge_mode)
             assert torch.equal(batched[s:s + 1], solo), (W, s)
 
 
-def test_run_to_run_bitwise_determinism():
+@pytest.mark.parametrize("merge_mode", [0, 2])
+def test_run_to_run_bitwise_determinism(merge_mode):
     inp = make_inputs((5000, 1234, 77), 16, 8, 256, True, seed_base=7600)
     dev = to_device(inp)
-    a = run_gpu(inp, 0, dev_tensors=dev)
-    b = run_gpu(inp, 0, dev_tensors=dev)
+    a = run_gpu(inp, 0, dev_tensors=dev, merge_mode=merge_mode)
+    b = run_gpu(inp, 0, dev_tensors=dev, merge_mode=merge_mode)
     assert torch.equal(a, b)
 
 
-def test_recycled_workspace_is_never_read_stale():
+@pytest.mark.parametrize("merge_mode", [0, 2])
+def test_recycled_workspace_is_never_read_stale(merge_mode):
     # A long call with a NaN query leaves NaN partials all over the workspace;
     # shorter and longer calls afterwards must not read any of them.
     long_nan = make_inputs((20000, 9000), 16, 8, 256, False, seed_base=7700)
     long_nan.q[:] = float("nan")
-    run_gpu(long_nan, 0)
+    run_gpu(long_nan, 0, merge_mode=merge_mode)
     for seq, seed in (((3000,), 7701), ((600, 20000), 7702), ((9000, 100, 5), 7703)):
         inp = make_inputs(seq, 16, 8, 256, False, seed_base=seed)
-        got = run_gpu(inp, 0).cpu().numpy()
+        got = run_gpu(inp, 0, merge_mode=merge_mode).cpu().numpy()
         ref = run_oracle(inp, 0)
         assert_parity(got, ref, f"after NaN workspace {seq}")
-        run_gpu(long_nan, 0)
+        run_gpu(long_nan, 0, merge_mode=merge_mode)
 
 
 def test_side_stream():
