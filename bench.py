@@ -17,14 +17,18 @@ each slot's attended range, read once:
 
 One JSON line is printed.  Besides the contract fields it carries
   * ``roofline``: the partial kernel's algorithmic bytes / its average launch
-    duration (HIP events recorded by the library around the partial launch, on
-    the call's stream, inside the timed region) against the 8 TB/s HBM peak,
-    and ``traffic`` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary
-    when that summary was taken on the current kernel source, else null;
+    duration against the 8 TB/s HBM peak.  The duration comes from HIP event
+    pairs that the library records around the partial-kernel launch, on the
+    call's stream, on every ``--event-every``-th step of the timed region (an
+    event between two kernels leaves the GPU idle for several microseconds, so
+    they are not recorded on every step).  ``traffic`` comes from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary when that summary was taken on
+    the current kernel source, else null;
   * ``cpu_baseline``: the CPU fp64 oracle timed on a bounded sample of the same
     workload on this host's cores;
-  * ``per_config``: every workload preset, cold (a 1 GiB cache-flush read
-    before each timed call) and warm (back-to-back calls).
+  * ``per_config``: every workload preset, warm (back-to-back calls, wall clock
+    between device synchronisations) and cold (the same with a 1 GiB read of
+    another buffer before every call, minus the time of those reads alone).
 """
 from __future__ import annotations
 
@@ -86,7 +90,9 @@ def parse_args(argv=None):
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--quick", action="store_true", help="headline workload only (no per_config, no cpu_baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--reps", type=int, default=50, help="timed reps per preset for per_config")
+    ap.add_argument("--reps", type=int, default=50, help="calls per timing sample for per_config")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="time the partial kernel with HIP events on every N-th timed step")
     ap.add_argument("--chunk", type=int, default=0, help="forced chunk size (tuning only)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), to scale "
@@ -166,16 +172,23 @@ def main(argv=None) -> int:
         call(inp, tens, out, window)
     torch.cuda.synchronize()
 
-    evs = [(new_event(), new_event()) for _ in range(args.steps)]
+    # Event pairs around the partial kernel on every `event_every`-th step only:
+    # each event between kernels idles the GPU for several microseconds, so
+    # recording them on every step would slow the steps being timed.
+    sampled = set(range(0, args.steps, max(1, args.event_every)))
+    evs = {i: (new_event(), new_event()) for i in sampled}
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        call(inp, tens, out, window, e0, e1)
+    for i in range(args.steps):
+        if i in evs:
+            call(inp, tens, out, window, *evs[i])
+        else:
+            call(inp, tens, out, window)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    partial_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    partial_ms = [e0.elapsed_time(e1) for e0, e1 in evs.values()]
     partial_avg_s = statistics.fmean(partial_ms) * 1e-3
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / partial_avg_s / 1e9
@@ -219,6 +232,7 @@ def main(argv=None) -> int:
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "avg_launch_us": round(partial_avg_s * 1e6, 2),
+            "launches_timed": len(partial_ms),
             "algorithmic_bytes_per_launch": nbytes,
         },
     }
@@ -240,40 +254,48 @@ def main(argv=None) -> int:
                 nb = kv_bytes(pin.seq_lens, W, pin.n_kv_heads, pin.head_dim, pin.v_int8)
                 for _ in range(3):
                     call(pin, ptens, pout, W)
-                cold = []
-                pk = []
-                for _ in range(args.reps):
-                    flush.sum()  # read 1 GiB: evicts the inputs, leaves no dirty lines
-                    a, b, c0, c1 = new_event(), new_event(), new_event(), new_event()
-                    a.record(stream)
-                    call(pin, ptens, pout, W, c0, c1)
-                    b.record(stream)
+
+                def per_call_us(fn, n):
                     torch.cuda.synchronize()
-                    cold.append(a.elapsed_time(b) * 1e3)
-                    pk.append(c0.elapsed_time(c1) * 1e3)
-                warm_n = max(args.reps, 20)
-                torch.cuda.synchronize()
-                a, b = new_event(), new_event()
-                a.record(stream)
-                for _ in range(warm_n):
+                    t0 = time.perf_counter()
+                    for _ in range(n):
+                        fn()
+                    torch.cuda.synchronize()
+                    return (time.perf_counter() - t0) * 1e6 / n
+
+                def one_call():
                     call(pin, ptens, pout, W)
-                b.record(stream)
-                torch.cuda.synchronize()
-                warm = a.elapsed_time(b) * 1e3 / warm_n
-                med = statistics.median(cold)
+
+                def flush_only():
+                    flush.sum()  # reads 1 GiB: evicts the inputs, leaves no dirty lines
+
+                def flush_then_call():
+                    flush.sum()
+                    call(pin, ptens, pout, W)
+
+                warm = statistics.median(per_call_us(one_call, args.reps) for _ in range(3))
+                cold_samples = [per_call_us(flush_then_call, args.reps) - per_call_us(flush_only, args.reps)
+                                for _ in range(5)]
+                cold = statistics.median(cold_samples)
+                pk = []
+                for _ in range(5):
+                    c0, c1 = new_event(), new_event()
+                    call(pin, ptens, pout, W, c0, c1)
+                    torch.cuda.synchronize()
+                    pk.append(c0.elapsed_time(c1) * 1e3)
                 per.append({
                     "workload": w.name, "window": W, "kv_bytes": nb,
-                    "cold_us_median": round(med, 2),
-                    "cold_us_p10": round(float(np.percentile(cold, 10)), 2),
-                    "cold_us_p90": round(float(np.percentile(cold, 90)), 2),
-                    "cold_gbs": round(nb / (med * 1e-6) / 1e9, 1),
-                    "cold_hbm_frac": round(nb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                    "partial_kernel_us_median": round(statistics.median(pk), 2),
                     "warm_us_per_call": round(warm, 2),
                     "warm_gbs": round(nb / (warm * 1e-6) / 1e9, 1),
+                    "warm_hbm_frac": round(nb / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "cold_us_per_call": round(cold, 2),
+                    "cold_gbs": round(nb / (cold * 1e-6) / 1e9, 1),
+                    "cold_hbm_frac": round(nb / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "cold_us_samples": [round(x, 2) for x in cold_samples],
+                    "partial_kernel_us_median": round(statistics.median(pk), 2),
                 })
-                print(f"[bench] {w.name} W={W}: cold {med:.2f} us ({per[-1]['cold_gbs']} GB/s), "
-                      f"warm {warm:.2f} us", file=sys.stderr, flush=True)
+                print(f"[bench] {w.name} W={W}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), "
+                      f"cold {cold:.2f} us ({per[-1]['cold_gbs']} GB/s)", file=sys.stderr, flush=True)
             if w.name != cfg.name:
                 del ptens
                 torch.cuda.empty_cache()

@@ -229,12 +229,12 @@ int run(const void *q, const void *k_cache, const void *v_cache, const void *v_s
     args.scale_log2 = (float)scale_log2;
 
     auto fill = [&](const LaunchGroup &lg) {
-        args.n_slots = lg.slot_end - lg.slot_begin;
-        args.slot0 = lg.slot_begin;
+        args.n_slots = (int32_t)lg.slots.size();
         int32_t item = 0, comb = 0;
-        for (int s = lg.slot_begin; s < lg.slot_end; ++s) {
+        for (size_t i = 0; i < lg.slots.size(); ++i) {
+            const int32_t s = lg.slots[i];
             const SlotPlan &sp = plan.slots[s];
-            SlotDesc &sd = args.slot[s - lg.slot_begin];
+            SlotDesc &sd = args.slot[i];
             sd.kv_row0 = sp.kv_row0;
             sd.part_row0 = sp.part_row0;
             sd.L = sp.L;
@@ -244,6 +244,7 @@ int run(const void *q, const void *k_cache, const void *v_cache, const void *v_s
             sd.item_begin = item;
             sd.comb_begin = comb;
             sd.cnt_base = sp.cnt_base;
+            sd.slot_idx = s;
             item += n_kv * plan.n_sub * sp.n_chunks;
             if (sp.n_chunks > 1 && !sp.fused) comb += n_q;
         }

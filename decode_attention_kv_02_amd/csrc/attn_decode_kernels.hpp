@@ -50,7 +50,7 @@ struct SlotDesc {
     int32_t item_begin; // first partial workgroup of the slot in this launch
     int32_t comb_begin; // first combine-kernel row of the slot in this launch
     int32_t cnt_base;   // first arrival counter of the slot (in-kernel merge)
-    int32_t pad0;
+    int32_t slot_idx;   // index of the slot in the call (q / out rows)
 };
 
 struct LaunchArgs {
@@ -62,8 +62,8 @@ struct LaunchArgs {
     float *ws_o;            // partial O rows [part_rows][D]
     float *ws_ml;           // partial (M, S) [part_rows][2]
     uint32_t *counters;     // arrival counters of in-kernel merges, zero between calls
-    int32_t n_slots;        // slots in this launch
-    int32_t slot0;          // global index of the launch's first slot
+    int32_t n_slots;        // slots in this launch (table entries, longest chunks first)
+    int32_t pad0;
     int32_t n_q;
     int32_t G;              // query heads per kv head
     int32_t n_sub;          // G / GB
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     const int cbeg = sd.lo + c * sd.chunk;
     const int cend = min(cbeg + sd.chunk, sd.L);
     const int h0 = kvh * args.G + sub * GB;            // first query head of the block (in the slot)
-    const int64_t slot_g = (int64_t)args.slot0 + si;  // global slot index
+    const int64_t slot_g = sd.slot_idx;
     const int64_t rowbase = sd.kv_row0 + (int64_t)kvh * sd.L;
 
     const int tid = threadIdx.x;
@@ -518,11 +518,15 @@ constexpr int kCombineMaxChunks = 4096;
 
 // Dims of one output row merged by one combine workgroup.
 constexpr int kCombineDims = 64;
+// Partial rows each combine thread loads before the chunk weights are known.
+constexpr int kCombinePreload = 4;
 
 // One workgroup per (slot, query head, 64-dim slice).  16 groups of 16
 // threads split the chunks; each thread owns 4 dims (16-byte loads of the
-// partial rows, coalesced over the 16 threads) and sums its share of the
-// chunks; the 16 group sums are added in LDS in a fixed order.
+// partial rows, coalesced over the 16 threads).  The first loads of the
+// partial rows are issued together with the loads of the chunk statistics,
+// so the merge costs about one memory round trip; the 16 group sums are added
+// in LDS in a fixed order.
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const LaunchArgs args) {
     constexpr int SLICES = D / kCombineDims;
@@ -539,13 +543,26 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const LaunchArgs
     const int h = row - sd.comb_begin;
     const int nc = sd.n_chunks;
     const int64_t base = sd.part_row0 + (int64_t)h * nc;
-    const int64_t slot_g = (int64_t)args.slot0 + si;
+    const int64_t slot_g = sd.slot_idx;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
+    const int cg = tid / TPR;
+    const int j = tid - cg * TPR;
+    const int d0 = slice * kCombineDims + 4 * j;
+    const float *src = args.ws_o + base * D + d0;
+    const float *ml = args.ws_ml + base * 2;
+
+    // partial rows of this thread's first chunks (independent of the weights)
+    float4 pre[kCombinePreload];
+#pragma unroll
+    for (int u = 0; u < kCombinePreload; ++u) {
+        const int c = cg + u * CG;
+        pre[u] = c < nc ? *(const float4 *)(src + (int64_t)c * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 
     // M* over chunks
     float mx = -INFINITY;
-    for (int c = tid; c < nc; c += kThreads) mx = fmaxf(mx, args.ws_ml[(base + c) * 2]);
+    for (int c = tid; c < nc; c += kThreads) mx = fmaxf(mx, ml[2 * c]);
     mx = wave_max(mx);
     if ((tid & 63) == 0) s_red[w] = mx;
     __syncthreads();
@@ -558,9 +575,9 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const LaunchArgs
     // chunk weights 2^(M_c - M*) and S*
     float ls = 0.f;
     for (int c = tid; c < nc; c += kThreads) {
-        const float wc = fast_exp2(args.ws_ml[(base + c) * 2] - ms);
+        const float wc = fast_exp2(ml[2 * c] - ms);
         s_w[c] = wc;
-        ls += wc * args.ws_ml[(base + c) * 2 + 1];
+        ls += wc * ml[2 * c + 1];
     }
     ls = wave_sum(ls);
     if ((tid & 63) == 0) s_red[w] = ls;
@@ -569,13 +586,20 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const LaunchArgs
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) lsum += s_red[ww];
 
-    // weighted sum of the partial O rows over this thread's chunks
-    const int cg = tid / TPR;
-    const int j = tid - cg * TPR;
-    const int d0 = slice * kCombineDims + 4 * j;
-    const float *src = args.ws_o + base * D + d0;
+    // weighted sum of the partial O rows over this thread's chunks, in chunk order
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int c = cg;
+#pragma unroll
+    for (int u = 0; u < kCombinePreload; ++u) {
+        const int c = cg + u * CG;
+        if (c < nc) {
+            const float wc = s_w[c];
+            acc.x = fmaf(wc, pre[u].x, acc.x);
+            acc.y = fmaf(wc, pre[u].y, acc.y);
+            acc.z = fmaf(wc, pre[u].z, acc.z);
+            acc.w = fmaf(wc, pre[u].w, acc.w);
+        }
+    }
+    int c = cg + kCombinePreload * CG;
     for (; c + 3 * CG < nc; c += 4 * CG) {
         float4 v[4];
 #pragma unroll

@@ -12,6 +12,7 @@
 // at most `chunk` positions (a flat list instead of a padded grid).
 #pragma once
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 #include <string>
@@ -40,7 +41,7 @@ struct SlotPlan {
 };
 
 struct LaunchGroup {
-    int slot_begin = 0, slot_end = 0;  // [begin, end) global slot indices
+    std::vector<int32_t> slots;        // slot indices, in work-list order
     int64_t items = 0;                 // partial-kernel workgroups
     int64_t combine_rows = 0;          // combine-kernel workgroups
 };
@@ -176,25 +177,31 @@ inline std::string make_plan(const int32_t *seq_lens, int32_t n_slots, int32_t w
     plan.workspace_bytes = counter_region_bytes(plan.n_counters) +
                            part * (int64_t)(head_dim + 2) * (int64_t)sizeof(float);
 
+    // Work-list order: longest chunks first (ties by slot index), so the
+    // longest workgroups start first and short ones fill the tail.  The order
+    // decides only which workgroup runs when, never a slot's arithmetic.
+    std::vector<int32_t> order(n_slots);
+    for (int32_t s = 0; s < n_slots; ++s) order[s] = s;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+        return plan.slots[a].chunk > plan.slots[b].chunk;
+    });
+
     // launch groups: at most kMaxSlotsPerLaunch slots and kMaxItemsPerLaunch workgroups
     LaunchGroup g;
-    g.slot_begin = 0;
-    for (int32_t s = 0; s < n_slots; ++s) {
+    for (int32_t s : order) {
         const SlotPlan &sp = plan.slots[s];
         const int64_t items = (int64_t)n_kv * plan.n_sub * sp.n_chunks;
         if (items > kMaxItemsPerLaunch) return "too many workgroups for one slot (n_kv_heads too large)";
-        const bool full = (s - g.slot_begin) >= kMaxSlotsPerLaunch || g.items + items > kMaxItemsPerLaunch;
+        const bool full = (int)g.slots.size() >= kMaxSlotsPerLaunch || g.items + items > kMaxItemsPerLaunch;
         if (full) {
-            g.slot_end = s;
             plan.groups.push_back(g);
             g = LaunchGroup();
-            g.slot_begin = s;
         }
+        g.slots.push_back(s);
         g.items += items;
         if (sp.n_chunks > 1 && !sp.fused) g.combine_rows += n_q;
     }
-    g.slot_end = n_slots;
-    if (n_slots > 0) plan.groups.push_back(g);
+    if (!g.slots.empty()) plan.groups.push_back(g);
     for (const LaunchGroup &lg : plan.groups) plan.total_items += lg.items;
     return "";
 }
