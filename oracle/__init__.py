@@ -12,5 +12,6 @@ from .oracle import (  # noqa: F401
     build_oracle,
     half_to_double,
     oracle_attn_decode,
+    oracle_attn_decode_cache,
     oracle_library_path,
 )

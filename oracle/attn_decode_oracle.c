@@ -39,6 +39,16 @@
  * [kv_head][pos][dim]; V codes are packed identically; V scales are laid out
  * [kv_head][pos][D/32] per slot, packed the same way.
  *
+ * Cache layout (fixed capacity, per query row): query row i reads cache slot
+ * slot_ids[i], whose K occupies rows [(slot * n_kv + kvh) * cap, ... + cap)
+ * for kv head kvh.  The query's token sits at absolute position
+ * positions[i], so it attends positions [lo, positions[i] + 1).  Linear
+ * storage keeps position p in row p (p < cap).  Ring storage keeps position p
+ * in row p mod cap, so only the last cap positions exist and
+ * lo >= positions[i] + 1 - cap (mlx-native flash_attn_vec_hybrid.metal,
+ * the batched kernels: kv_seq_len = min(pos + 1, capacity) for the ring,
+ * ring_start and the logical-to-physical row remap).
+ *
  * All arithmetic is IEEE double.  fp16 -> double is exact (decoded from the
  * bit pattern below).  Built without fast-math and without FP contraction.
  */
@@ -72,11 +82,17 @@ typedef struct {
     const uint16_t *k;
     const void *v;
     const uint16_t *v_scales; /* NULL => V is fp16 */
+    /* packed ragged slots */
     const int32_t *seq_lens;
     const int64_t *slot_first_pos; /* sum of L_t for t < s */
+    /* fixed-capacity cache (used when slot_ids != NULL) */
+    const int32_t *slot_ids;
+    const int32_t *positions;
+    int32_t capacity;
+    int32_t ring;
     int32_t window;
     double *out;
-    int32_t n_slots, n_q, n_kv, d;
+    int32_t n_slots, n_q, n_kv, d; /* n_slots: query rows (slots or cache queries) */
     double scale;
     const int32_t *rows; /* NULL => every (s, h) row in order */
     int64_t n_rows;
@@ -85,28 +101,17 @@ typedef struct {
     int status;
 } oracle_job;
 
-/* One output row (slot s, query head h) by the plain definition. */
-static int oracle_row(const oracle_job *jb, int64_t row, double *dst)
+/* Attention of one fp16 query over the cache rows row_idx[0..n) (row indices
+ * into the K / V-code arrays, in position order) by the plain definition. */
+static int oracle_attend(const oracle_job *jb, const uint16_t *qrow, const int64_t *row_idx,
+                         int64_t n, double *dst)
 {
-    const int32_t s = (int32_t)(row / jb->n_q);
-    const int32_t h = (int32_t)(row % jb->n_q);
     const int32_t D = jb->d;
-    const int32_t G = jb->n_q / jb->n_kv;
-    const int32_t kvh = h / G;
-    const int32_t L = jb->seq_lens[s];
-    const int32_t W = jb->window;
-    const int32_t lo = (W > 0 && L > W) ? L - W : 0;
-    const int32_t hi = L;
-
-    /* element index of row (s, kvh, pos 0) in the packed K / V-code arrays */
-    const int64_t kv_row0 = (int64_t)jb->n_kv * jb->slot_first_pos[s] + (int64_t)kvh * L;
-    const uint16_t *qrow = jb->q + ((int64_t)s * jb->n_q + h) * D;
-
     int d;
     for (d = 0; d < D; ++d) dst[d] = 0.0;
-    if (hi <= lo) return 0; /* empty range: zeros */
+    if (n <= 0) return 0; /* empty range: zeros */
 
-    double *x = (double *)malloc(sizeof(double) * (size_t)(hi - lo));
+    double *x = (double *)malloc(sizeof(double) * (size_t)n);
     double *qd = (double *)malloc(sizeof(double) * (size_t)D);
     double *acc = (double *)malloc(sizeof(double) * (size_t)D);
     if (!x || !qd || !acc) {
@@ -117,26 +122,26 @@ static int oracle_row(const oracle_job *jb, int64_t row, double *dst)
 
     /* pass 1: logits and their maximum */
     double m = -INFINITY;
-    int32_t j;
-    for (j = lo; j < hi; ++j) {
-        const uint16_t *krow = jb->k + (kv_row0 + j) * D;
+    int64_t j;
+    for (j = 0; j < n; ++j) {
+        const uint16_t *krow = jb->k + row_idx[j] * D;
         double dot = 0.0;
         for (d = 0; d < D; ++d) dot += qd[d] * oracle_half_to_double(krow[d]);
-        x[j - lo] = jb->scale * dot;
-        if (x[j - lo] > m) m = x[j - lo];
+        x[j] = jb->scale * dot;
+        if (x[j] > m) m = x[j];
     }
 
     /* pass 2: weights, their sum, and the weighted sum of dequantised V */
     double Z = 0.0;
-    for (j = lo; j < hi; ++j) {
-        const double w = exp(x[j - lo] - m);
+    for (j = 0; j < n; ++j) {
+        const double w = exp(x[j] - m);
         Z += w;
         if (jb->v_scales == NULL) {
-            const uint16_t *vrow = (const uint16_t *)jb->v + (kv_row0 + j) * D;
+            const uint16_t *vrow = (const uint16_t *)jb->v + row_idx[j] * D;
             for (d = 0; d < D; ++d) acc[d] += w * oracle_half_to_double(vrow[d]);
         } else {
-            const int8_t *vrow = (const int8_t *)jb->v + (kv_row0 + j) * D;
-            const uint16_t *srow = jb->v_scales + (kv_row0 + j) * (D / 32);
+            const int8_t *vrow = (const int8_t *)jb->v + row_idx[j] * D;
+            const uint16_t *srow = jb->v_scales + row_idx[j] * (D / 32);
             for (d = 0; d < D; ++d) {
                 const double vdq = (double)vrow[d] * oracle_half_to_double(srow[d / 32]);
                 acc[d] += w * vdq;
@@ -147,6 +152,43 @@ static int oracle_row(const oracle_job *jb, int64_t row, double *dst)
 
     free(x); free(qd); free(acc);
     return 0;
+}
+
+/* One output row (query row s, query head h): list the attended cache rows, then attend. */
+static int oracle_row(const oracle_job *jb, int64_t row, double *dst)
+{
+    const int32_t s = (int32_t)(row / jb->n_q);
+    const int32_t h = (int32_t)(row % jb->n_q);
+    const int32_t G = jb->n_q / jb->n_kv;
+    const int32_t kvh = h / G;
+    const int32_t W = jb->window;
+    const uint16_t *qrow = jb->q + ((int64_t)s * jb->n_q + h) * jb->d;
+    int64_t L, lo, base, p;
+
+    if (jb->slot_ids == NULL) {
+        /* packed ragged slots: position p of (s, kvh) is row n_kv * first[s] + kvh * L + p */
+        L = jb->seq_lens[s];
+        lo = (W > 0 && L > W) ? L - W : 0;
+        base = (int64_t)jb->n_kv * jb->slot_first_pos[s] + (int64_t)kvh * L;
+    } else {
+        /* fixed-capacity cache: position p of (slot, kvh) is row (slot*n_kv + kvh)*cap + phys(p) */
+        const int64_t cap = jb->capacity;
+        L = (int64_t)jb->positions[s] + 1;
+        lo = 0;
+        if (jb->ring && L > cap) lo = L - cap;
+        if (W > 0 && L - W > lo) lo = L - W;
+        base = ((int64_t)jb->slot_ids[s] * jb->n_kv + kvh) * cap;
+    }
+    int64_t *idx = (int64_t *)malloc(sizeof(int64_t) * (size_t)(L > lo ? L - lo : 1));
+    if (!idx) return -1;
+    for (p = lo; p < L; ++p) {
+        int64_t phys = p;
+        if (jb->slot_ids != NULL && jb->ring) phys = p % jb->capacity;
+        idx[p - lo] = base + phys;
+    }
+    const int rc = oracle_attend(jb, qrow, idx, L - lo, dst);
+    free(idx);
+    return rc;
 }
 
 static void *oracle_worker(void *arg)
@@ -163,8 +205,49 @@ static void *oracle_worker(void *arg)
     return NULL;
 }
 
+static int oracle_run(oracle_job *proto, int32_t n_threads)
+{
+    int t;
+    oracle_job *jobs = (oracle_job *)malloc(sizeof(oracle_job) * (size_t)n_threads);
+    pthread_t *tids = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
+    if (!jobs || !tids) {
+        free(jobs); free(tids);
+        return -2;
+    }
+    for (t = 0; t < n_threads; ++t) {
+        jobs[t] = *proto;
+        jobs[t].n_threads = n_threads;
+        jobs[t].thread_id = t;
+        jobs[t].status = 0;
+    }
+    int started = 0;
+    for (t = 1; t < n_threads; ++t) {
+        if (pthread_create(&tids[t], NULL, oracle_worker, &jobs[t]) != 0) break;
+        started = t;
+    }
+    /* threads that failed to start: run their share here */
+    for (t = started + 1; t < n_threads; ++t) oracle_worker(&jobs[t]);
+    oracle_worker(&jobs[0]);
+    for (t = 1; t <= started; ++t) pthread_join(tids[t], NULL);
+
+    int status = 0;
+    for (t = 0; t < n_threads; ++t)
+        if (jobs[t].status != 0) status = jobs[t].status;
+    free(jobs); free(tids);
+    return status;
+}
+
+static int check_rows(const int32_t *rows, int64_t n_rows, int64_t n_all)
+{
+    int64_t i;
+    if (rows == NULL) return 0;
+    for (i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= n_all) return -1;
+    return 0;
+}
+
 /*
- * oracle_attn_decode_f64
+ * oracle_attn_decode_f64 -- packed ragged slots
  *   q         fp16 bits [n_slots][n_q][D]
  *   k         fp16 bits, packed ragged [slot][n_kv][L_s][D]
  *   v         fp16 bits (v_scales == NULL) or int8 codes, same layout as k
@@ -183,7 +266,6 @@ int oracle_attn_decode_f64(const uint16_t *q, const uint16_t *k, const void *v,
                            const int32_t *rows, int64_t n_rows, int32_t n_threads)
 {
     int32_t s;
-    int t;
     if (n_slots < 0 || n_q <= 0 || n_kv <= 0 || head_dim <= 0 || window < 0) return -1;
     if (n_q % n_kv != 0) return -1;
     if (v_scales != NULL && head_dim % 32 != 0) return -1;
@@ -192,44 +274,64 @@ int oracle_attn_decode_f64(const uint16_t *q, const uint16_t *k, const void *v,
     if (n_rows == 0) return 0;
     for (s = 0; s < n_slots; ++s)
         if (seq_lens[s] < 0) return -1;
-    if (rows != NULL) {
-        int64_t i;
-        for (i = 0; i < n_rows; ++i)
-            if (rows[i] < 0 || rows[i] >= (int64_t)n_slots * n_q) return -1;
-    }
+    if (check_rows(rows, n_rows, (int64_t)n_slots * n_q) != 0) return -1;
 
     int64_t *first = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_slots + 1));
-    oracle_job *jobs = (oracle_job *)malloc(sizeof(oracle_job) * (size_t)n_threads);
-    pthread_t *tids = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)n_threads);
-    if (!first || !jobs || !tids) {
-        free(first); free(jobs); free(tids);
-        return -2;
-    }
+    if (!first) return -2;
     first[0] = 0;
     for (s = 0; s < n_slots; ++s) first[s + 1] = first[s] + seq_lens[s];
 
-    for (t = 0; t < n_threads; ++t) {
-        oracle_job *jb = &jobs[t];
-        jb->q = q; jb->k = k; jb->v = v; jb->v_scales = v_scales;
-        jb->seq_lens = seq_lens; jb->slot_first_pos = first; jb->window = window;
-        jb->out = out; jb->n_slots = n_slots; jb->n_q = n_q; jb->n_kv = n_kv;
-        jb->d = head_dim; jb->scale = (double)scale; jb->rows = rows;
-        jb->n_rows = n_rows; jb->n_threads = n_threads; jb->thread_id = t;
-        jb->status = 0;
-    }
-    int started = 0;
-    for (t = 1; t < n_threads; ++t) {
-        if (pthread_create(&tids[t], NULL, oracle_worker, &jobs[t]) != 0) break;
-        started = t;
-    }
-    /* threads that failed to start: run their share here */
-    for (t = started + 1; t < n_threads; ++t) oracle_worker(&jobs[t]);
-    oracle_worker(&jobs[0]);
-    for (t = 1; t <= started; ++t) pthread_join(tids[t], NULL);
-
-    int status = 0;
-    for (t = 0; t < n_threads; ++t)
-        if (jobs[t].status != 0) status = jobs[t].status;
-    free(first); free(jobs); free(tids);
+    oracle_job jb;
+    memset(&jb, 0, sizeof(jb));
+    jb.q = q; jb.k = k; jb.v = v; jb.v_scales = v_scales;
+    jb.seq_lens = seq_lens; jb.slot_first_pos = first; jb.window = window;
+    jb.out = out; jb.n_slots = n_slots; jb.n_q = n_q; jb.n_kv = n_kv;
+    jb.d = head_dim; jb.scale = (double)scale; jb.rows = rows; jb.n_rows = n_rows;
+    const int status = oracle_run(&jb, n_threads);
+    free(first);
     return status;
+}
+
+/*
+ * oracle_attn_decode_cache_f64 -- fixed-capacity (linear or ring) cache
+ *   q          fp16 bits [n_queries][n_q][D]
+ *   k          fp16 bits [n_cache_slots][n_kv][capacity][D]
+ *   v          fp16 bits (v_scales == NULL) or int8 codes, same layout as k
+ *   v_scales   fp16 bits [n_cache_slots][n_kv][capacity][D/32], or NULL
+ *   slot_ids   [n_queries], each in [0, n_cache_slots)
+ *   positions  [n_queries], each >= 0; < capacity when ring == 0
+ *   ring       0 = linear storage (row p), 1 = ring storage (row p mod capacity)
+ *   window     0 = every stored position, W > 0 = last W positions
+ *   out, rows, n_rows, n_threads as for oracle_attn_decode_f64 (row i = query * n_q + h)
+ */
+int oracle_attn_decode_cache_f64(const uint16_t *q, const uint16_t *k, const void *v,
+                                 const uint16_t *v_scales, const int32_t *slot_ids,
+                                 const int32_t *positions, int32_t n_queries,
+                                 int32_t n_cache_slots, int32_t capacity, int32_t ring,
+                                 int32_t window, double *out, int32_t n_q, int32_t n_kv,
+                                 int32_t head_dim, float scale, const int32_t *rows,
+                                 int64_t n_rows, int32_t n_threads)
+{
+    int32_t i;
+    if (n_queries < 0 || n_cache_slots < 0 || capacity <= 0 || n_q <= 0 || n_kv <= 0 ||
+        head_dim <= 0 || window < 0 || (ring != 0 && ring != 1))
+        return -1;
+    if (n_q % n_kv != 0) return -1;
+    if (v_scales != NULL && head_dim % 32 != 0) return -1;
+    if (n_threads < 1) n_threads = 1;
+    if (rows == NULL) n_rows = (int64_t)n_queries * n_q;
+    if (n_rows == 0) return 0;
+    for (i = 0; i < n_queries; ++i) {
+        if (slot_ids[i] < 0 || slot_ids[i] >= n_cache_slots) return -1;
+        if (positions[i] < 0 || (!ring && positions[i] >= capacity)) return -1;
+    }
+    if (check_rows(rows, n_rows, (int64_t)n_queries * n_q) != 0) return -1;
+
+    oracle_job jb;
+    memset(&jb, 0, sizeof(jb));
+    jb.q = q; jb.k = k; jb.v = v; jb.v_scales = v_scales;
+    jb.slot_ids = slot_ids; jb.positions = positions; jb.capacity = capacity; jb.ring = ring;
+    jb.window = window; jb.out = out; jb.n_slots = n_queries; jb.n_q = n_q; jb.n_kv = n_kv;
+    jb.d = head_dim; jb.scale = (double)scale; jb.rows = rows; jb.n_rows = n_rows;
+    return oracle_run(&jb, n_threads);
 }

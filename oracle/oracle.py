@@ -56,6 +56,13 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         lib.oracle_half_to_double.restype = ctypes.c_double
         lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_attn_decode_cache_f64.restype = ctypes.c_int
+        lib.oracle_attn_decode_cache_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+        ]
         lib.oracle_attn_decode_f64.restype = ctypes.c_int
         lib.oracle_attn_decode_f64.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -130,4 +137,58 @@ def oracle_attn_decode(q, k, v, v_scales, seq_lens, window, n_q, n_kv, head_dim,
     )
     if rc != 0:
         raise ValueError(f"oracle_attn_decode_f64 returned {rc}")
+    return out
+
+
+def oracle_attn_decode_cache(q, k, v, v_scales, slot_ids, positions, n_cache_slots, capacity, ring,
+                             window, n_q, n_kv, head_dim, scale, rows=None, threads=None) -> np.ndarray:
+    """Plain fp64 decode attention over a fixed-capacity (linear or ring) cache.
+
+    q: float16 [n_queries, n_q, D]; k: float16 [n_cache_slots, n_kv, capacity, D]
+    (any shape with that many elements); v: float16 or int8 like k; v_scales:
+    float16 [n_cache_slots, n_kv, capacity, D/32] or None.  Query i reads cache
+    slot ``slot_ids[i]`` and attends positions up to ``positions[i]``; linear
+    storage keeps position p in row p, ring storage in row p % capacity.
+    Returns float64 ``[n_queries, n_q, D]`` (or ``[len(rows), D]``).
+    """
+    lib = _load()
+    sid = np.ascontiguousarray(np.asarray(slot_ids, dtype=np.int32))
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    nqry = int(sid.shape[0])
+    if pos.shape[0] != nqry:
+        raise ValueError("slot_ids and positions differ in length")
+    q16 = _as_c(q, np.float16)
+    if q16.size != nqry * n_q * head_dim:
+        raise ValueError("q has the wrong number of elements")
+    total = int(n_cache_slots) * n_kv * int(capacity) * head_dim
+    k16 = _as_c(k, np.float16).reshape(-1)
+    if k16.size != total:
+        raise ValueError("k has the wrong number of elements")
+    if v_scales is None:
+        vv = _as_c(v, np.float16).reshape(-1)
+        sc = None
+    else:
+        vv = _as_c(v, np.int8).reshape(-1)
+        sc = _as_c(v_scales, np.float16).reshape(-1)
+        if sc.size != total // 32:
+            raise ValueError("v_scales has the wrong number of elements")
+    if vv.size != total:
+        raise ValueError("v has the wrong number of elements")
+    if rows is None:
+        rows_arr = None
+        n_rows = nqry * n_q
+        out = np.zeros((nqry, n_q, head_dim), dtype=np.float64)
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(list(rows), dtype=np.int32))
+        n_rows = int(rows_arr.shape[0])
+        out = np.zeros((n_rows, head_dim), dtype=np.float64)
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+    rc = lib.oracle_attn_decode_cache_f64(
+        _ptr(q16), _ptr(k16), _ptr(vv), _ptr(sc), _ptr(sid), _ptr(pos), nqry, int(n_cache_slots),
+        int(capacity), int(ring), int(window), _ptr(out), int(n_q), int(n_kv), int(head_dim),
+        float(scale), _ptr(rows_arr), n_rows, int(threads),
+    )
+    if rc != 0:
+        raise ValueError(f"oracle_attn_decode_cache_f64 returned {rc}")
     return out
