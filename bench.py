@@ -28,7 +28,11 @@ One JSON line is printed.  Besides the contract fields it carries
     workload on this host's cores;
   * ``per_config``: every workload preset, warm (back-to-back calls, wall clock
     between device synchronisations) and cold (the same with a 1 GiB read of
-    another buffer before every call, minus the time of those reads alone).
+    another buffer before every call, minus the time of those reads alone),
+    plus the fixed-capacity cache presets (``attn_decode_cache``: a
+    sliding-window ring layer and a speculative-verify shape; for the latter
+    ``kv_bytes`` counts what the kernels read, every query its own rows, and
+    ``unique_kv_bytes`` each cache row once).
 """
 from __future__ import annotations
 
@@ -57,6 +61,31 @@ def attended(L: int, window: int) -> int:
 def kv_bytes(seq_lens, window, n_kv, d, v_int8) -> int:
     per_row = 2 * d + (d + 2 * (d // 32) if v_int8 else 2 * d)
     return sum(attended(L, window) for L in seq_lens) * n_kv * per_row
+
+
+def cache_attended(pos: int, capacity: int, ring: int, window: int) -> int:
+    L = pos + 1
+    lo = L - capacity if (ring and L > capacity) else 0
+    if window > 0 and L - window > lo:
+        lo = L - window
+    return L - lo
+
+
+def cache_kv_bytes(cfg) -> tuple:
+    """(bytes the kernels read: every query reads its own attended rows,
+        unique bytes: each cache row counted once however many queries read it)."""
+    d = cfg.head_dim
+    per_row = 2 * d + (d + 2 * (d // 32) if cfg.v_int8 else 2 * d)
+    read = sum(cache_attended(p, cfg.capacity, cfg.ring, cfg.window)
+               for p in cfg.positions) * cfg.n_kv_heads * per_row
+    spans = {}
+    for sid, p in zip(cfg.slot_ids, cfg.positions):
+        L = p + 1
+        lo = L - cache_attended(p, cfg.capacity, cfg.ring, cfg.window)
+        a, b = spans.get(sid, (lo, L))
+        spans[sid] = (min(a, lo), max(b, L))
+    unique = sum(min(b - a, cfg.capacity) for a, b in spans.values()) * cfg.n_kv_heads * per_row
+    return read, unique
 
 
 def kernel_source_digest() -> str:
@@ -128,7 +157,8 @@ def main(argv=None) -> int:
     import torch
 
     from decode_attention_kv_02_amd import binding
-    from decode_attention_kv_02_amd.workloads import WORKLOADS, workload_inputs
+    from decode_attention_kv_02_amd.workloads import (CACHE_WORKLOADS, WORKLOADS, cache_workload_inputs,
+                                                      workload_inputs)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -299,6 +329,53 @@ def main(argv=None) -> int:
             if w.name != cfg.name:
                 del ptens
                 torch.cuda.empty_cache()
+
+        # fixed-capacity cache presets (attn_decode_cache)
+        for cw in CACHE_WORKLOADS:
+            print(f"[bench] generating {cw.name}", file=sys.stderr, flush=True)
+            ci = cache_workload_inputs(cw)
+            ct = upload(ci)
+            del ci.k, ci.v
+            cout = torch.empty((ci.n_queries, ci.n_q_heads, ci.head_dim), dtype=torch.float32, device=dev)
+
+            def cache_call(e0=None, e1=None):
+                binding.attn_decode_cache(*ct, ci.slot_ids, ci.positions, ci.n_queries, ci.n_cache_slots,
+                                          ci.capacity, ci.ring, cw.window, cout, ci.n_q_heads,
+                                          ci.n_kv_heads, ci.head_dim, ci.scale, stream=stream,
+                                          ev_partial_begin=e0.cuda_event if e0 is not None else None,
+                                          ev_partial_end=e1.cuda_event if e1 is not None else None)
+
+            def per_call_us(fn, n):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(n):
+                    fn()
+                torch.cuda.synchronize()
+                return (time.perf_counter() - t0) * 1e6 / n
+
+            def flush_then_cache_call():
+                flush.sum()
+                cache_call()
+
+            for _ in range(3):
+                cache_call()
+            read_b, uniq_b = cache_kv_bytes(cw)
+            warm = statistics.median(per_call_us(cache_call, args.reps) for _ in range(3))
+            cold = statistics.median(per_call_us(flush_then_cache_call, args.reps) -
+                                     per_call_us(lambda: flush.sum(), args.reps) for _ in range(5))
+            per.append({
+                "workload": cw.name, "window": cw.window, "kv_bytes": read_b, "unique_kv_bytes": uniq_b,
+                "warm_us_per_call": round(warm, 2),
+                "warm_gbs": round(read_b / (warm * 1e-6) / 1e9, 1),
+                "warm_hbm_frac": round(read_b / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "cold_us_per_call": round(cold, 2),
+                "cold_gbs": round(read_b / (cold * 1e-6) / 1e9, 1),
+                "cold_hbm_frac": round(read_b / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            })
+            print(f"[bench] {cw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), cold {cold:.2f} us",
+                  file=sys.stderr, flush=True)
+            del ct
+            torch.cuda.empty_cache()
         result["per_config"] = per
 
     # ---- CPU fp64 oracle on a bounded sample of the headline workload

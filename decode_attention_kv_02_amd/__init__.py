@@ -8,6 +8,7 @@ first call does, and raises if it is missing (there is no fallback).
 from .binding import (  # noqa: F401
     AttnDecodeError,
     attn_decode,
+    attn_decode_cache,
     attn_decode_ex,
     attn_decode_plan,
     attn_decode_release,

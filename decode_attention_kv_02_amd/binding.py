@@ -27,6 +27,7 @@ ATTN_DECODE_EHIP = -3
 
 EXPORTED_SYMBOLS = (
     "attn_decode",
+    "attn_decode_cache",
     "attn_decode_ex",
     "attn_decode_plan",
     "attn_decode_last_error",
@@ -76,6 +77,12 @@ def load_library():
         lib.attn_decode.argtypes = common
         lib.attn_decode_ex.restype = ctypes.c_int
         lib.attn_decode_ex.argtypes = common + [ctypes.POINTER(_Options)]
+        lib.attn_decode_cache.restype = ctypes.c_int
+        lib.attn_decode_cache.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(_Options)]
         lib.attn_decode_plan.restype = ctypes.c_int
         lib.attn_decode_plan.argtypes = [
             ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -178,9 +185,53 @@ def attn_decode_ex(q, k_cache, v_cache, v_scales, seq_lens, window: int, out,
         _raise(lib, rc)
 
 
+def attn_decode_cache(q, k_cache, v_cache, v_scales, slot_ids, positions, n_queries: Optional[int],
+                      n_cache_slots: int, capacity: int, ring: int, window: int, out, n_q_heads: int,
+                      n_kv_heads: int, head_dim: int, scale: float, stream=None, chunk: int = 0,
+                      merge_mode: int = 0, ev_partial_begin: Optional[int] = None,
+                      ev_partial_end: Optional[int] = None) -> None:
+    """Enqueue decode attention over a fixed-capacity (linear or ring) cache."""
+    lib = load_library()
+    sid, n = _seq_array(slot_ids)
+    pos, n2 = _seq_array(positions)
+    if n_queries is None:
+        n_queries = n
+    if n != n_queries or n2 != n_queries:
+        raise ValueError("slot_ids / positions do not match n_queries")
+    if not isinstance(out, torch.Tensor) or out.device.type != "cuda":
+        raise ValueError("out must be a CUDA tensor")
+    dev = out.device.index
+    kv = int(n_cache_slots) * int(n_kv_heads) * int(capacity) * int(head_dim)
+    int8 = v_scales is not None
+    pq = _dev_ptr(q, "q", torch.float16, n_queries * n_q_heads * head_dim, dev)
+    pk = _dev_ptr(k_cache, "k_cache", torch.float16, kv, dev)
+    pv = _dev_ptr(v_cache, "v_cache", torch.int8 if int8 else torch.float16, kv, dev)
+    ps = _dev_ptr(v_scales, "v_scales", torch.float16, kv // 32, dev) if int8 else None
+    po = _dev_ptr(out, "out", torch.float32, n_queries * n_q_heads * head_dim, dev)
+    opts = _Options(int(chunk), int(merge_mode), ev_partial_begin or None, ev_partial_end or None)
+    rc = lib.attn_decode_cache(pq, pk, pv, ps, sid, pos, int(n_queries), int(n_cache_slots),
+                               int(capacity), int(ring), int(window), po, int(n_q_heads),
+                               int(n_kv_heads), int(head_dim), float(scale),
+                               _stream_handle(stream, dev), ctypes.byref(opts))
+    if rc != ATTN_DECODE_OK:
+        _raise(lib, rc)
+
+
+def attn_decode_cache_raw(q_ptr, k_ptr, v_ptr, vs_ptr, slot_ids, positions, n_queries, n_cache_slots,
+                          capacity, ring, window, out_ptr, n_q_heads, n_kv_heads, head_dim, scale,
+                          stream_ptr=None) -> int:
+    """Direct call with raw pointers (tests of the C-side validation); returns the C return code."""
+    lib = load_library()
+    sid, _ = _seq_array(slot_ids)
+    pos, _ = _seq_array(positions)
+    return lib.attn_decode_cache(q_ptr, k_ptr, v_ptr, vs_ptr, sid, pos, int(n_queries), int(n_cache_slots),
+                                 int(capacity), int(ring), int(window), out_ptr, int(n_q_heads),
+                                 int(n_kv_heads), int(head_dim), float(scale), stream_ptr, None)
+
+
 def attn_decode_raw(q_ptr, k_ptr, v_ptr, vs_ptr, seq_lens, window, out_ptr, n_slots, n_q_heads,
                     n_kv_heads, head_dim, scale, stream_ptr=None) -> int:
-    """Direct call with raw pointers (no checks); returns the C return code."""
+    """Direct call with raw pointers (tests of the C-side validation); returns the C return code."""
     lib = load_library()
     seq_arr, _ = _seq_array(seq_lens)
     return lib.attn_decode(q_ptr, k_ptr, v_ptr, vs_ptr, seq_arr, int(window), out_ptr, int(n_slots),

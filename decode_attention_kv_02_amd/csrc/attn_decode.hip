@@ -17,6 +17,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "../../include/attn_decode.h"
 #include "planner.hpp"
@@ -153,45 +154,16 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
     return x < y + nb && y < x + na;
 }
 
-int run(const void *q, const void *k_cache, const void *v_cache, const void *v_scales,
-        const int32_t *seq_lens, int32_t window, float *out, int32_t n_slots, int32_t n_q,
-        int32_t n_kv, int32_t D, float scale, void *stream_ptr, const attn_decode_options *opts) {
-    g_last_error.clear();
+// Everything after the layout-specific checks: plan, workspace, launches.
+int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cache,
+           const void *v_cache, const void *v_scales, float *out, int32_t n_q, int32_t n_kv,
+           int32_t D, float scale, void *stream_ptr, const attn_decode_options *opts) {
     const bool v_int8 = v_scales != nullptr;
     const int32_t chunk = opts ? opts->chunk : 0;
     const int32_t merge_mode = opts ? opts->merge_mode : 0;
 
-    std::string err = check_shapes(seq_lens, n_slots, window, n_q, n_kv, D, v_int8, chunk, merge_mode);
-    if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
-    if (!std::isfinite(scale)) return fail(ATTN_DECODE_EINVAL, "scale must be finite");
-    if (n_slots == 0) return ATTN_DECODE_OK;
-
-    // sizes (64-bit, overflow-checked)
-    uint64_t total_pos = 0;
-    for (int32_t s = 0; s < n_slots; ++s) total_pos += (uint64_t)seq_lens[s];
-    const uint64_t kv_elems = total_pos * (uint64_t)n_kv * (uint64_t)D;
-    if (total_pos > (uint64_t(1) << 40) || kv_elems > (uint64_t(1) << 46))
-        return fail(ATTN_DECODE_EINVAL, "KV cache too large");
-    const uint64_t q_bytes = (uint64_t)n_slots * n_q * D * 2;
-    const uint64_t out_bytes = (uint64_t)n_slots * n_q * D * 4;
-    const uint64_t k_bytes = kv_elems * 2;
-    const uint64_t v_bytes = kv_elems * (v_int8 ? 1 : 2);
-    const uint64_t s_bytes = v_int8 ? kv_elems / kQuantBlock * 2 : 0;
-
-    if (q == nullptr) return fail(ATTN_DECODE_EINVAL, "q is NULL");
-    if (out == nullptr) return fail(ATTN_DECODE_EINVAL, "out is NULL");
-    if (kv_elems > 0 && (k_cache == nullptr || v_cache == nullptr))
-        return fail(ATTN_DECODE_EINVAL, "k_cache / v_cache is NULL");
-    if (!aligned(q, 16) || !aligned(out, 16)) return fail(ATTN_DECODE_EINVAL, "q and out must be 16-byte aligned");
-    if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
-        return fail(ATTN_DECODE_EINVAL, "k_cache and v_cache must be 16-byte aligned");
-    if (v_int8 && !aligned(v_scales, 2)) return fail(ATTN_DECODE_EINVAL, "v_scales must be 2-byte aligned");
-    if (overlaps(out, out_bytes, q, q_bytes) || overlaps(out, out_bytes, k_cache, k_bytes) ||
-        overlaps(out, out_bytes, v_cache, v_bytes) || overlaps(out, out_bytes, v_scales, s_bytes))
-        return fail(ATTN_DECODE_EINVAL, "out overlaps an input");
-
     CallPlan plan;
-    err = make_plan(seq_lens, n_slots, window, n_q, n_kv, D, chunk, merge_mode, plan);
+    std::string err = make_plan(spans, n_q, n_kv, D, chunk, merge_mode, plan);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
 
     const partial_fn pk = select_partial(D, plan.GB, v_int8);
@@ -245,6 +217,10 @@ int run(const void *q, const void *k_cache, const void *v_cache, const void *v_s
             sd.comb_begin = comb;
             sd.cnt_base = sp.cnt_base;
             sd.slot_idx = s;
+            sd.kv_stride = sp.kv_stride;
+            sd.ring_cap = sp.ring_cap;
+            sd.ring_base = sp.ring_base;
+            sd.pad0 = 0;
             item += n_kv * plan.n_sub * sp.n_chunks;
             if (sp.n_chunks > 1 && !sp.fused) comb += n_q;
         }
@@ -275,6 +251,85 @@ int run(const void *q, const void *k_cache, const void *v_cache, const void *v_s
     return ATTN_DECODE_OK;
 }
 
+// Pointer checks shared by both layouts: NULLs, alignment, and out overlapping an input.
+int check_pointers(const void *q, const void *k_cache, const void *v_cache, const void *v_scales,
+                   const float *out, uint64_t n_rows_q, int32_t n_q, int32_t D, uint64_t kv_elems,
+                   bool v_int8) {
+    const uint64_t q_bytes = n_rows_q * n_q * D * 2;
+    const uint64_t out_bytes = n_rows_q * n_q * D * 4;
+    const uint64_t k_bytes = kv_elems * 2;
+    const uint64_t v_bytes = kv_elems * (v_int8 ? 1 : 2);
+    const uint64_t s_bytes = v_int8 ? kv_elems / kQuantBlock * 2 : 0;
+    if (q == nullptr) return fail(ATTN_DECODE_EINVAL, "q is NULL");
+    if (out == nullptr) return fail(ATTN_DECODE_EINVAL, "out is NULL");
+    if (kv_elems > 0 && (k_cache == nullptr || v_cache == nullptr))
+        return fail(ATTN_DECODE_EINVAL, "k_cache / v_cache is NULL");
+    if (!aligned(q, 16) || !aligned(out, 16)) return fail(ATTN_DECODE_EINVAL, "q and out must be 16-byte aligned");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return fail(ATTN_DECODE_EINVAL, "k_cache and v_cache must be 16-byte aligned");
+    if (v_int8 && !aligned(v_scales, 2)) return fail(ATTN_DECODE_EINVAL, "v_scales must be 2-byte aligned");
+    if (overlaps(out, out_bytes, q, q_bytes) || overlaps(out, out_bytes, k_cache, k_bytes) ||
+        overlaps(out, out_bytes, v_cache, v_bytes) || overlaps(out, out_bytes, v_scales, s_bytes))
+        return fail(ATTN_DECODE_EINVAL, "out overlaps an input");
+    return ATTN_DECODE_OK;
+}
+
+int run(const void *q, const void *k_cache, const void *v_cache, const void *v_scales,
+        const int32_t *seq_lens, int32_t window, float *out, int32_t n_slots, int32_t n_q,
+        int32_t n_kv, int32_t D, float scale, void *stream_ptr, const attn_decode_options *opts) {
+    g_last_error.clear();
+    const bool v_int8 = v_scales != nullptr;
+    const int32_t chunk = opts ? opts->chunk : 0;
+    const int32_t merge_mode = opts ? opts->merge_mode : 0;
+
+    std::string err = check_shapes(seq_lens, n_slots, window, n_q, n_kv, D, v_int8, chunk, merge_mode);
+    if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
+    if (!std::isfinite(scale)) return fail(ATTN_DECODE_EINVAL, "scale must be finite");
+    if (n_slots == 0) return ATTN_DECODE_OK;
+
+    // sizes (64-bit, overflow-checked)
+    uint64_t total_pos = 0;
+    for (int32_t s = 0; s < n_slots; ++s) total_pos += (uint64_t)seq_lens[s];
+    const uint64_t kv_elems = total_pos * (uint64_t)n_kv * (uint64_t)D;
+    if (total_pos > (uint64_t(1) << 40) || kv_elems > (uint64_t(1) << 46))
+        return fail(ATTN_DECODE_EINVAL, "KV cache too large");
+    int rc = check_pointers(q, k_cache, v_cache, v_scales, out, (uint64_t)n_slots, n_q, D, kv_elems, v_int8);
+    if (rc != ATTN_DECODE_OK) return rc;
+
+    std::vector<QuerySpan> spans;
+    spans_packed(seq_lens, n_slots, window, n_kv, spans);
+    return launch(spans, q, k_cache, v_cache, v_scales, out, n_q, n_kv, D, scale, stream_ptr, opts);
+}
+
+int run_cache(const void *q, const void *k_cache, const void *v_cache, const void *v_scales,
+              const int32_t *slot_ids, const int32_t *positions, int32_t n_queries,
+              int32_t n_cache_slots, int32_t capacity, int32_t ring, int32_t window, float *out,
+              int32_t n_q, int32_t n_kv, int32_t D, float scale, void *stream_ptr,
+              const attn_decode_options *opts) {
+    g_last_error.clear();
+    const bool v_int8 = v_scales != nullptr;
+    const int32_t chunk = opts ? opts->chunk : 0;
+    const int32_t merge_mode = opts ? opts->merge_mode : 0;
+
+    if (n_cache_slots < 0) return fail(ATTN_DECODE_EINVAL, "n_cache_slots must be >= 0");
+    std::string err = check_common(n_q, n_kv, D, v_int8, window, chunk, merge_mode);
+    if (err.empty()) err = check_cache(slot_ids, positions, n_queries, n_cache_slots, capacity, ring);
+    if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
+    if (!std::isfinite(scale)) return fail(ATTN_DECODE_EINVAL, "scale must be finite");
+    if (n_queries == 0) return ATTN_DECODE_OK;
+
+    const uint64_t rows = (uint64_t)n_cache_slots * (uint64_t)n_kv * (uint64_t)capacity;
+    const uint64_t kv_elems = rows * (uint64_t)D;
+    if (rows > (uint64_t(1) << 40) || kv_elems > (uint64_t(1) << 46))
+        return fail(ATTN_DECODE_EINVAL, "KV cache too large");
+    int rc = check_pointers(q, k_cache, v_cache, v_scales, out, (uint64_t)n_queries, n_q, D, kv_elems, v_int8);
+    if (rc != ATTN_DECODE_OK) return rc;
+
+    std::vector<QuerySpan> spans;
+    spans_cache(slot_ids, positions, n_queries, capacity, ring, window, n_kv, spans);
+    return launch(spans, q, k_cache, v_cache, v_scales, out, n_q, n_kv, D, scale, stream_ptr, opts);
+}
+
 }  // namespace
 
 // ============================================================ C ABI
@@ -296,6 +351,16 @@ extern "C" int attn_decode_ex(const void *q, const void *k_cache, const void *v_
                n_kv_heads, head_dim, scale, stream, opts);
 }
 
+extern "C" int attn_decode_cache(const void *q, const void *k_cache, const void *v_cache,
+                                 const void *v_scales, const int32_t *slot_ids,
+                                 const int32_t *positions, int32_t n_queries, int32_t n_cache_slots,
+                                 int32_t capacity, int32_t ring, int32_t window, float *out,
+                                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                                 void *stream, const attn_decode_options *opts) {
+    return run_cache(q, k_cache, v_cache, v_scales, slot_ids, positions, n_queries, n_cache_slots,
+                     capacity, ring, window, out, n_q_heads, n_kv_heads, head_dim, scale, stream, opts);
+}
+
 extern "C" int attn_decode_plan(const int32_t *seq_lens, int32_t n_slots, int32_t window,
                                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                                 int32_t v_int8, int32_t chunk, int32_t *chunk_keys,
@@ -306,7 +371,9 @@ extern "C" int attn_decode_plan(const int32_t *seq_lens, int32_t n_slots, int32_
                                    v_int8 != 0, chunk);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
     CallPlan plan;
-    err = make_plan(seq_lens, n_slots, window, n_q_heads, n_kv_heads, head_dim, chunk, kMergeAuto, plan);
+    std::vector<QuerySpan> spans;
+    spans_packed(seq_lens, n_slots, window, n_kv_heads, spans);
+    err = make_plan(spans, n_q_heads, n_kv_heads, head_dim, chunk, kMergeAuto, plan);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
     for (int32_t s = 0; s < n_slots; ++s) {
         if (chunk_keys) chunk_keys[s] = plan.slots[s].chunk;

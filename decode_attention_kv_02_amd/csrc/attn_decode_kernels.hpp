@@ -40,18 +40,24 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
+// One query row of a launch (a decode slot, or one query of a cache call).
 struct SlotDesc {
-    int64_t kv_row0;    // row (position) index of (slot, kv head 0, pos 0) in the packed cache
-    int64_t part_row0;  // first partial row of the slot, -1 when it has one chunk
-    int32_t L;          // slot length: row stride between kv heads of the slot
+    int64_t kv_row0;    // row of (slot, kv head 0, position-row 0) in the K / V arrays
+    int64_t part_row0;  // first partial row of the query, -1 when it has one chunk
+    int32_t L;          // one past the last attended position
     int32_t lo;         // first attended position
     int32_t chunk;      // positions per chunk
-    int32_t n_chunks;   // chunks of the slot
-    int32_t item_begin; // first partial workgroup of the slot in this launch
-    int32_t comb_begin; // first combine-kernel row of the slot in this launch
-    int32_t cnt_base;   // first arrival counter of the slot (in-kernel merge)
-    int32_t slot_idx;   // index of the slot in the call (q / out rows)
+    int32_t n_chunks;   // chunks of the query
+    int32_t item_begin; // first partial workgroup of the query in this launch
+    int32_t comb_begin; // first combine-kernel row of the query in this launch
+    int32_t cnt_base;   // first arrival counter of the query (in-kernel merge)
+    int32_t slot_idx;   // index of the query row in the call (q / out rows)
+    int32_t kv_stride;  // rows between consecutive kv heads
+    int32_t ring_cap;   // ring capacity, INT32_MAX when rows do not wrap
+    int32_t ring_base;  // position held by row 0 of the current ring lap (multiple of ring_cap)
+    int32_t pad0;
 };
+static_assert(sizeof(SlotDesc) == 64, "query descriptor layout");
 
 struct LaunchArgs {
     const uint16_t *q;      // fp16 [n_slots_total][n_q][D]
@@ -70,7 +76,7 @@ struct LaunchArgs {
     float scale_log2;       // scale * log2(e)
     int32_t n_items;
     int32_t fuse_limit;     // slots with 2..fuse_limit chunks merge inside the partial kernel
-    SlotDesc slot[64];
+    SlotDesc slot[48];
 };
 
 // ---------------------------------------------------------------- helpers
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     const int cend = min(cbeg + sd.chunk, sd.L);
     const int h0 = kvh * args.G + sub * GB;            // first query head of the block (in the slot)
     const int64_t slot_g = sd.slot_idx;
-    const int64_t rowbase = sd.kv_row0 + (int64_t)kvh * sd.L;
+    const int64_t rowbase = sd.kv_row0 + (int64_t)kvh * sd.kv_stride;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -300,7 +306,9 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int row = wb + u * P + rg;
-            const int rc = row < cend ? row : cend - 1;
+            // position -> row: clamp past the chunk end (masked below), then wrap the ring
+            int rc = (row < cend ? row : cend - 1) - sd.ring_base;
+            if (rc >= sd.ring_cap) rc -= sd.ring_cap;
             const uint16_t *kp = kbase + (int64_t)rc * D;
             f.ka[u] = load_stream16(kp + sl * 8);
             f.kb[u] = load_stream16(kp + HALF + sl * 8);

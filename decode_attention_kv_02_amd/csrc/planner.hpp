@@ -10,6 +10,13 @@
 // function of that slot's attended length alone, so batching slots never
 // changes any slot's result, and every workgroup of a launch does one chunk of
 // at most `chunk` positions (a flat list instead of a padded grid).
+//
+// Every query row is first described by a span: its attended positions
+// [lo, L), where its (slot, kv head 0) rows start, the row stride between kv
+// heads, and the ring wrap.  Packed ragged slots and fixed-capacity linear or
+// ring caches differ only in how the spans are made (mlx-native batched
+// kernels: per-slot offset slot * n_kv * capacity * D, kv_seq_len =
+// min(pos + 1, capacity) on the ring, physical row = position mod capacity).
 #pragma once
 
 #include <algorithm>
@@ -20,7 +27,7 @@
 
 namespace attn_decode_impl {
 
-constexpr int kMaxSlotsPerLaunch = 64;   // slot table passed by value in the kernel arguments
+constexpr int kMaxSlotsPerLaunch = 48;   // query table passed by value in the kernel arguments
 constexpr int kMaxChunks = 4096;         // per slot; bounds the combine kernel's LDS weights
 constexpr int kChunkQuantum = 64;        // chunk sizes are multiples of this (one workgroup iteration at D=256)
 constexpr int kChunkMin = 64;
@@ -28,13 +35,26 @@ constexpr int kChunkMax = 2048;
 constexpr int64_t kMaxItemsPerLaunch = int64_t(1) << 24;  // 2^24 workgroups x 256 threads < 2^32
 constexpr int kQuantBlock = 32;          // int8 V: dims per fp16 scale
 
+// Positions and rows one query row attends.
+struct QuerySpan {
+    int32_t L = 0;             // one past the last attended position
+    int32_t lo = 0;            // first attended position
+    int64_t kv_row0 = 0;       // row of (slot, kv head 0) holding position-row 0
+    int32_t kv_stride = 0;     // rows between consecutive kv heads of the slot
+    int32_t ring_cap = INT32_MAX;  // ring capacity (INT32_MAX: rows never wrap)
+    int32_t ring_base = 0;     // multiple of ring_cap <= lo: row of position p is p - ring_base (mod ring_cap)
+};
+
 struct SlotPlan {
-    int32_t L = 0;          // slot KV length
+    int32_t L = 0;          // one past the last attended position
     int32_t lo = 0;         // first attended position
     int32_t n = 0;          // attended positions (L - lo)
+    int32_t kv_stride = 0;
+    int32_t ring_cap = INT32_MAX;
+    int32_t ring_base = 0;
     int32_t chunk = 0;      // positions per chunk
     int32_t n_chunks = 1;   // >= 1 (an empty slot has one empty chunk)
-    int64_t kv_row0 = 0;    // n_kv * sum_{t<s} L_t : row of (slot, kv head 0, pos 0)
+    int64_t kv_row0 = 0;    // row of (slot, kv head 0, position-row 0)
     int64_t part_row0 = -1; // first partial row when n_chunks > 1, else -1
     bool fused = false;     // 2..fuse_limit chunks: merged inside the partial kernel
     int32_t cnt_base = 0;   // first arrival counter when fused
@@ -111,22 +131,85 @@ inline int64_t chunk_for(int64_t n, int32_t forced) {
 }
 
 // Shape checks shared by every entry point.  Returns "" when valid.
-inline std::string check_shapes(const int32_t *seq_lens, int32_t n_slots, int32_t window,
-                                int32_t n_q, int32_t n_kv, int32_t head_dim, bool v_int8,
-                                int32_t chunk, int32_t merge_mode = 0) {
-    if (n_slots < 0) return "n_slots must be >= 0";
+inline std::string check_common(int32_t n_q, int32_t n_kv, int32_t head_dim, bool v_int8,
+                                int32_t window, int32_t chunk, int32_t merge_mode) {
     if (merge_mode != kMergeAuto && merge_mode != kMergeCombineKernel && merge_mode != kMergeInKernel)
         return "unknown merge_mode";
-    if (n_slots > 0 && seq_lens == nullptr) return "seq_lens is NULL";
     if (n_q <= 0 || n_kv <= 0) return "n_q_heads and n_kv_heads must be positive";
     if (n_q % n_kv != 0) return "n_q_heads must be a multiple of n_kv_heads";
     if (!supported_head_dim(head_dim)) return "head_dim must be 64, 128, 256 or 512";
     if (v_int8 && head_dim % kQuantBlock != 0) return "int8 V needs head_dim % 32 == 0";
     if (window < 0) return "window must be >= 0";
     if (chunk < 0) return "chunk override must be >= 0";
+    return "";
+}
+
+inline std::string check_shapes(const int32_t *seq_lens, int32_t n_slots, int32_t window,
+                                int32_t n_q, int32_t n_kv, int32_t head_dim, bool v_int8,
+                                int32_t chunk, int32_t merge_mode = 0) {
+    if (n_slots < 0) return "n_slots must be >= 0";
+    std::string err = check_common(n_q, n_kv, head_dim, v_int8, window, chunk, merge_mode);
+    if (!err.empty()) return err;
+    if (n_slots > 0 && seq_lens == nullptr) return "seq_lens is NULL";
     for (int32_t s = 0; s < n_slots; ++s)
         if (seq_lens[s] < 0) return "seq_lens[" + std::to_string(s) + "] is negative";
     return "";
+}
+
+// Spans of packed ragged slots: slot s's rows follow those of slots t < s.
+inline void spans_packed(const int32_t *seq_lens, int32_t n_slots, int32_t window, int32_t n_kv,
+                         std::vector<QuerySpan> &spans) {
+    spans.assign(n_slots, QuerySpan());
+    int64_t rows = 0;   // running sum of L_t (positions)
+    for (int32_t s = 0; s < n_slots; ++s) {
+        QuerySpan &q = spans[s];
+        q.L = seq_lens[s];
+        q.lo = (window > 0 && q.L > window) ? q.L - window : 0;
+        q.kv_row0 = rows * n_kv;
+        q.kv_stride = q.L;
+        rows += q.L;
+    }
+}
+
+// Checks of the fixed-capacity cache entry point.  Returns "" when valid.
+inline std::string check_cache(const int32_t *slot_ids, const int32_t *positions, int32_t n_queries,
+                               int32_t n_cache_slots, int32_t capacity, int32_t ring) {
+    if (n_queries < 0) return "n_queries must be >= 0";
+    if (ring != 0 && ring != 1) return "ring must be 0 or 1";
+    if (capacity <= 0) return "capacity must be positive";
+    if (n_queries > 0 && (slot_ids == nullptr || positions == nullptr)) return "slot_ids / positions is NULL";
+    for (int32_t i = 0; i < n_queries; ++i) {
+        if (slot_ids[i] < 0 || slot_ids[i] >= n_cache_slots)
+            return "slot_ids[" + std::to_string(i) + "] is outside [0, n_cache_slots)";
+        if (positions[i] < 0) return "positions[" + std::to_string(i) + "] is negative";
+        if (positions[i] == INT32_MAX) return "positions[" + std::to_string(i) + "] is too large";
+        if (!ring && positions[i] >= capacity)
+            return "positions[" + std::to_string(i) + "] is not below the capacity of a linear cache";
+    }
+    return "";
+}
+
+// Spans of a [slot][kv head][capacity][D] cache: query i attends positions up to
+// positions[i] of cache slot slot_ids[i]; linear storage keeps position p in row
+// p, ring storage in row p mod capacity (only the last `capacity` positions).
+inline void spans_cache(const int32_t *slot_ids, const int32_t *positions, int32_t n_queries,
+                        int32_t capacity, int32_t ring, int32_t window, int32_t n_kv,
+                        std::vector<QuerySpan> &spans) {
+    spans.assign(n_queries, QuerySpan());
+    for (int32_t i = 0; i < n_queries; ++i) {
+        QuerySpan &q = spans[i];
+        q.L = positions[i] + 1;
+        int32_t lo = 0;
+        if (ring && q.L > capacity) lo = q.L - capacity;
+        if (window > 0 && q.L - window > lo) lo = q.L - window;
+        q.lo = lo;
+        q.kv_row0 = (int64_t)slot_ids[i] * n_kv * capacity;
+        q.kv_stride = capacity;
+        if (ring) {
+            q.ring_cap = capacity;
+            q.ring_base = lo / capacity * capacity;
+        }
+    }
 }
 
 inline int heads_per_workgroup(int G) {
@@ -135,25 +218,27 @@ inline int heads_per_workgroup(int G) {
     return 1;
 }
 
-// Builds the plan; returns "" on success or an error message.
-inline std::string make_plan(const int32_t *seq_lens, int32_t n_slots, int32_t window,
-                             int32_t n_q, int32_t n_kv, int32_t head_dim, int32_t chunk,
-                             int32_t merge_mode, CallPlan &plan) {
+// Builds the plan from the query spans; returns "" on success or an error message.
+inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, int32_t n_kv,
+                             int32_t head_dim, int32_t chunk, int32_t merge_mode, CallPlan &plan) {
     plan = CallPlan();
+    const int32_t n_slots = (int32_t)spans.size();
     plan.fuse_limit = merge_mode == kMergeInKernel ? kFusedMaxChunks : 1;
     plan.G = n_q / n_kv;
     plan.GB = heads_per_workgroup(plan.G);
     plan.n_sub = plan.G / plan.GB;
     plan.slots.resize(n_slots);
-    int64_t rows = 0;   // running sum of L_t (positions)
     int64_t part = 0;
     for (int32_t s = 0; s < n_slots; ++s) {
         SlotPlan &sp = plan.slots[s];
-        sp.L = seq_lens[s];
-        sp.lo = (window > 0 && sp.L > window) ? sp.L - window : 0;
+        const QuerySpan &qs = spans[s];
+        sp.L = qs.L;
+        sp.lo = qs.lo;
         sp.n = sp.L - sp.lo;
-        sp.kv_row0 = rows * n_kv;
-        rows += sp.L;
+        sp.kv_row0 = qs.kv_row0;
+        sp.kv_stride = qs.kv_stride;
+        sp.ring_cap = qs.ring_cap;
+        sp.ring_base = qs.ring_base;
         if (sp.n == 0) {
             sp.chunk = 0;
             sp.n_chunks = 1;

@@ -150,3 +150,77 @@ def make_inputs(seq_lens: Sequence[int], n_q_heads: int, n_kv_heads: int, head_d
 def workload_inputs(cfg: WorkloadConfig) -> DecodeInputs:
     return make_inputs(cfg.seq_lens, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
                        cfg.v_int8, cfg.seed_base)
+
+
+@dataclasses.dataclass
+class CacheInputs:
+    """Host tensors of one fixed-capacity-cache call (every cache row is filled)."""
+    q: torch.Tensor                    # float16 [n_queries, n_q, D]
+    k: torch.Tensor                    # float16 [n_cache_slots * n_kv * capacity * D]
+    v: torch.Tensor                    # float16 or int8, same layout as k
+    v_scales: Optional[torch.Tensor]   # float16 [n_cache_slots * n_kv * capacity * D/32] or None
+    slot_ids: Tuple[int, ...]
+    positions: Tuple[int, ...]
+    n_cache_slots: int
+    capacity: int
+    ring: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    scale: float
+
+    @property
+    def n_queries(self) -> int:
+        return len(self.slot_ids)
+
+
+def make_cache_inputs(n_cache_slots: int, capacity: int, ring: int, slot_ids: Sequence[int],
+                      positions: Sequence[int], n_q_heads: int, n_kv_heads: int, head_dim: int,
+                      v_int8: bool, seed_base: int, scale: Optional[float] = None) -> CacheInputs:
+    """A [slot][kv][capacity][D] cache with every row drawn (same recipe as make_inputs)."""
+    slot_ids = tuple(int(x) for x in slot_ids)
+    positions = tuple(int(x) for x in positions)
+    base = make_inputs((capacity,) * n_cache_slots, n_q_heads, n_kv_heads, head_dim, v_int8, seed_base, scale)
+    gq = torch.Generator("cpu").manual_seed(seed_base + 4)
+    q = torch.randn((len(slot_ids), n_q_heads, head_dim), generator=gq, dtype=torch.float32).to(torch.float16)
+    return CacheInputs(q, base.k, base.v, base.v_scales, slot_ids, positions, n_cache_slots, capacity,
+                       int(ring), n_q_heads, n_kv_heads, head_dim, base.scale)
+
+
+@dataclasses.dataclass(frozen=True)
+class CacheWorkloadConfig:
+    """A fixed-capacity-cache call: query rows (slot id, position) over a [slot][kv][capacity][D] cache."""
+    index: int
+    name: str
+    description: str
+    n_cache_slots: int
+    capacity: int
+    ring: int
+    slot_ids: Tuple[int, ...]
+    positions: Tuple[int, ...]
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    v_int8: bool
+    window: int = 0
+
+    @property
+    def seed_base(self) -> int:
+        return 1000 * self.index
+
+
+CACHE_WORKLOADS = (
+    CacheWorkloadConfig(10, "ring1024_8slot_d256",
+                        "sliding-window layer: 8 slots, a 1024-row ring each, tokens deep into long contexts",
+                        8, 1024, 1, tuple(range(8)), (131071, 90000, 50001, 77777, 2047, 300000, 1024, 65536),
+                        16, 8, 256, False),
+    CacheWorkloadConfig(11, "verify4x4_linear32768_d256",
+                        "speculative verify: 4 slots x 4 consecutive draft positions over a 32768-row linear cache",
+                        4, 32768, 0, tuple(s for s in range(4) for _ in range(4)),
+                        tuple(32764 + t for _ in range(4) for t in range(4)), 16, 8, 256, False),
+)
+
+
+def cache_workload_inputs(cfg: CacheWorkloadConfig) -> CacheInputs:
+    return make_cache_inputs(cfg.n_cache_slots, cfg.capacity, cfg.ring, cfg.slot_ids, cfg.positions,
+                             cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.v_int8, cfg.seed_base)

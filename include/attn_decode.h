@@ -74,9 +74,9 @@ extern "C" {
 #define ATTN_DECODE_ENOMEM (-2) /* workspace allocation failed */
 #define ATTN_DECODE_EHIP (-3)   /* a HIP runtime call or kernel launch failed */
 
-/* Largest number of slots one kernel launch covers; more slots are split
- * into several launch groups inside one call. */
-#define ATTN_DECODE_MAX_SLOTS_PER_LAUNCH 64
+/* Largest number of query rows (slots, or cache queries) one kernel launch
+ * covers; more are split into several launch groups inside one call. */
+#define ATTN_DECODE_MAX_SLOTS_PER_LAUNCH 48
 /* Upper bound of KV chunks per slot; the planner widens chunks to stay below. */
 #define ATTN_DECODE_MAX_CHUNKS 4096
 
@@ -124,6 +124,39 @@ int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                    float *out, int32_t n_slots, int32_t n_q_heads, int32_t n_kv_heads,
                    int32_t head_dim, float scale, void *stream,
                    const attn_decode_options *opts);
+
+/*
+ * attn_decode_cache -- decode attention over a fixed-capacity KV cache.
+ *
+ * The cache holds n_cache_slots slots of `capacity` rows per KV head (the
+ * layout of mlx-native flash_attn_vec_hybrid.metal's batched kernels, slot
+ * offset slot * n_kv * capacity * D):
+ *   k_cache  fp16  [n_cache_slots][n_kv_heads][capacity][head_dim]
+ *   v_cache  fp16 or int8 codes, same layout; v_scales fp16
+ *            [n_cache_slots][n_kv_heads][capacity][head_dim/32] or NULL
+ *   q        fp16  [n_queries][n_q_heads][head_dim]; out fp32, same shape
+ *   slot_ids HOST  int32 [n_queries]: the cache slot query row i reads
+ *   positions HOST int32 [n_queries]: absolute position of query i's token;
+ *            it attends positions <= positions[i] (its own K/V row must
+ *            already be in the cache)
+ * ring = 0: linear storage, position p in row p; positions[i] < capacity.
+ * ring = 1: ring storage, position p in row p mod capacity, so only the last
+ *           `capacity` positions exist (the pages' sliding-window ring:
+ *           kv_seq_len = min(pos + 1, capacity), rows remapped from
+ *           ring_start).
+ * window > 0 further keeps only the last `window` positions; 0 keeps every
+ * stored one.  Several queries may read the same slot, e.g. consecutive
+ * positions of draft tokens in a speculative-decoding verify step: each is
+ * causal on its own position.  Rows the query does not attend are never read.
+ * Alignment, asynchrony, workspace, determinism (per query row) and errors
+ * are as for attn_decode; opts may be NULL.
+ */
+int attn_decode_cache(const void *q, const void *k_cache, const void *v_cache,
+                      const void *v_scales, const int32_t *slot_ids, const int32_t *positions,
+                      int32_t n_queries, int32_t n_cache_slots, int32_t capacity, int32_t ring,
+                      int32_t window, float *out, int32_t n_q_heads, int32_t n_kv_heads,
+                      int32_t head_dim, float scale, void *stream,
+                      const attn_decode_options *opts);
 
 /*
  * attn_decode_plan -- the host planner alone (no HIP call, usable without a

@@ -5,7 +5,7 @@ import numpy as np
 import torch
 
 from decode_attention_kv_02_amd import binding
-from oracle import oracle_attn_decode
+from oracle import oracle_attn_decode, oracle_attn_decode_cache
 
 MAX_ABS = 2e-3
 REL_L2 = 1e-3
@@ -55,3 +55,22 @@ def assert_parity(got, ref, what=""):
     else:
         assert max_abs <= MAX_ABS and rel <= REL_L2, f"{what}: max-abs {max_abs:.3e}, rel-L2 {rel:.3e}"
     return max_abs, rel
+
+
+def run_gpu_cache(ci, window, chunk=0, dev_tensors=None, merge_mode=0):
+    q, k, v, vs = dev_tensors if dev_tensors is not None else to_device(ci)
+    out = torch.full((ci.n_queries, ci.n_q_heads, ci.head_dim), float("nan"), dtype=torch.float32,
+                     device=q.device)
+    binding.attn_decode_cache(q, k, v, vs, ci.slot_ids, ci.positions, ci.n_queries, ci.n_cache_slots,
+                              ci.capacity, ci.ring, window, out, ci.n_q_heads, ci.n_kv_heads,
+                              ci.head_dim, ci.scale, chunk=chunk, merge_mode=merge_mode)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_oracle_cache(ci, window, rows=None):
+    return oracle_attn_decode_cache(
+        ci.q.numpy(), ci.k.numpy(), ci.v.numpy(),
+        None if ci.v_scales is None else ci.v_scales.numpy(),
+        ci.slot_ids, ci.positions, ci.n_cache_slots, ci.capacity, ci.ring, window,
+        ci.n_q_heads, ci.n_kv_heads, ci.head_dim, ci.scale, rows=rows)

@@ -1,0 +1,118 @@
+"""Parity of attn_decode_cache (fixed-capacity linear / ring caches) with the oracle.
+
+Query rows name a cache slot and the absolute position of their token; ring
+storage keeps position p in row p mod capacity (mlx-native
+flash_attn_vec_hybrid.metal, batched kernels: kv_seq_len = min(pos + 1,
+capacity) on the ring and the logical-to-physical row remap).  Bar as for the
+packed path: max-abs <= 2e-3 and relative L2 <= 1e-3 against the fp64 oracle,
+bitwise per-query independence, bitwise agreement with the packed entry point
+when both hold the same rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_kv_02_amd import binding
+from decode_attention_kv_02_amd.workloads import CacheInputs, make_cache_inputs, make_inputs
+
+from gpu_util import assert_parity, run_gpu, run_gpu_cache, run_oracle_cache, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _report(name, err):
+    print(f"[parity] {name}: max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}", flush=True)
+
+
+CASES = [
+    # n_cache_slots, capacity, ring, slot_ids, positions, n_q, n_kv, D, v_int8, window
+    (3, 300, 0, (2, 0, 1, 1), (299, 0, 150, 151), 4, 2, 128, False, 0),
+    (2, 256, 1, (0, 1, 1), (255, 256, 1000), 8, 4, 256, True, 0),          # exactly full, one wrap, many laps
+    (2, 1024, 1, (1, 0), (5000, 1023), 16, 8, 256, False, 700),            # window inside the ring
+    (1, 64, 1, (0, 0, 0, 0), (63, 64, 65, 127), 2, 1, 64, True, 0),       # every wrap offset
+    (4, 512, 0, (3, 3, 3, 3), (400, 401, 402, 403), 16, 2, 512, False, 0),  # verify shape, G = 8
+    (2, 777, 1, (1, 0), (777 * 3 + 5, 776), 6, 2, 256, True, 100),         # odd capacity, G = 3
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_cache_parity(case):
+    nc, cap, ring, sid, pos, nq, nkv, d, i8, W = case
+    ci = make_cache_inputs(nc, cap, ring, sid, pos, nq, nkv, d, i8, seed_base=9000 + 31 * CASES.index(case))
+    got = run_gpu_cache(ci, W).cpu().numpy()
+    ref = run_oracle_cache(ci, W)
+    _report(f"cache {case}", assert_parity(got, ref, str(case)))
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 64, 300])
+def test_ring_chunks_across_the_wrap(chunk):
+    ci = make_cache_inputs(2, 500, 1, (0, 1), (1234, 499), 8, 4, 256, True, seed_base=9100)
+    got = run_gpu_cache(ci, 0, chunk=chunk).cpu().numpy()
+    ref = run_oracle_cache(ci, 0)
+    _report(f"ring chunk {chunk}", assert_parity(got, ref, f"chunk={chunk}"))
+
+
+def test_queries_are_bitwise_independent():
+    sid, pos = (1, 0, 1, 1, 0), (4000, 100, 4001, 1, 4095)
+    ci = make_cache_inputs(2, 4096, 1, sid, pos, 16, 8, 256, True, seed_base=9200)
+    dev = to_device(ci)
+    batched = run_gpu_cache(ci, 0, dev_tensors=dev)
+    for i in range(len(sid)):
+        one = CacheInputs(ci.q[i:i + 1].clone(), ci.k, ci.v, ci.v_scales, (sid[i],), (pos[i],), ci.n_cache_slots,
+                       ci.capacity, ci.ring, ci.n_q_heads, ci.n_kv_heads, ci.head_dim, ci.scale)
+        solo = run_gpu_cache(one, 0, dev_tensors=(dev[0][i:i + 1].contiguous(), dev[1], dev[2], dev[3]))
+        assert torch.equal(batched[i:i + 1], solo), i
+
+
+@pytest.mark.parametrize("i8", [False, True])
+def test_linear_cache_matches_packed_entry_bitwise(i8):
+    # the same rows in a [slot][kv][capacity][D] cache and packed back to back
+    seq = (700, 2048, 1)
+    cap = 2048
+    inp = make_inputs(seq, 16, 8, 256, i8, seed_base=9300)
+    d, nkv = 256, 8
+    k = torch.zeros((3, nkv, cap, d), dtype=torch.float16)
+    v = torch.zeros((3, nkv, cap, d), dtype=torch.int8 if i8 else torch.float16)
+    vs = torch.zeros((3, nkv, cap, d // 32), dtype=torch.float16) if i8 else None
+    off = 0
+    for s, L in enumerate(seq):
+        n = nkv * L * d
+        k[s, :, :L] = inp.k[off:off + n].view(nkv, L, d)
+        v[s, :, :L] = inp.v[off:off + n].view(nkv, L, d)
+        if i8:
+            vs[s, :, :L] = inp.v_scales[off // 32:(off + n) // 32].view(nkv, L, d // 32)
+        off += n
+    ci = CacheInputs(
+        inp.q, k.reshape(-1), v.reshape(-1), None if vs is None else vs.reshape(-1), (0, 1, 2),
+        tuple(L - 1 for L in seq), 3, cap, 0, 16, nkv, d, inp.scale)
+    for W in (0, 500):
+        packed = run_gpu(inp, W)
+        cached = run_gpu_cache(ci, W)
+        assert torch.equal(packed, cached), W
+
+
+def test_cache_rejects_out_of_range_before_launch():
+    ci = make_cache_inputs(2, 64, 0, (0,), (10,), 2, 1, 64, False, seed_base=9400)
+    q, k, v, _ = to_device(ci)
+    out = torch.empty((1, 2, 64), dtype=torch.float32, device=q.device)
+    for sid, pos in (((2,), (10,)), ((0,), (64,)), ((0,), (-1,))):
+        with pytest.raises(binding.AttnDecodeError):
+            binding.attn_decode_cache(q, k, v, None, sid, pos, 1, 2, 64, 0, 0, out, 2, 1, 64, ci.scale)
+
+
+def test_sliding_window_ring_at_serving_shape():
+    # 8 slots, a 1024-position ring each (a sliding-window layer), tokens deep into long contexts
+    pos = (131071, 90000, 1023, 1024, 50001, 77777, 2047, 300000)
+    ci = make_cache_inputs(8, 1024, 1, tuple(range(8)), pos, 16, 8, 256, False, seed_base=9500)
+    got = run_gpu_cache(ci, 0).cpu().numpy()
+    ref = run_oracle_cache(ci, 0)
+    _report("ring 8 x 1024", assert_parity(got, ref, "ring serving shape"))
