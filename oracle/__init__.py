@@ -10,8 +10,11 @@ and marshals numpy arrays through ctypes.
 """
 from .oracle import (  # noqa: F401
     build_oracle,
+    float_to_half_bits,
     half_to_double,
     oracle_attn_decode,
     oracle_attn_decode_cache,
+    oracle_kv_append,
     oracle_library_path,
+    quantize_blocks,
 )

@@ -335,3 +335,140 @@ int oracle_attn_decode_cache_f64(const uint16_t *q, const uint16_t *k, const voi
     jb.d = head_dim; jb.scale = (double)scale; jb.rows = rows; jb.n_rows = n_rows;
     return oracle_run(&jb, n_threads);
 }
+
+/* ------------------------------------------------------------------------
+ * KV append: the step before the path.  Each new token's K is stored as fp16
+ * and its V as fp16 or as symmetric int8 codes in blocks of 32 dims with one
+ * fp16 scale (this build's V format), into the cache row of its (slot,
+ * position): row p for linear storage, row p mod capacity for a ring
+ * (mlx-native flash_attn_vec_hybrid.metal, batched kernels: physical row of a
+ * position; hf2q gemma4 batched_body.rs, the attention phase's KV encode:
+ * F16 copy of K and quantisation of V per slot and position).
+ *
+ * Quantisation of one block b of 32 float values (every rounding decision in
+ * IEEE single precision, round to nearest even):
+ *   amax  = max_i |b_i|
+ *   scale = fp16(amax / 127)
+ *   code  = clamp(rint(b_i / (float)scale), -127, 127), or 0 when scale == 0
+ * ------------------------------------------------------------------------ */
+
+/* IEEE-754 single -> binary16, round to nearest, ties to even (from the
+ * formats' definitions: 1 sign, 5 exponent bits with bias 15, 10 fraction
+ * bits; subnormals below 2^-14; overflow to infinity). */
+uint16_t oracle_float_to_half(float f)
+{
+    uint32_t x;
+    memcpy(&x, &f, sizeof x);
+    const uint16_t sign = (uint16_t)((x >> 16) & 0x8000u);
+    const uint32_t absx = x & 0x7fffffffu;
+    if (absx >= 0x7f800000u) /* inf or NaN */
+        return (uint16_t)(sign | 0x7c00u | (absx > 0x7f800000u ? 0x200u : 0u));
+    const int e = (int)(absx >> 23) - 127; /* unbiased exponent */
+    uint32_t mant = (absx & 0x7fffffu) | (absx >= 0x00800000u ? 0x800000u : 0u); /* 24-bit significand */
+    if (e > 15) return (uint16_t)(sign | 0x7c00u);
+    int shift; /* bits of the 24-bit significand dropped to reach the 11-bit (normal) or fewer (subnormal) */
+    uint32_t exp_field;
+    if (e >= -14) {
+        shift = 13;
+        exp_field = (uint32_t)(e + 15);
+    } else {
+        shift = 13 + (-14 - e); /* subnormal: value = m * 2^-24 */
+        exp_field = 0;
+        if (shift > 24) return sign; /* below half the smallest subnormal: +-0 */
+    }
+    uint32_t q = mant >> shift;
+    const uint32_t rem = mant & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u))) q += 1u;
+    /* q carries the implicit bit for normals; a carry out of the significand bumps the exponent */
+    uint32_t h;
+    if (exp_field == 0) {
+        h = q; /* may round up into the smallest normal: encoding 0x400 is exactly that */
+    } else {
+        h = ((exp_field << 10) + (q - 0x400u)); /* q in [0x400, 0x800]; 0x800 carries into the exponent */
+        if (q == 0x800u) h = (exp_field + 1u) << 10;
+        if (h >= 0x7c00u) h = 0x7c00u;
+    }
+    return (uint16_t)(sign | h);
+}
+
+/* Quantises one block of 32 values; returns the fp16 scale bits. */
+static uint16_t oracle_quantize_block(const float *b, int8_t *codes)
+{
+    float amax = 0.0f;
+    int i;
+    for (i = 0; i < 32; ++i) {
+        const float a = fabsf(b[i]);
+        if (a > amax) amax = a;
+    }
+    const uint16_t s16 = oracle_float_to_half(amax / 127.0f);
+    const float s = (float)oracle_half_to_double(s16);
+    for (i = 0; i < 32; ++i) {
+        if (s == 0.0f) {
+            codes[i] = 0;
+        } else {
+            float c = rintf(b[i] / s);
+            if (c > 127.0f) c = 127.0f;
+            if (c < -127.0f) c = -127.0f;
+            codes[i] = (int8_t)c;
+        }
+    }
+    return s16;
+}
+
+/* Exposed for pinning: quantises n_blocks blocks of 32 floats. */
+void oracle_quantize_blocks(const float *v, int64_t n_blocks, int8_t *codes, uint16_t *scales)
+{
+    int64_t b;
+    for (b = 0; b < n_blocks; ++b) scales[b] = oracle_quantize_block(v + b * 32, codes + b * 32);
+}
+
+/*
+ * oracle_kv_append -- writes n_rows new tokens into a host copy of the cache.
+ *   k_new, v_new  float [n_rows][n_kv][D]
+ *   k_cache       fp16 bits [n_cache_slots][n_kv][capacity][D]
+ *   v_cache       fp16 bits (v_scales == NULL) or int8 codes, same layout
+ *   v_scales      fp16 bits [n_cache_slots][n_kv][capacity][D/32] or NULL
+ * Returns 0, or -1 for invalid arguments (including two rows landing on one cache row).
+ */
+int oracle_kv_append(const float *k_new, const float *v_new, uint16_t *k_cache, void *v_cache,
+                     uint16_t *v_scales, const int32_t *slot_ids, const int32_t *positions,
+                     int32_t n_rows, int32_t n_cache_slots, int32_t capacity, int32_t ring,
+                     int32_t n_kv, int32_t head_dim)
+{
+    int32_t i, j;
+    if (n_rows < 0 || n_cache_slots < 0 || capacity <= 0 || n_kv <= 0 || head_dim <= 0) return -1;
+    if (ring != 0 && ring != 1) return -1;
+    if (v_scales != NULL && head_dim % 32 != 0) return -1;
+    for (i = 0; i < n_rows; ++i) {
+        if (slot_ids[i] < 0 || slot_ids[i] >= n_cache_slots || positions[i] < 0) return -1;
+        if (!ring && positions[i] >= capacity) return -1;
+        for (j = 0; j < i; ++j) {
+            const int64_t ri = ring ? positions[i] % capacity : positions[i];
+            const int64_t rj = ring ? positions[j] % capacity : positions[j];
+            if (slot_ids[i] == slot_ids[j] && ri == rj) return -1;
+        }
+    }
+    const int32_t D = head_dim;
+    for (i = 0; i < n_rows; ++i) {
+        const int64_t phys = ring ? positions[i] % capacity : positions[i];
+        int32_t h;
+        for (h = 0; h < n_kv; ++h) {
+            const int64_t row = ((int64_t)slot_ids[i] * n_kv + h) * capacity + phys;
+            const float *ks = k_new + ((int64_t)i * n_kv + h) * D;
+            const float *vs = v_new + ((int64_t)i * n_kv + h) * D;
+            int32_t d;
+            for (d = 0; d < D; ++d) k_cache[row * D + d] = oracle_float_to_half(ks[d]);
+            if (v_scales == NULL) {
+                uint16_t *vr = (uint16_t *)v_cache + row * D;
+                for (d = 0; d < D; ++d) vr[d] = oracle_float_to_half(vs[d]);
+            } else {
+                int8_t *vr = (int8_t *)v_cache + row * D;
+                int32_t b;
+                for (b = 0; b < D / 32; ++b)
+                    v_scales[row * (D / 32) + b] = oracle_quantize_block(vs + 32 * b, vr + 32 * b);
+            }
+        }
+    }
+    return 0;
+}

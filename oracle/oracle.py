@@ -56,6 +56,15 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         lib.oracle_half_to_double.restype = ctypes.c_double
         lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_float_to_half.restype = ctypes.c_uint16
+        lib.oracle_float_to_half.argtypes = [ctypes.c_float]
+        lib.oracle_quantize_blocks.restype = None
+        lib.oracle_quantize_blocks.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_kv_append.restype = ctypes.c_int
+        lib.oracle_kv_append.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         lib.oracle_attn_decode_cache_f64.restype = ctypes.c_int
         lib.oracle_attn_decode_cache_f64.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -192,3 +201,48 @@ def oracle_attn_decode_cache(q, k, v, v_scales, slot_ids, positions, n_cache_slo
     if rc != 0:
         raise ValueError(f"oracle_attn_decode_cache_f64 returned {rc}")
     return out
+
+
+def float_to_half_bits(x: float) -> int:
+    """The oracle's own float32 -> binary16 (round to nearest even), as bits."""
+    return int(_load().oracle_float_to_half(float(np.float32(x))))
+
+
+def quantize_blocks(v) -> tuple:
+    """The oracle's block-int8 quantiser on float32 values (length a multiple of 32)."""
+    lib = _load()
+    vv = _as_c(np.asarray(v, dtype=np.float32), np.float32).reshape(-1)
+    if vv.size % 32:
+        raise ValueError("length must be a multiple of 32")
+    codes = np.zeros(vv.size, dtype=np.int8)
+    scales = np.zeros(vv.size // 32, dtype=np.uint16)
+    lib.oracle_quantize_blocks(_ptr(vv), vv.size // 32, _ptr(codes), _ptr(scales))
+    return codes, scales.view(np.float16)
+
+
+def oracle_kv_append(k_new, v_new, k_cache, v_cache, v_scales, slot_ids, positions, n_cache_slots,
+                     capacity, ring, n_kv, head_dim):
+    """Writes new tokens into copies of the cache arrays; returns (k_cache, v_cache, v_scales).
+
+    k_new, v_new: float32 [n_rows, n_kv, D]; caches as for oracle_attn_decode_cache.
+    """
+    lib = _load()
+    sid = np.ascontiguousarray(np.asarray(slot_ids, dtype=np.int32))
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    n_rows = int(sid.shape[0])
+    kn = _as_c(np.asarray(k_new), np.float32)
+    vn = _as_c(np.asarray(v_new), np.float32)
+    if kn.size != n_rows * n_kv * head_dim or vn.size != kn.size:
+        raise ValueError("k_new / v_new have the wrong number of elements")
+    kc = np.array(k_cache, dtype=np.float16, copy=True).reshape(-1)
+    vc = np.array(v_cache, copy=True).reshape(-1)
+    sc = None if v_scales is None else np.array(v_scales, dtype=np.float16, copy=True).reshape(-1)
+    if v_scales is None and vc.dtype != np.float16:
+        raise TypeError("fp16 V cache expected")
+    if v_scales is not None and vc.dtype != np.int8:
+        raise TypeError("int8 V cache expected")
+    rc = lib.oracle_kv_append(_ptr(kn), _ptr(vn), _ptr(kc), _ptr(vc), _ptr(sc), _ptr(sid), _ptr(pos),
+                              n_rows, int(n_cache_slots), int(capacity), int(ring), int(n_kv), int(head_dim))
+    if rc != 0:
+        raise ValueError(f"oracle_kv_append returned {rc}")
+    return kc, vc, sc
