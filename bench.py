@@ -32,7 +32,9 @@ One JSON line is printed.  Besides the contract fields it carries
     plus the fixed-capacity cache presets (``attn_decode_cache``: a
     sliding-window ring layer and a speculative-verify shape; for the latter
     ``kv_bytes`` counts what the kernels read, every query its own rows, and
-    ``unique_kv_bytes`` each cache row once).
+    ``unique_kv_bytes`` each cache row once), and the KV-append presets
+    (``attn_kv_append``; ``bytes`` = fp32 K and V read plus the fp16 K and the
+    fp16 or int8 V and scales written).
 """
 from __future__ import annotations
 
@@ -157,7 +159,8 @@ def main(argv=None) -> int:
     import torch
 
     from decode_attention_kv_02_amd import binding
-    from decode_attention_kv_02_amd.workloads import (CACHE_WORKLOADS, WORKLOADS, cache_workload_inputs,
+    from decode_attention_kv_02_amd.workloads import (APPEND_WORKLOADS, CACHE_WORKLOADS, WORKLOADS,
+                                                      append_new_rows, cache_workload_inputs,
                                                       workload_inputs)
 
     if not torch.cuda.is_available():
@@ -338,8 +341,11 @@ def main(argv=None) -> int:
             del ci.k, ci.v
             cout = torch.empty((ci.n_queries, ci.n_q_heads, ci.head_dim), dtype=torch.float32, device=dev)
 
+            c_sid = np.asarray(ci.slot_ids, dtype=np.int32)
+            c_pos = np.asarray(ci.positions, dtype=np.int32)
+
             def cache_call(e0=None, e1=None):
-                binding.attn_decode_cache(*ct, ci.slot_ids, ci.positions, ci.n_queries, ci.n_cache_slots,
+                binding.attn_decode_cache(*ct, c_sid, c_pos, ci.n_queries, ci.n_cache_slots,
                                           ci.capacity, ci.ring, cw.window, cout, ci.n_q_heads,
                                           ci.n_kv_heads, ci.head_dim, ci.scale, stream=stream,
                                           ev_partial_begin=e0.cuda_event if e0 is not None else None,
@@ -375,6 +381,44 @@ def main(argv=None) -> int:
             print(f"[bench] {cw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), cold {cold:.2f} us",
                   file=sys.stderr, flush=True)
             del ct
+            torch.cuda.empty_cache()
+        # KV append presets (attn_kv_append): bytes = fp32 K and V read + fp16 K and V (+ scales) written
+        for aw in APPEND_WORKLOADS:
+            d = aw.head_dim
+            n_el = aw.n_rows * aw.n_kv_heads * d
+            cache_el = aw.n_cache_slots * aw.n_kv_heads * aw.capacity * d
+            kc = torch.zeros(cache_el, dtype=torch.float16, device=dev)
+            vc = torch.zeros(cache_el, dtype=torch.int8 if aw.v_int8 else torch.float16, device=dev)
+            sc = torch.zeros(cache_el // 32, dtype=torch.float16, device=dev) if aw.v_int8 else None
+            kn, vn = (t.to(dev) for t in append_new_rows(aw))
+            a_sid = np.asarray(aw.slot_ids, dtype=np.int32)
+            a_pos = np.asarray(aw.positions, dtype=np.int32)
+
+            def append_call():
+                binding.attn_kv_append(kn, vn, kc, vc, sc, a_sid, a_pos, aw.n_rows,
+                                       aw.n_cache_slots, aw.capacity, aw.ring, aw.n_kv_heads, d,
+                                       stream=stream)
+
+            def per_call_us(fn, n):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(n):
+                    fn()
+                torch.cuda.synchronize()
+                return (time.perf_counter() - t0) * 1e6 / n
+
+            for _ in range(3):
+                append_call()
+            nb = n_el * 8 + n_el * (2 + (1 + 2 / 32 if aw.v_int8 else 2))
+            warm = statistics.median(per_call_us(append_call, args.reps) for _ in range(3))
+            per.append({
+                "workload": aw.name, "window": 0, "bytes": int(nb),
+                "warm_us_per_call": round(warm, 2),
+                "warm_gbs": round(nb / (warm * 1e-6) / 1e9, 1),
+                "warm_hbm_frac": round(nb / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            })
+            print(f"[bench] {aw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s)", file=sys.stderr, flush=True)
+            del kc, vc, sc, kn, vn
             torch.cuda.empty_cache()
         result["per_config"] = per
 

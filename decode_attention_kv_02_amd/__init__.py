@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     attn_decode_ex,
     attn_decode_plan,
     attn_decode_release,
+    attn_kv_append,
     library_path,
     load_library,
 )

@@ -15,6 +15,7 @@ import os
 import threading
 from typing import Optional, Sequence
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "attn_decode_plan",
     "attn_decode_last_error",
     "attn_decode_release",
+    "attn_kv_append",
 )
 
 
@@ -83,6 +85,11 @@ def load_library():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(_Options)]
+        lib.attn_kv_append.restype = ctypes.c_int
+        lib.attn_kv_append.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
         lib.attn_decode_plan.restype = ctypes.c_int
         lib.attn_decode_plan.argtypes = [
             ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -101,9 +108,24 @@ def _raise(lib, rc: int):
     raise AttnDecodeError(rc, msg.decode() if msg else "")
 
 
-def _seq_array(seq_lens: Sequence[int]):
-    vals = [int(x) for x in seq_lens]
-    return (ctypes.c_int32 * max(len(vals), 1))(*vals), len(vals)
+class _HostInts:
+    """A host int32 array for the C ABI; numpy int32 arrays are passed without a copy."""
+
+    def __init__(self, values):
+        if isinstance(values, torch.Tensor):
+            values = values.detach().cpu().numpy()
+        arr = np.ascontiguousarray(np.asarray(values, dtype=np.int32).reshape(-1))
+        self.arr = arr if arr.size else np.zeros(1, dtype=np.int32)
+        self.n = int(arr.size)
+        self._as_parameter_ = ctypes.c_void_p(self.arr.ctypes.data)
+
+    def __iter__(self):
+        return iter(self.arr[:self.n].tolist())
+
+
+def _seq_array(seq_lens):
+    h = _HostInts(seq_lens)
+    return h, h.n
 
 
 def _dev_ptr(t, name: str, dtype, numel: int, device_index: int):
@@ -129,13 +151,13 @@ def _marshal(q, k_cache, v_cache, v_scales, seq_lens, out, n_slots, n_q_heads, n
         n_slots = n
     if n_slots != n:
         raise ValueError("n_slots does not match len(seq_lens)")
-    if any(int(x) < 0 for x in seq_lens):
+    if n and int(seq_arr.arr[:n].min()) < 0:
         # the library rejects this too; checked here because sizes below depend on it
         raise AttnDecodeError(ATTN_DECODE_EINVAL, "seq_lens must be >= 0")
     dev = out.device.index if isinstance(out, torch.Tensor) and out.device.type == "cuda" else None
     if dev is None:
         raise ValueError("out must be a CUDA tensor")
-    kv = sum(int(x) for x in seq_lens) * n_kv_heads * head_dim
+    kv = int(seq_arr.arr[:n].astype(np.int64).sum()) * n_kv_heads * head_dim
     int8 = v_scales is not None
     ptrs = (
         _dev_ptr(q, "q", torch.float16, n_slots * n_q_heads * head_dim, dev),
@@ -217,6 +239,33 @@ def attn_decode_cache(q, k_cache, v_cache, v_scales, slot_ids, positions, n_quer
         _raise(lib, rc)
 
 
+def attn_kv_append(k_new, v_new, k_cache, v_cache, v_scales, slot_ids, positions, n_rows: Optional[int],
+                   n_cache_slots: int, capacity: int, ring: int, n_kv_heads: int, head_dim: int,
+                   stream=None) -> None:
+    """Enqueue the write of new tokens' K (fp16) and V (fp16 or block-int8) into the cache."""
+    lib = load_library()
+    sid, n = _seq_array(slot_ids)
+    pos, n2 = _seq_array(positions)
+    if n_rows is None:
+        n_rows = n
+    if n != n_rows or n2 != n_rows:
+        raise ValueError("slot_ids / positions do not match n_rows")
+    if not isinstance(k_cache, torch.Tensor) or k_cache.device.type != "cuda":
+        raise ValueError("k_cache must be a CUDA tensor")
+    dev = k_cache.device.index
+    kv = int(n_cache_slots) * int(n_kv_heads) * int(capacity) * int(head_dim)
+    int8 = v_scales is not None
+    pkn = _dev_ptr(k_new, "k_new", torch.float32, n_rows * n_kv_heads * head_dim, dev)
+    pvn = _dev_ptr(v_new, "v_new", torch.float32, n_rows * n_kv_heads * head_dim, dev)
+    pk = _dev_ptr(k_cache, "k_cache", torch.float16, kv, dev)
+    pv = _dev_ptr(v_cache, "v_cache", torch.int8 if int8 else torch.float16, kv, dev)
+    ps = _dev_ptr(v_scales, "v_scales", torch.float16, kv // 32, dev) if int8 else None
+    rc = lib.attn_kv_append(pkn, pvn, pk, pv, ps, sid, pos, int(n_rows), int(n_cache_slots), int(capacity),
+                            int(ring), int(n_kv_heads), int(head_dim), _stream_handle(stream, dev))
+    if rc != ATTN_DECODE_OK:
+        _raise(lib, rc)
+
+
 def attn_decode_cache_raw(q_ptr, k_ptr, v_ptr, vs_ptr, slot_ids, positions, n_queries, n_cache_slots,
                           capacity, ring, window, out_ptr, n_q_heads, n_kv_heads, head_dim, scale,
                           stream_ptr=None) -> int:
@@ -243,15 +292,16 @@ def attn_decode_plan(seq_lens, window: int, n_q_heads: int, n_kv_heads: int, hea
     """The host planner alone (no GPU needed)."""
     lib = load_library()
     seq_arr, n = _seq_array(seq_lens)
-    ck = (ctypes.c_int32 * max(n, 1))()
-    nc = (ctypes.c_int32 * max(n, 1))()
+    ck = np.zeros(max(n, 1), dtype=np.int32)
+    nc = np.zeros(max(n, 1), dtype=np.int32)
     ws = ctypes.c_int64(0)
     items = ctypes.c_int64(0)
     rc = lib.attn_decode_plan(seq_arr, n, int(window), int(n_q_heads), int(n_kv_heads), int(head_dim),
-                              int(bool(v_int8)), int(chunk), ck, nc, ctypes.byref(ws), ctypes.byref(items))
+                              int(bool(v_int8)), int(chunk), ck.ctypes.data_as(ctypes.c_void_p),
+                              nc.ctypes.data_as(ctypes.c_void_p), ctypes.byref(ws), ctypes.byref(items))
     if rc != ATTN_DECODE_OK:
         _raise(lib, rc)
-    return {"chunk": list(ck)[:n], "n_chunks": list(nc)[:n], "workspace_bytes": ws.value,
+    return {"chunk": ck[:n].tolist(), "n_chunks": nc[:n].tolist(), "workspace_bytes": ws.value,
             "partial_workgroups": items.value}
 
 

@@ -22,6 +22,7 @@
 #include "../../include/attn_decode.h"
 #include "planner.hpp"
 #include "attn_decode_kernels.hpp"
+#include "kv_append_kernels.hpp"
 
 using namespace attn_decode_impl;
 
@@ -30,6 +31,7 @@ static_assert(ATTN_DECODE_MAX_CHUNKS == kMaxChunks, "chunk bound");
 static_assert(kCombineMaxChunks >= kMaxChunks, "combine LDS holds every chunk weight");
 static_assert(kFusedMaxChunks <= kMaxChunks, "in-kernel merge bound");
 static_assert(sizeof(LaunchArgs) <= 4096, "kernel arguments stay within 4 KiB");
+static_assert(sizeof(AppendArgs) <= 4096, "kernel arguments stay within 4 KiB");
 
 namespace {
 
@@ -330,6 +332,97 @@ int run_cache(const void *q, const void *k_cache, const void *v_cache, const voi
     return launch(spans, q, k_cache, v_cache, v_scales, out, n_q, n_kv, D, scale, stream_ptr, opts);
 }
 
+typedef void (*append_fn)(const AppendArgs);
+
+template <int D>
+append_fn append_for(bool v_int8) {
+    return v_int8 ? kv_append_kernel<D, true> : kv_append_kernel<D, false>;
+}
+
+append_fn select_append(int D, bool v_int8) {
+    switch (D) {
+        case 64: return append_for<64>(v_int8);
+        case 128: return append_for<128>(v_int8);
+        case 256: return append_for<256>(v_int8);
+        case 512: return append_for<512>(v_int8);
+    }
+    return nullptr;
+}
+
+int run_append(const float *k_new, const float *v_new, void *k_cache, void *v_cache, void *v_scales,
+               const int32_t *slot_ids, const int32_t *positions, int32_t n_rows,
+               int32_t n_cache_slots, int32_t capacity, int32_t ring, int32_t n_kv, int32_t D,
+               void *stream_ptr) {
+    g_last_error.clear();
+    const bool v_int8 = v_scales != nullptr;
+    if (n_rows < 0) return fail(ATTN_DECODE_EINVAL, "n_rows must be >= 0");
+    if (n_cache_slots < 0) return fail(ATTN_DECODE_EINVAL, "n_cache_slots must be >= 0");
+    if (n_kv <= 0) return fail(ATTN_DECODE_EINVAL, "n_kv_heads must be positive");
+    if (!supported_head_dim(D)) return fail(ATTN_DECODE_EINVAL, "head_dim must be 64, 128, 256 or 512");
+    std::string err = check_cache(slot_ids, positions, n_rows, n_cache_slots, capacity, ring);
+    if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
+    if (n_rows == 0) return ATTN_DECODE_OK;
+
+    // every new row must land on its own cache row
+    std::vector<std::pair<int32_t, int32_t>> dst(n_rows);
+    for (int32_t i = 0; i < n_rows; ++i)
+        dst[i] = std::make_pair(slot_ids[i], ring ? positions[i] % capacity : positions[i]);
+    std::sort(dst.begin(), dst.end());
+    for (int32_t i = 1; i < n_rows; ++i)
+        if (dst[i] == dst[i - 1]) return fail(ATTN_DECODE_EINVAL, "two new rows land on the same cache row");
+
+    const uint64_t rows = (uint64_t)n_cache_slots * (uint64_t)n_kv * (uint64_t)capacity;
+    const uint64_t kv_elems = rows * (uint64_t)D;
+    if (rows > (uint64_t(1) << 40) || kv_elems > (uint64_t(1) << 46))
+        return fail(ATTN_DECODE_EINVAL, "KV cache too large");
+    const uint64_t new_bytes = (uint64_t)n_rows * n_kv * D * 4;
+    const uint64_t k_bytes = kv_elems * 2, v_bytes = kv_elems * (v_int8 ? 1 : 2);
+    const uint64_t s_bytes = v_int8 ? kv_elems / kQuantBlock * 2 : 0;
+    if (k_new == nullptr || v_new == nullptr) return fail(ATTN_DECODE_EINVAL, "k_new / v_new is NULL");
+    if (k_cache == nullptr || v_cache == nullptr) return fail(ATTN_DECODE_EINVAL, "k_cache / v_cache is NULL");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(ATTN_DECODE_EINVAL, "k_new and v_new must be 16-byte aligned");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return fail(ATTN_DECODE_EINVAL, "k_cache and v_cache must be 16-byte aligned");
+    if (v_int8 && !aligned(v_scales, 2)) return fail(ATTN_DECODE_EINVAL, "v_scales must be 2-byte aligned");
+    const void *outs[3] = {k_cache, v_cache, v_scales};
+    const uint64_t out_bytes[3] = {k_bytes, v_bytes, s_bytes};
+    for (int a = 0; a < 3; ++a) {
+        if (overlaps(k_new, new_bytes, outs[a], out_bytes[a]) || overlaps(v_new, new_bytes, outs[a], out_bytes[a]))
+            return fail(ATTN_DECODE_EINVAL, "k_new / v_new overlaps the cache");
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b]))
+                return fail(ATTN_DECODE_EINVAL, "cache arrays overlap");
+    }
+    const append_fn fn = select_append(D, v_int8);
+    if (fn == nullptr) return fail(ATTN_DECODE_EINVAL, "no kernel for this shape");
+
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    AppendArgs args;
+    std::memset(&args, 0, sizeof(args));
+    args.k_new = k_new;
+    args.v_new = v_new;
+    args.k_cache = static_cast<uint16_t *>(k_cache);
+    args.v_cache = v_cache;
+    args.v_scales = static_cast<uint16_t *>(v_scales);
+    args.n_kv = n_kv;
+    args.capacity = capacity;
+    for (int32_t r0 = 0; r0 < n_rows; r0 += kAppendMaxRows) {
+        const int32_t nr = std::min<int32_t>(kAppendMaxRows, n_rows - r0);
+        args.n_rows = nr;
+        args.row0 = r0;
+        for (int32_t i = 0; i < nr; ++i) {
+            const int32_t p = positions[r0 + i];
+            const int64_t phys = ring ? p % capacity : p;
+            args.cache_row[i] = (int64_t)slot_ids[r0 + i] * n_kv * capacity + phys;
+        }
+        const int64_t units = (int64_t)nr * n_kv;
+        hipLaunchKernelGGL(fn, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, args);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("append kernel launch: ") + hipGetErrorString(e));
+    }
+    return ATTN_DECODE_OK;
+}
+
 }  // namespace
 
 // ============================================================ C ABI
@@ -359,6 +452,14 @@ extern "C" int attn_decode_cache(const void *q, const void *k_cache, const void 
                                  void *stream, const attn_decode_options *opts) {
     return run_cache(q, k_cache, v_cache, v_scales, slot_ids, positions, n_queries, n_cache_slots,
                      capacity, ring, window, out, n_q_heads, n_kv_heads, head_dim, scale, stream, opts);
+}
+
+extern "C" int attn_kv_append(const float *k_new, const float *v_new, void *k_cache, void *v_cache,
+                              void *v_scales, const int32_t *slot_ids, const int32_t *positions,
+                              int32_t n_rows, int32_t n_cache_slots, int32_t capacity, int32_t ring,
+                              int32_t n_kv_heads, int32_t head_dim, void *stream) {
+    return run_append(k_new, v_new, k_cache, v_cache, v_scales, slot_ids, positions, n_rows,
+                      n_cache_slots, capacity, ring, n_kv_heads, head_dim, stream);
 }
 
 extern "C" int attn_decode_plan(const int32_t *seq_lens, int32_t n_slots, int32_t window,

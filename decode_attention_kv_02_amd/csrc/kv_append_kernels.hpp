@@ -1,0 +1,138 @@
+// kv_append_kernels.hpp -- gfx950 kernel that writes new tokens into the KV cache.
+//
+// The step before decode attention (hf2q gemma4 batched_body.rs, the
+// attention phase's KV encode: an F16 copy of K and the quantisation of V,
+// per slot and position; mlx-native flash_attn_vec_hybrid.metal, batched
+// kernels: the physical row of a position).  Each new token's K is stored as
+// fp16 and its V as fp16 or as symmetric int8 codes in blocks of 32 dims with
+// one fp16 scale per block:
+//     scale = fp16(max|v| / 127),  code = clamp(rint(v / scale), -127, 127)
+// (codes 0 when the scale is 0).  Every rounding decision is made in IEEE
+// single precision: the divisions are the correctly rounded fp32 divide,
+// rint rounds half to even, and the fp16 conversions round to nearest even.
+//
+// One wave per (new row, kv head); each lane owns D/64 consecutive dims, so a
+// block of 32 dims spans 2048/D lanes and its max |v| is an all-reduce over
+// those lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn_decode_impl {
+
+constexpr int kAppendMaxRows = 480;   // rows per launch (row table passed by value, < 4 KiB)
+
+struct AppendArgs {
+    const float *k_new;        // [n_rows][n_kv][D]
+    const float *v_new;        // [n_rows][n_kv][D]
+    uint16_t *k_cache;         // fp16 [n_cache_slots][n_kv][capacity][D]
+    void *v_cache;             // fp16 or int8, same layout
+    uint16_t *v_scales;        // fp16 [..][D/32] or null
+    int32_t n_rows;            // rows in this launch
+    int32_t n_kv;
+    int32_t capacity;
+    int32_t row0;              // index of the launch's first row in k_new / v_new
+    int64_t cache_row[kAppendMaxRows];  // (slot * n_kv) * capacity + physical row, per new row
+};
+
+__device__ __forceinline__ float lane_max_xor(float x, int mask) {
+    const int lane = __lane_id();
+    return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2,
+                                                                           __builtin_bit_cast(int, x))));
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);   // v_cvt_f16_f32: round to nearest even
+}
+
+// E consecutive floats / halves / bytes moved with the widest aligned access.
+template <int E>
+__device__ __forceinline__ void load_f32(const float *p, float (&x)[E]) {
+    if constexpr (E % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < E; j += 4) {
+            const float4 t = *(const float4 *)(p + j);
+            x[j] = t.x; x[j + 1] = t.y; x[j + 2] = t.z; x[j + 3] = t.w;
+        }
+    } else if constexpr (E == 2) {
+        const float2 t = *(const float2 *)p;
+        x[0] = t.x; x[1] = t.y;
+    } else {
+        x[0] = p[0];
+    }
+}
+
+template <int E>
+__device__ __forceinline__ void store_f16(uint16_t *p, const float (&x)[E]) {
+    uint16_t h[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) h[i] = f32_to_f16_bits(x[i]);
+    if constexpr (E == 8) {
+        *(uint4 *)p = make_uint4(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16,
+                                 h[4] | (uint32_t)h[5] << 16, h[6] | (uint32_t)h[7] << 16);
+    } else if constexpr (E == 4) {
+        *(uint2 *)p = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
+    } else if constexpr (E == 2) {
+        *(uint32_t *)p = h[0] | (uint32_t)h[1] << 16;
+    } else {
+        p[0] = h[0];
+    }
+}
+
+template <int E>
+__device__ __forceinline__ void store_i8(int8_t *p, const int8_t (&c)[E]) {
+    uint32_t w[(E + 3) / 4] = {};
+#pragma unroll
+    for (int i = 0; i < E; ++i) w[i / 4] |= (uint32_t)(uint8_t)c[i] << (8 * (i % 4));
+    if constexpr (E == 8) {
+        *(uint2 *)p = make_uint2(w[0], w[1]);
+    } else if constexpr (E == 4) {
+        *(uint32_t *)p = w[0];
+    } else if constexpr (E == 2) {
+        *(uint16_t *)p = (uint16_t)w[0];
+    } else {
+        p[0] = c[0];
+    }
+}
+
+template <int D, bool VINT8>
+__global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs args) {
+    constexpr int E = D / 64;          // dims per lane
+    constexpr int LPB = 32 / E;        // lanes per 32-dim block
+    const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);   // (row, kv head) of this wave
+    if (unit >= args.n_rows * args.n_kv) return;             // whole wave leaves; no barriers follow
+    const int lane = threadIdx.x & 63;
+    const int r = unit / args.n_kv;
+    const int h = unit - r * args.n_kv;
+    const int64_t src = ((int64_t)(args.row0 + r) * args.n_kv + h) * D + lane * E;
+    const int64_t dst_row = args.cache_row[r] + (int64_t)h * args.capacity;
+
+    float kx[E], vx[E];
+    load_f32<E>(args.k_new + src, kx);
+    load_f32<E>(args.v_new + src, vx);
+    store_f16<E>(args.k_cache + dst_row * D + lane * E, kx);
+
+    if constexpr (!VINT8) {
+        store_f16<E>((uint16_t *)args.v_cache + dst_row * D + lane * E, vx);
+    } else {
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(vx[i]));
+#pragma unroll
+        for (int m = 1; m < LPB; m <<= 1) amax = lane_max_xor(amax, m);
+        const uint16_t s16 = f32_to_f16_bits(amax / 127.0f);
+        const float s = (float)__builtin_bit_cast(_Float16, s16);
+        int8_t codes[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            float c = 0.f;
+            if (s != 0.f) c = fminf(fmaxf(rintf(vx[i] / s), -127.f), 127.f);
+            codes[i] = (int8_t)c;
+        }
+        store_i8<E>((int8_t *)args.v_cache + dst_row * D + lane * E, codes);
+        if (lane % LPB == 0) args.v_scales[dst_row * (D / 32) + (lane * E) / 32] = s16;
+    }
+}
+
+}  // namespace attn_decode_impl

@@ -224,3 +224,42 @@ CACHE_WORKLOADS = (
 def cache_workload_inputs(cfg: CacheWorkloadConfig) -> CacheInputs:
     return make_cache_inputs(cfg.n_cache_slots, cfg.capacity, cfg.ring, cfg.slot_ids, cfg.positions,
                              cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.v_int8, cfg.seed_base)
+
+
+@dataclasses.dataclass(frozen=True)
+class AppendWorkloadConfig:
+    """A KV append: n_rows new tokens (fp32 K and V) written into a fixed-capacity cache."""
+    index: int
+    name: str
+    description: str
+    n_cache_slots: int
+    capacity: int
+    ring: int
+    slot_ids: Tuple[int, ...]
+    positions: Tuple[int, ...]
+    n_kv_heads: int
+    head_dim: int
+    v_int8: bool
+
+    @property
+    def n_rows(self) -> int:
+        return len(self.slot_ids)
+
+
+APPEND_WORKLOADS = (
+    AppendWorkloadConfig(20, "append_decode_8slot_d256_int8",
+                         "one decode step: a new token for each of 8 slots (8 kv heads, head_dim 256, int8 V)",
+                         8, 32768, 0, tuple(range(8)), (32767,) * 8, 8, 256, True),
+    AppendWorkloadConfig(21, "append_4096tok_d256_int8",
+                         "4096 consecutive tokens into one slot (8 kv heads, head_dim 256, int8 V)",
+                         1, 32768, 0, (0,) * 4096, tuple(range(4096)), 8, 256, True),
+)
+
+
+def append_new_rows(cfg: AppendWorkloadConfig) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fp32 N(0, 1) K and V rows [n_rows, n_kv, D] (seeds seed_base + 5 and + 6)."""
+    gk = torch.Generator("cpu").manual_seed(1000 * cfg.index + 5)
+    gv = torch.Generator("cpu").manual_seed(1000 * cfg.index + 6)
+    shape = (cfg.n_rows, cfg.n_kv_heads, cfg.head_dim)
+    return (torch.randn(shape, generator=gk, dtype=torch.float32),
+            torch.randn(shape, generator=gv, dtype=torch.float32))

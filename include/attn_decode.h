@@ -159,6 +159,29 @@ int attn_decode_cache(const void *q, const void *k_cache, const void *v_cache,
                       const attn_decode_options *opts);
 
 /*
+ * attn_kv_append -- write new tokens' K and V into a fixed-capacity cache (the
+ * step before decode attention: hf2q gemma4 batched_body.rs, the attention
+ * phase's KV encode, an F16 copy of K and the quantisation of V per slot and
+ * position).
+ *   k_new, v_new  fp32 [n_rows][n_kv_heads][head_dim], 16-byte aligned
+ *   k_cache, v_cache, v_scales: the cache of attn_decode_cache (v_scales NULL
+ *                 selects fp16 V); written in place
+ *   slot_ids, positions HOST int32 [n_rows]: row i goes to cache slot
+ *                 slot_ids[i] at position positions[i], i.e. row
+ *                 positions[i] (ring = 0, positions[i] < capacity) or
+ *                 positions[i] mod capacity (ring = 1)
+ * K and fp16 V are rounded to fp16 (nearest even).  int8 V, per block of 32
+ * dims: scale = fp16(max|v| / 127), code = clamp(rint(v / scale), -127, 127),
+ * all in IEEE fp32 (codes 0 when the scale is 0); finite inputs with
+ * |v| <= 127 * 65504.  Two rows may not land on the same cache row (EINVAL).
+ * Only the rows named are written.  Asynchronous on `stream`; no workspace.
+ */
+int attn_kv_append(const float *k_new, const float *v_new, void *k_cache, void *v_cache,
+                   void *v_scales, const int32_t *slot_ids, const int32_t *positions,
+                   int32_t n_rows, int32_t n_cache_slots, int32_t capacity, int32_t ring,
+                   int32_t n_kv_heads, int32_t head_dim, void *stream);
+
+/*
  * attn_decode_plan -- the host planner alone (no HIP call, usable without a
  * GPU).  For the given shapes it writes, per slot, the KV positions per chunk
  * and the number of chunks (arrays of n_slots, may be NULL), the workspace

@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "attn_decode.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_decode\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_symbols():
@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
                         capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (attn_decode\w*)", nm))
+    exported = set(re.findall(r"\bT (attn_\w+)", nm))
     assert exported == set(_declared_functions())
 
 
