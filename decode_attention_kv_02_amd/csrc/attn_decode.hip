@@ -108,30 +108,28 @@ int acquire_workspace(int device, hipStream_t stream, int64_t n_counters, int64_
 typedef void (*partial_fn)(const LaunchArgs);
 typedef void (*combine_fn)(const LaunchArgs);
 
-template <int D>
-partial_fn partial_for(int GB, bool v_int8) {
-    if (v_int8) {
+template <int D, bool V8>
+partial_fn partial_for(int QB, int GB) {
+    if (QB == 1) {
         switch (GB) {
-            case 1: return attn_partial_kernel<D, 1, true>;
-            case 2: return attn_partial_kernel<D, 2, true>;
-            case 4: return attn_partial_kernel<D, 4, true>;
+            case 1: return attn_partial_kernel<D, 1, 1, V8>;
+            case 2: return attn_partial_kernel<D, 1, 2, V8>;
+            case 4: return attn_partial_kernel<D, 1, 4, V8>;
         }
-    } else {
-        switch (GB) {
-            case 1: return attn_partial_kernel<D, 1, false>;
-            case 2: return attn_partial_kernel<D, 2, false>;
-            case 4: return attn_partial_kernel<D, 4, false>;
-        }
+    } else if (QB == 2 && GB == 2) {
+        return attn_partial_kernel<D, 2, 2, V8>;
+    } else if (QB == 4 && GB == 1) {
+        return attn_partial_kernel<D, 4, 1, V8>;
     }
     return nullptr;
 }
 
-partial_fn select_partial(int D, int GB, bool v_int8) {
+partial_fn select_partial(int D, int QB, int GB, bool v_int8) {
     switch (D) {
-        case 64: return partial_for<64>(GB, v_int8);
-        case 128: return partial_for<128>(GB, v_int8);
-        case 256: return partial_for<256>(GB, v_int8);
-        case 512: return partial_for<512>(GB, v_int8);
+        case 64: return v_int8 ? partial_for<64, true>(QB, GB) : partial_for<64, false>(QB, GB);
+        case 128: return v_int8 ? partial_for<128, true>(QB, GB) : partial_for<128, false>(QB, GB);
+        case 256: return v_int8 ? partial_for<256, true>(QB, GB) : partial_for<256, false>(QB, GB);
+        case 512: return v_int8 ? partial_for<512, true>(QB, GB) : partial_for<512, false>(QB, GB);
     }
     return nullptr;
 }
@@ -168,7 +166,7 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     std::string err = make_plan(spans, n_q, n_kv, D, chunk, merge_mode, plan);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
 
-    const partial_fn pk = select_partial(D, plan.GB, v_int8);
+    const partial_fn pk = select_partial(D, plan.QB, plan.GB, v_int8);
     const combine_fn ck = select_combine(D);
     if (pk == nullptr || ck == nullptr) return fail(ATTN_DECODE_EINVAL, "no kernel for this shape");
 
@@ -205,25 +203,28 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     auto fill = [&](const LaunchGroup &lg) {
         args.n_slots = (int32_t)lg.slots.size();
         int32_t item = 0, comb = 0;
+        int32_t lead_pos = 0;
         for (size_t i = 0; i < lg.slots.size(); ++i) {
             const int32_t s = lg.slots[i];
             const SlotPlan &sp = plan.slots[s];
             SlotDesc &sd = args.slot[i];
+            if (sp.group_n > 0) lead_pos = (int32_t)i;   // a leader or an ungrouped query
             sd.kv_row0 = sp.kv_row0;
             sd.part_row0 = sp.part_row0;
             sd.L = sp.L;
             sd.lo = sp.lo;
             sd.chunk = sp.chunk;
             sd.n_chunks = sp.n_chunks;
-            sd.item_begin = item;
+            sd.item_begin = sp.group_n > 0 ? item : args.slot[lead_pos].item_begin;
             sd.comb_begin = comb;
             sd.cnt_base = sp.cnt_base;
             sd.slot_idx = s;
             sd.kv_stride = sp.kv_stride;
             sd.ring_cap = sp.ring_cap;
             sd.ring_base = sp.ring_base;
-            sd.pad0 = 0;
-            item += n_kv * plan.n_sub * sp.n_chunks;
+            sd.group_n = (int16_t)sp.group_n;
+            sd.lead_off = (int16_t)(i - lead_pos);
+            if (sp.group_n > 0) item += n_kv * plan.n_sub * sp.n_chunks;
             if (sp.n_chunks > 1 && !sp.fused) comb += n_q;
         }
         args.n_items = item;

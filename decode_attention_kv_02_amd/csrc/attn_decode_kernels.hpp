@@ -55,7 +55,8 @@ struct SlotDesc {
     int32_t kv_stride;  // rows between consecutive kv heads
     int32_t ring_cap;   // ring capacity, INT32_MAX when rows do not wrap
     int32_t ring_base;  // position held by row 0 of the current ring lap (multiple of ring_cap)
-    int32_t pad0;
+    int16_t group_n;    // on a group leader: queries in the group (leader first), else 0
+    int16_t lead_off;   // table entries back to the group leader (0 on the leader)
 };
 static_assert(sizeof(SlotDesc) == 64, "query descriptor layout");
 
@@ -252,14 +253,24 @@ struct Frag {
     uint16_t vsc[U];
 };
 
-template <int D, int GB, bool VINT8>
+// One workgroup per (query group, kv head, chunk, block of GB heads).  A group
+// is QB queries of one slot that share the attended start and the chunk size
+// (draft tokens of a speculative-verify step): its NR = QB * GB rows are
+// (query, head) pairs that all read the same K and V rows once.  Each row
+// masks the positions at or past its own end, and a chunk past a query's own
+// last chunk is computed fully masked and not written, so every query gets
+// exactly the arithmetic it would get alone (the row-to-lane assignment does
+// not depend on QB).
+template <int D, int QB, int GB, bool VINT8>
 __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs args) {
     using Geo = Geometry<D>;
     constexpr int R = Geo::R, P = Geo::P, U = Geo::U, RW = Geo::RW, HALF = Geo::HALF;
+    constexpr int NR = QB * GB;   // rows: (query of the group, head of the block)
 
     const int item = blockIdx.x;
-    const int si = upper_index(args.n_slots, item, [&](int i) { return args.slot[i].item_begin; });
-    const SlotDesc sd = args.slot[si];
+    int si = upper_index(args.n_slots, item, [&](int i) { return args.slot[i].item_begin; });
+    si -= args.slot[si].lead_off;
+    const SlotDesc sd = args.slot[si];   // group leader: the longest query of the group
     const int local = item - sd.item_begin;
     const int sub = local % args.n_sub;
     const int t = local / args.n_sub;
@@ -270,6 +281,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     const int h0 = kvh * args.G + sub * GB;            // first query head of the block (in the slot)
     const int64_t slot_g = sd.slot_idx;
     const int64_t rowbase = sd.kv_row0 + (int64_t)kvh * sd.kv_stride;
+    const int n_mem = QB == 1 ? 1 : (int)sd.group_n;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -277,20 +289,39 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     const int rg = lane / R;   // lane group = row within a wave load
     const int sl = lane % R;   // lane within the group
 
-    // q fragment of each head: dims [sl*8, sl*8+8) and [HALF + sl*8, HALF + sl*8 + 8)
-    half2_t qv[GB][8];
+    // per row: query row in q / out, and the end of the positions it attends in this chunk
+    int64_t qrow[NR];
+    int rend[NR];
 #pragma unroll
-    for (int g = 0; g < GB; ++g) {
-        const uint16_t *qp = args.q + (slot_g * args.n_q + h0 + g) * D;
-        const uint4 a = *(const uint4 *)(qp + sl * 8);
-        const uint4 b = *(const uint4 *)(qp + HALF + sl * 8);
-        qv[g][0] = as_h2(a.x); qv[g][1] = as_h2(a.y); qv[g][2] = as_h2(a.z); qv[g][3] = as_h2(a.w);
-        qv[g][4] = as_h2(b.x); qv[g][5] = as_h2(b.y); qv[g][6] = as_h2(b.z); qv[g][7] = as_h2(b.w);
+    for (int r = 0; r < NR; ++r) {
+        const int mt = r / GB;
+        if (mt < n_mem) {
+            const SlotDesc &mb = args.slot[si + mt];
+            qrow[r] = mb.slot_idx * (int64_t)args.n_q + h0 + (r % GB);
+            rend[r] = min(cend, mb.L);
+        } else {
+            qrow[r] = -1;
+            rend[r] = cbeg;   // an absent member: every position masked
+        }
     }
 
-    float m[GB], l[GB], o[GB][16];
+    // q fragment of each row: dims [sl*8, sl*8+8) and [HALF + sl*8, HALF + sl*8 + 8)
+    half2_t qv[NR][8];
 #pragma unroll
-    for (int g = 0; g < GB; ++g) {
+    for (int r = 0; r < NR; ++r) {
+        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+        if (qrow[r] >= 0) {
+            const uint16_t *qp = args.q + qrow[r] * D;
+            a = *(const uint4 *)(qp + sl * 8);
+            b = *(const uint4 *)(qp + HALF + sl * 8);
+        }
+        qv[r][0] = as_h2(a.x); qv[r][1] = as_h2(a.y); qv[r][2] = as_h2(a.z); qv[r][3] = as_h2(a.w);
+        qv[r][4] = as_h2(b.x); qv[r][5] = as_h2(b.y); qv[r][6] = as_h2(b.z); qv[r][7] = as_h2(b.w);
+    }
+
+    float m[NR], l[NR], o[NR][16];
+#pragma unroll
+    for (int g = 0; g < NR; ++g) {
         m[g] = -INFINITY;
         l[g] = 0.f;
 #pragma unroll
@@ -326,11 +357,11 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
 
     auto consume = [&](int wb, const Frag<U> &f) {
         // ---- logits (log2 domain)
-        float s[U][GB];
+        float s[U][NR];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
-            for (int g = 0; g < GB; ++g) {
+            for (int g = 0; g < NR; ++g) {
                 float acc = 0.f;
                 acc = __builtin_amdgcn_fdot2(as_h2(f.ka[u].x), qv[g][0], acc, false);
                 acc = __builtin_amdgcn_fdot2(as_h2(f.ka[u].y), qv[g][1], acc, false);
@@ -341,14 +372,14 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
                 acc = __builtin_amdgcn_fdot2(as_h2(f.kb[u].z), qv[g][6], acc, false);
                 acc = __builtin_amdgcn_fdot2(as_h2(f.kb[u].w), qv[g][7], acc, false);
                 acc = group_sum<R>(acc);
-                s[u][g] = (wb + u * P + rg) < cend ? acc * sl2 : -INFINITY;
+                s[u][g] = (wb + u * P + rg) < rend[g] ? acc * sl2 : -INFINITY;
             }
         }
 
         // ---- online softmax: new running max, rescale, weights of the U rows
-        float p[U][GB];
+        float p[U][NR];
 #pragma unroll
-        for (int g = 0; g < GB; ++g) {
+        for (int g = 0; g < NR; ++g) {
             float mx = m[g];
 #pragma unroll
             for (int u = 0; u < U; ++u) mx = fmaxf(mx, s[u][g]);
@@ -366,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
             for (int i = 0; i < 16; ++i) o[g][i] *= alpha;
         }
 
-        // ---- V accumulation: each row is converted to fp32 once and used by the GB heads
+        // ---- V accumulation: each row is converted to fp32 once and used by the NR rows
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float vf[16];
@@ -389,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
                 }
             }
 #pragma unroll
-            for (int g = 0; g < GB; ++g) {
+            for (int g = 0; g < NR; ++g) {
                 float wgt = p[u][g];
                 if constexpr (VINT8) wgt *= h2f(f.vsc[u]);
 #pragma unroll
@@ -420,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
 #pragma unroll
     for (int off = R; off < 64; off <<= 1) {
 #pragma unroll
-        for (int g = 0; g < GB; ++g) {
+        for (int g = 0; g < NR; ++g) {
             const float m2 = shfl_xor_f32(m[g], off);
             const float l2 = shfl_xor_f32(l[g], off);
             const float mx = fmaxf(m[g], m2);
@@ -438,11 +469,11 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     }
 
     // ---- merge the waves through LDS
-    __shared__ float s_o[kWaves][GB][D];
-    __shared__ float s_ml[kWaves][GB][2];
+    __shared__ float s_o[kWaves][NR][D];
+    __shared__ float s_ml[kWaves][NR][2];
     if (rg == 0) {
 #pragma unroll
-        for (int g = 0; g < GB; ++g) {
+        for (int g = 0; g < NR; ++g) {
             if constexpr (VINT8) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s_o[w][g][sl * 16 + i] = o[g][i];
@@ -461,11 +492,15 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     }
     __syncthreads();
 
-    const bool single = sd.n_chunks == 1;
-    const bool fused = !single && sd.n_chunks <= args.fuse_limit;
-    for (int idx = tid; idx < GB * D; idx += kThreads) {
+    // the leader decides the in-kernel merge; groups (QB > 1) always use the combine kernel
+    const bool fused = QB == 1 && sd.n_chunks > 1 && sd.n_chunks <= args.fuse_limit;
+    for (int idx = tid; idx < NR * D; idx += kThreads) {
         const int g = idx / D;
         const int d = idx - g * D;
+        const int mt = g / GB;
+        if (mt >= n_mem) continue;
+        const SlotDesc &mb = args.slot[si + mt];
+        if (c >= mb.n_chunks) continue;   // past this query's last chunk: nothing to write
         float mx = -INFINITY;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) mx = fmaxf(mx, s_ml[ww][g][0]);
@@ -477,10 +512,10 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
             acc += s_o[ww][g][d] * a;
             lsum += s_ml[ww][g][1] * a;
         }
-        if (single) {
-            args.out[(slot_g * args.n_q + h0 + g) * D + d] = (lsum == 0.f) ? 0.f : acc / lsum;
+        if (mb.n_chunks == 1) {
+            args.out[qrow[g] * D + d] = (lsum == 0.f) ? 0.f : acc / lsum;
         } else {
-            const int64_t prow = sd.part_row0 + (int64_t)(h0 + g) * sd.n_chunks + c;
+            const int64_t prow = mb.part_row0 + (int64_t)(h0 + g % GB) * mb.n_chunks + c;
             if (fused) {
                 // agent-scope stores (sc1): coherent across XCDs without an L2 write-back
                 __hip_atomic_store(args.ws_o + prow * D + d, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -497,6 +532,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
             }
         }
     }
+    if constexpr (QB != 1) return;
     if (!fused) return;
 
     // ---- in-kernel merge: the last chunk of this (slot, kv head, head block) to finish merges all

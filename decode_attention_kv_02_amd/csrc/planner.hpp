@@ -34,6 +34,7 @@ constexpr int kChunkMin = 64;
 constexpr int kChunkMax = 2048;
 constexpr int64_t kMaxItemsPerLaunch = int64_t(1) << 24;  // 2^24 workgroups x 256 threads < 2^32
 constexpr int kQuantBlock = 32;          // int8 V: dims per fp16 scale
+constexpr int GROUP_ROWS = 4;            // (query, head) rows one workgroup may carry
 
 // Positions and rows one query row attends.
 struct QuerySpan {
@@ -58,6 +59,9 @@ struct SlotPlan {
     int64_t part_row0 = -1; // first partial row when n_chunks > 1, else -1
     bool fused = false;     // 2..fuse_limit chunks: merged inside the partial kernel
     int32_t cnt_base = 0;   // first arrival counter when fused
+    int32_t group_n = 1;    // on a group leader: queries of its group; 0 on a follower
+    int32_t leader = -1;    // on a follower: the leader's index
+    std::vector<int32_t> members;   // on a leader: followers in table order
 };
 
 struct LaunchGroup {
@@ -69,6 +73,7 @@ struct LaunchGroup {
 struct CallPlan {
     int G = 1;           // query heads per KV head
     int GB = 1;          // query heads per workgroup (1, 2 or 4; divides G)
+    int QB = 1;          // queries per workgroup (QB * GB <= 4); 1 when no group formed
     int n_sub = 1;       // G / GB workgroups share one (slot, kv head, chunk)
     std::vector<SlotPlan> slots;
     std::vector<LaunchGroup> groups;
@@ -262,29 +267,78 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
     plan.workspace_bytes = counter_region_bytes(plan.n_counters) +
                            part * (int64_t)(head_dim + 2) * (int64_t)sizeof(float);
 
+    // Query groups: queries of one slot with the same attended start and chunk
+    // size (draft tokens of a speculative-verify step) share one workgroup, up
+    // to 4 / GB of them, so their K and V rows are read once.  Not with the
+    // in-kernel merge.
+    const int qb_max = merge_mode == kMergeInKernel ? 1 : (GROUP_ROWS / plan.GB);
+    if (qb_max > 1) {
+        std::vector<int32_t> idx;
+        for (int32_t s = 0; s < n_slots; ++s)
+            if (plan.slots[s].n > 0) idx.push_back(s);
+        auto key_less = [&](int32_t a, int32_t b) {
+            const SlotPlan &x = plan.slots[a], &y = plan.slots[b];
+            if (x.kv_row0 != y.kv_row0) return x.kv_row0 < y.kv_row0;
+            if (x.kv_stride != y.kv_stride) return x.kv_stride < y.kv_stride;
+            if (x.ring_cap != y.ring_cap) return x.ring_cap < y.ring_cap;
+            if (x.ring_base != y.ring_base) return x.ring_base < y.ring_base;
+            if (x.lo != y.lo) return x.lo < y.lo;
+            if (x.chunk != y.chunk) return x.chunk < y.chunk;
+            if (x.L != y.L) return x.L > y.L;   // longest first: the leader
+            return a < b;
+        };
+        std::sort(idx.begin(), idx.end(), key_less);
+        auto same_key = [&](int32_t a, int32_t b) {
+            const SlotPlan &x = plan.slots[a], &y = plan.slots[b];
+            return x.kv_row0 == y.kv_row0 && x.kv_stride == y.kv_stride && x.ring_cap == y.ring_cap &&
+                   x.ring_base == y.ring_base && x.lo == y.lo && x.chunk == y.chunk;
+        };
+        for (size_t i = 0; i < idx.size();) {
+            size_t j = i + 1;
+            while (j < idx.size() && (int)(j - i) < qb_max && same_key(idx[i], idx[j])) ++j;
+            if (j - i > 1) {
+                SlotPlan &lead = plan.slots[idx[i]];
+                lead.group_n = (int32_t)(j - i);
+                for (size_t k = i + 1; k < j; ++k) {
+                    lead.members.push_back(idx[k]);
+                    plan.slots[idx[k]].group_n = 0;
+                    plan.slots[idx[k]].leader = idx[i];
+                }
+                plan.QB = qb_max;
+            }
+            i = j;
+        }
+    }
+
     // Work-list order: longest chunks first (ties by slot index), so the
     // longest workgroups start first and short ones fill the tail.  The order
     // decides only which workgroup runs when, never a slot's arithmetic.
-    std::vector<int32_t> order(n_slots);
-    for (int32_t s = 0; s < n_slots; ++s) order[s] = s;
+    std::vector<int32_t> order;
+    for (int32_t s = 0; s < n_slots; ++s)
+        if (plan.slots[s].group_n > 0) order.push_back(s);   // leaders and ungrouped queries
     std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
         return plan.slots[a].chunk > plan.slots[b].chunk;
     });
 
-    // launch groups: at most kMaxSlotsPerLaunch slots and kMaxItemsPerLaunch workgroups
+    // launch groups: at most kMaxSlotsPerLaunch table entries and kMaxItemsPerLaunch workgroups;
+    // a query group's entries (leader, then followers) stay in one launch
     LaunchGroup g;
     for (int32_t s : order) {
         const SlotPlan &sp = plan.slots[s];
         const int64_t items = (int64_t)n_kv * plan.n_sub * sp.n_chunks;
         if (items > kMaxItemsPerLaunch) return "too many workgroups for one slot (n_kv_heads too large)";
-        const bool full = (int)g.slots.size() >= kMaxSlotsPerLaunch || g.items + items > kMaxItemsPerLaunch;
+        const int entries = sp.group_n;
+        const bool full = (int)g.slots.size() + entries > kMaxSlotsPerLaunch || g.items + items > kMaxItemsPerLaunch;
         if (full) {
             plan.groups.push_back(g);
             g = LaunchGroup();
         }
         g.slots.push_back(s);
+        for (int32_t f : sp.members) g.slots.push_back(f);
         g.items += items;
         if (sp.n_chunks > 1 && !sp.fused) g.combine_rows += n_q;
+        for (int32_t f : sp.members)
+            if (plan.slots[f].n_chunks > 1 && !plan.slots[f].fused) g.combine_rows += n_q;
     }
     if (!g.slots.empty()) plan.groups.push_back(g);
     for (const LaunchGroup &lg : plan.groups) plan.total_items += lg.items;

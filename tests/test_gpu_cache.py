@@ -116,3 +116,33 @@ def test_sliding_window_ring_at_serving_shape():
     got = run_gpu_cache(ci, 0).cpu().numpy()
     ref = run_oracle_cache(ci, 0)
     _report("ring 8 x 1024", assert_parity(got, ref, "ring serving shape"))
+
+
+@pytest.mark.parametrize("nq,nkv,i8", [(16, 8, False), (8, 8, True), (4, 4, False), (16, 2, True)])
+def test_draft_queries_share_a_workgroup_and_match_solo(nq, nkv, i8):
+    # 4 consecutive draft positions per slot (G = 2 groups pairs, G = 1 groups all four,
+    # G = 8 does not group); results equal the per-query calls bitwise and the oracle
+    sid = (0, 0, 0, 0, 1, 1, 1, 1, 2)
+    pos = (3000, 3001, 3002, 3003, 700, 701, 702, 703, 50)
+    ci = make_cache_inputs(3, 4096, 0, sid, pos, nq, nkv, 256, i8, seed_base=9600 + nq + nkv)
+    dev = to_device(ci)
+    got = run_gpu_cache(ci, 0, dev_tensors=dev)
+    ref = run_oracle_cache(ci, 0)
+    _report(f"drafts G={nq // nkv}", assert_parity(got.cpu().numpy(), ref, "drafts"))
+    for i in range(len(sid)):
+        one = CacheInputs(ci.q[i:i + 1].clone(), ci.k, ci.v, ci.v_scales, (sid[i],), (pos[i],), ci.n_cache_slots,
+                          ci.capacity, ci.ring, ci.n_q_heads, ci.n_kv_heads, ci.head_dim, ci.scale)
+        solo = run_gpu_cache(one, 0, dev_tensors=(dev[0][i:i + 1].contiguous(), dev[1], dev[2], dev[3]))
+        assert torch.equal(got[i:i + 1], solo), i
+
+
+def test_draft_queries_with_forced_chunks_and_windows():
+    # small forced chunks: members end in different chunks; a window gives each draft its own
+    # start (no grouping), the full range groups them
+    sid = (1, 1, 1, 1)
+    pos = (1000, 1001, 1002, 1003)
+    ci = make_cache_inputs(2, 2048, 0, sid, pos, 8, 8, 128, False, seed_base=9650)
+    for W, chunk in ((0, 7), (0, 250), (300, 0), (300, 13)):
+        got = run_gpu_cache(ci, W, chunk=chunk).cpu().numpy()
+        ref = run_oracle_cache(ci, W)
+        _report(f"drafts W={W} chunk={chunk}", assert_parity(got, ref, f"W={W} chunk={chunk}"))
