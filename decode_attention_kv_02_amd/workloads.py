@@ -24,6 +24,7 @@ describe them (hf2q gemma4 batched_body.rs; tessl nn.rs decode tuning tables).
 from __future__ import annotations
 
 import dataclasses
+import functools
 import math
 from typing import Optional, Sequence, Tuple
 
@@ -263,3 +264,123 @@ def append_new_rows(cfg: AppendWorkloadConfig) -> Tuple[torch.Tensor, torch.Tens
     shape = (cfg.n_rows, cfg.n_kv_heads, cfg.head_dim)
     return (torch.randn(shape, generator=gk, dtype=torch.float32),
             torch.randn(shape, generator=gv, dtype=torch.float32))
+
+
+# ----------------------------------------------------------------------------
+# Codebook V (the pages' hybrid format): V is stored rotated by a sign-flipped,
+# normalised Walsh-Hadamard transform, as one byte per coordinate indexing a
+# codebook, with one fp32 norm per block of min(D, 256) rotated coordinates
+# (mlx-native flash_attn_vec_hybrid.metal: header layouts, the codebook
+# dequant, the per-block norms at D = 512; hf2q gemma4 batched_body.rs: the
+# FWHT-undo of the attention output).  Everything below is input generation.
+
+CB_BLOCK = 256
+
+
+@functools.lru_cache(maxsize=None)
+def _lloyd_levels(bits: int, iters: int) -> Tuple[float, ...]:
+    import numpy as np
+    from scipy.stats import norm
+    n = 1 << bits
+    c = norm.ppf((np.arange(n) + 0.5) / n)
+    for _ in range(iters):
+        b = np.concatenate([[-np.inf], (c[1:] + c[:-1]) / 2, [np.inf]])
+        mass = norm.cdf(b[1:]) - norm.cdf(b[:-1])
+        c = (norm.pdf(b[:-1]) - norm.pdf(b[1:])) / mass
+    return tuple(float(x) for x in c)
+
+
+def lloyd_max_gaussian(bits: int, iters: int = 2000) -> torch.Tensor:
+    """Lloyd-Max quantiser levels for N(0, 1) with 2**bits levels (float32, ascending).
+
+    Lloyd's iteration from the quantile midpoints: cell boundaries at the
+    midpoints of neighbouring levels, each level moved to the conditional mean
+    of N(0, 1) on its cell, (phi(a) - phi(b)) / (Phi(b) - Phi(a)).  It
+    converges slowly for many levels: after 2000 steps the levels are within
+    2e-4 of the fixed point at 8 bits and within 1e-6 at 5 bits.
+    """
+    return torch.tensor(_lloyd_levels(int(bits), int(iters)), dtype=torch.float32)
+
+
+def fwht_rows(x: torch.Tensor) -> torch.Tensor:
+    """Unnormalised Walsh-Hadamard transform along the last dim (a power of two), float64."""
+    y = x.to(torch.float64).clone()
+    d = y.shape[-1]
+    h = 1
+    while h < d:
+        y = y.reshape(*y.shape[:-1], d // (2 * h), 2, h)
+        a, b = y[..., 0, :], y[..., 1, :]
+        y = torch.stack((a + b, a - b), dim=-2).reshape(*y.shape[:-3], d)
+        h *= 2
+    return y
+
+
+def make_signs(head_dim: int, seed: int) -> torch.Tensor:
+    """A seeded +-1 vector (as fp32) of length head_dim."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    return (torch.randint(0, 2, (head_dim,), generator=g) * 2 - 1).to(torch.float32)
+
+
+def codebook_quantize(v: torch.Tensor, signs: torch.Tensor, codebook: torch.Tensor):
+    """Rotate rows of v ([..., D] fp32) by fwht(signs * v) / sqrt(D), then per block of
+    min(D, 256): norm = ||block|| (fp32), index = nearest level to x * sqrt(B) / norm.
+    Returns (uint8 indices [..., D], fp32 norms [..., D / B])."""
+    d = v.shape[-1]
+    B = min(d, CB_BLOCK)
+    rot = (fwht_rows(v.to(torch.float64) * signs.to(torch.float64)) / math.sqrt(d)).to(torch.float32)
+    blocks = rot.reshape(*rot.shape[:-1], d // B, B)
+    norms = blocks.to(torch.float64).pow(2).sum(-1).sqrt().to(torch.float32)
+    safe = torch.where(norms == 0, torch.ones_like(norms), norms)
+    u = blocks * (math.sqrt(B) / safe).unsqueeze(-1)
+    idx = torch.bucketize(u.contiguous(), (codebook[1:] + codebook[:-1]) / 2)
+    return idx.to(torch.uint8).reshape(rot.shape), norms
+
+
+@dataclasses.dataclass
+class CodebookInputs:
+    """Host tensors of a packed-slot call with codebook V (the pages' hybrid KV regime)."""
+    q: torch.Tensor            # float16 [n_slots, n_q, D]
+    k: torch.Tensor            # float16 packed [sum_s n_kv*L_s*D]
+    v_codes: torch.Tensor      # uint8 packed like k (indices into the codebook)
+    v_norms: torch.Tensor      # float32 [sum_s n_kv*L_s*D/B], B = min(D, 256)
+    codebook: torch.Tensor     # float32 [2**bits]
+    codebook_bits: int
+    signs: torch.Tensor        # float32 +-1 [D]: the rotation's sign flips
+    seq_lens: Tuple[int, ...]
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    scale: float
+    v_plain: Optional[torch.Tensor] = None   # float32 packed like k: V before rotation (on request)
+
+    @property
+    def n_slots(self) -> int:
+        return len(self.seq_lens)
+
+
+def make_codebook_inputs(seq_lens: Sequence[int], n_q_heads: int, n_kv_heads: int, head_dim: int,
+                         bits: int, seed_base: int, keep_plain: bool = False) -> CodebookInputs:
+    """K and q as make_inputs; V drawn N(0, 1) (seed_base + 3), rotated and codebook-quantised.
+    keep_plain also returns V itself (float32), for checks of the whole encode / attend / undo chain."""
+    base = make_inputs(seq_lens, n_q_heads, n_kv_heads, head_dim, False, seed_base)
+    cb = lloyd_max_gaussian(bits)
+    signs = make_signs(head_dim, seed_base + 7)
+    gv = torch.Generator("cpu").manual_seed(seed_base + 3)
+    B = min(head_dim, CB_BLOCK)
+    total = sum(seq_lens) * n_kv_heads
+    codes = torch.empty(total * head_dim, dtype=torch.uint8)
+    norms = torch.empty(total * head_dim // B, dtype=torch.float32)
+    plain = torch.empty(total * head_dim, dtype=torch.float32) if keep_plain else None
+    off = 0
+    for L in seq_lens:
+        n = n_kv_heads * L
+        if n:
+            vb = torch.randn((n, head_dim), generator=gv, dtype=torch.float32)
+            c, nr = codebook_quantize(vb, signs, cb)
+            codes[off * head_dim:(off + n) * head_dim] = c.reshape(-1)
+            norms[off * head_dim // B:(off + n) * head_dim // B] = nr.reshape(-1)
+            if plain is not None:
+                plain[off * head_dim:(off + n) * head_dim] = vb.reshape(-1)
+        off += n
+    return CodebookInputs(base.q, base.k, codes, norms, cb, bits, signs, tuple(int(x) for x in seq_lens),
+                          n_q_heads, n_kv_heads, head_dim, base.scale, plain)

@@ -14,6 +14,8 @@ from .oracle import (  # noqa: F401
     half_to_double,
     oracle_attn_decode,
     oracle_attn_decode_cache,
+    oracle_attn_decode_cb,
+    oracle_fwht_undo,
     oracle_kv_append,
     oracle_library_path,
     quantize_blocks,

@@ -81,7 +81,12 @@ typedef struct {
     const uint16_t *q;
     const uint16_t *k;
     const void *v;
-    const uint16_t *v_scales; /* NULL => V is fp16 */
+    const uint16_t *v_scales; /* NULL => V is fp16 (unless codebook != NULL) */
+    /* codebook V: byte indices into codebook, one fp32 norm per block of cb_block coordinates */
+    const float *codebook;
+    const float *v_norms;
+    uint32_t cb_mask;
+    int32_t cb_block;
     /* packed ragged slots */
     const int32_t *seq_lens;
     const int64_t *slot_first_pos; /* sum of L_t for t < s */
@@ -136,7 +141,16 @@ static int oracle_attend(const oracle_job *jb, const uint16_t *qrow, const int64
     for (j = 0; j < n; ++j) {
         const double w = exp(x[j] - m);
         Z += w;
-        if (jb->v_scales == NULL) {
+        if (jb->codebook != NULL) {
+            const uint8_t *vrow = (const uint8_t *)jb->v + row_idx[j] * D;
+            const float *nrow = jb->v_norms + row_idx[j] * (D / jb->cb_block);
+            const double inv_sqrt_b = 1.0 / sqrt((double)jb->cb_block);
+            for (d = 0; d < D; ++d) {
+                const double vdq = (double)jb->codebook[vrow[d] & jb->cb_mask] *
+                                   (double)nrow[d / jb->cb_block] * inv_sqrt_b;
+                acc[d] += w * vdq;
+            }
+        } else if (jb->v_scales == NULL) {
             const uint16_t *vrow = (const uint16_t *)jb->v + row_idx[j] * D;
             for (d = 0; d < D; ++d) acc[d] += w * oracle_half_to_double(vrow[d]);
         } else {
@@ -334,6 +348,89 @@ int oracle_attn_decode_cache_f64(const uint16_t *q, const uint16_t *k, const voi
     jb.window = window; jb.out = out; jb.n_slots = n_queries; jb.n_q = n_q; jb.n_kv = n_kv;
     jb.d = head_dim; jb.scale = (double)scale; jb.rows = rows; jb.n_rows = n_rows;
     return oracle_run(&jb, n_threads);
+}
+
+/*
+ * oracle_attn_decode_cb_f64 -- packed ragged slots with codebook V (the pages'
+ * hybrid regime: F16 K, V stored rotated as byte indices into a codebook with
+ * one fp32 norm per block of B = min(D, 256) coordinates; mlx-native
+ * flash_attn_vec_hybrid.metal, dequant_hb_single and the D = 512 per-block
+ * norms).  V[j][d] = codebook[code & (2^bits - 1)] * norm[j][d / B] / sqrt(B).
+ * The result is in the rotated basis (see oracle_fwht_undo_f64).
+ *   v_codes  uint8 packed like k; v_norms fp32 [rows][D / B]; codebook fp32 [2^bits]
+ */
+int oracle_attn_decode_cb_f64(const uint16_t *q, const uint16_t *k, const uint8_t *v_codes,
+                              const float *v_norms, const float *codebook, int32_t codebook_bits,
+                              const int32_t *seq_lens, int32_t window, double *out,
+                              int32_t n_slots, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                              float scale, const int32_t *rows, int64_t n_rows, int32_t n_threads)
+{
+    int32_t s;
+    if (n_slots < 0 || n_q <= 0 || n_kv <= 0 || head_dim <= 0 || window < 0) return -1;
+    if (n_q % n_kv != 0) return -1;
+    if (codebook_bits < 1 || codebook_bits > 8) return -1;
+    const int32_t B = head_dim < 256 ? head_dim : 256;
+    if (head_dim % B != 0) return -1;
+    if (n_threads < 1) n_threads = 1;
+    if (rows == NULL) n_rows = (int64_t)n_slots * n_q;
+    if (n_rows == 0) return 0;
+    for (s = 0; s < n_slots; ++s)
+        if (seq_lens[s] < 0) return -1;
+    if (check_rows(rows, n_rows, (int64_t)n_slots * n_q) != 0) return -1;
+
+    int64_t *first = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_slots + 1));
+    if (!first) return -2;
+    first[0] = 0;
+    for (s = 0; s < n_slots; ++s) first[s + 1] = first[s] + seq_lens[s];
+
+    oracle_job jb;
+    memset(&jb, 0, sizeof(jb));
+    jb.q = q; jb.k = k; jb.v = v_codes; jb.v_scales = NULL;
+    jb.codebook = codebook; jb.v_norms = v_norms;
+    jb.cb_mask = (1u << codebook_bits) - 1u; jb.cb_block = B;
+    jb.seq_lens = seq_lens; jb.slot_first_pos = first; jb.window = window;
+    jb.out = out; jb.n_slots = n_slots; jb.n_q = n_q; jb.n_kv = n_kv;
+    jb.d = head_dim; jb.scale = (double)scale; jb.rows = rows; jb.n_rows = n_rows;
+    const int status = oracle_run(&jb, n_threads);
+    free(first);
+    return status;
+}
+
+/* Entry (i, j) of the unnormalised Walsh-Hadamard matrix of order 2^k: (-1)^popcount(i & j). */
+static int hadamard_sign(uint32_t i, uint32_t j)
+{
+    uint32_t x = i & j;
+    int parity = 0;
+    while (x) { parity ^= 1; x &= x - 1; }
+    return parity ? -1 : 1;
+}
+
+/*
+ * oracle_fwht_undo_f64 -- back from the rotated basis: the rotation is
+ * v_rot = H (s * v) / sqrt(D) with H the Walsh-Hadamard matrix (symmetric,
+ * H H = D I) and s a vector of +-1, so v = s * (H v_rot) / sqrt(D)
+ * (hf2q gemma4 batched_body.rs, the FWHT sign-undo after the attention).
+ *   x, y  double [n_rows][D] (y may equal x); signs float +-1 [D]; D a power of two
+ */
+int oracle_fwht_undo_f64(const double *x, const float *signs, double *y, int64_t n_rows, int32_t head_dim)
+{
+    int64_t r;
+    int32_t i, j;
+    if (head_dim <= 0 || (head_dim & (head_dim - 1)) != 0 || n_rows < 0) return -1;
+    double *tmp = (double *)malloc(sizeof(double) * (size_t)head_dim);
+    if (!tmp) return -2;
+    const double inv = 1.0 / sqrt((double)head_dim);
+    for (r = 0; r < n_rows; ++r) {
+        const double *xr = x + r * head_dim;
+        for (i = 0; i < head_dim; ++i) {
+            double acc = 0.0;
+            for (j = 0; j < head_dim; ++j) acc += hadamard_sign((uint32_t)i, (uint32_t)j) * xr[j];
+            tmp[i] = (double)signs[i] * acc * inv;
+        }
+        memcpy(y + r * head_dim, tmp, sizeof(double) * (size_t)head_dim);
+    }
+    free(tmp);
+    return 0;
 }
 
 /* ------------------------------------------------------------------------

@@ -56,6 +56,15 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         lib.oracle_half_to_double.restype = ctypes.c_double
         lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_attn_decode_cb_f64.restype = ctypes.c_int
+        lib.oracle_attn_decode_cb_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int32]
+        lib.oracle_fwht_undo_f64.restype = ctypes.c_int
+        lib.oracle_fwht_undo_f64.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int64, ctypes.c_int32]
         lib.oracle_float_to_half.restype = ctypes.c_uint16
         lib.oracle_float_to_half.argtypes = [ctypes.c_float]
         lib.oracle_quantize_blocks.restype = None
@@ -246,3 +255,60 @@ def oracle_kv_append(k_new, v_new, k_cache, v_cache, v_scales, slot_ids, positio
     if rc != 0:
         raise ValueError(f"oracle_kv_append returned {rc}")
     return kc, vc, sc
+
+
+def oracle_attn_decode_cb(q, k, v_codes, v_norms, codebook, codebook_bits, seq_lens, window, n_q, n_kv,
+                          head_dim, scale, rows=None, threads=None) -> np.ndarray:
+    """Plain fp64 decode attention over packed slots with codebook V (result in the rotated basis).
+
+    v_codes: uint8 packed like k; v_norms: float32 [rows_total * D / B], B = min(D, 256);
+    codebook: float32 [2**codebook_bits].
+    """
+    lib = _load()
+    seq = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    n_slots = int(seq.shape[0])
+    q16 = _as_c(q, np.float16)
+    if q16.size != n_slots * n_q * head_dim:
+        raise ValueError("q has the wrong number of elements")
+    B = min(head_dim, 256)
+    total = int(seq.astype(np.int64).sum()) * n_kv * head_dim
+    k16 = _as_c(k, np.float16).reshape(-1)
+    vc = _as_c(v_codes, np.uint8).reshape(-1)
+    vn = _as_c(v_norms, np.float32).reshape(-1)
+    cb = _as_c(codebook, np.float32).reshape(-1)
+    if k16.size != total or vc.size != total or vn.size != total // B:
+        raise ValueError("k / v_codes / v_norms have the wrong number of elements")
+    if cb.size < (1 << int(codebook_bits)):
+        raise ValueError("codebook is shorter than 2**codebook_bits")
+    if rows is None:
+        rows_arr = None
+        n_rows = n_slots * n_q
+        out = np.zeros((n_slots, n_q, head_dim), dtype=np.float64)
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(list(rows), dtype=np.int32))
+        n_rows = int(rows_arr.shape[0])
+        out = np.zeros((n_rows, head_dim), dtype=np.float64)
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+    rc = lib.oracle_attn_decode_cb_f64(
+        _ptr(q16), _ptr(k16), _ptr(vc), _ptr(vn), _ptr(cb), int(codebook_bits), _ptr(seq), int(window),
+        _ptr(out), n_slots, int(n_q), int(n_kv), int(head_dim), float(scale), _ptr(rows_arr), n_rows,
+        int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_decode_cb_f64 returned {rc}")
+    return out
+
+
+def oracle_fwht_undo(x, signs) -> np.ndarray:
+    """signs * (H x) / sqrt(D) per row of x (float64 [..., D]), H the Walsh-Hadamard matrix."""
+    lib = _load()
+    xx = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    d = xx.shape[-1]
+    sg = _as_c(np.asarray(signs, dtype=np.float32), np.float32).reshape(-1)
+    if sg.size != d:
+        raise ValueError("signs must have head_dim entries")
+    y = np.empty_like(xx)
+    rc = lib.oracle_fwht_undo_f64(_ptr(xx), _ptr(sg), _ptr(y), xx.size // d, d)
+    if rc != 0:
+        raise ValueError(f"oracle_fwht_undo_f64 returned {rc}")
+    return y
