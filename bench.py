@@ -29,7 +29,9 @@ One JSON line is printed.  Besides the contract fields it carries
   * ``per_config``: every workload preset, warm (back-to-back calls, wall clock
     between device synchronisations) and cold (the same with a 1 GiB read of
     another buffer before every call, minus the time of those reads alone),
-    plus the fixed-capacity cache presets (``attn_decode_cache``: a
+    plus the codebook-V presets (``attn_decode_cb`` followed by ``attn_fwht_undo``
+    in place; bytes = fp16 K, one index byte per V element and the fp32 norms),
+    the fixed-capacity cache presets (``attn_decode_cache``: a
     sliding-window ring layer and a speculative-verify shape; for the latter
     ``kv_bytes`` counts what the kernels read, every query its own rows, and
     ``unique_kv_bytes`` each cache row once), and the KV-append presets
@@ -62,6 +64,12 @@ def attended(L: int, window: int) -> int:
 
 def kv_bytes(seq_lens, window, n_kv, d, v_int8) -> int:
     per_row = 2 * d + (d + 2 * (d // 32) if v_int8 else 2 * d)
+    return sum(attended(L, window) for L in seq_lens) * n_kv * per_row
+
+
+def cb_kv_bytes(seq_lens, window, n_kv, d) -> int:
+    """Codebook V: fp16 K, one index byte per V element and one fp32 norm per min(D, 256) dims."""
+    per_row = 2 * d + d + 4 * (d // min(d, 256))
     return sum(attended(L, window) for L in seq_lens) * n_kv * per_row
 
 
@@ -159,9 +167,9 @@ def main(argv=None) -> int:
     import torch
 
     from decode_attention_kv_02_amd import binding
-    from decode_attention_kv_02_amd.workloads import (APPEND_WORKLOADS, CACHE_WORKLOADS, WORKLOADS,
-                                                      append_new_rows, cache_workload_inputs,
-                                                      workload_inputs)
+    from decode_attention_kv_02_amd.workloads import (APPEND_WORKLOADS, CACHE_WORKLOADS, CODEBOOK_WORKLOADS,
+                                                      WORKLOADS, append_new_rows, cache_workload_inputs,
+                                                      codebook_workload_inputs, workload_inputs)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -332,6 +340,67 @@ def main(argv=None) -> int:
             if w.name != cfg.name:
                 del ptens
                 torch.cuda.empty_cache()
+
+        # codebook-V presets (attn_decode_cb + attn_fwht_undo in place on the output)
+        for bw in CODEBOOK_WORKLOADS:
+            print(f"[bench] generating {bw.name}", file=sys.stderr, flush=True)
+            bi = codebook_workload_inputs(bw)
+            bq, bk, bvc, bvn, bcb = (t.to(dev) for t in (bi.q, bi.k, bi.v_codes, bi.v_norms, bi.codebook))
+            bsg = bi.signs.to(dev)
+            del bi.k, bi.v_codes, bi.v_norms
+            bout = torch.empty((bi.n_slots, bi.n_q_heads, bi.head_dim), dtype=torch.float32, device=dev)
+            b_seq = np.asarray(bi.seq_lens, dtype=np.int32)
+
+            def cb_call(e0=None, e1=None):
+                binding.attn_decode_cb(bq, bk, bvc, bvn, bcb, bi.codebook_bits, b_seq, bw.window, bout,
+                                       bi.n_slots, bi.n_q_heads, bi.n_kv_heads, bi.head_dim, bi.scale,
+                                       stream=stream,
+                                       ev_partial_begin=e0.cuda_event if e0 is not None else None,
+                                       ev_partial_end=e1.cuda_event if e1 is not None else None)
+                binding.attn_fwht_undo(bout, bsg, bout, stream=stream)
+
+            def per_call_us(fn, n):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(n):
+                    fn()
+                torch.cuda.synchronize()
+                return (time.perf_counter() - t0) * 1e6 / n
+
+            def flush_then_cb_call():
+                flush.sum()
+                cb_call()
+
+            for _ in range(3):
+                cb_call()
+            nb = cb_kv_bytes(bi.seq_lens, bw.window, bi.n_kv_heads, bi.head_dim)
+            warm = statistics.median(per_call_us(cb_call, args.reps) for _ in range(3))
+            cold = statistics.median(per_call_us(flush_then_cb_call, args.reps) -
+                                     per_call_us(lambda: flush.sum(), args.reps) for _ in range(5))
+            pk = []
+            for _ in range(5):
+                c0, c1 = new_event(), new_event()
+                cb_call(c0, c1)
+                torch.cuda.synchronize()
+                pk.append(c0.elapsed_time(c1) * 1e3)
+            assert torch.isfinite(bout).all().item(), "non-finite output"
+            per.append({
+                "workload": bw.name, "window": bw.window, "kv_bytes": nb,
+                "v_format": f"{bi.codebook_bits}-bit codebook indices, fp32 norm per {min(bi.head_dim, 256)} dims",
+                "step": "attn_decode_cb + attn_fwht_undo",
+                "warm_us_per_call": round(warm, 2),
+                "warm_gbs": round(nb / (warm * 1e-6) / 1e9, 1),
+                "warm_hbm_frac": round(nb / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "cold_us_per_call": round(cold, 2),
+                "cold_gbs": round(nb / (cold * 1e-6) / 1e9, 1),
+                "cold_hbm_frac": round(nb / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "partial_kernel_us_median": round(statistics.median(pk), 2),
+                "partial_kernel_gbs": round(nb / (statistics.median(pk) * 1e-6) / 1e9, 1),
+            })
+            print(f"[bench] {bw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), cold {cold:.2f} us, "
+                  f"partial {per[-1]['partial_kernel_gbs']} GB/s", file=sys.stderr, flush=True)
+            del bq, bk, bvc, bvn, bcb, bsg, bout
+            torch.cuda.empty_cache()
 
         # fixed-capacity cache presets (attn_decode_cache)
         for cw in CACHE_WORKLOADS:

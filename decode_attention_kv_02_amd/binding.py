@@ -29,10 +29,12 @@ ATTN_DECODE_EHIP = -3
 EXPORTED_SYMBOLS = (
     "attn_decode",
     "attn_decode_cache",
+    "attn_decode_cb",
     "attn_decode_ex",
     "attn_decode_plan",
     "attn_decode_last_error",
     "attn_decode_release",
+    "attn_fwht_undo",
     "attn_kv_append",
 )
 
@@ -85,6 +87,15 @@ def load_library():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(_Options)]
+        lib.attn_decode_cb.restype = ctypes.c_int
+        lib.attn_decode_cb.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+            ctypes.POINTER(_Options)]
+        lib.attn_fwht_undo.restype = ctypes.c_int
+        lib.attn_fwht_undo.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int32, ctypes.c_void_p]
         lib.attn_kv_append.restype = ctypes.c_int
         lib.attn_kv_append.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -145,7 +156,8 @@ def _dev_ptr(t, name: str, dtype, numel: int, device_index: int):
     return t.data_ptr() if numel else None
 
 
-def _marshal(q, k_cache, v_cache, v_scales, seq_lens, out, n_slots, n_q_heads, n_kv_heads, head_dim):
+def _marshal(q, k_cache, v_cache, v_scales, seq_lens, out, n_slots, n_q_heads, n_kv_heads, head_dim,
+             check_v=True):
     seq_arr, n = _seq_array(seq_lens)
     if n_slots is None:
         n_slots = n
@@ -162,7 +174,7 @@ def _marshal(q, k_cache, v_cache, v_scales, seq_lens, out, n_slots, n_q_heads, n
     ptrs = (
         _dev_ptr(q, "q", torch.float16, n_slots * n_q_heads * head_dim, dev),
         _dev_ptr(k_cache, "k_cache", torch.float16, kv, dev),
-        _dev_ptr(v_cache, "v_cache", torch.int8 if int8 else torch.float16, kv, dev),
+        _dev_ptr(v_cache, "v_cache", torch.int8 if int8 else torch.float16, kv, dev) if check_v else None,
         _dev_ptr(v_scales, "v_scales", torch.float16, kv // 32, dev) if int8 else None,
         _dev_ptr(out, "out", torch.float32, n_slots * n_q_heads * head_dim, dev),
     )
@@ -203,6 +215,47 @@ def attn_decode_ex(q, k_cache, v_cache, v_scales, seq_lens, window: int, out,
     rc = lib.attn_decode_ex(pq, pk, pv, ps, seq_arr, int(window), po, int(n_slots), int(n_q_heads),
                             int(n_kv_heads), int(head_dim), float(scale), _stream_handle(stream, dev),
                             ctypes.byref(opts))
+    if rc != ATTN_DECODE_OK:
+        _raise(lib, rc)
+
+
+def attn_decode_cb(q, k_cache, v_codes, v_norms, codebook, codebook_bits: int, seq_lens, window: int, out,
+                   n_slots: Optional[int], n_q_heads: int, n_kv_heads: int, head_dim: int, scale: float,
+                   stream=None, chunk: int = 0, merge_mode: int = 0,
+                   ev_partial_begin: Optional[int] = None, ev_partial_end: Optional[int] = None) -> None:
+    """Decode attention with codebook V (uint8 indices, fp32 norms per min(D, 256) dims, fp32
+    codebook of 2**codebook_bits levels); out is in the rotated basis (see attn_fwht_undo)."""
+    lib = load_library()
+    seq_arr, n_slots, dev, (pq, pk, _, _, po) = _marshal(
+        q, k_cache, None, None, seq_lens, out, n_slots, n_q_heads, n_kv_heads, head_dim, check_v=False)
+    kv = int(seq_arr.arr[:seq_arr.n].astype(np.int64).sum()) * n_kv_heads * head_dim
+    B = min(head_dim, 256)
+    pv = _dev_ptr(v_codes, "v_codes", torch.uint8, kv, dev)
+    pn = _dev_ptr(v_norms, "v_norms", torch.float32, kv // B, dev)
+    bits = int(codebook_bits)
+    if not 1 <= bits <= 8:
+        raise AttnDecodeError(ATTN_DECODE_EINVAL, "codebook_bits must be in 1..8")
+    pc = _dev_ptr(codebook, "codebook", torch.float32, 1 << bits, dev)
+    opts = _Options(int(chunk), int(merge_mode), ev_partial_begin or None, ev_partial_end or None)
+    rc = lib.attn_decode_cb(pq, pk, pv, pn, pc, bits, seq_arr, int(window), po, int(n_slots), int(n_q_heads),
+                            int(n_kv_heads), int(head_dim), float(scale), _stream_handle(stream, dev),
+                            ctypes.byref(opts))
+    if rc != ATTN_DECODE_OK:
+        _raise(lib, rc)
+
+
+def attn_fwht_undo(x, signs, y, stream=None) -> None:
+    """y = signs * (H x) / sqrt(D) per row of x (fp32 [..., D]); y may be x."""
+    lib = load_library()
+    if not isinstance(y, torch.Tensor) or y.device.type != "cuda":
+        raise ValueError("y must be a CUDA tensor")
+    dev = y.device.index
+    d = int(x.shape[-1])
+    n_rows = x.numel() // d if d else 0
+    px = _dev_ptr(x, "x", torch.float32, n_rows * d, dev)
+    py = _dev_ptr(y, "y", torch.float32, n_rows * d, dev)
+    ps = _dev_ptr(signs, "signs", torch.float32, d, dev)
+    rc = lib.attn_fwht_undo(px, ps, py, int(n_rows), d, _stream_handle(stream, dev))
     if rc != ATTN_DECODE_OK:
         _raise(lib, rc)
 

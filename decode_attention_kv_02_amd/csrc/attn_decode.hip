@@ -23,6 +23,7 @@
 #include "planner.hpp"
 #include "attn_decode_kernels.hpp"
 #include "kv_append_kernels.hpp"
+#include "fwht_kernels.hpp"
 
 using namespace attn_decode_impl;
 
@@ -108,28 +109,38 @@ int acquire_workspace(int device, hipStream_t stream, int64_t n_counters, int64_
 typedef void (*partial_fn)(const LaunchArgs);
 typedef void (*combine_fn)(const LaunchArgs);
 
-template <int D, bool V8>
+template <int D, int VF>
 partial_fn partial_for(int QB, int GB) {
     if (QB == 1) {
         switch (GB) {
-            case 1: return attn_partial_kernel<D, 1, 1, V8>;
-            case 2: return attn_partial_kernel<D, 1, 2, V8>;
-            case 4: return attn_partial_kernel<D, 1, 4, V8>;
+            case 1: return attn_partial_kernel<D, 1, 1, VF>;
+            case 2: return attn_partial_kernel<D, 1, 2, VF>;
+            case 4: return attn_partial_kernel<D, 1, 4, VF>;
         }
     } else if (QB == 2 && GB == 2) {
-        return attn_partial_kernel<D, 2, 2, V8>;
+        return attn_partial_kernel<D, 2, 2, VF>;
     } else if (QB == 4 && GB == 1) {
-        return attn_partial_kernel<D, 4, 1, V8>;
+        return attn_partial_kernel<D, 4, 1, VF>;
     }
     return nullptr;
 }
 
-partial_fn select_partial(int D, int QB, int GB, bool v_int8) {
+template <int D>
+partial_fn partial_for_format(int vf, int QB, int GB) {
+    switch (vf) {
+        case kVF16: return partial_for<D, kVF16>(QB, GB);
+        case kVI8: return partial_for<D, kVI8>(QB, GB);
+        case kVCB: return partial_for<D, kVCB>(QB, GB);
+    }
+    return nullptr;
+}
+
+partial_fn select_partial(int D, int QB, int GB, int vf) {
     switch (D) {
-        case 64: return v_int8 ? partial_for<64, true>(QB, GB) : partial_for<64, false>(QB, GB);
-        case 128: return v_int8 ? partial_for<128, true>(QB, GB) : partial_for<128, false>(QB, GB);
-        case 256: return v_int8 ? partial_for<256, true>(QB, GB) : partial_for<256, false>(QB, GB);
-        case 512: return v_int8 ? partial_for<512, true>(QB, GB) : partial_for<512, false>(QB, GB);
+        case 64: return partial_for_format<64>(vf, QB, GB);
+        case 128: return partial_for_format<128>(vf, QB, GB);
+        case 256: return partial_for_format<256>(vf, QB, GB);
+        case 512: return partial_for_format<512>(vf, QB, GB);
     }
     return nullptr;
 }
@@ -154,11 +165,34 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// How V is stored: fp16 values; int8 codes with fp16 block scales; or
+// codebook indices with fp32 block norms and a table of 2^bits levels.
+struct VSource {
+    const void *v = nullptr;
+    int format = kVF16;
+    const void *side = nullptr;        // int8: scales; codebook: norms
+    const float *codebook = nullptr;
+    int32_t bits = 0;
+
+    static VSource plain_or_int8(const void *v, const void *v_scales) {
+        VSource s;
+        s.v = v;
+        s.format = v_scales ? kVI8 : kVF16;
+        s.side = v_scales;
+        return s;
+    }
+    uint64_t bytes(uint64_t kv_elems) const { return kv_elems * (format == kVF16 ? 2 : 1); }
+    uint64_t side_bytes(uint64_t kv_elems, int32_t D) const {
+        if (format == kVI8) return kv_elems / kQuantBlock * 2;
+        if (format == kVCB) return kv_elems / (D < 256 ? D : 256) * 4;
+        return 0;
+    }
+};
+
 // Everything after the layout-specific checks: plan, workspace, launches.
 int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cache,
-           const void *v_cache, const void *v_scales, float *out, int32_t n_q, int32_t n_kv,
+           const VSource &vsrc, float *out, int32_t n_q, int32_t n_kv,
            int32_t D, float scale, void *stream_ptr, const attn_decode_options *opts) {
-    const bool v_int8 = v_scales != nullptr;
     const int32_t chunk = opts ? opts->chunk : 0;
     const int32_t merge_mode = opts ? opts->merge_mode : 0;
 
@@ -166,7 +200,7 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     std::string err = make_plan(spans, n_q, n_kv, D, chunk, merge_mode, plan);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
 
-    const partial_fn pk = select_partial(D, plan.QB, plan.GB, v_int8);
+    const partial_fn pk = select_partial(D, plan.QB, plan.GB, vsrc.format);
     const combine_fn ck = select_combine(D);
     if (pk == nullptr || ck == nullptr) return fail(ATTN_DECODE_EINVAL, "no kernel for this shape");
 
@@ -188,8 +222,11 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     std::memset(&args, 0, sizeof(args));
     args.q = static_cast<const uint16_t *>(q);
     args.k = static_cast<const uint16_t *>(k_cache);
-    args.v = v_cache;
-    args.vs = static_cast<const uint16_t *>(v_scales);
+    args.v = vsrc.v;
+    args.vs = vsrc.side;
+    args.codebook = vsrc.codebook;
+    args.cb_mask = vsrc.format == kVCB ? (1 << vsrc.bits) - 1 : 0;
+    args.cb_scale = (float)(1.0 / std::sqrt((double)(D < 256 ? D : 256)));
     args.out = out;
     args.ws_o = ws_o;
     args.ws_ml = ws_ml;
@@ -255,37 +292,47 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
 }
 
 // Pointer checks shared by both layouts: NULLs, alignment, and out overlapping an input.
-int check_pointers(const void *q, const void *k_cache, const void *v_cache, const void *v_scales,
-                   const float *out, uint64_t n_rows_q, int32_t n_q, int32_t D, uint64_t kv_elems,
-                   bool v_int8) {
+int check_pointers(const void *q, const void *k_cache, const VSource &vsrc,
+                   const float *out, uint64_t n_rows_q, int32_t n_q, int32_t D, uint64_t kv_elems) {
     const uint64_t q_bytes = n_rows_q * n_q * D * 2;
     const uint64_t out_bytes = n_rows_q * n_q * D * 4;
     const uint64_t k_bytes = kv_elems * 2;
-    const uint64_t v_bytes = kv_elems * (v_int8 ? 1 : 2);
-    const uint64_t s_bytes = v_int8 ? kv_elems / kQuantBlock * 2 : 0;
+    const uint64_t v_bytes = vsrc.bytes(kv_elems);
+    const uint64_t s_bytes = vsrc.side_bytes(kv_elems, D);
+    const uint64_t cb_bytes = vsrc.format == kVCB ? (uint64_t(4) << vsrc.bits) : 0;
     if (q == nullptr) return fail(ATTN_DECODE_EINVAL, "q is NULL");
     if (out == nullptr) return fail(ATTN_DECODE_EINVAL, "out is NULL");
-    if (kv_elems > 0 && (k_cache == nullptr || v_cache == nullptr))
+    if (kv_elems > 0 && (k_cache == nullptr || vsrc.v == nullptr))
         return fail(ATTN_DECODE_EINVAL, "k_cache / v_cache is NULL");
     if (!aligned(q, 16) || !aligned(out, 16)) return fail(ATTN_DECODE_EINVAL, "q and out must be 16-byte aligned");
-    if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+    if (!aligned(k_cache, 16) || !aligned(vsrc.v, 16))
         return fail(ATTN_DECODE_EINVAL, "k_cache and v_cache must be 16-byte aligned");
-    if (v_int8 && !aligned(v_scales, 2)) return fail(ATTN_DECODE_EINVAL, "v_scales must be 2-byte aligned");
+    if (vsrc.format == kVI8 && !aligned(vsrc.side, 2))
+        return fail(ATTN_DECODE_EINVAL, "v_scales must be 2-byte aligned");
+    if (vsrc.format == kVCB) {
+        if (kv_elems > 0 && vsrc.side == nullptr) return fail(ATTN_DECODE_EINVAL, "v_norms is NULL");
+        if (vsrc.codebook == nullptr) return fail(ATTN_DECODE_EINVAL, "codebook is NULL");
+        if (!aligned(vsrc.side, 4) || !aligned(vsrc.codebook, 4))
+            return fail(ATTN_DECODE_EINVAL, "v_norms and codebook must be 4-byte aligned");
+    }
     if (overlaps(out, out_bytes, q, q_bytes) || overlaps(out, out_bytes, k_cache, k_bytes) ||
-        overlaps(out, out_bytes, v_cache, v_bytes) || overlaps(out, out_bytes, v_scales, s_bytes))
+        overlaps(out, out_bytes, vsrc.v, v_bytes) || overlaps(out, out_bytes, vsrc.side, s_bytes) ||
+        overlaps(out, out_bytes, vsrc.codebook, cb_bytes))
         return fail(ATTN_DECODE_EINVAL, "out overlaps an input");
     return ATTN_DECODE_OK;
 }
 
-int run(const void *q, const void *k_cache, const void *v_cache, const void *v_scales,
+int run(const void *q, const void *k_cache, const VSource &vsrc,
         const int32_t *seq_lens, int32_t window, float *out, int32_t n_slots, int32_t n_q,
         int32_t n_kv, int32_t D, float scale, void *stream_ptr, const attn_decode_options *opts) {
     g_last_error.clear();
-    const bool v_int8 = v_scales != nullptr;
     const int32_t chunk = opts ? opts->chunk : 0;
     const int32_t merge_mode = opts ? opts->merge_mode : 0;
 
-    std::string err = check_shapes(seq_lens, n_slots, window, n_q, n_kv, D, v_int8, chunk, merge_mode);
+    if (vsrc.format == kVCB && (vsrc.bits < 1 || vsrc.bits > 8))
+        return fail(ATTN_DECODE_EINVAL, "codebook_bits must be in 1..8");
+    std::string err = check_shapes(seq_lens, n_slots, window, n_q, n_kv, D, vsrc.format == kVI8, chunk,
+                                   merge_mode);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
     if (!std::isfinite(scale)) return fail(ATTN_DECODE_EINVAL, "scale must be finite");
     if (n_slots == 0) return ATTN_DECODE_OK;
@@ -296,12 +343,12 @@ int run(const void *q, const void *k_cache, const void *v_cache, const void *v_s
     const uint64_t kv_elems = total_pos * (uint64_t)n_kv * (uint64_t)D;
     if (total_pos > (uint64_t(1) << 40) || kv_elems > (uint64_t(1) << 46))
         return fail(ATTN_DECODE_EINVAL, "KV cache too large");
-    int rc = check_pointers(q, k_cache, v_cache, v_scales, out, (uint64_t)n_slots, n_q, D, kv_elems, v_int8);
+    int rc = check_pointers(q, k_cache, vsrc, out, (uint64_t)n_slots, n_q, D, kv_elems);
     if (rc != ATTN_DECODE_OK) return rc;
 
     std::vector<QuerySpan> spans;
     spans_packed(seq_lens, n_slots, window, n_kv, spans);
-    return launch(spans, q, k_cache, v_cache, v_scales, out, n_q, n_kv, D, scale, stream_ptr, opts);
+    return launch(spans, q, k_cache, vsrc, out, n_q, n_kv, D, scale, stream_ptr, opts);
 }
 
 int run_cache(const void *q, const void *k_cache, const void *v_cache, const void *v_scales,
@@ -325,12 +372,13 @@ int run_cache(const void *q, const void *k_cache, const void *v_cache, const voi
     const uint64_t kv_elems = rows * (uint64_t)D;
     if (rows > (uint64_t(1) << 40) || kv_elems > (uint64_t(1) << 46))
         return fail(ATTN_DECODE_EINVAL, "KV cache too large");
-    int rc = check_pointers(q, k_cache, v_cache, v_scales, out, (uint64_t)n_queries, n_q, D, kv_elems, v_int8);
+    const VSource vsrc = VSource::plain_or_int8(v_cache, v_scales);
+    int rc = check_pointers(q, k_cache, vsrc, out, (uint64_t)n_queries, n_q, D, kv_elems);
     if (rc != ATTN_DECODE_OK) return rc;
 
     std::vector<QuerySpan> spans;
     spans_cache(slot_ids, positions, n_queries, capacity, ring, window, n_kv, spans);
-    return launch(spans, q, k_cache, v_cache, v_scales, out, n_q, n_kv, D, scale, stream_ptr, opts);
+    return launch(spans, q, k_cache, vsrc, out, n_q, n_kv, D, scale, stream_ptr, opts);
 }
 
 typedef void (*append_fn)(const AppendArgs);
@@ -432,7 +480,7 @@ extern "C" int attn_decode(const void *q, const void *k_cache, const void *v_cac
                            const void *v_scales, const int32_t *seq_lens, int32_t window,
                            float *out, int32_t n_slots, int32_t n_q_heads, int32_t n_kv_heads,
                            int32_t head_dim, float scale, void *stream) {
-    return run(q, k_cache, v_cache, v_scales, seq_lens, window, out, n_slots, n_q_heads,
+    return run(q, k_cache, VSource::plain_or_int8(v_cache, v_scales), seq_lens, window, out, n_slots, n_q_heads,
                n_kv_heads, head_dim, scale, stream, nullptr);
 }
 
@@ -441,8 +489,52 @@ extern "C" int attn_decode_ex(const void *q, const void *k_cache, const void *v_
                               float *out, int32_t n_slots, int32_t n_q_heads, int32_t n_kv_heads,
                               int32_t head_dim, float scale, void *stream,
                               const attn_decode_options *opts) {
-    return run(q, k_cache, v_cache, v_scales, seq_lens, window, out, n_slots, n_q_heads,
+    return run(q, k_cache, VSource::plain_or_int8(v_cache, v_scales), seq_lens, window, out, n_slots, n_q_heads,
                n_kv_heads, head_dim, scale, stream, opts);
+}
+
+extern "C" int attn_decode_cb(const void *q, const void *k_cache, const void *v_codes,
+                              const float *v_norms, const float *codebook, int32_t codebook_bits,
+                              const int32_t *seq_lens, int32_t window, float *out, int32_t n_slots,
+                              int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                              void *stream, const attn_decode_options *opts) {
+    VSource vsrc;
+    vsrc.v = v_codes;
+    vsrc.format = kVCB;
+    vsrc.side = v_norms;
+    vsrc.codebook = codebook;
+    vsrc.bits = codebook_bits;
+    return run(q, k_cache, vsrc, seq_lens, window, out, n_slots, n_q_heads, n_kv_heads, head_dim,
+               scale, stream, opts);
+}
+
+extern "C" int attn_fwht_undo(const float *x, const float *signs, float *y, int64_t n_rows,
+                              int32_t head_dim, void *stream) {
+    g_last_error.clear();
+    typedef void (*undo_fn)(const float *, const float *, float *, int64_t, float);
+    undo_fn fn = nullptr;
+    switch (head_dim) {
+        case 64: fn = fwht_undo_kernel<64>; break;
+        case 128: fn = fwht_undo_kernel<128>; break;
+        case 256: fn = fwht_undo_kernel<256>; break;
+        case 512: fn = fwht_undo_kernel<512>; break;
+        default: return fail(ATTN_DECODE_EINVAL, "head_dim must be 64, 128, 256 or 512");
+    }
+    if (n_rows < 0) return fail(ATTN_DECODE_EINVAL, "n_rows must be >= 0");
+    if (n_rows > (int64_t)4 * 0x7fffffff) return fail(ATTN_DECODE_EINVAL, "n_rows too large");
+    if (n_rows == 0) return ATTN_DECODE_OK;
+    if (x == nullptr || signs == nullptr || y == nullptr) return fail(ATTN_DECODE_EINVAL, "x / signs / y is NULL");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(ATTN_DECODE_EINVAL, "x and y must be 16-byte aligned");
+    if (!aligned(signs, 4)) return fail(ATTN_DECODE_EINVAL, "signs must be 4-byte aligned");
+    const uint64_t bytes = (uint64_t)n_rows * (uint64_t)head_dim * 4;
+    if (x != y && overlaps(x, bytes, y, bytes)) return fail(ATTN_DECODE_EINVAL, "y overlaps x without being x");
+    if (overlaps(y, bytes, signs, (uint64_t)head_dim * 4)) return fail(ATTN_DECODE_EINVAL, "y overlaps signs");
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const float inv = (float)(1.0 / std::sqrt((double)head_dim));
+    hipLaunchKernelGGL(fn, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, st, x, signs, y, n_rows, inv);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("fwht undo launch: ") + hipGetErrorString(e));
+    return ATTN_DECODE_OK;
 }
 
 extern "C" int attn_decode_cache(const void *q, const void *k_cache, const void *v_cache,

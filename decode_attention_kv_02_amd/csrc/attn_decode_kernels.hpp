@@ -60,23 +60,33 @@ struct SlotDesc {
 };
 static_assert(sizeof(SlotDesc) == 64, "query descriptor layout");
 
+// Formats of the V cache.
+enum VFormat : int {
+    kVF16 = 0,   // fp16 values
+    kVI8 = 1,    // int8 codes, one fp16 scale per 32 dims
+    kVCB = 2,    // byte indices into a codebook, one fp32 norm per block of min(D, 256) dims
+};
+
 struct LaunchArgs {
     const uint16_t *q;      // fp16 [n_slots_total][n_q][D]
     const uint16_t *k;      // fp16 packed cache
-    const void *v;          // fp16 or int8 packed cache
-    const uint16_t *vs;     // fp16 scales or null
+    const void *v;          // fp16, int8 or codebook-index cache
+    const void *vs;         // int8: fp16 block scales; codebook: fp32 block norms; fp16: null
+    const float *codebook;  // codebook levels [cb_mask + 1], codebook V only
     float *out;             // fp32 [n_slots_total][n_q][D]
     float *ws_o;            // partial O rows [part_rows][D]
     float *ws_ml;           // partial (M, S) [part_rows][2]
     uint32_t *counters;     // arrival counters of in-kernel merges, zero between calls
     int32_t n_slots;        // slots in this launch (table entries, longest chunks first)
-    int32_t pad0;
+    int32_t cb_mask;        // codebook V: 2^bits - 1 (the index bits that are used)
     int32_t n_q;
     int32_t G;              // query heads per kv head
     int32_t n_sub;          // G / GB
     float scale_log2;       // scale * log2(e)
     int32_t n_items;
     int32_t fuse_limit;     // slots with 2..fuse_limit chunks merge inside the partial kernel
+    float cb_scale;         // codebook V: 1 / sqrt(min(D, 256))
+    int32_t pad0;
     SlotDesc slot[48];
 };
 
@@ -245,12 +255,14 @@ struct Geometry {
 };
 
 // Registers of one wave iteration: U K rows (two 16-byte halves per lane) and
-// U V rows (fp16: two halves; int8: one 16-byte code load and one scale).
+// U V rows (fp16: two halves; int8: one 16-byte code load and one fp16 scale;
+// codebook: one 16-byte index load and one fp32 norm).
 template <int U>
 struct Frag {
     uint4 ka[U], kb[U];
     uint4 va[U], vb[U];
     uint16_t vsc[U];
+    float vn[U];
 };
 
 // One workgroup per (query group, kv head, chunk, block of GB heads).  A group
@@ -261,11 +273,23 @@ struct Frag {
 // last chunk is computed fully masked and not written, so every query gets
 // exactly the arithmetic it would get alone (the row-to-lane assignment does
 // not depend on QB).
-template <int D, int QB, int GB, bool VINT8>
+//
+// V formats (VF): fp16; int8 codes times the fp16 scale of their 32-dim block;
+// codebook indices, where an element is level[index & mask] * norm / sqrt(B)
+// with one norm per block of B = min(D, 256) dims (the pages' hybrid V).  For
+// the byte formats each lane reads 16 consecutive dims of a row, which lie in
+// one scale block, so the block's scale (or norm) is folded into the row's
+// softmax weight.  The codebook is expanded once per workgroup into a
+// 256-entry LDS table already masked and multiplied by 1/sqrt(B), so an
+// element costs one byte extract and one LDS read.
+template <int D, int QB, int GB, int VF>
 __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs args) {
     using Geo = Geometry<D>;
     constexpr int R = Geo::R, P = Geo::P, U = Geo::U, RW = Geo::RW, HALF = Geo::HALF;
     constexpr int NR = QB * GB;   // rows: (query of the group, head of the block)
+    constexpr bool BYTES = VF != kVF16;                 // one byte per V element
+    constexpr int CB_B = D < 256 ? D : 256;             // codebook norm block
+    static_assert(kThreads == 256, "one thread per codebook table entry");
 
     const int item = blockIdx.x;
     int si = upper_index(args.n_slots, item, [&](int i) { return args.slot[i].item_begin; });
@@ -330,6 +354,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
 
     const float sl2 = args.scale_log2;
     const uint16_t *kbase = args.k + rowbase * D;
+    __shared__ float s_cb[VF == kVCB ? 256 : 1];   // codebook V: level[i & mask] / sqrt(B)
 
     // Rows [wb, wb + RW) of one wave iteration: lane group rg reads row wb + u*P + rg.
     // Rows past the chunk end are clamped to its last row (in bounds) and masked.
@@ -343,10 +368,14 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
             const uint16_t *kp = kbase + (int64_t)rc * D;
             f.ka[u] = load_stream16(kp + sl * 8);
             f.kb[u] = load_stream16(kp + HALF + sl * 8);
-            if constexpr (VINT8) {
+            if constexpr (VF == kVI8) {
                 const int8_t *vp = (const int8_t *)args.v + (rowbase + rc) * D;
                 f.va[u] = load_stream16(vp + sl * 16);
-                f.vsc[u] = args.vs[(rowbase + rc) * (D / 32) + (sl >> 1)];
+                f.vsc[u] = ((const uint16_t *)args.vs)[(rowbase + rc) * (D / 32) + (sl >> 1)];
+            } else if constexpr (VF == kVCB) {
+                const uint8_t *vp = (const uint8_t *)args.v + (rowbase + rc) * D;
+                f.va[u] = load_stream16(vp + sl * 16);
+                f.vn[u] = ((const float *)args.vs)[(rowbase + rc) * (D / CB_B) + (sl * 16) / CB_B];
             } else {
                 const uint16_t *vp = (const uint16_t *)args.v + (rowbase + rc) * D;
                 f.va[u] = load_stream16(vp + sl * 8);
@@ -401,7 +430,14 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float vf[16];
-            if constexpr (VINT8) {
+            if constexpr (VF == kVCB) {
+                const uint32_t wd[4] = {f.va[u].x, f.va[u].y, f.va[u].z, f.va[u].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) vf[4 * j + b] = s_cb[(wd[j] >> (8 * b)) & 0xFF];
+                }
+            } else if constexpr (VF == kVI8) {
                 const uint32_t wd[4] = {f.va[u].x, f.va[u].y, f.va[u].z, f.va[u].w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -422,7 +458,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
 #pragma unroll
             for (int g = 0; g < NR; ++g) {
                 float wgt = p[u][g];
-                if constexpr (VINT8) wgt *= h2f(f.vsc[u]);
+                if constexpr (VF == kVI8) wgt *= h2f(f.vsc[u]);
+                if constexpr (VF == kVCB) wgt *= f.vn[u];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[g][i] = fmaf(wgt, vf[i], o[g][i]);
             }
@@ -435,6 +472,10 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     Frag<U> fa, fb;
     int wb = cbeg + w * RW;
     if (wb < cend) load(wb, fa);
+    if constexpr (VF == kVCB) {
+        s_cb[tid] = args.codebook[tid & args.cb_mask] * args.cb_scale;
+        __syncthreads();
+    }
     while (wb < cend) {
         int wn = wb + STEP;
         if (wn < cend) load(wn, fb);
@@ -474,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     if (rg == 0) {
 #pragma unroll
         for (int g = 0; g < NR; ++g) {
-            if constexpr (VINT8) {
+            if constexpr (BYTES) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s_o[w][g][sl * 16 + i] = o[g][i];
             } else {

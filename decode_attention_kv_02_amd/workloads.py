@@ -322,12 +322,18 @@ def make_signs(head_dim: int, seed: int) -> torch.Tensor:
 
 
 def codebook_quantize(v: torch.Tensor, signs: torch.Tensor, codebook: torch.Tensor):
-    """Rotate rows of v ([..., D] fp32) by fwht(signs * v) / sqrt(D), then per block of
-    min(D, 256): norm = ||block|| (fp32), index = nearest level to x * sqrt(B) / norm.
-    Returns (uint8 indices [..., D], fp32 norms [..., D / B])."""
+    """Rotate rows of v ([..., D] fp32) by fwht(signs * v) / sqrt(D), then encode them
+    (codebook_encode_rotated).  Returns (uint8 indices [..., D], fp32 norms [..., D / B])."""
     d = v.shape[-1]
-    B = min(d, CB_BLOCK)
     rot = (fwht_rows(v.to(torch.float64) * signs.to(torch.float64)) / math.sqrt(d)).to(torch.float32)
+    return codebook_encode_rotated(rot, codebook)
+
+
+def codebook_encode_rotated(rot: torch.Tensor, codebook: torch.Tensor):
+    """Per block of B = min(D, 256) coordinates of already rotated rows: norm = ||block||
+    (fp32), index = nearest level to x * sqrt(B) / norm."""
+    d = rot.shape[-1]
+    B = min(d, CB_BLOCK)
     blocks = rot.reshape(*rot.shape[:-1], d // B, B)
     norms = blocks.to(torch.float64).pow(2).sum(-1).sqrt().to(torch.float32)
     safe = torch.where(norms == 0, torch.ones_like(norms), norms)
@@ -359,9 +365,15 @@ class CodebookInputs:
 
 
 def make_codebook_inputs(seq_lens: Sequence[int], n_q_heads: int, n_kv_heads: int, head_dim: int,
-                         bits: int, seed_base: int, keep_plain: bool = False) -> CodebookInputs:
+                         bits: int, seed_base: int, keep_plain: bool = False,
+                         direct: bool = False) -> CodebookInputs:
     """K and q as make_inputs; V drawn N(0, 1) (seed_base + 3), rotated and codebook-quantised.
-    keep_plain also returns V itself (float32), for checks of the whole encode / attend / undo chain."""
+    keep_plain also returns V itself (float32), for checks of the whole encode / attend / undo chain.
+    direct draws the rotated coordinates themselves: an orthogonal rotation of i.i.d. N(0, 1)
+    coordinates is again i.i.d. N(0, 1), so codes and norms have the same distribution, without
+    the transform's cost at full cache sizes (and with no plain V to keep)."""
+    if direct and keep_plain:
+        raise ValueError("direct draws no plain V")
     base = make_inputs(seq_lens, n_q_heads, n_kv_heads, head_dim, False, seed_base)
     cb = lloyd_max_gaussian(bits)
     signs = make_signs(head_dim, seed_base + 7)
@@ -374,13 +386,45 @@ def make_codebook_inputs(seq_lens: Sequence[int], n_q_heads: int, n_kv_heads: in
     off = 0
     for L in seq_lens:
         n = n_kv_heads * L
-        if n:
-            vb = torch.randn((n, head_dim), generator=gv, dtype=torch.float32)
-            c, nr = codebook_quantize(vb, signs, cb)
-            codes[off * head_dim:(off + n) * head_dim] = c.reshape(-1)
-            norms[off * head_dim // B:(off + n) * head_dim // B] = nr.reshape(-1)
+        for r0 in range(0, n, 1 << 16):          # bounded temporaries at full cache sizes
+            r1 = min(n, r0 + (1 << 16))
+            vb = torch.randn((r1 - r0, head_dim), generator=gv, dtype=torch.float32)
+            c, nr = codebook_encode_rotated(vb, cb) if direct else codebook_quantize(vb, signs, cb)
+            a = off + r0
+            codes[a * head_dim:(a + r1 - r0) * head_dim] = c.reshape(-1)
+            norms[a * head_dim // B:(a + r1 - r0) * head_dim // B] = nr.reshape(-1)
             if plain is not None:
-                plain[off * head_dim:(off + n) * head_dim] = vb.reshape(-1)
+                plain[a * head_dim:(a + r1 - r0) * head_dim] = vb.reshape(-1)
         off += n
     return CodebookInputs(base.q, base.k, codes, norms, cb, bits, signs, tuple(int(x) for x in seq_lens),
                           n_q_heads, n_kv_heads, head_dim, base.scale, plain)
+
+
+@dataclasses.dataclass(frozen=True)
+class CodebookWorkloadConfig:
+    """A packed-slot workload with codebook V (byte indices, Lloyd-Max levels, block norms)."""
+    name: str
+    index: int
+    seq_lens: Tuple[int, ...]
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    bits: int
+    window: int = 0
+
+    @property
+    def seed_base(self) -> int:
+        return 1000 * self.index
+
+
+CODEBOOK_WORKLOADS = (
+    # the hybrid workload's shape with the pages' own V format (8-bit levels, D 256 sliding layers)
+    CodebookWorkloadConfig("hybrid_codebook8_8x32768", 30, (32768,) * 8, 16, 8, 256, 8),
+    # a global layer: head_dim 512 with 2 KV heads (gemma4's global layers), two norms per row
+    CodebookWorkloadConfig("global_d512_codebook8_8x32768", 31, (32768,) * 8, 16, 2, 512, 8),
+)
+
+
+def codebook_workload_inputs(cfg: CodebookWorkloadConfig) -> CodebookInputs:
+    return make_codebook_inputs(cfg.seq_lens, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.bits,
+                                cfg.seed_base, direct=True)

@@ -34,7 +34,7 @@
  *
  * Execution: every entry point that takes a stream is asynchronous on it
  * (a hipStream_t passed as void*; NULL = the null stream of the current
- * device).  A call enqueues one partial kernel per launch group of up to 64
+ * device).  A call enqueues one partial kernel per launch group of up to 48
  * slots (normally one group) and, when some slot is split into several KV
  * chunks, one log-sum-exp combine kernel per such group.  It never
  * synchronises the host and never reads device memory from the host.  Inputs
@@ -157,6 +157,50 @@ int attn_decode_cache(const void *q, const void *k_cache, const void *v_cache,
                       int32_t window, float *out, int32_t n_q_heads, int32_t n_kv_heads,
                       int32_t head_dim, float scale, void *stream,
                       const attn_decode_options *opts);
+
+/*
+ * attn_decode_cb -- attn_decode with codebook V (the pages' own hybrid KV
+ * regime: mlx-native flash_attn_vec_hybrid.metal, the TQ-HB V layout and its
+ * byte-index dequant with 5-, 6- or 8-bit Lloyd-Max codebooks; hf2q gemma4
+ * batched_body.rs, the KV encode and the FWHT sign-undo).
+ *
+ * V is stored in a rotated basis, v_rot = H (s * v) / sqrt(head_dim) (H the
+ * Walsh-Hadamard matrix, s a vector of +-1), as one byte per element: the
+ * element is
+ *     codebook[code & (2^codebook_bits - 1)] * norm[block] / sqrt(B)
+ * with B = min(head_dim, 256) and one fp32 norm per block of B consecutive
+ * dims (one per row up to head_dim 256, two at 512).  The output is the
+ * attention result in the same rotated basis; attn_fwht_undo takes it back.
+ *   v_codes   uint8 indices, packed like k_cache; 16-byte aligned
+ *   v_norms   fp32 [slot][n_kv_heads][L_s][head_dim / B], packed like
+ *             k_cache; 4-byte aligned
+ *   codebook  fp32 [2^codebook_bits] levels, device memory; 4-byte aligned
+ *   codebook_bits  1..8 (the pages use 5, 6 and 8)
+ * Everything else (q, k_cache, seq_lens, window, out, head_dim, asynchrony,
+ * workspace, determinism, errors) is as for attn_decode; opts may be NULL.
+ * out must not overlap v_norms or the codebook either.
+ */
+int attn_decode_cb(const void *q, const void *k_cache, const void *v_codes, const float *v_norms,
+                   const float *codebook, int32_t codebook_bits, const int32_t *seq_lens,
+                   int32_t window, float *out, int32_t n_slots, int32_t n_q_heads,
+                   int32_t n_kv_heads, int32_t head_dim, float scale, void *stream,
+                   const attn_decode_options *opts);
+
+/*
+ * attn_fwht_undo -- y = s * (H x) / sqrt(head_dim) per row: the output of
+ * attn_decode_cb back in the original basis (hf2q gemma4 batched_body.rs, the
+ * FWHT sign-undo after the attention; the inverse of the rotation of codebook
+ * V, since H H = head_dim * I).
+ *   x, y   fp32 [n_rows][head_dim], device, 16-byte aligned; y == x (in
+ *          place) is allowed, any other overlap is rejected
+ *   signs  fp32 [head_dim], device, 4-byte aligned: the diagonal s (normally
+ *          +-1, the rotation's sign flips)
+ * head_dim 64, 128, 256 or 512.  fp32 butterflies: the error is a few fp32
+ * ulps of the row's norm.  n_rows = 0 is a no-op.  Asynchronous on `stream`;
+ * no workspace.
+ */
+int attn_fwht_undo(const float *x, const float *signs, float *y, int64_t n_rows, int32_t head_dim,
+                   void *stream);
 
 /*
  * attn_kv_append -- write new tokens' K and V into a fixed-capacity cache (the
