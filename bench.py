@@ -180,11 +180,11 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream(dev)
 
     by_name = {w.name: w for w in WORKLOADS}
-    if args.workload not in by_name:
-        print(f"unknown workload {args.workload}; choose from {sorted(by_name)}", file=sys.stderr)
+    cb_by_name = {w.name: w for w in CODEBOOK_WORKLOADS}
+    if args.workload not in by_name and args.workload not in cb_by_name:
+        print(f"unknown workload {args.workload}; choose from {sorted(by_name) + sorted(cb_by_name)}",
+              file=sys.stderr)
         return 2
-    cfg = by_name[args.workload]
-    window = cfg.windows[0]
 
     def upload(inp):
         return (inp.q.to(dev), inp.k.to(dev), inp.v.to(dev),
@@ -203,14 +203,40 @@ def main(argv=None) -> int:
                                ev_partial_begin=ev0.cuda_event if ev0 is not None else None,
                                ev_partial_end=ev1.cuda_event if ev1 is not None else None)
 
-    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
-    inp = workload_inputs(cfg)
-    tens = upload(inp)
-    out = torch.empty((inp.n_slots, inp.n_q_heads, inp.head_dim), dtype=torch.float32, device=dev)
-    nbytes = kv_bytes(inp.seq_lens, window, inp.n_kv_heads, inp.head_dim, inp.v_int8)
+    if args.workload in by_name:
+        cfg = by_name[args.workload]
+        window = cfg.windows[0]
+        print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+        inp = workload_inputs(cfg)
+        tens = upload(inp)
+        out = torch.empty((inp.n_slots, inp.n_q_heads, inp.head_dim), dtype=torch.float32, device=dev)
+        nbytes = kv_bytes(inp.seq_lens, window, inp.n_kv_heads, inp.head_dim, inp.v_int8)
+        v_format = "int8 codes, fp16 scale per 32 dims" if inp.v_int8 else "fp16"
+
+        def step(ev0=None, ev1=None):
+            call(inp, tens, out, window, ev0, ev1)
+    else:
+        cfg = cb_by_name[args.workload]
+        window = cfg.window
+        print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+        inp = codebook_workload_inputs(cfg)
+        cb_t = tuple(t.to(dev) for t in (inp.q, inp.k, inp.v_codes, inp.v_norms, inp.codebook, inp.signs))
+        out = torch.empty((inp.n_slots, inp.n_q_heads, inp.head_dim), dtype=torch.float32, device=dev)
+        nbytes = cb_kv_bytes(inp.seq_lens, window, inp.n_kv_heads, inp.head_dim)
+        v_format = f"{inp.codebook_bits}-bit codebook indices, fp32 norm per {min(inp.head_dim, 256)} dims"
+        cb_seq = np.asarray(inp.seq_lens, dtype=np.int32)
+
+        def step(ev0=None, ev1=None):
+            q, k, vc, vn, cb, sg = cb_t
+            binding.attn_decode_cb(q, k, vc, vn, cb, inp.codebook_bits, cb_seq, window, out, inp.n_slots,
+                                   inp.n_q_heads, inp.n_kv_heads, inp.head_dim, inp.scale, stream=stream,
+                                   chunk=args.chunk,
+                                   ev_partial_begin=ev0.cuda_event if ev0 is not None else None,
+                                   ev_partial_end=ev1.cuda_event if ev1 is not None else None)
+            binding.attn_fwht_undo(out, sg, out, stream=stream)
 
     for _ in range(args.warmup):
-        call(inp, tens, out, window)
+        step()
     torch.cuda.synchronize()
 
     # Event pairs around the partial kernel on every `event_every`-th step only:
@@ -223,9 +249,9 @@ def main(argv=None) -> int:
     t0 = time.perf_counter()
     for i in range(args.steps):
         if i in evs:
-            call(inp, tens, out, window, *evs[i])
+            step(*evs[i])
         else:
-            call(inp, tens, out, window)
+            step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -258,7 +284,7 @@ def main(argv=None) -> int:
             "head_dim": inp.head_dim,
             "window": window,
             "k_format": "fp16",
-            "v_format": "int8 codes, fp16 scale per 32 dims" if inp.v_int8 else "fp16",
+            "v_format": v_format,
             "kv_bytes_per_call": nbytes,
             "us_per_call": round(ms_per_step * 1e3, 2),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -283,7 +309,7 @@ def main(argv=None) -> int:
         flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         per = []
         for w in WORKLOADS:
-            if w.name != cfg.name:
+            if w.name != cfg.name or args.workload not in by_name:
                 print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
                 pin = workload_inputs(w)
                 ptens = upload(pin)
@@ -337,7 +363,7 @@ def main(argv=None) -> int:
                 })
                 print(f"[bench] {w.name} W={W}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), "
                       f"cold {cold:.2f} us ({per[-1]['cold_gbs']} GB/s)", file=sys.stderr, flush=True)
-            if w.name != cfg.name:
+            if w.name != cfg.name or args.workload not in by_name:
                 del ptens
                 torch.cuda.empty_cache()
 
@@ -492,7 +518,7 @@ def main(argv=None) -> int:
         result["per_config"] = per
 
     # ---- CPU fp64 oracle on a bounded sample of the headline workload
-    if not args.quick and not args.no_cpu_baseline:
+    if not args.quick and not args.no_cpu_baseline and args.workload in by_name:
         from oracle import oracle_attn_decode
         threads = len(os.sched_getaffinity(0))
         n_sample_slots = inp.n_slots

@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import glob
 import os
 import subprocess
 import sys
@@ -11,12 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "attn_decode.hip")
-DEPS = [
-    SRC,
-    os.path.join(PKG, "csrc", "attn_decode_kernels.hpp"),
-    os.path.join(PKG, "csrc", "planner.hpp"),
-    os.path.join(ROOT, "include", "attn_decode.h"),
-]
+DEPS = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + [os.path.join(ROOT, "include", "attn_decode.h")]
 LIB = os.path.join(PKG, "libattn_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

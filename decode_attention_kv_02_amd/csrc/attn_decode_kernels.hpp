@@ -151,6 +151,22 @@ __device__ __forceinline__ int upper_index(int n, int x, F key) {
     return lo;
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD
+// b mod 8) and each XCD has its own L2.  The n_sub head blocks of one chunk
+// read the same K and V rows, so they get workgroup ids b, b + 8, b + 16, ...:
+// the same XCD, dispatched close together, so the reads after the first are
+// served by that XCD's L2.  Maps a workgroup id to its work item; a
+// permutation of [0, n_items) (the tail that does not fill 8 * n_sub ids is
+// left in place).
+__device__ __forceinline__ int xcd_item(int b, int n_items, int n_sub) {
+    if (n_sub == 1) return b;
+    const int z = 8 * n_sub;
+    if (b >= (n_items / z) * z) return b;
+    const int grp = b / z;
+    const int rem = b - grp * z;
+    return (grp * 8 + (rem & 7)) * n_sub + (rem >> 3);
+}
+
 // ---------------------------------------------------------------- chunk merge
 
 // Log-sum-exp merge of the nc chunk partials of GB consecutive query heads
@@ -291,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     constexpr int CB_B = D < 256 ? D : 256;             // codebook norm block
     static_assert(kThreads == 256, "one thread per codebook table entry");
 
-    const int item = blockIdx.x;
+    const int item = xcd_item(blockIdx.x, args.n_items, args.n_sub);
     int si = upper_index(args.n_slots, item, [&](int i) { return args.slot[i].item_begin; });
     si -= args.slot[si].lead_off;
     const SlotDesc sd = args.slot[si];   // group leader: the longest query of the group

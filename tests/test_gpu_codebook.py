@@ -64,6 +64,7 @@ CASES = [
     ((3000, 129), 16, 4, 512, 6, 300),
     ((5000,), 16, 8, 256, 8, 1024),
     ((63, 65, 1), 4, 1, 64, 5, 0),
+    ((6000, 2049), 16, 2, 512, 8, 0),      # G = 8: the global-layer shape
 ]
 
 

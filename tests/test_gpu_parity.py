@@ -81,6 +81,8 @@ EDGE = [
     ((1500, 1500), 32, 8, 128, False, 999),
     ((0, 0), 2, 2, 256, False, 0),
     ((63, 64, 65, 4095, 4096, 4097), 16, 8, 256, False, 0),
+    ((5000, 3000, 1), 32, 2, 256, True, 0),     # G = 16: four head blocks per chunk
+    ((9000, 700), 16, 2, 512, False, 0),        # G = 8 at D = 512
 ]
 
 
