@@ -27,8 +27,11 @@ One JSON line is printed.  Besides the contract fields it carries
   * ``cpu_baseline``: the CPU fp64 oracle timed on a bounded sample of the same
     workload on this host's cores;
   * ``per_config``: every workload preset, warm (back-to-back calls, wall clock
-    between device synchronisations) and cold (the same with a 1 GiB read of
-    another buffer before every call, minus the time of those reads alone),
+    between device synchronisations), cold (the same with a 1 GiB read of
+    another buffer before every call, minus the time of those reads alone) and
+    graph (20 calls captured into one HIP graph and replayed: the GPU time per
+    call without the Python and launch cost on the host, as a decode loop that
+    captures its step sees it),
     plus the codebook-V presets (``attn_decode_cb`` followed by ``attn_fwht_undo``
     in place; bytes = fp16 K, one index byte per V element and the fp32 norms),
     the fixed-capacity cache presets (``attn_decode_cache``: a
@@ -195,10 +198,10 @@ def main(argv=None) -> int:
         e.record(stream)  # materialise the underlying hipEvent_t
         return e
 
-    def call(inp, tens, out, W, ev0=None, ev1=None):
+    def call(inp, tens, out, W, ev0=None, ev1=None, st=None):
         q, k, v, vs = tens
         binding.attn_decode_ex(q, k, v, vs, inp.seq_lens, W, out, inp.n_slots, inp.n_q_heads,
-                               inp.n_kv_heads, inp.head_dim, inp.scale, stream=stream,
+                               inp.n_kv_heads, inp.head_dim, inp.scale, stream=st or stream,
                                chunk=args.chunk,
                                ev_partial_begin=ev0.cuda_event if ev0 is not None else None,
                                ev_partial_end=ev1.cuda_event if ev1 is not None else None)
@@ -238,6 +241,30 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    def graph_us_per_call(fn, n_calls=20, n_replays=10):
+        """GPU time per call with the host out of the loop: n_calls calls captured into one
+        graph on a side stream (each call only enqueues kernels; the workspace was sized by
+        the warm-up calls), replayed n_replays times back to back."""
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fn(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(n_calls):
+                fn(side)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_replays):
+            graph.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / (n_replays * n_calls)
+        del graph
+        return us
 
     # Event pairs around the partial kernel on every `event_every`-th step only:
     # each event between kernels idles the GPU for several microseconds, so
@@ -350,6 +377,7 @@ def main(argv=None) -> int:
                     call(pin, ptens, pout, W, c0, c1)
                     torch.cuda.synchronize()
                     pk.append(c0.elapsed_time(c1) * 1e3)
+                g_us = graph_us_per_call(lambda st: call(pin, ptens, pout, W, st=st))
                 per.append({
                     "workload": w.name, "window": W, "kv_bytes": nb,
                     "warm_us_per_call": round(warm, 2),
@@ -360,9 +388,13 @@ def main(argv=None) -> int:
                     "cold_hbm_frac": round(nb / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     "cold_us_samples": [round(x, 2) for x in cold_samples],
                     "partial_kernel_us_median": round(statistics.median(pk), 2),
+                    "graph_us_per_call": round(g_us, 2),
+                    "graph_gbs": round(nb / (g_us * 1e-6) / 1e9, 1),
+                    "graph_hbm_frac": round(nb / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 })
                 print(f"[bench] {w.name} W={W}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), "
-                      f"cold {cold:.2f} us ({per[-1]['cold_gbs']} GB/s)", file=sys.stderr, flush=True)
+                      f"cold {cold:.2f} us ({per[-1]['cold_gbs']} GB/s), graph {g_us:.2f} us",
+                      file=sys.stderr, flush=True)
             if w.name != cfg.name or args.workload not in by_name:
                 del ptens
                 torch.cuda.empty_cache()
@@ -377,13 +409,13 @@ def main(argv=None) -> int:
             bout = torch.empty((bi.n_slots, bi.n_q_heads, bi.head_dim), dtype=torch.float32, device=dev)
             b_seq = np.asarray(bi.seq_lens, dtype=np.int32)
 
-            def cb_call(e0=None, e1=None):
+            def cb_call(e0=None, e1=None, st=None):
                 binding.attn_decode_cb(bq, bk, bvc, bvn, bcb, bi.codebook_bits, b_seq, bw.window, bout,
                                        bi.n_slots, bi.n_q_heads, bi.n_kv_heads, bi.head_dim, bi.scale,
-                                       stream=stream,
+                                       stream=st or stream,
                                        ev_partial_begin=e0.cuda_event if e0 is not None else None,
                                        ev_partial_end=e1.cuda_event if e1 is not None else None)
-                binding.attn_fwht_undo(bout, bsg, bout, stream=stream)
+                binding.attn_fwht_undo(bout, bsg, bout, stream=st or stream)
 
             def per_call_us(fn, n):
                 torch.cuda.synchronize()
@@ -410,6 +442,7 @@ def main(argv=None) -> int:
                 torch.cuda.synchronize()
                 pk.append(c0.elapsed_time(c1) * 1e3)
             assert torch.isfinite(bout).all().item(), "non-finite output"
+            g_us = graph_us_per_call(lambda st: cb_call(st=st))
             per.append({
                 "workload": bw.name, "window": bw.window, "kv_bytes": nb,
                 "v_format": f"{bi.codebook_bits}-bit codebook indices, fp32 norm per {min(bi.head_dim, 256)} dims",
@@ -422,6 +455,8 @@ def main(argv=None) -> int:
                 "cold_hbm_frac": round(nb / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "partial_kernel_us_median": round(statistics.median(pk), 2),
                 "partial_kernel_gbs": round(nb / (statistics.median(pk) * 1e-6) / 1e9, 1),
+                "graph_us_per_call": round(g_us, 2),
+                "graph_gbs": round(nb / (g_us * 1e-6) / 1e9, 1),
             })
             print(f"[bench] {bw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), cold {cold:.2f} us, "
                   f"partial {per[-1]['partial_kernel_gbs']} GB/s", file=sys.stderr, flush=True)
@@ -439,10 +474,10 @@ def main(argv=None) -> int:
             c_sid = np.asarray(ci.slot_ids, dtype=np.int32)
             c_pos = np.asarray(ci.positions, dtype=np.int32)
 
-            def cache_call(e0=None, e1=None):
+            def cache_call(e0=None, e1=None, st=None):
                 binding.attn_decode_cache(*ct, c_sid, c_pos, ci.n_queries, ci.n_cache_slots,
                                           ci.capacity, ci.ring, cw.window, cout, ci.n_q_heads,
-                                          ci.n_kv_heads, ci.head_dim, ci.scale, stream=stream,
+                                          ci.n_kv_heads, ci.head_dim, ci.scale, stream=st or stream,
                                           ev_partial_begin=e0.cuda_event if e0 is not None else None,
                                           ev_partial_end=e1.cuda_event if e1 is not None else None)
 
@@ -464,6 +499,7 @@ def main(argv=None) -> int:
             warm = statistics.median(per_call_us(cache_call, args.reps) for _ in range(3))
             cold = statistics.median(per_call_us(flush_then_cache_call, args.reps) -
                                      per_call_us(lambda: flush.sum(), args.reps) for _ in range(5))
+            g_us = graph_us_per_call(lambda st: cache_call(st=st))
             per.append({
                 "workload": cw.name, "window": cw.window, "kv_bytes": read_b, "unique_kv_bytes": uniq_b,
                 "warm_us_per_call": round(warm, 2),
@@ -472,6 +508,8 @@ def main(argv=None) -> int:
                 "cold_us_per_call": round(cold, 2),
                 "cold_gbs": round(read_b / (cold * 1e-6) / 1e9, 1),
                 "cold_hbm_frac": round(read_b / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "graph_us_per_call": round(g_us, 2),
+                "graph_gbs": round(read_b / (g_us * 1e-6) / 1e9, 1),
             })
             print(f"[bench] {cw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), cold {cold:.2f} us",
                   file=sys.stderr, flush=True)

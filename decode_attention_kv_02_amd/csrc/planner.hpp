@@ -118,12 +118,21 @@ inline int64_t target_chunks(int64_t n) {
     return 16;
 }
 
+// A slot whose fp16 K and V rows of one kv head fit in this many bytes is not
+// split: one workgroup streams it in about the time of the first-load latency,
+// and splitting it would add the combine launch (measured: 1 x 256 at
+// head_dim 64 takes the same partial-kernel time in one chunk as in four).
+constexpr int64_t kSingleChunkBytes = 128 * 1024;
+
 // Positions per chunk for a slot attending n positions (n >= 1).  Depends on
-// the slot's own length only, so a slot is split the same way in every batch.
-inline int64_t chunk_for(int64_t n, int32_t forced) {
+// the slot's own length and head_dim only, so a slot is split the same way in
+// every batch.
+inline int64_t chunk_for(int64_t n, int32_t head_dim, int32_t forced) {
     int64_t c;
     if (forced > 0) {
         c = forced;
+    } else if (n * 4 * head_dim <= kSingleChunkBytes) {
+        c = ceil_div(n, kChunkQuantum) * kChunkQuantum;
     } else {
         c = ceil_div(n, target_chunks(n));
         c = ceil_div(c, kChunkQuantum) * kChunkQuantum;
@@ -248,7 +257,7 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
             sp.chunk = 0;
             sp.n_chunks = 1;
         } else {
-            const int64_t c = chunk_for(sp.n, chunk);
+            const int64_t c = chunk_for(sp.n, head_dim, chunk);
             sp.chunk = (int32_t)(c > sp.n ? sp.n : c);
             sp.n_chunks = (int32_t)ceil_div(sp.n, sp.chunk);
         }
