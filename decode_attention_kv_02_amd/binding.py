@@ -52,6 +52,7 @@ class _Options(ctypes.Structure):
         ("merge_mode", ctypes.c_int32),
         ("ev_partial_begin", ctypes.c_void_p),
         ("ev_partial_end", ctypes.c_void_p),
+        ("path", ctypes.c_int32),
     ]
 
 
@@ -205,13 +206,15 @@ def attn_decode(q, k_cache, v_cache, v_scales, seq_lens, window: int, out,
 def attn_decode_ex(q, k_cache, v_cache, v_scales, seq_lens, window: int, out,
                    n_slots: Optional[int], n_q_heads: int, n_kv_heads: int, head_dim: int,
                    scale: float, stream=None, chunk: int = 0, merge_mode: int = 0,
-                   ev_partial_begin: Optional[int] = None, ev_partial_end: Optional[int] = None) -> None:
+                   ev_partial_begin: Optional[int] = None, ev_partial_end: Optional[int] = None,
+                   path: int = 0) -> None:
     """attn_decode with a forced chunk size, a merge mode (0 automatic, 1 combine kernel,
-    2 in-kernel merge) and/or raw hipEvent_t handles around the partial kernel."""
+    2 in-kernel merge), raw hipEvent_t handles around the partial kernel, and/or a forced
+    partial kernel (path: 0 automatic, 1 lanes, 2 matrix cores)."""
     lib = load_library()
     seq_arr, n_slots, dev, (pq, pk, pv, ps, po) = _marshal(
         q, k_cache, v_cache, v_scales, seq_lens, out, n_slots, n_q_heads, n_kv_heads, head_dim)
-    opts = _Options(int(chunk), int(merge_mode), ev_partial_begin or None, ev_partial_end or None)
+    opts = _Options(int(chunk), int(merge_mode), ev_partial_begin or None, ev_partial_end or None, int(path))
     rc = lib.attn_decode_ex(pq, pk, pv, ps, seq_arr, int(window), po, int(n_slots), int(n_q_heads),
                             int(n_kv_heads), int(head_dim), float(scale), _stream_handle(stream, dev),
                             ctypes.byref(opts))
@@ -222,7 +225,8 @@ def attn_decode_ex(q, k_cache, v_cache, v_scales, seq_lens, window: int, out,
 def attn_decode_cb(q, k_cache, v_codes, v_norms, codebook, codebook_bits: int, seq_lens, window: int, out,
                    n_slots: Optional[int], n_q_heads: int, n_kv_heads: int, head_dim: int, scale: float,
                    stream=None, chunk: int = 0, merge_mode: int = 0,
-                   ev_partial_begin: Optional[int] = None, ev_partial_end: Optional[int] = None) -> None:
+                   ev_partial_begin: Optional[int] = None, ev_partial_end: Optional[int] = None,
+                   path: int = 0) -> None:
     """Decode attention with codebook V (uint8 indices, fp32 norms per min(D, 256) dims, fp32
     codebook of 2**codebook_bits levels); out is in the rotated basis (see attn_fwht_undo)."""
     lib = load_library()
@@ -236,7 +240,7 @@ def attn_decode_cb(q, k_cache, v_codes, v_norms, codebook, codebook_bits: int, s
     if not 1 <= bits <= 8:
         raise AttnDecodeError(ATTN_DECODE_EINVAL, "codebook_bits must be in 1..8")
     pc = _dev_ptr(codebook, "codebook", torch.float32, 1 << bits, dev)
-    opts = _Options(int(chunk), int(merge_mode), ev_partial_begin or None, ev_partial_end or None)
+    opts = _Options(int(chunk), int(merge_mode), ev_partial_begin or None, ev_partial_end or None, int(path))
     rc = lib.attn_decode_cb(pq, pk, pv, pn, pc, bits, seq_arr, int(window), po, int(n_slots), int(n_q_heads),
                             int(n_kv_heads), int(head_dim), float(scale), _stream_handle(stream, dev),
                             ctypes.byref(opts))
@@ -264,7 +268,7 @@ def attn_decode_cache(q, k_cache, v_cache, v_scales, slot_ids, positions, n_quer
                       n_cache_slots: int, capacity: int, ring: int, window: int, out, n_q_heads: int,
                       n_kv_heads: int, head_dim: int, scale: float, stream=None, chunk: int = 0,
                       merge_mode: int = 0, ev_partial_begin: Optional[int] = None,
-                      ev_partial_end: Optional[int] = None) -> None:
+                      ev_partial_end: Optional[int] = None, path: int = 0) -> None:
     """Enqueue decode attention over a fixed-capacity (linear or ring) cache."""
     lib = load_library()
     sid, n = _seq_array(slot_ids)
@@ -283,7 +287,7 @@ def attn_decode_cache(q, k_cache, v_cache, v_scales, slot_ids, positions, n_quer
     pv = _dev_ptr(v_cache, "v_cache", torch.int8 if int8 else torch.float16, kv, dev)
     ps = _dev_ptr(v_scales, "v_scales", torch.float16, kv // 32, dev) if int8 else None
     po = _dev_ptr(out, "out", torch.float32, n_queries * n_q_heads * head_dim, dev)
-    opts = _Options(int(chunk), int(merge_mode), ev_partial_begin or None, ev_partial_end or None)
+    opts = _Options(int(chunk), int(merge_mode), ev_partial_begin or None, ev_partial_end or None, int(path))
     rc = lib.attn_decode_cache(pq, pk, pv, ps, sid, pos, int(n_queries), int(n_cache_slots),
                                int(capacity), int(ring), int(window), po, int(n_q_heads),
                                int(n_kv_heads), int(head_dim), float(scale),

@@ -22,6 +22,7 @@
 #include "../../include/attn_decode.h"
 #include "planner.hpp"
 #include "attn_decode_kernels.hpp"
+#include "attn_mfma_kernels.hpp"
 #include "kv_append_kernels.hpp"
 #include "fwht_kernels.hpp"
 
@@ -145,6 +146,25 @@ partial_fn select_partial(int D, int QB, int GB, int vf) {
     return nullptr;
 }
 
+template <int D>
+partial_fn mfma_for_format(int vf) {
+    switch (vf) {
+        case kVF16: return attn_partial_mfma_kernel<D, kVF16>;
+        case kVI8: return attn_partial_mfma_kernel<D, kVI8>;
+        case kVCB: return attn_partial_mfma_kernel<D, kVCB>;
+    }
+    return nullptr;
+}
+
+partial_fn select_partial_mfma(int D, int vf) {
+    switch (D) {
+        case 128: return mfma_for_format<128>(vf);
+        case 256: return mfma_for_format<256>(vf);
+        case 512: return mfma_for_format<512>(vf);
+    }
+    return nullptr;
+}
+
 combine_fn select_combine(int D) {
     switch (D) {
         case 64: return attn_combine_kernel<64>;
@@ -195,12 +215,14 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
            int32_t D, float scale, void *stream_ptr, const attn_decode_options *opts) {
     const int32_t chunk = opts ? opts->chunk : 0;
     const int32_t merge_mode = opts ? opts->merge_mode : 0;
+    const int32_t path = opts ? opts->path : 0;
 
     CallPlan plan;
-    std::string err = make_plan(spans, n_q, n_kv, D, chunk, merge_mode, plan);
+    std::string err = make_plan(spans, n_q, n_kv, D, chunk, merge_mode, plan, path);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
 
-    const partial_fn pk = select_partial(D, plan.QB, plan.GB, vsrc.format);
+    const partial_fn pk = plan.mfma ? select_partial_mfma(D, vsrc.format)
+                                    : select_partial(D, plan.QB, plan.GB, vsrc.format);
     const combine_fn ck = select_combine(D);
     if (pk == nullptr || ck == nullptr) return fail(ATTN_DECODE_EINVAL, "no kernel for this shape");
 

@@ -71,8 +71,9 @@ struct LaunchGroup {
 };
 
 struct CallPlan {
+    bool mfma = false;   // matrix-core partial kernel (groups of 8 or 16 heads per workgroup)
     int G = 1;           // query heads per KV head
-    int GB = 1;          // query heads per workgroup (1, 2 or 4; divides G)
+    int GB = 1;          // query heads per workgroup (1, 2 or 4 on the lanes, 8 or 16 on the matrix cores; divides G)
     int QB = 1;          // queries per workgroup (QB * GB <= 4); 1 when no group formed
     int n_sub = 1;       // G / GB workgroups share one (slot, kv head, chunk)
     std::vector<SlotPlan> slots;
@@ -232,14 +233,35 @@ inline int heads_per_workgroup(int G) {
     return 1;
 }
 
+// Which partial kernel computes a call.  The matrix-core kernel
+// (attn_partial_mfma_kernel) applies to a multiple of 8 query heads per kv
+// head at head_dim >= 128.  kPathAuto takes it where it measured faster than
+// the lane kernel on MI355X (graph-replayed calls over 0.27-1.1 GB caches):
+// 16 or more heads per kv head at any head_dim (2.0-3.4x: e.g. 32 q / 2 kv
+// heads at 512, 170 -> 84 us) and 8 at head_dim 128 (2.2-2.6x); with 8 heads
+// at 256 or 512 the lane kernel stays ahead (fp16 74 vs 94 us at 256, codebook
+// 125 vs 156 us at 512).  kPathLanes / kPathMatrix force one.
+enum KernelPath { kPathAuto = 0, kPathLanes = 1, kPathMatrix = 2 };
+
+inline bool mfma_applies(int G, int head_dim) { return G % 8 == 0 && head_dim >= 128; }
+inline bool mfma_preferred(int G, int head_dim) {
+    return mfma_applies(G, head_dim) && (G % 16 == 0 || head_dim == 128);
+}
+
 // Builds the plan from the query spans; returns "" on success or an error message.
 inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, int32_t n_kv,
-                             int32_t head_dim, int32_t chunk, int32_t merge_mode, CallPlan &plan) {
+                             int32_t head_dim, int32_t chunk, int32_t merge_mode, CallPlan &plan,
+                             int32_t path = kPathAuto) {
     plan = CallPlan();
     const int32_t n_slots = (int32_t)spans.size();
-    plan.fuse_limit = merge_mode == kMergeInKernel ? kFusedMaxChunks : 1;
     plan.G = n_q / n_kv;
-    plan.GB = heads_per_workgroup(plan.G);
+    if (path != kPathAuto && path != kPathLanes && path != kPathMatrix) return "unknown kernel path";
+    if (path == kPathMatrix && !mfma_applies(plan.G, head_dim))
+        return "the matrix-core path needs a multiple of 8 query heads per kv head and head_dim >= 128";
+    plan.mfma = path == kPathMatrix || (path == kPathAuto && mfma_preferred(plan.G, head_dim));
+    // the matrix-core kernel always merges in the combine kernel
+    plan.fuse_limit = merge_mode == kMergeInKernel && !plan.mfma ? kFusedMaxChunks : 1;
+    plan.GB = plan.mfma ? (plan.G % 16 == 0 ? 16 : 8) : heads_per_workgroup(plan.G);
     plan.n_sub = plan.G / plan.GB;
     plan.slots.resize(n_slots);
     int64_t part = 0;
@@ -280,7 +302,7 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
     // size (draft tokens of a speculative-verify step) share one workgroup, up
     // to 4 / GB of them, so their K and V rows are read once.  Not with the
     // in-kernel merge.
-    const int qb_max = merge_mode == kMergeInKernel ? 1 : (GROUP_ROWS / plan.GB);
+    const int qb_max = (merge_mode == kMergeInKernel || plan.mfma) ? 1 : (GROUP_ROWS / plan.GB);
     if (qb_max > 1) {
         std::vector<int32_t> idx;
         for (int32_t s = 0; s < n_slots; ++s)
