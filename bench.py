@@ -113,7 +113,7 @@ def read_traffic(workload: str, window: int):
         return None
     vals = {}
     for line in open(path):
-        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        m = re.match(r"^\s*([a-z0-9_]+)\s*:\s*(\S+)", line)
         if m:
             vals[m.group(1)] = m.group(2)
     if vals.get("kernel_source_sha256_16") != kernel_source_digest():
@@ -136,6 +136,9 @@ def parse_args(argv=None):
     ap.add_argument("--event-every", type=int, default=8,
                     help="time the partial kernel with HIP events on every N-th timed step")
     ap.add_argument("--chunk", type=int, default=0, help="forced chunk size (tuning only)")
+    ap.add_argument("--gqa-sweep", action="store_true",
+                    help="only time the lane and the matrix-core partial kernels on groups of 8 and 16 "
+                         "query heads per kv head (graph-replayed calls, one JSON line per shape)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -155,6 +158,88 @@ def calibrate_copy(nbytes: int) -> int:
     return 0
 
 
+# Shapes with 8 or 16 query heads per kv head (gemma4's global layers have 8 at head_dim 512),
+# inputs drawn on the GPU (timing only): name, slots x length, q heads, kv heads, head_dim, V format
+GQA_SHAPES = (
+    ("g8_d512_fp16_4x32768", (32768,) * 4, 16, 2, 512, "fp16"),
+    ("g8_d512_codebook_4x32768", (32768,) * 4, 16, 2, 512, "codebook"),
+    ("g8_d256_fp16_4x32768", (32768,) * 4, 16, 2, 256, "fp16"),
+    ("g8_d256_codebook_4x32768", (32768,) * 4, 16, 2, 256, "codebook"),
+    ("g8_d128_fp16_8x8192", (8192,) * 8, 64, 8, 128, "fp16"),
+    ("g8_d128_int8_8x8192", (8192,) * 8, 64, 8, 128, "int8"),
+    ("g8_d128_codebook_8x8192", (8192,) * 8, 64, 8, 128, "codebook"),
+    ("g16_d512_fp16_4x16384", (16384,) * 4, 32, 2, 512, "fp16"),
+    ("g16_d256_fp16_4x16384", (16384,) * 4, 32, 2, 256, "fp16"),
+    ("g16_d256_int8_4x16384", (16384,) * 4, 32, 2, 256, "int8"),
+    ("g16_d128_fp16_8x8192", (8192,) * 8, 64, 4, 128, "fp16"),
+)
+
+
+def gqa_sweep() -> int:
+    import numpy as np
+    import torch
+    from decode_attention_kv_02_amd import binding
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    for name, seq, nq, nkv, d, fmt in GQA_SHAPES:
+        n = sum(seq) * nkv * d
+        q = torch.randn(len(seq) * nq * d, generator=gen, device=dev).half()
+        k = torch.randn(n, generator=gen, device=dev).half()
+        out = torch.empty((len(seq), nq, d), dtype=torch.float32, device=dev)
+        seq_a = np.asarray(seq, dtype=np.int32)
+        if fmt == "codebook":
+            vc = torch.randint(0, 256, (n,), generator=gen, device=dev, dtype=torch.uint8)
+            vn = torch.rand(n // min(d, 256), generator=gen, device=dev) * 4 + 14
+            cb = torch.randn(256, generator=gen, device=dev)
+            nb = cb_kv_bytes(seq, 0, nkv, d)
+
+            def call(st, path):
+                binding.attn_decode_cb(q, k, vc, vn, cb, 8, seq_a, 0, out, len(seq), nq, nkv, d, d ** -0.5,
+                                       stream=st, path=path)
+        else:
+            if fmt == "fp16":
+                v, vs = torch.randn(n, generator=gen, device=dev).half(), None
+            else:
+                v = torch.randint(-127, 128, (n,), generator=gen, device=dev, dtype=torch.int8)
+                vs = (torch.rand(n // 32, generator=gen, device=dev) * 0.03).half()
+            nb = kv_bytes(seq, 0, nkv, d, fmt == "int8")
+
+            def call(st, path):
+                binding.attn_decode_ex(q, k, v, vs, seq_a, 0, out, len(seq), nq, nkv, d, d ** -0.5, stream=st,
+                                       path=path)
+        res = {"shape": name, "kv_bytes": nb}
+        for path, key in ((1, "lanes"), (2, "matrix")):
+            side = torch.cuda.Stream(device=dev)
+            side.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(side):
+                for _ in range(3):
+                    call(side, path)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(20):
+                    call(side, path)
+            torch.cuda.synchronize()
+            samples = []
+            for _ in range(5):
+                t0 = time.perf_counter()
+                for _ in range(10):
+                    graph.replay()
+                torch.cuda.synchronize()
+                samples.append((time.perf_counter() - t0) * 1e6 / 200)
+            us = statistics.median(samples)
+            res[key + "_us"] = round(us, 2)
+            res[key + "_hbm_frac"] = round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            del graph
+        res["automatic"] = "matrix" if ((nq // nkv) % 16 == 0 or d == 128) else "lanes"
+        print(json.dumps(res), flush=True)
+        del q, k, out
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
@@ -165,6 +250,8 @@ def main(argv=None) -> int:
 
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy)
+    if args.gqa_sweep:
+        return gqa_sweep()
 
     import numpy as np
     import torch
