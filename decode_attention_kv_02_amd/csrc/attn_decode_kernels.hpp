@@ -261,11 +261,19 @@ __device__ __forceinline__ void merge_chunks(const LaunchArgs &args, int64_t par
 
 // ---------------------------------------------------------------- partial kernel
 
-template <int D>
+// U: rows per lane group in flight per register buffer.  fp16 V at
+// head_dim >= 256 takes half of it, which keeps 4-row variants at two waves
+// per SIMD (the full U needs more than 256 VGPRs).  Measured on graph-replayed
+// calls: a speculative verify with 4 drafts at 2 heads 357 -> 335 us, 4 heads
+// per kv head at 256 187 -> 177 us, the ragged 4-slot call 63.4 -> 61.9 us; the
+// byte formats lose with it.  U depends on head_dim and the V format only, so
+// a query computed in a group of drafts and alone takes the same steps.
+template <int D, int VF>
 struct Geometry {
     static constexpr int R = D / 16;                        // lanes per KV row (16 dims each)
     static constexpr int P = 64 / R;                        // rows per wave load
-    static constexpr int U = (D == 512) ? 4 : (16 / P);     // loads per wave iteration
+    static constexpr int U0 = (D == 512) ? 4 : (16 / P);
+    static constexpr int U = (VF == kVF16 && D >= 256) ? U0 / 2 : U0;   // loads per wave iteration
     static constexpr int RW = P * U;                        // rows per wave iteration
     static constexpr int HALF = D / 2;
 };
@@ -300,7 +308,7 @@ struct Frag {
 // element costs one byte extract and one LDS read.
 template <int D, int QB, int GB, int VF>
 __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs args) {
-    using Geo = Geometry<D>;
+    using Geo = Geometry<D, VF>;
     constexpr int R = Geo::R, P = Geo::P, U = Geo::U, RW = Geo::RW, HALF = Geo::HALF;
     constexpr int NR = QB * GB;   // rows: (query of the group, head of the block)
     constexpr bool BYTES = VF != kVF16;                 // one byte per V element
