@@ -139,6 +139,7 @@ def parse_args(argv=None):
     ap.add_argument("--gqa-sweep", action="store_true",
                     help="only time the lane and the matrix-core partial kernels on groups of 8 and 16 "
                          "query heads per kv head (graph-replayed calls, one JSON line per shape)")
+    ap.add_argument("--only", default="", help="with --gqa-sweep: comma-separated shape names to run")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -175,7 +176,7 @@ GQA_SHAPES = (
 )
 
 
-def gqa_sweep() -> int:
+def gqa_sweep(only: str = "") -> int:
     import numpy as np
     import torch
     from decode_attention_kv_02_amd import binding
@@ -183,7 +184,14 @@ def gqa_sweep() -> int:
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(1)
+    names = [x for x in only.split(",") if x]
+    unknown = set(names) - {sh[0] for sh in GQA_SHAPES}
+    if unknown:
+        print(f"unknown shapes {sorted(unknown)}; choose from {[sh[0] for sh in GQA_SHAPES]}", file=sys.stderr)
+        return 2
     for name, seq, nq, nkv, d, fmt in GQA_SHAPES:
+        if names and name not in names:
+            continue
         n = sum(seq) * nkv * d
         q = torch.randn(len(seq) * nq * d, generator=gen, device=dev).half()
         k = torch.randn(n, generator=gen, device=dev).half()
@@ -251,7 +259,7 @@ def main(argv=None) -> int:
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy)
     if args.gqa_sweep:
-        return gqa_sweep()
+        return gqa_sweep(args.only)
 
     import numpy as np
     import torch
