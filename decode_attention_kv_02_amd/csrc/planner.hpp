@@ -236,11 +236,12 @@ inline int heads_per_workgroup(int G) {
 // Which partial kernel computes a call.  The matrix-core kernel
 // (attn_partial_mfma_kernel) applies to a multiple of 8 query heads per kv
 // head at head_dim >= 128.  kPathAuto takes it where it measured faster than
-// the lane kernel on MI355X (graph-replayed calls over 0.27-1.1 GB caches):
-// 16 or more heads per kv head at any head_dim (2.0-3.4x: e.g. 32 q / 2 kv
-// heads at 512, 170 -> 84 us) and 8 at head_dim 128 (2.2-2.6x); with 8 heads
-// at 256 or 512 the lane kernel stays ahead (fp16 74 vs 94 us at 256, codebook
-// 125 vs 156 us at 512).  kPathLanes / kPathMatrix force one.
+// the lane kernel on MI355X (graph-replayed calls over 0.1-0.5 GB caches):
+// 16 heads per kv head at any head_dim (1.1-3.4x: 32 q / 2 kv heads at 512,
+// 129 -> 84 us; 64 q / 4 kv at 128, 145 -> 43 us) and 8 at head_dim 128
+// (2.1-2.6x); with 8 heads at 256 or 512 the lane kernel stays ahead (fp16
+// 73 vs 94 us at 256, codebook 132 vs 156 us at 512).  kPathLanes /
+// kPathMatrix force one.
 enum KernelPath { kPathAuto = 0, kPathLanes = 1, kPathMatrix = 2 };
 
 inline bool mfma_applies(int G, int head_dim) { return G % 8 == 0 && head_dim >= 128; }
