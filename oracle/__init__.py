@@ -14,9 +14,12 @@ from .oracle import (  # noqa: F401
     half_to_double,
     oracle_attn_decode,
     oracle_attn_decode_cache,
+    oracle_attn_decode_cache_cb,
     oracle_attn_decode_cb,
+    oracle_codebook_encode,
     oracle_fwht_undo,
     oracle_kv_append,
+    oracle_kv_append_cb,
     oracle_library_path,
     quantize_blocks,
 )

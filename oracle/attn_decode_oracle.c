@@ -1,7 +1,8 @@
 /*
  * attn_decode_oracle.c -- CPU fp64 oracle for single-query (decode) attention
- * over a grouped-query KV cache with an F16 K cache and either an F16 V cache
- * or a block-int8 V cache.
+ * over a grouped-query KV cache with an F16 K cache and an F16, block-int8 or
+ * codebook V cache, and of the steps around it (the KV append and codebook
+ * encode before it, the undo of the codebook rotation after it).
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the correctness reference that the
  * HIP path is compared against.  Only the tests, the smoke check and the
@@ -513,6 +514,9 @@ static uint16_t oracle_quantize_block(const float *b, int8_t *codes)
     return s16;
 }
 
+static int check_append(const int32_t *slot_ids, const int32_t *positions, int32_t n_rows,
+                        int32_t n_cache_slots, int32_t capacity, int32_t ring);
+
 /* Exposed for pinning: quantises n_blocks blocks of 32 floats. */
 void oracle_quantize_blocks(const float *v, int64_t n_blocks, int8_t *codes, uint16_t *scales)
 {
@@ -533,19 +537,11 @@ int oracle_kv_append(const float *k_new, const float *v_new, uint16_t *k_cache, 
                      int32_t n_rows, int32_t n_cache_slots, int32_t capacity, int32_t ring,
                      int32_t n_kv, int32_t head_dim)
 {
-    int32_t i, j;
+    int32_t i;
     if (n_rows < 0 || n_cache_slots < 0 || capacity <= 0 || n_kv <= 0 || head_dim <= 0) return -1;
     if (ring != 0 && ring != 1) return -1;
     if (v_scales != NULL && head_dim % 32 != 0) return -1;
-    for (i = 0; i < n_rows; ++i) {
-        if (slot_ids[i] < 0 || slot_ids[i] >= n_cache_slots || positions[i] < 0) return -1;
-        if (!ring && positions[i] >= capacity) return -1;
-        for (j = 0; j < i; ++j) {
-            const int64_t ri = ring ? positions[i] % capacity : positions[i];
-            const int64_t rj = ring ? positions[j] % capacity : positions[j];
-            if (slot_ids[i] == slot_ids[j] && ri == rj) return -1;
-        }
-    }
+    if (check_append(slot_ids, positions, n_rows, n_cache_slots, capacity, ring) != 0) return -1;
     const int32_t D = head_dim;
     for (i = 0; i < n_rows; ++i) {
         const int64_t phys = ring ? positions[i] % capacity : positions[i];
@@ -568,4 +564,178 @@ int oracle_kv_append(const float *k_new, const float *v_new, uint16_t *k_cache, 
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Codebook V: the fixed-capacity cache and the encode of new rows (the
+ * hybrid regime's KV encode: hf2q gemma4 batched_body.rs, the attention
+ * phase's F16 copy of K and FWHT-V encode per slot and position into packed
+ * bytes plus norms; mlx-native flash_attn_vec_hybrid.metal, the TQ-HB V
+ * layout and the D = 512 per-block norms that the encode must produce).  The
+ * pages give the call and the layout it fills, not the encode's steps; the
+ * plain reading, taken here, is to rotate the row, take each block's norm,
+ * and quantise each normalised coordinate to its nearest level:
+ *   y      = H (s * v) / sqrt(D)       (H by its entries, see hadamard_sign)
+ *   norm_b = sqrt(sum_{i in block b} y_i^2),     blocks of B = min(D, 256)
+ *   u_i    = y_i * sqrt(B) / norm_b              (0 when norm_b == 0)
+ *   code_i = argmin_j |u_i - codebook[j]|, j < 2^bits, lowest j on a tie
+ *            (0 when norm_b == 0: every level then decodes to 0)
+ * so that codebook[code_i] * norm_b / sqrt(B) ~ y_i, the decode of
+ * oracle_attend.  Norms are stored as float (rounded from double).
+ * ------------------------------------------------------------------------ */
+
+/* Encodes one row of D floats; u_out (may be NULL) receives the u_i in double. */
+static int oracle_encode_row(const float *v, const float *signs, const float *codebook, int32_t n_levels,
+                             int32_t D, uint8_t *codes, float *norms, double *u_out)
+{
+    const int32_t B = D < 256 ? D : 256;
+    int32_t i, j, b;
+    double *y = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!y) return -2;
+    const double inv = 1.0 / sqrt((double)D);
+    for (i = 0; i < D; ++i) {
+        double acc = 0.0;
+        for (j = 0; j < D; ++j) acc += hadamard_sign((uint32_t)i, (uint32_t)j) * (double)signs[j] * (double)v[j];
+        y[i] = acc * inv;
+    }
+    for (b = 0; b < D / B; ++b) {
+        double ss = 0.0;
+        for (i = b * B; i < (b + 1) * B; ++i) ss += y[i] * y[i];
+        const double nb = sqrt(ss);
+        norms[b] = (float)nb;
+        for (i = b * B; i < (b + 1) * B; ++i) {
+            const double u = nb == 0.0 ? 0.0 : y[i] * sqrt((double)B) / nb;
+            int32_t best = 0;
+            if (nb != 0.0) {
+                double dbest = fabs(u - (double)codebook[0]);
+                for (j = 1; j < n_levels; ++j) {
+                    const double dj = fabs(u - (double)codebook[j]);
+                    if (dj < dbest) { dbest = dj; best = j; }
+                }
+            }
+            codes[i] = (uint8_t)best;
+            if (u_out) u_out[i] = u;
+        }
+    }
+    free(y);
+    return 0;
+}
+
+/*
+ * oracle_codebook_encode_f64 -- the encode above on n_rows rows.
+ *   v      float [n_rows][D]; signs float [D]; codebook float [2^bits]
+ *   codes  uint8 [n_rows][D]; norms float [n_rows][D / B]; u double [n_rows][D] or NULL
+ * D a power of two; bits 1..8.  Returns 0, -1 for invalid arguments, -2 for allocation failure.
+ */
+int oracle_codebook_encode_f64(const float *v, const float *signs, const float *codebook, int32_t bits,
+                               int64_t n_rows, int32_t head_dim, uint8_t *codes, float *norms, double *u)
+{
+    int64_t r;
+    if (head_dim <= 0 || (head_dim & (head_dim - 1)) != 0 || n_rows < 0) return -1;
+    if (bits < 1 || bits > 8) return -1;
+    const int32_t B = head_dim < 256 ? head_dim : 256;
+    for (r = 0; r < n_rows; ++r) {
+        const int rc = oracle_encode_row(v + r * head_dim, signs, codebook, 1 << bits, head_dim,
+                                         codes + r * head_dim, norms + r * (head_dim / B),
+                                         u ? u + r * head_dim : NULL);
+        if (rc != 0) return rc;
+    }
+    return 0;
+}
+
+/* Checks of an append's placement shared by both V formats: every row names a
+ * slot in range and a storable position, and no two rows share a cache row. */
+static int check_append(const int32_t *slot_ids, const int32_t *positions, int32_t n_rows,
+                        int32_t n_cache_slots, int32_t capacity, int32_t ring)
+{
+    int32_t i, j;
+    for (i = 0; i < n_rows; ++i) {
+        if (slot_ids[i] < 0 || slot_ids[i] >= n_cache_slots || positions[i] < 0) return -1;
+        if (!ring && positions[i] >= capacity) return -1;
+        for (j = 0; j < i; ++j) {
+            const int64_t ri = ring ? positions[i] % capacity : positions[i];
+            const int64_t rj = ring ? positions[j] % capacity : positions[j];
+            if (slot_ids[i] == slot_ids[j] && ri == rj) return -1;
+        }
+    }
+    return 0;
+}
+
+/*
+ * oracle_kv_append_cb -- writes n_rows new tokens into a host copy of a cache
+ * with codebook V: K as fp16, V encoded as above into the row of its (slot,
+ * position) (row p linear, p mod capacity ring).
+ *   k_new, v_new  float [n_rows][n_kv][D]; signs float [D]; codebook float [2^bits]
+ *   k_cache fp16 bits, v_codes uint8 [n_cache_slots][n_kv][capacity][D];
+ *   v_norms float [n_cache_slots][n_kv][capacity][D / B]
+ *   u_out   double [n_rows][n_kv][D] or NULL: the normalised coordinates
+ * Returns 0, -1 for invalid arguments (including two rows on one cache row), -2 on allocation failure.
+ */
+int oracle_kv_append_cb(const float *k_new, const float *v_new, const float *signs, const float *codebook,
+                        int32_t bits, uint16_t *k_cache, uint8_t *v_codes, float *v_norms,
+                        const int32_t *slot_ids, const int32_t *positions, int32_t n_rows,
+                        int32_t n_cache_slots, int32_t capacity, int32_t ring, int32_t n_kv,
+                        int32_t head_dim, double *u_out)
+{
+    int32_t i, h, d;
+    if (n_rows < 0 || n_cache_slots < 0 || capacity <= 0 || n_kv <= 0) return -1;
+    if (head_dim <= 0 || (head_dim & (head_dim - 1)) != 0) return -1;
+    if (ring != 0 && ring != 1) return -1;
+    if (bits < 1 || bits > 8) return -1;
+    if (check_append(slot_ids, positions, n_rows, n_cache_slots, capacity, ring) != 0) return -1;
+    const int32_t D = head_dim;
+    const int32_t B = D < 256 ? D : 256;
+    for (i = 0; i < n_rows; ++i) {
+        const int64_t phys = ring ? positions[i] % capacity : positions[i];
+        for (h = 0; h < n_kv; ++h) {
+            const int64_t row = ((int64_t)slot_ids[i] * n_kv + h) * capacity + phys;
+            const int64_t src = ((int64_t)i * n_kv + h) * D;
+            for (d = 0; d < D; ++d) k_cache[row * D + d] = oracle_float_to_half(k_new[src + d]);
+            const int rc = oracle_encode_row(v_new + src, signs, codebook, 1 << bits, D, v_codes + row * D,
+                                             v_norms + row * (D / B), u_out ? u_out + src : NULL);
+            if (rc != 0) return rc;
+        }
+    }
+    return 0;
+}
+
+/*
+ * oracle_attn_decode_cache_cb_f64 -- oracle_attn_decode_cache_f64 with codebook
+ * V (decoded as in oracle_attn_decode_cb_f64; the result is in the rotated basis).
+ *   v_codes uint8 [n_cache_slots][n_kv][capacity][D]; v_norms float [..][capacity][D / B]
+ */
+int oracle_attn_decode_cache_cb_f64(const uint16_t *q, const uint16_t *k, const uint8_t *v_codes,
+                                    const float *v_norms, const float *codebook, int32_t codebook_bits,
+                                    const int32_t *slot_ids, const int32_t *positions,
+                                    int32_t n_queries, int32_t n_cache_slots, int32_t capacity,
+                                    int32_t ring, int32_t window, double *out, int32_t n_q,
+                                    int32_t n_kv, int32_t head_dim, float scale, const int32_t *rows,
+                                    int64_t n_rows, int32_t n_threads)
+{
+    int32_t i;
+    if (n_queries < 0 || n_cache_slots < 0 || capacity <= 0 || n_q <= 0 || n_kv <= 0 ||
+        head_dim <= 0 || window < 0 || (ring != 0 && ring != 1))
+        return -1;
+    if (n_q % n_kv != 0) return -1;
+    if (codebook_bits < 1 || codebook_bits > 8) return -1;
+    const int32_t B = head_dim < 256 ? head_dim : 256;
+    if (head_dim % B != 0) return -1;
+    if (n_threads < 1) n_threads = 1;
+    if (rows == NULL) n_rows = (int64_t)n_queries * n_q;
+    if (n_rows == 0) return 0;
+    for (i = 0; i < n_queries; ++i) {
+        if (slot_ids[i] < 0 || slot_ids[i] >= n_cache_slots) return -1;
+        if (positions[i] < 0 || (!ring && positions[i] >= capacity)) return -1;
+    }
+    if (check_rows(rows, n_rows, (int64_t)n_queries * n_q) != 0) return -1;
+
+    oracle_job jb;
+    memset(&jb, 0, sizeof(jb));
+    jb.q = q; jb.k = k; jb.v = v_codes; jb.v_scales = NULL;
+    jb.codebook = codebook; jb.v_norms = v_norms;
+    jb.cb_mask = (1u << codebook_bits) - 1u; jb.cb_block = B;
+    jb.slot_ids = slot_ids; jb.positions = positions; jb.capacity = capacity; jb.ring = ring;
+    jb.window = window; jb.out = out; jb.n_slots = n_queries; jb.n_q = n_q; jb.n_kv = n_kv;
+    jb.d = head_dim; jb.scale = (double)scale; jb.rows = rows; jb.n_rows = n_rows;
+    return oracle_run(&jb, n_threads);
 }

@@ -81,6 +81,23 @@ def _load():
             ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
         ]
+        lib.oracle_codebook_encode_f64.restype = ctypes.c_int
+        lib.oracle_codebook_encode_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_kv_append_cb.restype = ctypes.c_int
+        lib.oracle_kv_append_cb.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_void_p]
+        lib.oracle_attn_decode_cache_cb_f64.restype = ctypes.c_int
+        lib.oracle_attn_decode_cache_cb_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_int32]
         lib.oracle_attn_decode_f64.restype = ctypes.c_int
         lib.oracle_attn_decode_f64.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -312,3 +329,103 @@ def oracle_fwht_undo(x, signs) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"oracle_fwht_undo_f64 returned {rc}")
     return y
+
+
+def _codebook_args(signs, codebook, bits, head_dim):
+    sg = _as_c(np.asarray(signs, dtype=np.float32), np.float32).reshape(-1)
+    cb = _as_c(np.asarray(codebook, dtype=np.float32), np.float32).reshape(-1)
+    if sg.size != head_dim:
+        raise ValueError("signs must have head_dim entries")
+    if cb.size < (1 << int(bits)):
+        raise ValueError("codebook is shorter than 2**bits")
+    return sg, cb
+
+
+def oracle_codebook_encode(v, signs, codebook, bits):
+    """The oracle's codebook encode of rows of float32 V (last axis D):
+    returns (codes uint8 like v, norms float32 [..., D / B], u float64 like v)."""
+    lib = _load()
+    vv = _as_c(np.asarray(v, dtype=np.float32), np.float32)
+    d = vv.shape[-1]
+    B = min(d, 256)
+    sg, cb = _codebook_args(signs, codebook, bits, d)
+    n = vv.size // d
+    codes = np.zeros(vv.shape, dtype=np.uint8)
+    norms = np.zeros(vv.shape[:-1] + (d // B,), dtype=np.float32)
+    u = np.zeros(vv.shape, dtype=np.float64)
+    rc = lib.oracle_codebook_encode_f64(_ptr(vv), _ptr(sg), _ptr(cb), int(bits), n, d, _ptr(codes),
+                                        _ptr(norms), _ptr(u))
+    if rc != 0:
+        raise ValueError(f"oracle_codebook_encode_f64 returned {rc}")
+    return codes, norms, u
+
+
+def oracle_kv_append_cb(k_new, v_new, signs, codebook, bits, k_cache, v_codes, v_norms, slot_ids,
+                        positions, n_cache_slots, capacity, ring, n_kv, head_dim):
+    """Writes new tokens into copies of a codebook-V cache; returns (k_cache, v_codes, v_norms, u)
+    with u float64 [n_rows, n_kv, D] the normalised coordinates each code was chosen for."""
+    lib = _load()
+    sid = np.ascontiguousarray(np.asarray(slot_ids, dtype=np.int32))
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    n_rows = int(sid.shape[0])
+    kn = _as_c(np.asarray(k_new), np.float32)
+    vn = _as_c(np.asarray(v_new), np.float32)
+    if kn.size != n_rows * n_kv * head_dim or vn.size != kn.size:
+        raise ValueError("k_new / v_new have the wrong number of elements")
+    sg, cb = _codebook_args(signs, codebook, bits, head_dim)
+    kc = np.array(k_cache, dtype=np.float16, copy=True).reshape(-1)
+    vc = np.array(v_codes, dtype=np.uint8, copy=True).reshape(-1)
+    nm = np.array(v_norms, dtype=np.float32, copy=True).reshape(-1)
+    if vc.size != kc.size or nm.size != kc.size // min(head_dim, 256):
+        raise ValueError("cache arrays have inconsistent sizes")
+    u = np.zeros((n_rows, n_kv, head_dim), dtype=np.float64)
+    rc = lib.oracle_kv_append_cb(_ptr(kn), _ptr(vn), _ptr(sg), _ptr(cb), int(bits), _ptr(kc), _ptr(vc),
+                                 _ptr(nm), _ptr(sid), _ptr(pos), n_rows, int(n_cache_slots), int(capacity),
+                                 int(ring), int(n_kv), int(head_dim), _ptr(u))
+    if rc != 0:
+        raise ValueError(f"oracle_kv_append_cb returned {rc}")
+    return kc, vc, nm, u
+
+
+def oracle_attn_decode_cache_cb(q, k, v_codes, v_norms, codebook, codebook_bits, slot_ids, positions,
+                                n_cache_slots, capacity, ring, window, n_q, n_kv, head_dim, scale,
+                                rows=None, threads=None) -> np.ndarray:
+    """oracle_attn_decode_cache with codebook V (result in the rotated basis).
+
+    v_codes: uint8 like k; v_norms: float32 [n_cache_slots, n_kv, capacity, D / B], B = min(D, 256).
+    """
+    lib = _load()
+    sid = np.ascontiguousarray(np.asarray(slot_ids, dtype=np.int32))
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    nqry = int(sid.shape[0])
+    if pos.shape[0] != nqry:
+        raise ValueError("slot_ids and positions differ in length")
+    q16 = _as_c(q, np.float16)
+    if q16.size != nqry * n_q * head_dim:
+        raise ValueError("q has the wrong number of elements")
+    total = int(n_cache_slots) * n_kv * int(capacity) * head_dim
+    k16 = _as_c(k, np.float16).reshape(-1)
+    vc = _as_c(v_codes, np.uint8).reshape(-1)
+    vn = _as_c(v_norms, np.float32).reshape(-1)
+    cb = _as_c(codebook, np.float32).reshape(-1)
+    if k16.size != total or vc.size != total or vn.size != total // min(head_dim, 256):
+        raise ValueError("k / v_codes / v_norms have the wrong number of elements")
+    if cb.size < (1 << int(codebook_bits)):
+        raise ValueError("codebook is shorter than 2**codebook_bits")
+    if rows is None:
+        rows_arr = None
+        n_rows = nqry * n_q
+        out = np.zeros((nqry, n_q, head_dim), dtype=np.float64)
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(list(rows), dtype=np.int32))
+        n_rows = int(rows_arr.shape[0])
+        out = np.zeros((n_rows, head_dim), dtype=np.float64)
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+    rc = lib.oracle_attn_decode_cache_cb_f64(
+        _ptr(q16), _ptr(k16), _ptr(vc), _ptr(vn), _ptr(cb), int(codebook_bits), _ptr(sid), _ptr(pos),
+        nqry, int(n_cache_slots), int(capacity), int(ring), int(window), _ptr(out), int(n_q), int(n_kv),
+        int(head_dim), float(scale), _ptr(rows_arr), n_rows, int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_decode_cache_cb_f64 returned {rc}")
+    return out
