@@ -29,6 +29,7 @@ ATTN_DECODE_EHIP = -3
 EXPORTED_SYMBOLS = (
     "attn_decode",
     "attn_decode_cache",
+    "attn_decode_cache_cb",
     "attn_decode_cb",
     "attn_decode_ex",
     "attn_decode_plan",
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "attn_decode_release",
     "attn_fwht_undo",
     "attn_kv_append",
+    "attn_kv_append_cb",
 )
 
 
@@ -102,6 +104,18 @@ def load_library():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        lib.attn_decode_cache_cb.restype = ctypes.c_int
+        lib.attn_decode_cache_cb.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(_Options)]
+        lib.attn_kv_append_cb.restype = ctypes.c_int
+        lib.attn_kv_append_cb.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_void_p]
         lib.attn_decode_plan.restype = ctypes.c_int
         lib.attn_decode_plan.argtypes = [
             ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -321,6 +335,86 @@ def attn_kv_append(k_new, v_new, k_cache, v_cache, v_scales, slot_ids, positions
                             int(ring), int(n_kv_heads), int(head_dim), _stream_handle(stream, dev))
     if rc != ATTN_DECODE_OK:
         _raise(lib, rc)
+
+
+def _cache_rows(slot_ids, positions, n_queries):
+    sid, n = _seq_array(slot_ids)
+    pos, n2 = _seq_array(positions)
+    if n_queries is None:
+        n_queries = n
+    if n != n_queries or n2 != n_queries:
+        raise ValueError("slot_ids / positions do not match the number of rows")
+    return sid, pos, n_queries
+
+
+def _codebook_ptr(codebook, codebook_bits, dev):
+    bits = int(codebook_bits)
+    if not 1 <= bits <= 8:
+        raise AttnDecodeError(ATTN_DECODE_EINVAL, "codebook_bits must be in 1..8")
+    return bits, _dev_ptr(codebook, "codebook", torch.float32, 1 << bits, dev)
+
+
+def attn_decode_cache_cb(q, k_cache, v_codes, v_norms, codebook, codebook_bits: int, slot_ids, positions,
+                         n_queries: Optional[int], n_cache_slots: int, capacity: int, ring: int, window: int,
+                         out, n_q_heads: int, n_kv_heads: int, head_dim: int, scale: float, stream=None,
+                         chunk: int = 0, merge_mode: int = 0, path: int = 0) -> None:
+    """attn_decode_cache with codebook V (uint8 indices and fp32 norms per min(D, 256) dims, laid out
+    like the cache); out is in the rotated basis (see attn_fwht_undo)."""
+    lib = load_library()
+    sid, pos, n_queries = _cache_rows(slot_ids, positions, n_queries)
+    if not isinstance(out, torch.Tensor) or out.device.type != "cuda":
+        raise ValueError("out must be a CUDA tensor")
+    dev = out.device.index
+    kv = int(n_cache_slots) * int(n_kv_heads) * int(capacity) * int(head_dim)
+    pq = _dev_ptr(q, "q", torch.float16, n_queries * n_q_heads * head_dim, dev)
+    pk = _dev_ptr(k_cache, "k_cache", torch.float16, kv, dev)
+    pv = _dev_ptr(v_codes, "v_codes", torch.uint8, kv, dev)
+    pn = _dev_ptr(v_norms, "v_norms", torch.float32, kv // min(head_dim, 256), dev)
+    bits, pc = _codebook_ptr(codebook, codebook_bits, dev)
+    po = _dev_ptr(out, "out", torch.float32, n_queries * n_q_heads * head_dim, dev)
+    opts = _Options(int(chunk), int(merge_mode), None, None, int(path))
+    rc = lib.attn_decode_cache_cb(pq, pk, pv, pn, pc, bits, sid, pos, int(n_queries), int(n_cache_slots),
+                                  int(capacity), int(ring), int(window), po, int(n_q_heads), int(n_kv_heads),
+                                  int(head_dim), float(scale), _stream_handle(stream, dev), ctypes.byref(opts))
+    if rc != ATTN_DECODE_OK:
+        _raise(lib, rc)
+
+
+def attn_kv_append_cb(k_new, v_new, k_cache, v_codes, v_norms, signs, codebook, codebook_bits: int, slot_ids,
+                      positions, n_rows: Optional[int], n_cache_slots: int, capacity: int, ring: int,
+                      n_kv_heads: int, head_dim: int, stream=None) -> None:
+    """Enqueue the write of new tokens' K (fp16) and codebook-encoded V (rotated with ``signs``,
+    nearest level of ``codebook``, fp32 norms per min(D, 256) dims) into the cache."""
+    lib = load_library()
+    sid, pos, n_rows = _cache_rows(slot_ids, positions, n_rows)
+    if not isinstance(k_cache, torch.Tensor) or k_cache.device.type != "cuda":
+        raise ValueError("k_cache must be a CUDA tensor")
+    dev = k_cache.device.index
+    kv = int(n_cache_slots) * int(n_kv_heads) * int(capacity) * int(head_dim)
+    pkn = _dev_ptr(k_new, "k_new", torch.float32, n_rows * n_kv_heads * head_dim, dev)
+    pvn = _dev_ptr(v_new, "v_new", torch.float32, n_rows * n_kv_heads * head_dim, dev)
+    pk = _dev_ptr(k_cache, "k_cache", torch.float16, kv, dev)
+    pv = _dev_ptr(v_codes, "v_codes", torch.uint8, kv, dev)
+    pn = _dev_ptr(v_norms, "v_norms", torch.float32, kv // min(head_dim, 256), dev)
+    ps = _dev_ptr(signs, "signs", torch.float32, int(head_dim), dev)
+    bits, pc = _codebook_ptr(codebook, codebook_bits, dev)
+    rc = lib.attn_kv_append_cb(pkn, pvn, pk, pv, pn, ps, pc, bits, sid, pos, int(n_rows), int(n_cache_slots),
+                               int(capacity), int(ring), int(n_kv_heads), int(head_dim),
+                               _stream_handle(stream, dev))
+    if rc != ATTN_DECODE_OK:
+        _raise(lib, rc)
+
+
+def attn_kv_append_cb_raw(k_new, v_new, k_cache, v_codes, v_norms, signs, codebook, codebook_bits, slot_ids,
+                          positions, n_rows, n_cache_slots, capacity, ring, n_kv_heads, head_dim,
+                          stream_ptr=None) -> int:
+    """Direct call with raw pointers (tests of the C-side validation); returns the C return code."""
+    lib = load_library()
+    sid, _ = _seq_array(slot_ids)
+    pos, _ = _seq_array(positions)
+    return lib.attn_kv_append_cb(k_new, v_new, k_cache, v_codes, v_norms, signs, codebook, int(codebook_bits),
+                                 sid, pos, int(n_rows), int(n_cache_slots), int(capacity), int(ring),
+                                 int(n_kv_heads), int(head_dim), stream_ptr)
 
 
 def attn_decode_cache_raw(q_ptr, k_ptr, v_ptr, vs_ptr, slot_ids, positions, n_queries, n_cache_slots,

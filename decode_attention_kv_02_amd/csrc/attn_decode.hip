@@ -373,18 +373,19 @@ int run(const void *q, const void *k_cache, const VSource &vsrc,
     return launch(spans, q, k_cache, vsrc, out, n_q, n_kv, D, scale, stream_ptr, opts);
 }
 
-int run_cache(const void *q, const void *k_cache, const void *v_cache, const void *v_scales,
+int run_cache(const void *q, const void *k_cache, const VSource &vsrc,
               const int32_t *slot_ids, const int32_t *positions, int32_t n_queries,
               int32_t n_cache_slots, int32_t capacity, int32_t ring, int32_t window, float *out,
               int32_t n_q, int32_t n_kv, int32_t D, float scale, void *stream_ptr,
               const attn_decode_options *opts) {
     g_last_error.clear();
-    const bool v_int8 = v_scales != nullptr;
     const int32_t chunk = opts ? opts->chunk : 0;
     const int32_t merge_mode = opts ? opts->merge_mode : 0;
 
+    if (vsrc.format == kVCB && (vsrc.bits < 1 || vsrc.bits > 8))
+        return fail(ATTN_DECODE_EINVAL, "codebook_bits must be in 1..8");
     if (n_cache_slots < 0) return fail(ATTN_DECODE_EINVAL, "n_cache_slots must be >= 0");
-    std::string err = check_common(n_q, n_kv, D, v_int8, window, chunk, merge_mode);
+    std::string err = check_common(n_q, n_kv, D, vsrc.format == kVI8, window, chunk, merge_mode);
     if (err.empty()) err = check_cache(slot_ids, positions, n_queries, n_cache_slots, capacity, ring);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
     if (!std::isfinite(scale)) return fail(ATTN_DECODE_EINVAL, "scale must be finite");
@@ -394,7 +395,6 @@ int run_cache(const void *q, const void *k_cache, const void *v_cache, const voi
     const uint64_t kv_elems = rows * (uint64_t)D;
     if (rows > (uint64_t(1) << 40) || kv_elems > (uint64_t(1) << 46))
         return fail(ATTN_DECODE_EINVAL, "KV cache too large");
-    const VSource vsrc = VSource::plain_or_int8(v_cache, v_scales);
     int rc = check_pointers(q, k_cache, vsrc, out, (uint64_t)n_queries, n_q, D, kv_elems);
     if (rc != ATTN_DECODE_OK) return rc;
 
@@ -406,30 +406,47 @@ int run_cache(const void *q, const void *k_cache, const void *v_cache, const voi
 typedef void (*append_fn)(const AppendArgs);
 
 template <int D>
-append_fn append_for(bool v_int8) {
-    return v_int8 ? kv_append_kernel<D, true> : kv_append_kernel<D, false>;
-}
-
-append_fn select_append(int D, bool v_int8) {
-    switch (D) {
-        case 64: return append_for<64>(v_int8);
-        case 128: return append_for<128>(v_int8);
-        case 256: return append_for<256>(v_int8);
-        case 512: return append_for<512>(v_int8);
+append_fn append_for(int vf) {
+    switch (vf) {
+        case kVF16: return kv_append_kernel<D, kVF16>;
+        case kVI8: return kv_append_kernel<D, kVI8>;
+        case kVCB: return kv_append_kernel<D, kVCB>;
     }
     return nullptr;
 }
 
-int run_append(const float *k_new, const float *v_new, void *k_cache, void *v_cache, void *v_scales,
+append_fn select_append(int D, int vf) {
+    switch (D) {
+        case 64: return append_for<64>(vf);
+        case 128: return append_for<128>(vf);
+        case 256: return append_for<256>(vf);
+        case 512: return append_for<512>(vf);
+    }
+    return nullptr;
+}
+
+// Where an append writes V: fp16 values; int8 codes plus fp16 block scales; or
+// codebook indices plus fp32 block norms, encoded with `signs` and `codebook`.
+struct AppendV {
+    void *v = nullptr;
+    int format = kVF16;
+    void *side = nullptr;              // int8: scales; codebook: norms
+    const float *signs = nullptr;
+    const float *codebook = nullptr;
+    int32_t bits = 0;
+};
+
+int run_append(const float *k_new, const float *v_new, void *k_cache, const AppendV &vd,
                const int32_t *slot_ids, const int32_t *positions, int32_t n_rows,
                int32_t n_cache_slots, int32_t capacity, int32_t ring, int32_t n_kv, int32_t D,
                void *stream_ptr) {
     g_last_error.clear();
-    const bool v_int8 = v_scales != nullptr;
     if (n_rows < 0) return fail(ATTN_DECODE_EINVAL, "n_rows must be >= 0");
     if (n_cache_slots < 0) return fail(ATTN_DECODE_EINVAL, "n_cache_slots must be >= 0");
     if (n_kv <= 0) return fail(ATTN_DECODE_EINVAL, "n_kv_heads must be positive");
     if (!supported_head_dim(D)) return fail(ATTN_DECODE_EINVAL, "head_dim must be 64, 128, 256 or 512");
+    if (vd.format == kVCB && (vd.bits < 1 || vd.bits > 8))
+        return fail(ATTN_DECODE_EINVAL, "codebook_bits must be in 1..8");
     std::string err = check_cache(slot_ids, positions, n_rows, n_cache_slots, capacity, ring);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
     if (n_rows == 0) return ATTN_DECODE_OK;
@@ -447,24 +464,38 @@ int run_append(const float *k_new, const float *v_new, void *k_cache, void *v_ca
     if (rows > (uint64_t(1) << 40) || kv_elems > (uint64_t(1) << 46))
         return fail(ATTN_DECODE_EINVAL, "KV cache too large");
     const uint64_t new_bytes = (uint64_t)n_rows * n_kv * D * 4;
-    const uint64_t k_bytes = kv_elems * 2, v_bytes = kv_elems * (v_int8 ? 1 : 2);
-    const uint64_t s_bytes = v_int8 ? kv_elems / kQuantBlock * 2 : 0;
+    const uint64_t k_bytes = kv_elems * 2, v_bytes = kv_elems * (vd.format == kVF16 ? 2 : 1);
+    const uint64_t s_bytes = vd.format == kVI8 ? kv_elems / kQuantBlock * 2
+                           : vd.format == kVCB ? kv_elems / (D < 256 ? D : 256) * 4 : 0;
     if (k_new == nullptr || v_new == nullptr) return fail(ATTN_DECODE_EINVAL, "k_new / v_new is NULL");
-    if (k_cache == nullptr || v_cache == nullptr) return fail(ATTN_DECODE_EINVAL, "k_cache / v_cache is NULL");
+    if (k_cache == nullptr || vd.v == nullptr) return fail(ATTN_DECODE_EINVAL, "k_cache / v_cache is NULL");
     if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(ATTN_DECODE_EINVAL, "k_new and v_new must be 16-byte aligned");
-    if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+    if (!aligned(k_cache, 16) || !aligned(vd.v, 16))
         return fail(ATTN_DECODE_EINVAL, "k_cache and v_cache must be 16-byte aligned");
-    if (v_int8 && !aligned(v_scales, 2)) return fail(ATTN_DECODE_EINVAL, "v_scales must be 2-byte aligned");
-    const void *outs[3] = {k_cache, v_cache, v_scales};
+    if (vd.format == kVI8 && !aligned(vd.side, 2)) return fail(ATTN_DECODE_EINVAL, "v_scales must be 2-byte aligned");
+    const uint64_t cb_bytes = vd.format == kVCB ? (uint64_t(4) << vd.bits) : 0;
+    const uint64_t sg_bytes = vd.format == kVCB ? (uint64_t)D * 4 : 0;
+    if (vd.format == kVCB) {
+        if (vd.side == nullptr || vd.signs == nullptr || vd.codebook == nullptr)
+            return fail(ATTN_DECODE_EINVAL, "v_norms / signs / codebook is NULL");
+        if (!aligned(vd.side, 4) || !aligned(vd.signs, 4) || !aligned(vd.codebook, 4))
+            return fail(ATTN_DECODE_EINVAL, "v_norms, signs and codebook must be 4-byte aligned");
+    }
+    // inputs (new rows, and for codebook V the signs and levels) against the three outputs
+    const void *ins[4] = {k_new, v_new, vd.signs, vd.codebook};
+    const uint64_t in_bytes[4] = {new_bytes, new_bytes, sg_bytes, cb_bytes};
+    const void *outs[3] = {k_cache, vd.v, vd.side};
     const uint64_t out_bytes[3] = {k_bytes, v_bytes, s_bytes};
     for (int a = 0; a < 3; ++a) {
-        if (overlaps(k_new, new_bytes, outs[a], out_bytes[a]) || overlaps(v_new, new_bytes, outs[a], out_bytes[a]))
-            return fail(ATTN_DECODE_EINVAL, "k_new / v_new overlaps the cache");
+        for (int b = 0; b < 4; ++b)
+            if (overlaps(ins[b], in_bytes[b], outs[a], out_bytes[a]))
+                return fail(ATTN_DECODE_EINVAL, b < 2 ? "k_new / v_new overlaps the cache"
+                                                      : "signs / codebook overlaps the cache");
         for (int b = a + 1; b < 3; ++b)
             if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b]))
                 return fail(ATTN_DECODE_EINVAL, "cache arrays overlap");
     }
-    const append_fn fn = select_append(D, v_int8);
+    const append_fn fn = select_append(D, vd.format);
     if (fn == nullptr) return fail(ATTN_DECODE_EINVAL, "no kernel for this shape");
 
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
@@ -473,8 +504,13 @@ int run_append(const float *k_new, const float *v_new, void *k_cache, void *v_ca
     args.k_new = k_new;
     args.v_new = v_new;
     args.k_cache = static_cast<uint16_t *>(k_cache);
-    args.v_cache = v_cache;
-    args.v_scales = static_cast<uint16_t *>(v_scales);
+    args.v_cache = vd.v;
+    if (vd.format == kVI8) args.v_scales = static_cast<uint16_t *>(vd.side);
+    if (vd.format == kVCB) args.v_norms = static_cast<float *>(vd.side);
+    args.signs = vd.signs;
+    args.codebook = vd.codebook;
+    args.cb_bits = vd.bits;
+    args.inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
     args.n_kv = n_kv;
     args.capacity = capacity;
     for (int32_t r0 = 0; r0 < n_rows; r0 += kAppendMaxRows) {
@@ -565,16 +601,53 @@ extern "C" int attn_decode_cache(const void *q, const void *k_cache, const void 
                                  int32_t capacity, int32_t ring, int32_t window, float *out,
                                  int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
                                  void *stream, const attn_decode_options *opts) {
-    return run_cache(q, k_cache, v_cache, v_scales, slot_ids, positions, n_queries, n_cache_slots,
-                     capacity, ring, window, out, n_q_heads, n_kv_heads, head_dim, scale, stream, opts);
+    return run_cache(q, k_cache, VSource::plain_or_int8(v_cache, v_scales), slot_ids, positions, n_queries,
+                     n_cache_slots, capacity, ring, window, out, n_q_heads, n_kv_heads, head_dim, scale, stream,
+                     opts);
+}
+
+extern "C" int attn_decode_cache_cb(const void *q, const void *k_cache, const void *v_codes,
+                                    const float *v_norms, const float *codebook, int32_t codebook_bits,
+                                    const int32_t *slot_ids, const int32_t *positions, int32_t n_queries,
+                                    int32_t n_cache_slots, int32_t capacity, int32_t ring, int32_t window,
+                                    float *out, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    float scale, void *stream, const attn_decode_options *opts) {
+    VSource vsrc;
+    vsrc.v = v_codes;
+    vsrc.format = kVCB;
+    vsrc.side = v_norms;
+    vsrc.codebook = codebook;
+    vsrc.bits = codebook_bits;
+    return run_cache(q, k_cache, vsrc, slot_ids, positions, n_queries, n_cache_slots, capacity, ring, window,
+                     out, n_q_heads, n_kv_heads, head_dim, scale, stream, opts);
 }
 
 extern "C" int attn_kv_append(const float *k_new, const float *v_new, void *k_cache, void *v_cache,
                               void *v_scales, const int32_t *slot_ids, const int32_t *positions,
                               int32_t n_rows, int32_t n_cache_slots, int32_t capacity, int32_t ring,
                               int32_t n_kv_heads, int32_t head_dim, void *stream) {
-    return run_append(k_new, v_new, k_cache, v_cache, v_scales, slot_ids, positions, n_rows,
-                      n_cache_slots, capacity, ring, n_kv_heads, head_dim, stream);
+    AppendV vd;
+    vd.v = v_cache;
+    vd.format = v_scales ? kVI8 : kVF16;
+    vd.side = v_scales;
+    return run_append(k_new, v_new, k_cache, vd, slot_ids, positions, n_rows, n_cache_slots, capacity, ring,
+                      n_kv_heads, head_dim, stream);
+}
+
+extern "C" int attn_kv_append_cb(const float *k_new, const float *v_new, void *k_cache, void *v_codes,
+                                 float *v_norms, const float *signs, const float *codebook,
+                                 int32_t codebook_bits, const int32_t *slot_ids, const int32_t *positions,
+                                 int32_t n_rows, int32_t n_cache_slots, int32_t capacity, int32_t ring,
+                                 int32_t n_kv_heads, int32_t head_dim, void *stream) {
+    AppendV vd;
+    vd.v = v_codes;
+    vd.format = kVCB;
+    vd.side = v_norms;
+    vd.signs = signs;
+    vd.codebook = codebook;
+    vd.bits = codebook_bits;
+    return run_append(k_new, v_new, k_cache, vd, slot_ids, positions, n_rows, n_cache_slots, capacity, ring,
+                      n_kv_heads, head_dim, stream);
 }
 
 extern "C" int attn_decode_plan(const int32_t *seq_lens, int32_t n_slots, int32_t window,

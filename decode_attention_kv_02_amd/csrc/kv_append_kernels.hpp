@@ -11,13 +11,26 @@
 // single precision: the divisions are the correctly rounded fp32 divide,
 // rint rounds half to even, and the fp16 conversions round to nearest even.
 //
+// Codebook V (the hybrid regime's FWHT-V encode; the TQ-HB layout of
+// mlx-native flash_attn_vec_hybrid.metal with its D = 512 per-block norms):
+// the row is rotated, y = H (s * v) / sqrt(D), one fp32 norm is kept per
+// block of B = min(D, 256) coordinates, and each coordinate is stored as the
+// index of the level nearest to u = y * sqrt(B) / norm (the first index on a
+// tie, 0 when the norm is 0).  The levels must increase; the nearest one is
+// found by binary search over the midpoints of neighbouring levels, which
+// every workgroup first stages in LDS.  All of it in fp32.
+//
 // One wave per (new row, kv head); each lane owns D/64 consecutive dims, so a
 // block of 32 dims spans 2048/D lanes and its max |v| is an all-reduce over
-// those lanes.
+// those lanes; a codebook block spans B/(D/64) lanes and its norm is an
+// all-reduce over those.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "attn_decode_kernels.hpp"
+#include "fwht_kernels.hpp"
 
 namespace attn_decode_impl {
 
@@ -28,7 +41,12 @@ struct AppendArgs {
     const float *v_new;        // [n_rows][n_kv][D]
     uint16_t *k_cache;         // fp16 [n_cache_slots][n_kv][capacity][D]
     void *v_cache;             // fp16 or int8, same layout
-    uint16_t *v_scales;        // fp16 [..][D/32] or null
+    uint16_t *v_scales;        // int8 V: fp16 [..][D/32]
+    float *v_norms;            // codebook V: fp32 [..][D/B]
+    const float *signs;        // codebook V: the rotation's sign flips [D]
+    const float *codebook;     // codebook V: increasing levels [2^cb_bits]
+    int32_t cb_bits;
+    float inv_sqrt_d;          // codebook V: 1 / sqrt(D)
     int32_t n_rows;            // rows in this launch
     int32_t n_kv;
     int32_t capacity;
@@ -96,10 +114,34 @@ __device__ __forceinline__ void store_i8(int8_t *p, const int8_t (&c)[E]) {
     }
 }
 
-template <int D, bool VINT8>
+template <int E>
+__device__ __forceinline__ void store_u8(uint8_t *p, const uint8_t (&c)[E]) {
+    uint32_t w[(E + 3) / 4] = {};
+#pragma unroll
+    for (int i = 0; i < E; ++i) w[i / 4] |= (uint32_t)c[i] << (8 * (i % 4));
+    if constexpr (E == 8) {
+        *(uint2 *)p = make_uint2(w[0], w[1]);
+    } else if constexpr (E == 4) {
+        *(uint32_t *)p = w[0];
+    } else if constexpr (E == 2) {
+        *(uint16_t *)p = (uint16_t)w[0];
+    } else {
+        p[0] = c[0];
+    }
+}
+
+template <int D, int VF>
 __global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs args) {
     constexpr int E = D / 64;          // dims per lane
-    constexpr int LPB = 32 / E;        // lanes per 32-dim block
+    constexpr int LPB = 32 / E;        // lanes per 32-dim block (int8 V)
+    constexpr int CB_B = D < 256 ? D : 256;
+    constexpr int LPN = CB_B / E;      // lanes per norm block (codebook V): 64, or 32 at D = 512
+    __shared__ float s_mid[VF == kVCB ? 255 : 1];
+    if constexpr (VF == kVCB) {
+        const int n_mid = (1 << args.cb_bits) - 1;
+        for (int j = threadIdx.x; j < n_mid; j += 256) s_mid[j] = 0.5f * (args.codebook[j] + args.codebook[j + 1]);
+        __syncthreads();
+    }
     const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);   // (row, kv head) of this wave
     if (unit >= args.n_rows * args.n_kv) return;             // whole wave leaves; no barriers follow
     const int lane = threadIdx.x & 63;
@@ -113,9 +155,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs args) {
     load_f32<E>(args.v_new + src, vx);
     store_f16<E>(args.k_cache + dst_row * D + lane * E, kx);
 
-    if constexpr (!VINT8) {
+    if constexpr (VF == kVF16) {
         store_f16<E>((uint16_t *)args.v_cache + dst_row * D + lane * E, vx);
-    } else {
+    } else if constexpr (VF == kVI8) {
         float amax = 0.f;
 #pragma unroll
         for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(vx[i]));
@@ -132,6 +174,34 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs args) {
         }
         store_i8<E>((int8_t *)args.v_cache + dst_row * D + lane * E, codes);
         if (lane % LPB == 0) args.v_scales[dst_row * (D / 32) + (lane * E) / 32] = s16;
+    } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) vx[i] *= args.signs[lane * E + i];
+        fwht_wave<E>(vx, lane);
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            vx[i] *= args.inv_sqrt_d;
+            ss += vx[i] * vx[i];
+        }
+        // xor butterflies: both lanes of a pair add the same two numbers, so the
+        // whole block ends with one bitwise-identical sum
+#pragma unroll
+        for (int m = 1; m < LPN; m <<= 1) ss += fwht_shfl_xor(ss, m);
+        const float norm = sqrtf(ss);
+        const float to_u = norm > 0.f ? sqrtf((float)CB_B) / norm : 0.f;
+        uint8_t codes[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            const float u = vx[i] * to_u;
+            int lo = 0;
+            if (norm > 0.f)
+                for (int step = 1 << (args.cb_bits - 1); step > 0; step >>= 1)
+                    if (u > s_mid[lo + step - 1]) lo += step;
+            codes[i] = (uint8_t)lo;
+        }
+        store_u8<E>((uint8_t *)args.v_cache + dst_row * D + lane * E, codes);
+        if (lane % LPN == 0) args.v_norms[dst_row * (D / CB_B) + lane / LPN] = norm;
     }
 }
 

@@ -428,3 +428,43 @@ CODEBOOK_WORKLOADS = (
 def codebook_workload_inputs(cfg: CodebookWorkloadConfig) -> CodebookInputs:
     return make_codebook_inputs(cfg.seq_lens, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.bits,
                                 cfg.seed_base, direct=True)
+
+
+@dataclasses.dataclass
+class CacheCodebookInputs:
+    """Host tensors of a fixed-capacity-cache call with codebook V."""
+    q: torch.Tensor            # float16 [n_queries, n_q, D]
+    k: torch.Tensor            # float16 [n_cache_slots * n_kv * capacity * D]
+    v_codes: torch.Tensor      # uint8, laid out like k
+    v_norms: torch.Tensor      # float32 [n_cache_slots * n_kv * capacity * D / B], B = min(D, 256)
+    codebook: torch.Tensor     # float32 [2**bits]
+    codebook_bits: int
+    signs: torch.Tensor        # float32 +-1 [D]
+    slot_ids: Tuple[int, ...]
+    positions: Tuple[int, ...]
+    n_cache_slots: int
+    capacity: int
+    ring: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    scale: float
+
+    @property
+    def n_queries(self) -> int:
+        return len(self.slot_ids)
+
+
+def make_cache_codebook_inputs(n_cache_slots: int, capacity: int, ring: int, slot_ids: Sequence[int],
+                               positions: Sequence[int], n_q_heads: int, n_kv_heads: int, head_dim: int,
+                               bits: int, seed_base: int) -> CacheCodebookInputs:
+    """A [slot][kv][capacity][D] cache with codebook V: the packed recipe of make_codebook_inputs
+    with every slot holding `capacity` rows (the same layout), rotated coordinates drawn directly;
+    q per query row as make_cache_inputs draws it."""
+    ci = make_codebook_inputs((capacity,) * n_cache_slots, n_q_heads, n_kv_heads, head_dim, bits, seed_base,
+                              direct=True)
+    gq = torch.Generator("cpu").manual_seed(seed_base + 4)
+    q = torch.randn((len(slot_ids), n_q_heads, head_dim), generator=gq, dtype=torch.float32).to(torch.float16)
+    return CacheCodebookInputs(q, ci.k, ci.v_codes, ci.v_norms, ci.codebook, bits, ci.signs,
+                               tuple(int(x) for x in slot_ids), tuple(int(x) for x in positions), n_cache_slots,
+                               capacity, int(ring), n_q_heads, n_kv_heads, head_dim, ci.scale)

@@ -195,6 +195,27 @@ int attn_decode_cb(const void *q, const void *k_cache, const void *v_codes, cons
                    const attn_decode_options *opts);
 
 /*
+ * attn_decode_cache_cb -- attn_decode_cache with codebook V (the pages' hybrid
+ * KV regime on their fixed-capacity serving cache: mlx-native
+ * flash_attn_vec_hybrid.metal, the batched kernels' slot / ring addressing
+ * and the TQ-HB V layout; hf2q gemma4 batched_body.rs, the batched flash
+ * over slot_id / position tables).
+ *   v_codes   uint8 [n_cache_slots][n_kv_heads][capacity][head_dim]; 16-byte aligned
+ *   v_norms   fp32  [n_cache_slots][n_kv_heads][capacity][head_dim / B],
+ *             B = min(head_dim, 256); 4-byte aligned
+ *   codebook, codebook_bits: as for attn_decode_cb (element = level * norm / sqrt(B))
+ * Everything else (q, k_cache, slot_ids, positions, ring, window, out, the
+ * rotated-basis result, asynchrony, workspace, determinism, errors) is as for
+ * attn_decode_cache and attn_decode_cb; opts may be NULL.
+ */
+int attn_decode_cache_cb(const void *q, const void *k_cache, const void *v_codes, const float *v_norms,
+                         const float *codebook, int32_t codebook_bits, const int32_t *slot_ids,
+                         const int32_t *positions, int32_t n_queries, int32_t n_cache_slots,
+                         int32_t capacity, int32_t ring, int32_t window, float *out, int32_t n_q_heads,
+                         int32_t n_kv_heads, int32_t head_dim, float scale, void *stream,
+                         const attn_decode_options *opts);
+
+/*
  * attn_fwht_undo -- y = s * (H x) / sqrt(head_dim) per row: the output of
  * attn_decode_cb back in the original basis (hf2q gemma4 batched_body.rs, the
  * FWHT sign-undo after the attention; the inverse of the rotation of codebook
@@ -232,6 +253,36 @@ int attn_kv_append(const float *k_new, const float *v_new, void *k_cache, void *
                    void *v_scales, const int32_t *slot_ids, const int32_t *positions,
                    int32_t n_rows, int32_t n_cache_slots, int32_t capacity, int32_t ring,
                    int32_t n_kv_heads, int32_t head_dim, void *stream);
+
+/*
+ * attn_kv_append_cb -- attn_kv_append into a cache with codebook V (the
+ * hybrid regime's KV encode: hf2q gemma4 batched_body.rs, the F16 copy of K
+ * and the FWHT-V encode per slot and position into packed bytes and norms;
+ * mlx-native flash_attn_vec_hybrid.metal, the TQ-HB layout with its D = 512
+ * per-block norms, which the encode fills).
+ *   k_new, v_new  fp32 [n_rows][n_kv_heads][head_dim], 16-byte aligned
+ *   k_cache, v_codes, v_norms: the cache of attn_decode_cache_cb, written in
+ *                 place (only the rows named)
+ *   signs         fp32 [head_dim] (+-1), device, 4-byte aligned: the rotation's
+ *                 sign flips (attn_fwht_undo takes results back with the same)
+ *   codebook      fp32 [2^codebook_bits], device, 4-byte aligned; the levels
+ *                 must increase (otherwise the codes are unspecified but stay
+ *                 below 2^codebook_bits); codebook_bits 1..8
+ *   slot_ids, positions, ring, capacity: as for attn_kv_append
+ * K is rounded to fp16 (nearest even).  Each V row is rotated,
+ * y = H (s * v) / sqrt(head_dim) (H the Walsh-Hadamard matrix), split into
+ * blocks of B = min(head_dim, 256) coordinates with norm_b = ||y_block||, and
+ * each coordinate stored as the index of the level nearest to
+ * u = y * sqrt(B) / norm_b (the lower index on a tie; 0 in a block whose norm
+ * is 0).  All in fp32: where u lies within fp32 rounding of the midpoint of
+ * two levels either index can result.  Finite inputs.  Two rows may not land
+ * on the same cache row (EINVAL).  Asynchronous on `stream`; no workspace.
+ */
+int attn_kv_append_cb(const float *k_new, const float *v_new, void *k_cache, void *v_codes, float *v_norms,
+                      const float *signs, const float *codebook, int32_t codebook_bits,
+                      const int32_t *slot_ids, const int32_t *positions, int32_t n_rows,
+                      int32_t n_cache_slots, int32_t capacity, int32_t ring, int32_t n_kv_heads,
+                      int32_t head_dim, void *stream);
 
 /*
  * attn_decode_plan -- the host planner alone (no HIP call, usable without a

@@ -165,3 +165,63 @@ def test_binding_refuses_host_tensors():
     out = torch.zeros((1, 1, 64), dtype=torch.float32)
     with pytest.raises(ValueError):
         binding.attn_decode(q, k, k, None, [1], 0, out, 1, 1, 1, 64, 0.125)
+
+
+# ------------------------------------------------------------------ codebook-V cache entry points
+
+KN, VN, KC, VC, NM, SG, CB = (0x60000000, 0x61000000, 0x62000000, 0x63000000, 0x64000000, 0x65000000,
+                              0x66000000)
+
+
+def _append_cb(**kw):
+    a = dict(kn=KN, vn=VN, k=KC, v=VC, n=NM, s=SG, cb=CB, bits=8, sid=[0], pos=[0], slots=1, cap=4, ring=0)
+    a.update(kw)
+    rc = binding.attn_kv_append_cb_raw(a["kn"], a["vn"], a["k"], a["v"], a["n"], a["s"], a["cb"], a["bits"],
+                                       a["sid"], a["pos"], len(a["sid"]), a["slots"], a["cap"], a["ring"], 1, 64)
+    return rc, binding.last_error()
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(bits=0), "codebook_bits"),
+    (dict(bits=9), "codebook_bits"),
+    (dict(s=0), "NULL"),
+    (dict(cb=0), "NULL"),
+    (dict(n=0), "NULL"),
+    (dict(cb=CB + 2), "aligned"),
+    (dict(n=NM + 1), "aligned"),
+    (dict(s=VC + 64), "signs / codebook overlaps"),
+    (dict(cb=NM), "signs / codebook overlaps"),
+    (dict(n=KC + 8), "overlap"),
+    (dict(sid=[0, 0], pos=[1, 5], ring=1), "same cache row"),
+    (dict(pos=[4]), "capacity"),
+])
+def test_codebook_append_rejects_before_any_gpu_work(kw, frag):
+    rc, msg = _append_cb(**kw)
+    assert rc == binding.ATTN_DECODE_EINVAL
+    assert frag in msg, msg
+
+
+def _cache_cb(**kw):
+    a = dict(q=Q, k=KC, v=VC, n=NM, cb=CB, bits=8, out=OUT, sid=[0], pos=[3], cap=4)
+    a.update(kw)
+    lib = binding.load_library()
+    sid = (ctypes.c_int32 * len(a["sid"]))(*a["sid"])
+    pos = (ctypes.c_int32 * len(a["pos"]))(*a["pos"])
+    rc = lib.attn_decode_cache_cb(a["q"], a["k"], a["v"], a["n"], a["cb"], a["bits"], sid, pos, len(a["sid"]), 1,
+                                  a["cap"], 0, 0, a["out"], 2, 1, 64, 0.125, None, None)
+    return rc, binding.last_error()
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(bits=0), "codebook_bits"),
+    (dict(n=0), "v_norms is NULL"),
+    (dict(cb=0), "codebook is NULL"),
+    (dict(cb=CB + 1), "aligned"),
+    (dict(out=CB), "overlaps"),
+    (dict(out=NM), "overlaps"),
+    (dict(pos=[4]), "capacity"),
+])
+def test_cache_codebook_attention_rejects_before_any_gpu_work(kw, frag):
+    rc, msg = _cache_cb(**kw)
+    assert rc == binding.ATTN_DECODE_EINVAL
+    assert frag in msg, msg
