@@ -20,6 +20,11 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU ops stay off: scalar fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the matrix-core kernel rescales its accumulators
+    # with VALU multiplies, and AGPR-resident accumulators cost a copy through VGPRs each time
+    # (and the AGPR half of the register budget); this lets it run 2 waves per SIMD at
+    # head_dim 256.  Kernels without MFMA instructions are unaffected.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

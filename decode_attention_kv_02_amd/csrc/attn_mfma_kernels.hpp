@@ -6,26 +6,32 @@
 // mlx-native flash_attn_vec_hybrid.metal, flash_attn_vec_hybrid_batched_gqa_impl:
 // every K and V row is read once for all the query heads of the group).  With
 // 8 or more heads per kv head the per-lane dot products and V FMAs of the
-// lane kernel make it VALU-bound (rocprof: 205 VALU instructions per KV row at
-// 8 heads, 74% busy, 37% of HBM peak), so here both products are MFMA tiles:
+// lane kernel make it VALU-bound, so here both products are MFMA tiles.
 //
-//  * The 4 waves split head_dim: wave w owns dims [w D/4, (w+1) D/4).  For a
-//    tile of 16 keys each wave computes its part of S^T (16 keys x 16 heads)
-//    with v_mfma_f32_16x16x16_f16 (A = K rows, B = q; fp16 products are exact,
-//    fp32 accumulation), the 4 parts are added in LDS in a fixed order, and
-//    every wave then holds the same S^T and runs the same online softmax
-//    (running max M and sum S per head, log2 domain).
-//  * O^T (dims x heads) += V^T P^T with v_mfma_f32_16x16x4_f32: the A operand
-//    is V (dequantised to fp32 in an LDS tile, exact for every V format), the
-//    B operand is P straight from the S^T accumulator registers (lane l holds
-//    keys 4(l/16)+i of head l%16, exactly the B layout of step i), so P never
-//    leaves the registers and stays fp32.  Each lane's O values belong to one
-//    head, so rescaling by exp(M_old - M_new) needs no cross-lane traffic.
-//  * Each wave writes the dims it owns; M and S are the same in every wave.
+//  * The 4 waves split the chunk's keys (the pages' simdgroups splitting the
+//    KV range, merged at the end): wave w takes the 16-key tiles w, w + 4,
+//    w + 8, ... and runs its own online softmax, with no barrier until the
+//    final merge of the 4 waves' (M, S, O) through LDS.
+//  * S^T (16 keys x 16 heads) = K q^T on v_mfma_f32_16x16x32_f16: A = K rows
+//    (key l%16, 8 dims per lane per step, one 16-byte load), B = q.  fp16
+//    products are exact, the accumulation fp32.
+//  * O^T (dims x heads) += V^T P^T on v_mfma_f32_16x16x4_f32, with both
+//    operands straight from registers.  B = P from the S^T accumulator: lane l
+//    holds keys 4(l/16) + i of head l%16, exactly the B operand (k = l/16) of
+//    step i.  A = V: in step i lane l loads key 4(l/16) + i, EV consecutive
+//    dims starting at EV (l%16) (16 bytes), and feeds element e of that load
+//    to instruction e as A[row l%16][k l/16].  Row l%16 of instruction e is
+//    then dim EV (l%16) + e, the same for every lane with that l%16, and k is
+//    the key, so each instruction is an exact 16-dims x 4-keys product; the
+//    accumulators cover every dim once.  Each V load reads 4 keys x 16 EV
+//    contiguous bytes, whole cache lines, and V is dequantised to fp32 in
+//    registers (exact for fp16, int8 and codebook), never staged in LDS.
+//  * Accumulator o[b EV + e] lane l component r holds head l%16, dim
+//    BW b + 4 EV (l/16) + EV r + e (BW = 16 EV dims per load).
 //
-// Lane layouts (checked on gfx950): 16x16x16 f16: A[l%16][4(l/16)+e],
-// B[4(l/16)+e][l%16]; 16x16x4 f32: A[l%16][l/16], B[l/16][l%16]; both
-// C[4(l/16)+i][l%16].
+// Lane layouts (checked on gfx950 with one-wave probes): 16x16x32 f16:
+// A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]; 16x16x4 f32: A[l%16][l/16],
+// B[l/16][l%16]; both C[4(l/16)+i][l%16].
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,37 +41,41 @@
 
 namespace attn_decode_impl {
 
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaKeys = 16;   // keys per tile (the MFMA M / N size)
+constexpr float kLazyMax = 8.f; // log2 headroom of the softmax reference before a rescale
 
-template <int D>
+template <int D, int VF>
 struct MfmaGeometry {
-    static constexpr int DW = D / kWaves;   // dims per wave
-    static constexpr int NT = DW / 16;      // 16-dim tiles per wave: QK k-steps and PV output tiles
-    static constexpr int KL = DW / 32;      // 16-byte K (and fp16 V) loads per lane per key tile
-    static constexpr int VB = DW / 4;       // bytes of int8 / codebook V per lane per key tile
-    static constexpr int VS = DW + 4;       // LDS row stride (floats) of the V tile: keys 4 apart land 16 banks apart
     static_assert(D >= 128 && D <= 512, "head_dim 128..512");
+    static constexpr int KS = D / 32;                                    // QK steps = 16-byte K loads per lane
+    static constexpr int EV = (VF == kVF16) ? 8 : (D >= 256 ? 16 : 8);   // V elements per lane per load
+    static constexpr int BW = 16 * EV;                                   // dims covered by one load
+    static constexpr int NB = D / BW;                                    // loads per key step
+    static constexpr int VBYTES = EV * (VF == kVF16 ? 2 : 1);            // 16, or 8 (byte V at D = 128)
+    static constexpr int NO = NB * EV;                                   // f32x4 accumulators = D / 16
+    static_assert(NO * 16 == D, "accumulators cover every dim once");
 };
 
-// Registers of one key tile for one lane: key row l%16, the lane group's dims.
-template <int D>
-struct MFrag {
-    uint4 k[MfmaGeometry<D>::KL];
-    uint4 v[MfmaGeometry<D>::KL];   // fp16 V: like k; byte formats use the first VB bytes
-    float side[2];                  // int8: fp16 scale of each 16-dim piece; codebook: the norm
+template <int D, int VF>
+struct MKTile {
+    uint4 k[MfmaGeometry<D, VF>::KS];   // key kb + l%16, dims 32 s + 8 (l/16) + [0, 8)
 };
 
-__device__ __forceinline__ half4_t as_h4(uint32_t lo, uint32_t hi) {
-    return __builtin_bit_cast(half4_t, make_uint2(lo, hi));
-}
+template <int D, int VF>
+struct MVTile {
+    uint4 v[4][MfmaGeometry<D, VF>::NB];     // step i: key kb + 4 (l/16) + i, dims BW b + EV (l%16) + [0, EV)
+    float side[4][MfmaGeometry<D, VF>::NB];  // int8: scale of the lane's 32-dim block; codebook: its norm
+};
+
+__device__ __forceinline__ half8_t as_h8(const uint4 &u) { return __builtin_bit_cast(half8_t, u); }
 
 template <int D, int VF>
 __global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const LaunchArgs args) {
-    using Geo = MfmaGeometry<D>;
-    constexpr int DW = Geo::DW, NT = Geo::NT, KL = Geo::KL, VB = Geo::VB, VS = Geo::VS;
+    using Geo = MfmaGeometry<D, VF>;
+    constexpr int KS = Geo::KS, EV = Geo::EV, BW = Geo::BW, NB = Geo::NB, NO = Geo::NO;
     constexpr int CB_B = D < 256 ? D : 256;   // codebook norm block
     static_assert(kThreads == 256, "one thread per codebook table entry");
 
@@ -85,202 +95,241 @@ __global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const Launc
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop control
     const int c16 = lane & 15;   // MFMA row / column of the lane
     const int g = lane >> 4;     // lane group
-    const int dw0 = w * DW;      // first dim of this wave
     const bool head_ok = c16 < GB;
     const int64_t qrow = (int64_t)sd.slot_idx * args.n_q + h0 + c16;
 
-    // q as the B operand of the QK tiles: step 2j covers dims dw0 + 32j + 8g + [0, 4),
-    // step 2j+1 dims dw0 + 32j + 8g + [4, 8) (the K loads use the same mapping)
-    half4_t qf[NT];
+    // q as the B operand of the QK steps: step s covers dims 32 s + 8 g + [0, 8), like the K loads.
+    // Held in registers up to head_dim 128; above, in LDS (rows padded by 16 bytes so the 16
+    // heads of one read fall in different banks), which leaves the registers to K and V.
+    constexpr bool QLDS = D >= 256;
+    constexpr int QS = D + 8;                      // LDS row stride of q, in halves
+    __shared__ uint16_t s_q[QLDS ? 16 * QS : 1];
+    half8_t qf[QLDS ? 1 : KS];
+    if constexpr (QLDS) {
+        // 4 waves x 64 lanes fill 16 rows of D halves, 16 bytes per thread per pass
+        for (int x = tid * 8; x < 16 * D; x += kThreads * 8) {
+            const int hr = x / D, dd = x % D;
+            uint4 a = make_uint4(0, 0, 0, 0);
+            if (hr < GB) a = *(const uint4 *)(args.q + ((int64_t)sd.slot_idx * args.n_q + h0 + hr) * D + dd);
+            *(uint4 *)(s_q + hr * QS + dd) = a;
+        }
+    } else {
 #pragma unroll
-    for (int j = 0; j < KL; ++j) {
-        uint4 a = make_uint4(0, 0, 0, 0);
-        if (head_ok) a = *(const uint4 *)(args.q + qrow * D + dw0 + 32 * j + 8 * g);
-        qf[2 * j] = as_h4(a.x, a.y);
-        qf[2 * j + 1] = as_h4(a.z, a.w);
+        for (int s = 0; s < KS; ++s) {
+            uint4 a = make_uint4(0, 0, 0, 0);
+            if (head_ok) a = *(const uint4 *)(args.q + qrow * D + 32 * s + 8 * g);
+            qf[s] = as_h8(a);
+        }
     }
 
-    __shared__ float s_cb[VF == kVCB ? 256 : 1];    // codebook V: level[i & mask] / sqrt(B)
-    __shared__ float s_v[kWaves][kMfmaKeys][VS];    // each wave's V tile, fp32
-    __shared__ f32x4_t s_s[2][kWaves][64];          // the waves' parts of S^T, by tile parity
+    __shared__ float s_cb[VF == kVCB ? 256 : 1];   // codebook V: level[i & mask] / sqrt(B)
+    __shared__ float s_m[kWaves][16], s_l[kWaves][16];
+    __shared__ f32x4_t s_o[NO][64];                // one wave's accumulators, for the final merge
 
-    // Loads of the tile starting at key kb: lane l reads key kb + l%16 (clamped
-    // to the chunk's last key past its end; those keys are masked).
-    auto load = [&](int kb, MFrag<D> &f) {
-        const int key = kb + c16;
+    // Cache row of a key of the chunk (keys past its end read its last key; they are masked).
+    auto row_of = [&](int key) -> int64_t {
         int rc = (key < cend ? key : cend - 1) - sd.ring_base;
         if (rc >= sd.ring_cap) rc -= sd.ring_cap;
-        const int64_t row = rowbase + rc;
-        const uint16_t *kp = args.k + row * D + dw0 + 8 * g;
-#pragma unroll
-        for (int j = 0; j < KL; ++j) f.k[j] = load_stream16(kp + 32 * j);
-        if constexpr (VF == kVF16) {
-            const uint16_t *vp = (const uint16_t *)args.v + row * D + dw0 + 8 * g;
-#pragma unroll
-            for (int j = 0; j < KL; ++j) f.v[j] = load_stream16(vp + 32 * j);
-        } else {
-            // VB = 32: dims 16g + [0,16) and 64 + 16g + [0,16); 16: 16g + [0,16); 8: 8g + [0,8)
-            const uint8_t *vp = (const uint8_t *)args.v + row * D + dw0;
-            if constexpr (VB == 32) {
-                f.v[0] = load_stream16(vp + 16 * g);
-                f.v[1] = load_stream16(vp + 64 + 16 * g);
-            } else if constexpr (VB == 16) {
-                f.v[0] = load_stream16(vp + 16 * g);
-            } else {
-                const uint2 x = *(const uint2 *)(vp + 8 * g);
-                f.v[0] = make_uint4(x.x, x.y, 0, 0);
-            }
-            if constexpr (VF == kVI8) {
-                const uint16_t *sp = (const uint16_t *)args.vs + row * (D / 32);
-                if constexpr (VB == 32) {
-                    f.side[0] = h2f(sp[(dw0 + 16 * g) / 32]);
-                    f.side[1] = h2f(sp[(dw0 + 64 + 16 * g) / 32]);
-                } else {
-                    f.side[0] = h2f(sp[(dw0 + (VB == 16 ? 16 : 8) * g) / 32]);
-                }
-            } else {
-                f.side[0] = ((const float *)args.vs)[row * (D / CB_B) + dw0 / CB_B];
-            }
-        }
+        return rowbase + rc;
     };
-
-    // This lane's key row of the wave's V tile, dequantised to fp32, into LDS.
-    auto stage_v = [&](const MFrag<D> &f) {
-        float *rowp = &s_v[w][c16][0];
-        if constexpr (VF == kVF16) {
+    // K: each load reads 64 bytes of 16 rows, so the two halves of a 128-byte line come
+    // from consecutive steps; plain (cached) loads let the second half hit in L1, where
+    // non-temporal ones measured 3-12% slower.  V reads whole lines and streams.
+    auto load_k = [&](int kb, MKTile<D, VF> &f) {
+        const uint16_t *kp = args.k + row_of(kb + c16) * D + 8 * g;
 #pragma unroll
-            for (int j = 0; j < KL; ++j) {
-                const uint32_t wd[4] = {f.v[j].x, f.v[j].y, f.v[j].z, f.v[j].w};
-                float x[8];
+        for (int s = 0; s < KS; ++s) f.k[s] = *(const uint4 *)(kp + 32 * s);
+    };
+    auto load_v = [&](int kb, MVTile<D, VF> &f) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    x[2 * q] = h2f((uint16_t)(wd[q] & 0xFFFF));
-                    x[2 * q + 1] = h2f((uint16_t)(wd[q] >> 16));
-                }
-                *(float4 *)(rowp + 32 * j + 8 * g) = make_float4(x[0], x[1], x[2], x[3]);
-                *(float4 *)(rowp + 32 * j + 8 * g + 4) = make_float4(x[4], x[5], x[6], x[7]);
-            }
-        } else {
-            constexpr int PIECES = VB == 32 ? 2 : 1;        // 16-byte pieces (VB = 8: one half piece)
-            constexpr int WORDS = VB == 8 ? 2 : 4;          // 32-bit words of codes per piece
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = row_of(kb + 4 * g + i);
 #pragma unroll
-            for (int pc = 0; pc < PIECES; ++pc) {
-                const uint32_t wd[4] = {f.v[pc].x, f.v[pc].y, f.v[pc].z, f.v[pc].w};
-                const int d0 = VB == 32 ? 64 * pc + 16 * g : (VB == 16 ? 16 * g : 8 * g);
-                const float sc = VF == kVI8 ? f.side[pc] : f.side[0];
-#pragma unroll
-                for (int q = 0; q < WORDS; ++q) {
-                    float x[4];
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const uint32_t code = (wd[q] >> (8 * b)) & 0xFF;
-                        if constexpr (VF == kVI8) x[b] = (float)(int8_t)code * sc;
-                        else x[b] = s_cb[code] * sc;
+            for (int b = 0; b < NB; ++b) {
+                const int d0 = BW * b + EV * c16;
+                if constexpr (VF == kVF16) {
+                    f.v[i][b] = load_stream16((const uint16_t *)args.v + row * D + d0);
+                } else {
+                    const uint8_t *vp = (const uint8_t *)args.v + row * D + d0;
+                    if constexpr (Geo::VBYTES == 16) {
+                        f.v[i][b] = load_stream16(vp);
+                    } else {
+                        const uint2 x = *(const uint2 *)vp;
+                        f.v[i][b] = make_uint4(x.x, x.y, 0, 0);
                     }
-                    *(float4 *)(rowp + d0 + 4 * q) = make_float4(x[0], x[1], x[2], x[3]);
+                    if constexpr (VF == kVI8)
+                        f.side[i][b] = h2f(((const uint16_t *)args.vs)[row * (D / 32) + d0 / 32]);
+                    else
+                        f.side[i][b] = ((const float *)args.vs)[row * (D / CB_B) + d0 / CB_B];
                 }
             }
         }
     };
 
     float m = -INFINITY, l = 0.f;   // running max (log2 domain) and this lane's part of the sum, head c16
-    f32x4_t o[NT];                  // O^T: o[tt][i] = dim dw0 + 16 tt + 4g + i of head c16
+    f32x4_t o[NO];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) o[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NO; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const float sl2 = args.scale_log2;
 
-    // One tile: QK part -> LDS, V tile -> LDS, barrier, whole S^T, softmax, PV.
-    auto step = [&](int tile, int kb, const MFrag<D> &f) {
+    // S^T of one tile of 16 keys
+    auto qk = [&](const MKTile<D, VF> &kt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < KL; ++j) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x16f16(as_h4(f.k[j].x, f.k[j].y), qf[2 * j], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x16f16(as_h4(f.k[j].z, f.k[j].w), qf[2 * j + 1], acc, 0, 0, 0);
+        for (int s = 0; s < KS; ++s) {
+            half8_t qb;
+            if constexpr (QLDS) qb = as_h8(*(const uint4 *)(s_q + c16 * QS + 32 * s + 8 * g));
+            else qb = qf[s];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kt.k[s]), qb, acc, 0, 0, 0);
         }
-        s_s[tile & 1][w][lane] = acc;
-        stage_v(f);
-        __syncthreads();
-        f32x4_t sv = s_s[tile & 1][0][lane];
-#pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) sv += s_s[tile & 1][ww][lane];
-
-        // online softmax over the tile's keys kb + 4g + i of head c16
-        float s[4], p[4];
+        return acc;
+    };
+    // The rest of the tile from kb: online softmax, O^T += V^T P^T.
+    auto step = [&](int kb, const f32x4_t acc, const MVTile<D, VF> &vt) {
+        float sc[4], p[4];
         float mt = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s[i] = (kb + 4 * g + i) < cend ? sv[i] * sl2 : -INFINITY;
-            mt = fmaxf(mt, s[i]);
+            sc[i] = (kb + 4 * g + i) < cend ? acc[i] * sl2 : -INFINITY;
+            mt = fmaxf(mt, sc[i]);
         }
         mt = fmaxf(mt, shfl_xor_f32(mt, 16));
         mt = fmaxf(mt, shfl_xor_f32(mt, 32));
-        const float mx = fmaxf(m, mt);
-        const float ms = (mx == -INFINITY) ? 0.f : mx;
-        const float alpha = fast_exp2(m - ms);
+        // The reference m (log2 domain) moves only when a logit passes it by more than
+        // kLazyMax, so the weights stay <= 2^kLazyMax and the accumulators are rescaled
+        // rarely (O and S share the reference, so O / S is unchanged).
+        if (__builtin_amdgcn_ballot_w64(mt > m + kLazyMax) != 0) {
+            const float mx = fmaxf(m, mt);
+            const float alpha = fast_exp2(m - ((mx == -INFINITY) ? 0.f : mx));
+            l *= alpha;
+#pragma unroll
+            for (int j = 0; j < NO; ++j) o[j] *= alpha;
+            m = mx;
+        }
+        const float ms = (m == -INFINITY) ? 0.f : m;
         float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = fast_exp2(s[i] - ms);
+            p[i] = fast_exp2(sc[i] - ms);
             psum += p[i];
         }
-        l = l * alpha + psum;
-        m = mx;
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) o[tt] *= alpha;
+        l += psum;
 
-        // O^T += V^T P^T, 4 keys per MFMA: step i takes keys 4g + i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                const float a = s_v[w][4 * g + i][16 * tt + c16];
-                o[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[i], o[tt], 0, 0, 0);
+            for (int b = 0; b < NB; ++b) {
+                float x[EV];
+                const uint32_t wd[4] = {vt.v[i][b].x, vt.v[i][b].y, vt.v[i][b].z, vt.v[i][b].w};
+                if constexpr (VF == kVF16) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        x[2 * q] = h2f((uint16_t)(wd[q] & 0xFFFF));
+                        x[2 * q + 1] = h2f((uint16_t)(wd[q] >> 16));
+                    }
+                } else {
+                    const float sd_ = vt.side[i][b];
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) {
+                        const uint32_t code = (wd[e / 4] >> (8 * (e % 4))) & 0xFF;
+                        if constexpr (VF == kVI8) x[e] = (float)(int8_t)code * sd_;
+                        else x[e] = s_cb[code] * sd_;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < EV; ++e)
+                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], p[i], o[b * EV + e], 0, 0, 0);
             }
         }
     };
 
-    const int ntiles = (cend - cbeg + kMfmaKeys - 1) / kMfmaKeys;   // the same in every wave
-    MFrag<D> fa, fb;
-    if (ntiles > 0) load(cbeg, fa);
-    if constexpr (VF == kVCB) {
-        s_cb[tid] = args.codebook[tid & args.cb_mask] * args.cb_scale;
-        __syncthreads();
+    const int ntiles = (cend - cbeg + kMfmaKeys - 1) / kMfmaKeys;
+    MKTile<D, VF> kt;
+    MVTile<D, VF> va, vb;
+    int tl = w;
+    if (tl < ntiles) {
+        load_k(cbeg + tl * kMfmaKeys, kt);
+        load_v(cbeg + tl * kMfmaKeys, va);
     }
-    for (int tl = 0; tl < ntiles; tl += 2) {
-        if (tl + 1 < ntiles) load(cbeg + (tl + 1) * kMfmaKeys, fb);
-        step(tl, cbeg + tl * kMfmaKeys, fa);
-        if (tl + 1 >= ntiles) break;
-        if (tl + 2 < ntiles) load(cbeg + (tl + 2) * kMfmaKeys, fa);
-        step(tl + 1, cbeg + (tl + 1) * kMfmaKeys, fb);
+    if constexpr (VF == kVCB) s_cb[tid] = args.codebook[tid & args.cb_mask] * args.cb_scale;
+    if constexpr (VF == kVCB || QLDS) __syncthreads();
+    // K: one buffer, refilled as soon as the QK steps have read it; V: two buffers.
+    for (; tl < ntiles; tl += 2 * kWaves) {
+        f32x4_t acc = qk(kt);
+        const bool more1 = tl + kWaves < ntiles;
+        if (more1) {
+            load_k(cbeg + (tl + kWaves) * kMfmaKeys, kt);
+            load_v(cbeg + (tl + kWaves) * kMfmaKeys, vb);
+        }
+        step(cbeg + tl * kMfmaKeys, acc, va);
+        if (!more1) break;
+        acc = qk(kt);
+        if (tl + 2 * kWaves < ntiles) {
+            load_k(cbeg + (tl + 2 * kWaves) * kMfmaKeys, kt);
+            load_v(cbeg + (tl + 2 * kWaves) * kMfmaKeys, va);
+        }
+        step(cbeg + (tl + kWaves) * kMfmaKeys, acc, vb);
     }
 
-    // the sum over the tile keys of the 4 lane groups of head c16
+    // merge the 4 waves: M = max of their maxima, each wave's O and S scaled by 2^(m_w - M)
     l += shfl_xor_f32(l, 16);
     l += shfl_xor_f32(l, 32);
-    if (!head_ok) return;   // no barriers follow
-    if (sd.n_chunks == 1) {
-        float *op = args.out + qrow * D + dw0 + 4 * g;
+    if (g == 0) {
+        s_m[w][c16] = m;
+        s_l[w][c16] = l;
+    }
+    __syncthreads();
+    float M = s_m[0][c16];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            float4 r;
-            r.x = (l == 0.f) ? 0.f : o[tt][0] / l;
-            r.y = (l == 0.f) ? 0.f : o[tt][1] / l;
-            r.z = (l == 0.f) ? 0.f : o[tt][2] / l;
-            r.w = (l == 0.f) ? 0.f : o[tt][3] / l;
-            *(float4 *)(op + 16 * tt) = r;
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][c16]);
+    const float Ms = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) L += s_l[ww][c16] * fast_exp2(s_m[ww][c16] - Ms);
+    const float f = fast_exp2(m - Ms);
+#pragma unroll
+    for (int j = 0; j < NO; ++j) o[j] *= f;
+    // ((o3 + o2) + o1) + o0 through one LDS buffer, in a fixed order
+#pragma unroll
+    for (int ww = kWaves - 1; ww >= 1; --ww) {
+        if (w == ww) {
+#pragma unroll
+            for (int j = 0; j < NO; ++j) {
+                if (ww < kWaves - 1) o[j] += s_o[j][lane];
+                s_o[j][lane] = o[j];
+            }
         }
+        __syncthreads();
+    }
+    if (w != 0 || !head_ok) return;   // no barriers follow
+#pragma unroll
+    for (int j = 0; j < NO; ++j) o[j] += s_o[j][lane];
+
+    float *op;
+    float scale_out = 1.f;
+    if (sd.n_chunks == 1) {
+        op = args.out + qrow * D;
+        scale_out = (L == 0.f) ? 0.f : 1.f / L;
     } else {
         const int64_t prow = sd.part_row0 + (int64_t)(h0 + c16) * sd.n_chunks + c;
-        float *op = args.ws_o + prow * D + dw0 + 4 * g;
+        op = args.ws_o + prow * D;
+        if (g == 0) {
+            args.ws_ml[prow * 2 + 0] = M;
+            args.ws_ml[prow * 2 + 1] = L;
+        }
+    }
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-            *(float4 *)(op + 16 * tt) = make_float4(o[tt][0], o[tt][1], o[tt][2], o[tt][3]);
-        if (w == 0 && g == 0) {
-            args.ws_ml[prow * 2 + 0] = m;
-            args.ws_ml[prow * 2 + 1] = l;
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float *dst = op + BW * b + 4 * EV * g + EV * r;
+#pragma unroll
+            for (int e = 0; e < EV; e += 4)
+                *(float4 *)(dst + e) = make_float4(o[b * EV + e][r] * scale_out, o[b * EV + e + 1][r] * scale_out,
+                                                   o[b * EV + e + 2][r] * scale_out, o[b * EV + e + 3][r] * scale_out);
         }
     }
 }

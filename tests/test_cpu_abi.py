@@ -91,12 +91,14 @@ def test_gqa_blocks_multiply_workgroups_for_large_groups():
     # lane kernel: G = 3 as three single heads; G = 8 at head_dim 64 as two blocks of 4
     assert binding.attn_decode_plan([640], 0, 6, 2, 128)["partial_workgroups"] == 2 * 3 * 10
     assert binding.attn_decode_plan([2560], 0, 16, 2, 64)["partial_workgroups"] == 2 * 2 * 40
-    # matrix-core kernel, automatic for 16k heads per kv head, or 8k at head_dim 128: blocks of 16, else 8
-    assert binding.attn_decode_plan([640], 0, 16, 2, 128)["partial_workgroups"] == 2 * 1 * 10
-    assert binding.attn_decode_plan([640], 0, 64, 2, 128)["partial_workgroups"] == 2 * 2 * 10
-    assert binding.attn_decode_plan([640], 0, 64, 2, 512)["partial_workgroups"] == 2 * 2 * 10
-    # 24 heads per kv head at 256 stay on the lane kernel: six blocks of 4
-    assert binding.attn_decode_plan([640], 0, 48, 2, 256)["partial_workgroups"] == 2 * 6 * 10
+    # matrix-core kernel, automatic for 8k heads per kv head at head_dim >= 128: blocks of 16, else 8,
+    # and chunks of at least 512 positions (640 -> 2 chunks)
+    assert binding.attn_decode_plan([640], 0, 16, 2, 128)["partial_workgroups"] == 2 * 1 * 2
+    assert binding.attn_decode_plan([640], 0, 64, 2, 128)["partial_workgroups"] == 2 * 2 * 2
+    assert binding.attn_decode_plan([640], 0, 64, 2, 512)["partial_workgroups"] == 2 * 2 * 2
+    assert binding.attn_decode_plan([640], 0, 48, 2, 256)["partial_workgroups"] == 2 * 3 * 2
+    p = binding.attn_decode_plan([8192, 16384, 32768, 131072], 0, 16, 2, 256)
+    assert p["chunk"] == [512, 512, 1024, 2048]
 
 
 @pytest.mark.parametrize("args,frag", [

@@ -64,10 +64,9 @@ def test_matrix_core_path_matches_oracle(case):
     _report(f"{case} matrix", assert_parity(got, ref, f"{case} matrix"))
     lanes = _run(inp, W, path=1, dev=dev).cpu().numpy()
     _report(f"{case} lanes", assert_parity(lanes, ref, f"{case} lanes"))
-    # the automatic choice: matrix cores for 16k heads per kv head, or 8k at head_dim 128
-    G = nq // nkv
+    # the automatic choice: the matrix cores wherever they apply (8k heads per kv head, head_dim >= 128)
     auto = _run(inp, W, path=0, dev=dev).cpu().numpy()
-    assert np.array_equal(auto, got if (G % 16 == 0 or d == 128) else lanes), "automatic choice"
+    assert np.array_equal(auto, got), "automatic choice"
     for s, L in enumerate(seq):
         if L == 0:
             assert np.all(got[s] == 0.0)
