@@ -241,7 +241,8 @@ def gqa_sweep(only: str = "") -> int:
             res[key + "_us"] = round(us, 2)
             res[key + "_hbm_frac"] = round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
             del graph
-        res["automatic"] = "matrix" if ((nq // nkv) % 16 == 0 or d == 128) else "lanes"
+        # the library's automatic choice (planner.hpp, mfma_preferred): matrix cores wherever they apply
+        res["automatic"] = "matrix" if ((nq // nkv) % 8 == 0 and d >= 128) else "lanes"
         print(json.dumps(res), flush=True)
         del q, k, out
         torch.cuda.empty_cache()

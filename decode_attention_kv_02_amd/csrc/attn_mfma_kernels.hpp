@@ -57,6 +57,7 @@ struct MfmaGeometry {
     static constexpr int VBYTES = EV * (VF == kVF16 ? 2 : 1);            // 16, or 8 (byte V at D = 128)
     static constexpr int NO = NB * EV;                                   // f32x4 accumulators = D / 16
     static_assert(NO * 16 == D, "accumulators cover every dim once");
+    static_assert(VF != kVCB || BW == (D < 256 ? D : 256), "one codebook norm block per load");
 };
 
 template <int D, int VF>
@@ -231,17 +232,21 @@ __global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const Launc
                         x[2 * q + 1] = h2f((uint16_t)(wd[q] >> 16));
                     }
                 } else {
-                    const float sd_ = vt.side[i][b];
 #pragma unroll
                     for (int e = 0; e < EV; ++e) {
                         const uint32_t code = (wd[e / 4] >> (8 * (e % 4))) & 0xFF;
-                        if constexpr (VF == kVI8) x[e] = (float)(int8_t)code * sd_;
-                        else x[e] = s_cb[code] * sd_;
+                        if constexpr (VF == kVI8) x[e] = (float)(int8_t)code * vt.side[i][b];
+                        else x[e] = s_cb[code];
                     }
                 }
+                // Codebook V: the 16 rows (dims) of these instructions lie in one norm block
+                // (BW = min(D, 256) dims), so the norm belongs to the key alone, the k index:
+                // it scales P, the B operand, once per load instead of every element.
+                float pb = p[i];
+                if constexpr (VF == kVCB) pb *= vt.side[i][b];
 #pragma unroll
                 for (int e = 0; e < EV; ++e)
-                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], p[i], o[b * EV + e], 0, 0, 0);
+                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], pb, o[b * EV + e], 0, 0, 0);
             }
         }
     };
