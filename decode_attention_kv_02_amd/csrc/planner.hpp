@@ -114,10 +114,24 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // gets 1024).  The pages make the same trade (tessl nn.rs DecodeChunk: grid
 // parallelism against the number of partials the reduce pass combines).
 inline int64_t target_chunks(int64_t n) {
-    if (n <= 8192) return 64;
+    if (n <= 4096) return 64;
     if (n <= 65536) return 32;
     return 16;
 }
+
+// Above 4096 positions a chunk also carries at least 64 KiB of fp16 K and V per
+// kv head (65536 / head_dim positions): slots that long usually come in
+// batches, where fine chunks leave each workgroup too little work for its
+// fixed cost.  Measured with forced chunks (lane kernel, graph-replayed):
+// 8 x 8192 at head_dim 128 with 4 heads per kv head 83.5 us at 128 positions,
+// 54.9 at 512; at head_dim 64 68.9 -> 36.0 us (1024); 8 x 8192 int8 V at 256
+// 82.2 -> 73.4 us (256), while a lone 8192 slot moves by 0.3-2 us.  Lone
+// slots of 4096 or less (1 x 4096: 12.0 us at 64 positions, 14.4 at 256)
+// keep the fine split.
+constexpr int64_t kLongSlot = 4096;
+constexpr int64_t kMinChunkKVBytes = 65536;   // fp16 K + V bytes per kv head: chunk * 2 * head_dim * 2
+
+inline int64_t min_chunk_long(int32_t head_dim) { return kMinChunkKVBytes / (4 * (int64_t)head_dim) * 4; }
 
 // A slot whose fp16 K and V rows of one kv head fit in this many bytes is not
 // split: one workgroup streams it in about the time of the first-load latency,
@@ -151,6 +165,7 @@ inline int64_t chunk_for(int64_t n, int32_t head_dim, int32_t forced, bool mfma 
         c = ceil_div(n, target_chunks(n));
         c = ceil_div(c, kChunkQuantum) * kChunkQuantum;
         if (c < kChunkMin) c = kChunkMin;
+        if (n > kLongSlot && c < min_chunk_long(head_dim)) c = min_chunk_long(head_dim);
         if (c > kChunkMax) c = kChunkMax;
     }
     const int64_t floor_c = ceil_div(n, kMaxChunks);
