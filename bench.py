@@ -267,6 +267,7 @@ def main(argv=None) -> int:
 
     from decode_attention_kv_02_amd import binding
     from decode_attention_kv_02_amd.workloads import (APPEND_WORKLOADS, CACHE_WORKLOADS, CODEBOOK_WORKLOADS,
+                                                      SERVE_STEP_WORKLOADS, serve_step_inputs,
                                                       WORKLOADS, append_new_rows, cache_workload_inputs,
                                                       codebook_workload_inputs, workload_inputs)
 
@@ -610,6 +611,57 @@ def main(argv=None) -> int:
             print(f"[bench] {cw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), cold {cold:.2f} us",
                   file=sys.stderr, flush=True)
             del ct
+            torch.cuda.empty_cache()
+        # serving steps on a codebook-V cache: attn_kv_append_cb + attn_decode_cache_cb + attn_fwht_undo
+        for sw in SERVE_STEP_WORKLOADS:
+            print(f"[bench] generating {sw.name}", file=sys.stderr, flush=True)
+            ci, kn_h, vn_h = serve_step_inputs(sw)
+            sq, sk, svc, svn, scb, ssg = (t.to(dev) for t in (ci.q, ci.k, ci.v_codes, ci.v_norms, ci.codebook,
+                                                              ci.signs))
+            skn, svn_new = kn_h.to(dev), vn_h.to(dev)
+            del ci.k, ci.v_codes
+            sout = torch.empty((ci.n_queries, ci.n_q_heads, ci.head_dim), dtype=torch.float32, device=dev)
+            s_sid = np.asarray(ci.slot_ids, dtype=np.int32)
+            s_pos = np.asarray(ci.positions, dtype=np.int32)
+
+            def serve_call(st=None):
+                st = st or stream
+                binding.attn_kv_append_cb(skn, svn_new, sk, svc, svn, ssg, scb, sw.bits, s_sid, s_pos, ci.n_queries,
+                                          ci.n_cache_slots, ci.capacity, ci.ring, ci.n_kv_heads, ci.head_dim,
+                                          stream=st)
+                binding.attn_decode_cache_cb(sq, sk, svc, svn, scb, sw.bits, s_sid, s_pos, ci.n_queries,
+                                             ci.n_cache_slots, ci.capacity, ci.ring, 0, sout, ci.n_q_heads,
+                                             ci.n_kv_heads, ci.head_dim, ci.scale, stream=st)
+                binding.attn_fwht_undo(sout, ssg, sout, stream=st)
+
+            def per_call_us(fn, n):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(n):
+                    fn()
+                torch.cuda.synchronize()
+                return (time.perf_counter() - t0) * 1e6 / n
+
+            for _ in range(3):
+                serve_call()
+            d, B = ci.head_dim, min(ci.head_dim, 256)
+            att = sum(cache_attended(p, ci.capacity, ci.ring, 0) for p in ci.positions)
+            nb = att * ci.n_kv_heads * (2 * d + d + 4 * (d // B))   # K fp16 + codes + norms read
+            warm = statistics.median(per_call_us(serve_call, args.reps) for _ in range(3))
+            g_us = graph_us_per_call(lambda st: serve_call(st=st))
+            assert torch.isfinite(sout).all().item(), "non-finite output"
+            per.append({
+                "workload": sw.name, "window": 0, "kv_bytes": nb,
+                "step": "attn_kv_append_cb + attn_decode_cache_cb + attn_fwht_undo",
+                "warm_us_per_call": round(warm, 2),
+                "warm_gbs": round(nb / (warm * 1e-6) / 1e9, 1),
+                "warm_hbm_frac": round(nb / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "graph_us_per_call": round(g_us, 2),
+                "graph_gbs": round(nb / (g_us * 1e-6) / 1e9, 1),
+            })
+            print(f"[bench] {sw.name}: warm {warm:.2f} us, graph {g_us:.2f} us ({per[-1]['graph_gbs']} GB/s)",
+                  file=sys.stderr, flush=True)
+            del sq, sk, svc, svn, scb, ssg, skn, svn_new, sout
             torch.cuda.empty_cache()
         # KV append presets (attn_kv_append): bytes = fp32 K and V read + fp16 K and V (+ scales) written
         for aw in APPEND_WORKLOADS:

@@ -468,3 +468,48 @@ def make_cache_codebook_inputs(n_cache_slots: int, capacity: int, ring: int, slo
     return CacheCodebookInputs(q, ci.k, ci.v_codes, ci.v_norms, ci.codebook, bits, ci.signs,
                                tuple(int(x) for x in slot_ids), tuple(int(x) for x in positions), n_cache_slots,
                                capacity, int(ring), n_q_heads, n_kv_heads, head_dim, ci.scale)
+
+
+@dataclasses.dataclass(frozen=True)
+class ServeStepWorkloadConfig:
+    """One decode step of the hybrid regime on a fixed-capacity codebook-V cache: append each
+    query's new token (K fp16, V codebook-encoded), attend from it, undo the rotation."""
+    index: int
+    name: str
+    description: str
+    n_cache_slots: int
+    capacity: int
+    ring: int
+    slot_ids: Tuple[int, ...]
+    positions: Tuple[int, ...]
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    bits: int
+
+    @property
+    def seed_base(self) -> int:
+        return 1000 * self.index
+
+
+SERVE_STEP_WORKLOADS = (
+    ServeStepWorkloadConfig(40, "serve_step_codebook8_8x32768_d256",
+                            "8 slots, each appending its token 32768 and attending 0..32767 (linear cache)",
+                            8, 32768, 0, tuple(range(8)), (32767,) * 8, 16, 8, 256, 8),
+    ServeStepWorkloadConfig(41, "serve_step_codebook8_ring1024_d256",
+                            "8 slots on 1024-row rings, tokens deep into long contexts",
+                            8, 1024, 1, tuple(range(8)), (131071, 90000, 50001, 77777, 2047, 300000, 1024, 65536),
+                            16, 8, 256, 8),
+)
+
+
+def serve_step_inputs(cfg: ServeStepWorkloadConfig):
+    """The cache (make_cache_codebook_inputs) and the step's new fp32 K and V rows [n_queries, n_kv, D]
+    (seeds seed_base + 5 and + 6)."""
+    ci = make_cache_codebook_inputs(cfg.n_cache_slots, cfg.capacity, cfg.ring, cfg.slot_ids, cfg.positions,
+                                    cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.bits, cfg.seed_base)
+    gk = torch.Generator("cpu").manual_seed(cfg.seed_base + 5)
+    gv = torch.Generator("cpu").manual_seed(cfg.seed_base + 6)
+    shape = (len(cfg.slot_ids), cfg.n_kv_heads, cfg.head_dim)
+    return ci, torch.randn(shape, generator=gk, dtype=torch.float32), torch.randn(shape, generator=gv,
+                                                                                    dtype=torch.float32)
