@@ -130,3 +130,41 @@ def test_matrix_core_path_is_rejected_where_it_does_not_apply():
         _run(inp, 0, path=2)
     ok = _run(inp, 0, path=0).cpu().numpy()                          # the lane kernel there
     assert_parity(ok, run_oracle(inp, 0), "auto at head_dim 64")
+
+
+@pytest.mark.parametrize("d,nq,nkv,i8", [(128, 16, 2, False), (256, 32, 2, True), (512, 16, 2, False)])
+def test_large_and_rising_logits(d, nq, nkv, i8):
+    """Logits of several hundred, and for head 0 a ramp rising by about 64 (natural log) over
+    each slot, so the running maximum moves at almost every tile: the softmax reference of the
+    matrix-core kernel (which moves only past a headroom) and the lanes' exact one must both
+    match the oracle."""
+    seq = (3000, 1500)
+    inp = make_inputs(seq, nq, nkv, d, i8, seed_base=7800 + d)
+    inp.q.mul_(3.0)
+    k = inp.k.numpy()                       # fp16 view, packed [slot][kv][pos][D]
+    off = 0
+    for s, L in enumerate(seq):
+        v = np.sign(inp.q[s, 0].numpy().astype(np.float32))   # q . v = sum |q|
+        ramp = (5.0 * np.arange(L) / L).astype(np.float32)[:, None] * v[None, :]
+        rows = k[off:off + L * d].reshape(L, d)                  # kv head 0 of slot s
+        rows[:] = (rows.astype(np.float32) * 0.5 + ramp).astype(np.float16)
+        off += nkv * L * d
+    ref = run_oracle(inp, 0)
+    dev = to_device(inp)
+    for path in (2, 1):
+        got = _run(inp, 0, path=path, dev=dev).cpu().numpy()
+        _report(f"rising logits D={d} path {path}", assert_parity(got, ref, f"path {path}"))
+
+
+@pytest.mark.parametrize("d,nq,nkv,bits", [(256, 16, 2, 5), (128, 64, 4, 6), (512, 32, 2, 6)])
+def test_matrix_core_codebook_bits(d, nq, nkv, bits):
+    seq = (2100, 700, 0)
+    ci = make_codebook_inputs(seq, nq, nkv, d, bits, 7900 + d + bits)
+    dv = torch.device("cuda:0")
+    q, k, vc, vn, cb = (t.to(dv) for t in (ci.q, ci.k, ci.v_codes, ci.v_norms, ci.codebook))
+    ref = oracle_attn_decode_cb(ci.q.numpy(), ci.k.numpy(), ci.v_codes.numpy(), ci.v_norms.numpy(),
+                                ci.codebook.numpy(), bits, seq, 0, nq, nkv, d, ci.scale)
+    out = torch.full((len(seq), nq, d), float("nan"), dtype=torch.float32, device=dv)
+    binding.attn_decode_cb(q, k, vc, vn, cb, bits, seq, 0, out, len(seq), nq, nkv, d, ci.scale, path=2)
+    torch.cuda.synchronize()
+    _report(f"codebook {bits}-bit D={d} G={nq // nkv}", assert_parity(out.cpu().numpy(), ref, "codebook"))
