@@ -89,3 +89,46 @@ def test_graph_of_codebook_attend_and_undo():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i}"
+
+
+def test_graph_of_codebook_serving_step():
+    """The hybrid decode step on a ring cache -- append (K fp16, V codebook-encoded), attend,
+    undo -- captured once and replayed; each replay rewrites the same cache rows and must give
+    the eager output and cache bit for bit."""
+    from decode_attention_kv_02_amd.workloads import make_cache_codebook_inputs
+    sid, pos = (0, 1, 2), (3000, 1023, 77)
+    ci = make_cache_codebook_inputs(3, 1024, 1, sid, pos, 16, 2, 256, 8, 9000)
+    dev = torch.device("cuda:0")
+    q, k, vc, vn, cb, sg = (t.to(dev) for t in (ci.q, ci.k, ci.v_codes, ci.v_norms, ci.codebook, ci.signs))
+    g = torch.Generator("cpu").manual_seed(9001)
+    kn = torch.randn((3, 2, 256), generator=g).to(dev)
+    vnew = torch.randn((3, 2, 256), generator=g).to(dev)
+    out = torch.empty((3, 16, 256), dtype=torch.float32, device=dev)
+    k0, vc0, vn0 = k.clone(), vc.clone(), vn.clone()
+    side = torch.cuda.Stream()
+
+    def call():
+        binding.attn_kv_append_cb(kn, vnew, k, vc, vn, sg, cb, 8, sid, pos, 3, 3, 1024, 1, 2, 256, stream=side)
+        binding.attn_decode_cache_cb(q, k, vc, vn, cb, 8, sid, pos, 3, 3, 1024, 1, 0, out, 16, 2, 256, ci.scale,
+                                     stream=side)
+        binding.attn_fwht_undo(out, sg, out, stream=side)
+
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.synchronize()
+    eager = (out.clone(), k.clone(), vc.clone(), vn.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call()
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        k.copy_(k0)
+        vc.copy_(vc0)
+        vn.copy_(vn0)             # the appended rows must be written again by the replay
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((out, k, vc, vn), eager, ("out", "k", "codes", "norms")):
+            assert torch.equal(got, want), f"replay {i}: {name}"
