@@ -117,12 +117,12 @@ typedef struct attn_decode_options {
     void *ev_partial_begin;
     void *ev_partial_end;
     /* Which partial kernel computes the call: 0 = automatic (the matrix-core
-     * kernel for 16k query heads per kv head at head_dim >= 128 and for 8k
-     * at head_dim 128, the lane kernel otherwise), 1 = the lane kernel, 2 =
-     * the matrix-core kernel (EINVAL unless the heads per kv head are a
-     * multiple of 8 and head_dim >= 128).  Results of the two differ only
-     * in fp32 rounding.  The matrix-core kernel always merges split slots in
-     * the combine kernel (merge_mode 2 then behaves like 1). */
+     * kernel wherever it applies, the lane kernel otherwise), 1 = the lane
+     * kernel, 2 = the matrix-core kernel (EINVAL unless the query heads per
+     * kv head are a multiple of 8 and head_dim >= 128).  The two kernels
+     * split a slot into different chunks and differ only in fp32 rounding.
+     * The matrix-core kernel always merges split slots in the combine kernel
+     * (merge_mode 2 then behaves like 1). */
     int32_t path;
 } attn_decode_options;
 
