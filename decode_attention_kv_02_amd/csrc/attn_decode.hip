@@ -221,10 +221,13 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     std::string err = make_plan(spans, n_q, n_kv, D, chunk, merge_mode, plan, path);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
 
-    const partial_fn pk = plan.mfma ? select_partial_mfma(D, vsrc.format)
-                                    : select_partial(D, plan.QB, plan.GB, vsrc.format);
+    bool any_mfma = false, any_lanes = false;
+    for (const LaunchGroup &lg : plan.groups) (lg.mfma ? any_mfma : any_lanes) = true;
+    const partial_fn pk_mfma = any_mfma ? select_partial_mfma(D, vsrc.format) : nullptr;
+    const partial_fn pk_lanes = any_lanes ? select_partial(D, plan.lanes.QB, plan.lanes.GB, vsrc.format) : nullptr;
     const combine_fn ck = select_combine(D);
-    if (pk == nullptr || ck == nullptr) return fail(ATTN_DECODE_EINVAL, "no kernel for this shape");
+    if ((any_mfma && pk_mfma == nullptr) || (any_lanes && pk_lanes == nullptr) || ck == nullptr)
+        return fail(ATTN_DECODE_EINVAL, "no kernel for this shape");
 
     // ---- HIP from here on
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
@@ -253,13 +256,14 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     args.ws_o = ws_o;
     args.ws_ml = ws_ml;
     args.counters = counters;
-    args.fuse_limit = plan.fuse_limit;
     args.n_q = n_q;
     args.G = plan.G;
-    args.n_sub = plan.n_sub;
     args.scale_log2 = (float)scale_log2;
 
     auto fill = [&](const LaunchGroup &lg) {
+        const KernelShape &ks = lg.mfma ? plan.matrix : plan.lanes;
+        args.n_sub = ks.n_sub;
+        args.fuse_limit = lg.mfma ? 1 : plan.fuse_limit;
         args.n_slots = (int32_t)lg.slots.size();
         int32_t item = 0, comb = 0;
         int32_t lead_pos = 0;
@@ -283,7 +287,7 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
             sd.ring_base = sp.ring_base;
             sd.group_n = (int16_t)sp.group_n;
             sd.lead_off = (int16_t)(i - lead_pos);
-            if (sp.group_n > 0) item += n_kv * plan.n_sub * sp.n_chunks;
+            if (sp.group_n > 0) item += n_kv * ks.n_sub * sp.n_chunks;
             if (sp.n_chunks > 1 && !sp.fused) comb += n_q;
         }
         args.n_items = item;
@@ -295,7 +299,7 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     }
     for (const LaunchGroup &lg : plan.groups) {
         fill(lg);
-        hipLaunchKernelGGL(pk, dim3((unsigned)lg.items), dim3(kThreads), 0, stream, args);
+        hipLaunchKernelGGL(lg.mfma ? pk_mfma : pk_lanes, dim3((unsigned)lg.items), dim3(kThreads), 0, stream, args);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
     }

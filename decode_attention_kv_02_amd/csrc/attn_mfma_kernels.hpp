@@ -81,8 +81,10 @@ __global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const Launc
     static_assert(kThreads == 256, "one thread per codebook table entry");
 
     const int item = xcd_item(blockIdx.x, args.n_items, args.n_sub);
-    const int si = upper_index(args.n_slots, item, [&](int i) { return args.slot[i].item_begin; });
-    const SlotDesc sd = args.slot[si];   // no query groups on this path
+    int si = upper_index(args.n_slots, item, [&](int i) { return args.slot[i].item_begin; });
+    si -= args.slot[si].lead_off;         // the query group's leader: its longest query
+    const SlotDesc sd = args.slot[si];
+    const int n_mem = sd.group_n;         // queries of the group (1 when alone); table entries si..
     const int local = item - sd.item_begin;
     const int sub = local % args.n_sub;
     const int t = local / args.n_sub;
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const Launc
     const int kvh = t / sd.n_chunks;
     const int cbeg = sd.lo + c * sd.chunk;
     const int cend = min(cbeg + sd.chunk, sd.L);
-    const int GB = args.G / args.n_sub;                 // heads of this block: 8 or 16
+    const int GB = args.G / args.n_sub;                 // heads per query of this block
     const int h0 = kvh * args.G + sub * GB;             // first head of the block (in the slot)
     const int64_t rowbase = sd.kv_row0 + (int64_t)kvh * sd.kv_stride;
 
@@ -99,8 +101,18 @@ __global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const Launc
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop control
     const int c16 = lane & 15;   // MFMA row / column of the lane
     const int g = lane >> 4;     // lane group
-    const bool head_ok = c16 < GB;
-    const int64_t qrow = (int64_t)sd.slot_idx * args.n_q + h0 + c16;
+    // Column c16 is head h0 + c16 % GB of the group's query c16 / GB: GB = 8 or 16 heads of one
+    // query, or, for the draft queries of a speculative-verify step, every head of the kv head
+    // for each of up to 16 / GB drafts.  Each query masks the positions past its own end.
+    const int mem = c16 / GB;
+    const bool head_ok = mem < n_mem;
+    const int mi = si + (head_ok ? mem : 0);
+    const int m_L = args.slot[mi].L;
+    const int m_nchunks = args.slot[mi].n_chunks;
+    const int64_t m_part = args.slot[mi].part_row0;
+    const int hh = c16 - mem * GB;
+    const int64_t qrow = (int64_t)args.slot[mi].slot_idx * args.n_q + h0 + hh;
+    const int cend_col = min(cbeg + sd.chunk, m_L);
 
     // q as the B operand of the QK steps: step s covers dims 32 s + 8 g + [0, 8), like the K loads.
     // Held in registers up to head_dim 128; above, in LDS (rows padded by 16 bytes so the 16
@@ -112,9 +124,12 @@ __global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const Launc
     if constexpr (QLDS) {
         // 4 waves x 64 lanes fill 16 rows of D halves, 16 bytes per thread per pass
         for (int x = tid * 8; x < 16 * D; x += kThreads * 8) {
-            const int hr = x / D, dd = x % D;
+            const int hr = x / D, dd = x % D;   // row hr: column hr's query and head
             uint4 a = make_uint4(0, 0, 0, 0);
-            if (hr < GB) a = *(const uint4 *)(args.q + ((int64_t)sd.slot_idx * args.n_q + h0 + hr) * D + dd);
+            if (hr / GB < n_mem) {
+                const int64_t qr = (int64_t)args.slot[si + hr / GB].slot_idx * args.n_q + h0 + hr % GB;
+                a = *(const uint4 *)(args.q + qr * D + dd);
+            }
             *(uint4 *)(s_q + hr * QS + dd) = a;
         }
     } else {
@@ -194,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const Launc
         float mt = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sc[i] = (kb + 4 * g + i) < cend ? acc[i] * sl2 : -INFINITY;
+            sc[i] = (kb + 4 * g + i) < cend_col ? acc[i] * sl2 : -INFINITY;
             mt = fmaxf(mt, sc[i]);
         }
         mt = fmaxf(mt, shfl_xor_f32(mt, 16));
@@ -309,17 +324,18 @@ __global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const Launc
         }
         __syncthreads();
     }
-    if (w != 0 || !head_ok) return;   // no barriers follow
+    // a group member whose last chunk is before c has nothing here
+    if (w != 0 || !head_ok || c >= m_nchunks) return;   // no barriers follow
 #pragma unroll
     for (int j = 0; j < NO; ++j) o[j] += s_o[j][lane];
 
     float *op;
     float scale_out = 1.f;
-    if (sd.n_chunks == 1) {
+    if (m_nchunks == 1) {
         op = args.out + qrow * D;
         scale_out = (L == 0.f) ? 0.f : 1.f / L;
     } else {
-        const int64_t prow = sd.part_row0 + (int64_t)(h0 + c16) * sd.n_chunks + c;
+        const int64_t prow = m_part + (int64_t)(h0 + hh) * m_nchunks + c;
         op = args.ws_o + prow * D;
         if (g == 0) {
             args.ws_ml[prow * 2 + 0] = M;

@@ -62,20 +62,29 @@ struct SlotPlan {
     int32_t group_n = 1;    // on a group leader: queries of its group; 0 on a follower
     int32_t leader = -1;    // on a follower: the leader's index
     std::vector<int32_t> members;   // on a leader: followers in table order
+    bool mfma = false;      // computed by the matrix-core partial kernel
+};
+
+// How one partial kernel splits the work: query heads per workgroup (GB, dividing G),
+// G / GB workgroups per (query group, kv head, chunk), queries per workgroup (QB).
+struct KernelShape {
+    int GB = 1;
+    int n_sub = 1;
+    int QB = 1;      // lane kernel: its template parameter (QB * GB <= 4); matrix cores: the largest group
 };
 
 struct LaunchGroup {
     std::vector<int32_t> slots;        // slot indices, in work-list order
     int64_t items = 0;                 // partial-kernel workgroups
     int64_t combine_rows = 0;          // combine-kernel workgroups
+    bool mfma = false;                 // which partial kernel computes this launch
 };
 
 struct CallPlan {
-    bool mfma = false;   // matrix-core partial kernel (groups of 8 or 16 heads per workgroup)
+    bool mfma = false;   // every query on the matrix-core kernel (8k heads per kv head, head_dim >= 128)
     int G = 1;           // query heads per KV head
-    int GB = 1;          // query heads per workgroup (1, 2 or 4 on the lanes, 8 or 16 on the matrix cores; divides G)
-    int QB = 1;          // queries per workgroup (QB * GB <= 4); 1 when no group formed
-    int n_sub = 1;       // G / GB workgroups share one (slot, kv head, chunk)
+    KernelShape lanes;   // the lane kernel's shape: GB 1, 2 or 4
+    KernelShape matrix;  // the matrix-core kernel's: GB 8 or 16, or GB = G for draft groups
     std::vector<SlotPlan> slots;
     std::vector<LaunchGroup> groups;
     int64_t part_rows = 0;         // partial rows (each head_dim floats + 2 stats)
@@ -261,22 +270,26 @@ inline int heads_per_workgroup(int G) {
     return 1;
 }
 
-// Which partial kernel computes a call.  The matrix-core kernel
-// (attn_partial_mfma_kernel) applies to a multiple of 8 query heads per kv
-// head at head_dim >= 128.  kPathAuto takes it where it measured faster than
-// the lane kernel on MI355X (graph-replayed calls over 0.1-0.5 GB caches):
-// 16 heads per kv head at any head_dim (1.1-3.4x: 32 q / 2 kv heads at 512,
-// 129 -> 84 us; 64 q / 4 kv at 128, 145 -> 43 us) and 8 at head_dim 128
-// (2.1-2.6x); with 8 heads at 256 or 512 the lane kernel stays ahead (fp16
-// 73 vs 94 us at 256, codebook 132 vs 156 us at 512).  kPathLanes /
-// kPathMatrix force one.
+// Which partial kernel computes a query.  The matrix-core kernel
+// (attn_partial_mfma_kernel) puts up to 16 (query, head) columns in one
+// workgroup.  It applies to a whole call at a multiple of 8 query heads per kv
+// head and head_dim >= 128, where it measured faster than the lane kernel on
+// every shape (graph-replayed, fp16 / int8 / codebook V, head_dim 128..512:
+// 1.3x at 8 heads and 512, up to 2.5x at 16 heads and 128).  With fewer heads
+// per kv head, the draft queries of one slot (a speculative-verify step) that
+// the lane kernel would group go to the matrix cores as one workgroup when
+// they fill at least 8 columns (drafts x heads; e.g. 4 drafts at 2 heads per
+// kv head), so each K and V byte is read once for all of them; the lane
+// kernel holds at most 4 rows.  Which kernel a query gets depends only on the
+// queries of its own slot, so a batched call equals per-slot calls bitwise.
+// kPathLanes forces the lane kernel everywhere, kPathMatrix the matrix cores
+// (where they apply to the whole call).
 enum KernelPath { kPathAuto = 0, kPathLanes = 1, kPathMatrix = 2 };
 
 inline bool mfma_applies(int G, int head_dim) { return G % 8 == 0 && head_dim >= 128; }
-// Measured (graph-replayed, 8 and 16 heads per kv head, head_dim 128..512, fp16 /
-// int8 / codebook V): the matrix-core kernel is faster than the lane kernel on
-// every shape where it applies, by 1.1x (8 heads at 256) to 3.4x (16 heads at 128).
 inline bool mfma_preferred(int G, int head_dim) { return mfma_applies(G, head_dim); }
+constexpr int kMfmaColumns = 16;      // (query, head) columns of one matrix-core workgroup
+constexpr int kMfmaGroupMinCols = 8;  // draft groups this wide go to the matrix cores
 
 // Builds the plan from the query spans; returns "" on success or an error message.
 inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, int32_t n_kv,
@@ -289,12 +302,23 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
     if (path == kPathMatrix && !mfma_applies(plan.G, head_dim))
         return "the matrix-core path needs a multiple of 8 query heads per kv head and head_dim >= 128";
     plan.mfma = path == kPathMatrix || (path == kPathAuto && mfma_preferred(plan.G, head_dim));
+    const int G = plan.G;
+    plan.lanes.GB = heads_per_workgroup(G);
+    plan.lanes.n_sub = G / plan.lanes.GB;
+    const int lane_qb_max = merge_mode == kMergeInKernel ? 1 : GROUP_ROWS / plan.lanes.GB;
+    int mfma_qb_max = 1;
+    if (plan.mfma) {
+        plan.matrix.GB = G % 16 == 0 ? 16 : 8;
+        plan.matrix.n_sub = G / plan.matrix.GB;
+        mfma_qb_max = kMfmaColumns / plan.matrix.GB;
+    } else if (path == kPathAuto && head_dim >= 128 && G <= kMfmaColumns / 2) {
+        plan.matrix.GB = G;             // draft groups: every head of the kv head, for each draft
+        plan.matrix.n_sub = 1;
+        mfma_qb_max = kMfmaColumns / G;
+    }
     // the matrix-core kernel always merges in the combine kernel
-    plan.fuse_limit = merge_mode == kMergeInKernel && !plan.mfma ? kFusedMaxChunks : 1;
-    plan.GB = plan.mfma ? (plan.G % 16 == 0 ? 16 : 8) : heads_per_workgroup(plan.G);
-    plan.n_sub = plan.G / plan.GB;
+    plan.fuse_limit = merge_mode == kMergeInKernel ? kFusedMaxChunks : 1;
     plan.slots.resize(n_slots);
-    int64_t part = 0;
     for (int32_t s = 0; s < n_slots; ++s) {
         SlotPlan &sp = plan.slots[s];
         const QuerySpan &qs = spans[s];
@@ -305,95 +329,160 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
         sp.kv_stride = qs.kv_stride;
         sp.ring_cap = qs.ring_cap;
         sp.ring_base = qs.ring_base;
+        sp.mfma = plan.mfma;
+    }
+    auto set_chunks = [&](SlotPlan &sp) {
         if (sp.n == 0) {
             sp.chunk = 0;
             sp.n_chunks = 1;
         } else {
-            const int64_t c = chunk_for(sp.n, head_dim, chunk, plan.mfma);
+            const int64_t c = chunk_for(sp.n, head_dim, chunk, sp.mfma);
             sp.chunk = (int32_t)(c > sp.n ? sp.n : c);
             sp.n_chunks = (int32_t)ceil_div(sp.n, sp.chunk);
         }
-        if (sp.n_chunks > 1) {
-            sp.part_row0 = part;
-            part += (int64_t)n_q * sp.n_chunks;
-            sp.fused = sp.n_chunks <= plan.fuse_limit;
-            if (sp.fused) {
-                if (plan.n_counters + (int64_t)n_kv * plan.n_sub > INT32_MAX) return "too many split slots";
-                sp.cnt_base = (int32_t)plan.n_counters;
-                plan.n_counters += (int64_t)n_kv * plan.n_sub;
+    };
+
+    // Query groups: queries of one slot with the same attended start and chunk
+    // size (draft tokens of a speculative-verify step) share one workgroup, so
+    // their K and V rows are read once: on the lane kernel up to 4 / GB of
+    // them (not with the in-kernel merge), on the matrix cores up to 16 / GB.
+    // Candidates are the non-empty queries with the same rows and start,
+    // longest first (a group's leader is its longest query).
+    std::vector<int32_t> idx;
+    for (int32_t s = 0; s < n_slots; ++s)
+        if (plan.slots[s].n > 0) idx.push_back(s);
+    auto same_rows = [&](int32_t a, int32_t b) {
+        const SlotPlan &x = plan.slots[a], &y = plan.slots[b];
+        return x.kv_row0 == y.kv_row0 && x.kv_stride == y.kv_stride && x.ring_cap == y.ring_cap &&
+               x.ring_base == y.ring_base && x.lo == y.lo;
+    };
+    std::sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
+        const SlotPlan &x = plan.slots[a], &y = plan.slots[b];
+        if (x.kv_row0 != y.kv_row0) return x.kv_row0 < y.kv_row0;
+        if (x.kv_stride != y.kv_stride) return x.kv_stride < y.kv_stride;
+        if (x.ring_cap != y.ring_cap) return x.ring_cap < y.ring_cap;
+        if (x.ring_base != y.ring_base) return x.ring_base < y.ring_base;
+        if (x.lo != y.lo) return x.lo < y.lo;
+        if (x.L != y.L) return x.L > y.L;
+        return a < b;
+    });
+    auto make_group = [&](const std::vector<int32_t> &q, size_t i, size_t j) {
+        SlotPlan &lead = plan.slots[q[i]];
+        lead.group_n = (int32_t)(j - i);
+        for (size_t k = i + 1; k < j; ++k) {
+            lead.members.push_back(q[k]);
+            plan.slots[q[k]].group_n = 0;
+            plan.slots[q[k]].leader = q[i];
+        }
+    };
+    // within a run of candidates, consecutive queries of one chunk size form groups of up to qb_max
+    auto group_run = [&](const std::vector<int32_t> &q, int qb_max, int min_size, int &qb_used,
+                         std::vector<int32_t> *rest) {
+        for (size_t i = 0; i < q.size();) {
+            size_t j = i + 1;
+            while (j < q.size() && (int)(j - i) < qb_max && plan.slots[q[j]].chunk == plan.slots[q[i]].chunk) ++j;
+            if ((int)(j - i) >= min_size && j - i > 1) {
+                make_group(q, i, j);
+                qb_used = std::max(qb_used, (int)(j - i));
+            } else if (rest) {
+                for (size_t k = i; k < j; ++k) rest->push_back(q[k]);
             }
+            i = j;
+        }
+    };
+    std::vector<int32_t> lane_q;   // queries left to the lane kernel, in candidate order
+    for (size_t i = 0; i < idx.size();) {
+        size_t j = i + 1;
+        while (j < idx.size() && same_rows(idx[i], idx[j])) ++j;
+        std::vector<int32_t> run(idx.begin() + i, idx.begin() + j);
+        if (plan.mfma) {
+            for (int32_t q : run) set_chunks(plan.slots[q]);
+            if (mfma_qb_max > 1) group_run(run, mfma_qb_max, 2, plan.matrix.QB, nullptr);
+        } else if (mfma_qb_max > 1 && (int64_t)run.size() * G >= kMfmaGroupMinCols) {
+            // draft groups for the matrix cores: chunks by their rule; what does not fill
+            // 8 columns goes back to the lane kernel
+            for (int32_t q : run) {
+                plan.slots[q].mfma = true;
+                set_chunks(plan.slots[q]);
+            }
+            std::vector<int32_t> back;
+            const int min_q = (kMfmaGroupMinCols + G - 1) / G;
+            group_run(run, mfma_qb_max, min_q, plan.matrix.QB, &back);
+            for (int32_t q : back) {
+                plan.slots[q].mfma = false;
+                lane_q.push_back(q);
+            }
+        } else {
+            lane_q.insert(lane_q.end(), run.begin(), run.end());
+        }
+        i = j;
+    }
+    for (int32_t s = 0; s < n_slots; ++s)
+        if (plan.slots[s].n == 0) set_chunks(plan.slots[s]);
+    for (int32_t q : lane_q) set_chunks(plan.slots[q]);
+    if (lane_qb_max > 1) {
+        // lane groups need equal chunks too: runs of same rows, split where the chunk changes
+        for (size_t i = 0; i < lane_q.size();) {
+            size_t j = i + 1;
+            while (j < lane_q.size() && same_rows(lane_q[i], lane_q[j])) ++j;
+            std::vector<int32_t> run(lane_q.begin() + i, lane_q.begin() + j);
+            std::stable_sort(run.begin(), run.end(), [&](int32_t a, int32_t b) {
+                return plan.slots[a].chunk < plan.slots[b].chunk;
+            });
+            int qb = 1;
+            group_run(run, lane_qb_max, 2, qb, nullptr);
+            if (qb > 1) plan.lanes.QB = lane_qb_max;
+            i = j;
+        }
+    }
+
+    // partial rows and, for the lane kernel's in-kernel merge, arrival counters
+    int64_t part = 0;
+    for (int32_t s = 0; s < n_slots; ++s) {
+        SlotPlan &sp = plan.slots[s];
+        if (sp.n_chunks <= 1) continue;
+        sp.part_row0 = part;
+        part += (int64_t)n_q * sp.n_chunks;
+        sp.fused = !sp.mfma && sp.n_chunks <= plan.fuse_limit;
+        if (sp.fused) {
+            if (plan.n_counters + (int64_t)n_kv * plan.lanes.n_sub > INT32_MAX) return "too many split slots";
+            sp.cnt_base = (int32_t)plan.n_counters;
+            plan.n_counters += (int64_t)n_kv * plan.lanes.n_sub;
         }
     }
     plan.part_rows = part;
     plan.workspace_bytes = counter_region_bytes(plan.n_counters) +
                            part * (int64_t)(head_dim + 2) * (int64_t)sizeof(float);
 
-    // Query groups: queries of one slot with the same attended start and chunk
-    // size (draft tokens of a speculative-verify step) share one workgroup, up
-    // to 4 / GB of them, so their K and V rows are read once.  Not with the
-    // in-kernel merge.
-    const int qb_max = (merge_mode == kMergeInKernel || plan.mfma) ? 1 : (GROUP_ROWS / plan.GB);
-    if (qb_max > 1) {
-        std::vector<int32_t> idx;
-        for (int32_t s = 0; s < n_slots; ++s)
-            if (plan.slots[s].n > 0) idx.push_back(s);
-        auto key_less = [&](int32_t a, int32_t b) {
-            const SlotPlan &x = plan.slots[a], &y = plan.slots[b];
-            if (x.kv_row0 != y.kv_row0) return x.kv_row0 < y.kv_row0;
-            if (x.kv_stride != y.kv_stride) return x.kv_stride < y.kv_stride;
-            if (x.ring_cap != y.ring_cap) return x.ring_cap < y.ring_cap;
-            if (x.ring_base != y.ring_base) return x.ring_base < y.ring_base;
-            if (x.lo != y.lo) return x.lo < y.lo;
-            if (x.chunk != y.chunk) return x.chunk < y.chunk;
-            if (x.L != y.L) return x.L > y.L;   // longest first: the leader
-            return a < b;
-        };
-        std::sort(idx.begin(), idx.end(), key_less);
-        auto same_key = [&](int32_t a, int32_t b) {
-            const SlotPlan &x = plan.slots[a], &y = plan.slots[b];
-            return x.kv_row0 == y.kv_row0 && x.kv_stride == y.kv_stride && x.ring_cap == y.ring_cap &&
-                   x.ring_base == y.ring_base && x.lo == y.lo && x.chunk == y.chunk;
-        };
-        for (size_t i = 0; i < idx.size();) {
-            size_t j = i + 1;
-            while (j < idx.size() && (int)(j - i) < qb_max && same_key(idx[i], idx[j])) ++j;
-            if (j - i > 1) {
-                SlotPlan &lead = plan.slots[idx[i]];
-                lead.group_n = (int32_t)(j - i);
-                for (size_t k = i + 1; k < j; ++k) {
-                    lead.members.push_back(idx[k]);
-                    plan.slots[idx[k]].group_n = 0;
-                    plan.slots[idx[k]].leader = idx[i];
-                }
-                plan.QB = qb_max;
-            }
-            i = j;
-        }
-    }
-
     // Work-list order: longest chunks first (ties by slot index), so the
     // longest workgroups start first and short ones fill the tail.  The order
     // decides only which workgroup runs when, never a slot's arithmetic.
+    // Matrix-core queries come first (their launches run longer chunks).
     std::vector<int32_t> order;
     for (int32_t s = 0; s < n_slots; ++s)
         if (plan.slots[s].group_n > 0) order.push_back(s);   // leaders and ungrouped queries
     std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+        if (plan.slots[a].mfma != plan.slots[b].mfma) return plan.slots[a].mfma;
         return plan.slots[a].chunk > plan.slots[b].chunk;
     });
 
-    // launch groups: at most kMaxSlotsPerLaunch table entries and kMaxItemsPerLaunch workgroups;
-    // a query group's entries (leader, then followers) stay in one launch
+    // launch groups: one kernel each, at most kMaxSlotsPerLaunch table entries and
+    // kMaxItemsPerLaunch workgroups; a query group's entries (leader, then followers)
+    // stay in one launch
     LaunchGroup g;
     for (int32_t s : order) {
         const SlotPlan &sp = plan.slots[s];
-        const int64_t items = (int64_t)n_kv * plan.n_sub * sp.n_chunks;
+        const int n_sub = sp.mfma ? plan.matrix.n_sub : plan.lanes.n_sub;
+        const int64_t items = (int64_t)n_kv * n_sub * sp.n_chunks;
         if (items > kMaxItemsPerLaunch) return "too many workgroups for one slot (n_kv_heads too large)";
         const int entries = sp.group_n;
-        const bool full = (int)g.slots.size() + entries > kMaxSlotsPerLaunch || g.items + items > kMaxItemsPerLaunch;
+        const bool full = (int)g.slots.size() + entries > kMaxSlotsPerLaunch || g.items + items > kMaxItemsPerLaunch ||
+                          (!g.slots.empty() && g.mfma != sp.mfma);
         if (full) {
             plan.groups.push_back(g);
             g = LaunchGroup();
         }
+        g.mfma = sp.mfma;
         g.slots.push_back(s);
         for (int32_t f : sp.members) g.slots.push_back(f);
         g.items += items;

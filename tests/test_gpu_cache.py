@@ -118,22 +118,71 @@ def test_sliding_window_ring_at_serving_shape():
     _report("ring 8 x 1024", assert_parity(got, ref, "ring serving shape"))
 
 
+def _sub_call(ci, dev, rows, W=0, chunk=0):
+    """The queries `rows` of a cache call on their own."""
+    one = CacheInputs(ci.q[rows].clone(), ci.k, ci.v, ci.v_scales, tuple(ci.slot_ids[i] for i in rows),
+                      tuple(ci.positions[i] for i in rows), ci.n_cache_slots, ci.capacity, ci.ring, ci.n_q_heads,
+                      ci.n_kv_heads, ci.head_dim, ci.scale)
+    return run_gpu_cache(one, W, chunk=chunk, dev_tensors=(dev[0][rows].contiguous(), dev[1], dev[2], dev[3]))
+
+
 @pytest.mark.parametrize("nq,nkv,i8", [(16, 8, False), (8, 8, True), (4, 4, False), (16, 2, True)])
 def test_draft_queries_share_a_workgroup_and_match_solo(nq, nkv, i8):
-    # 4 consecutive draft positions per slot (G = 2 groups pairs, G = 1 groups all four,
-    # G = 8 does not group); results equal the per-query calls bitwise and the oracle
+    # 4 consecutive draft positions per slot.  G = 1 groups all four on the lanes; G = 2 makes
+    # 8 (draft, head) columns, a matrix-core workgroup; G = 8 is on the matrix cores anyway and
+    # groups pairs.  Every query equals the oracle; each slot's rows equal a call with that
+    # slot's queries alone bitwise (a query's kernel depends only on its own slot's queries),
+    # and a single query's call too where grouping does not change its kernel.
     sid = (0, 0, 0, 0, 1, 1, 1, 1, 2)
     pos = (3000, 3001, 3002, 3003, 700, 701, 702, 703, 50)
+    G = nq // nkv
     ci = make_cache_inputs(3, 4096, 0, sid, pos, nq, nkv, 256, i8, seed_base=9600 + nq + nkv)
     dev = to_device(ci)
     got = run_gpu_cache(ci, 0, dev_tensors=dev)
     ref = run_oracle_cache(ci, 0)
-    _report(f"drafts G={nq // nkv}", assert_parity(got.cpu().numpy(), ref, "drafts"))
+    _report(f"drafts G={G}", assert_parity(got.cpu().numpy(), ref, "drafts"))
+    for rows in ([0, 1, 2, 3], [4, 5, 6, 7], [8]):
+        per_slot = _sub_call(ci, dev, rows)
+        assert torch.equal(got[rows], per_slot), rows
+    kernel_changes = G < 8 and 4 * G >= 8      # the four drafts fill 8 matrix-core columns
     for i in range(len(sid)):
-        one = CacheInputs(ci.q[i:i + 1].clone(), ci.k, ci.v, ci.v_scales, (sid[i],), (pos[i],), ci.n_cache_slots,
-                          ci.capacity, ci.ring, ci.n_q_heads, ci.n_kv_heads, ci.head_dim, ci.scale)
-        solo = run_gpu_cache(one, 0, dev_tensors=(dev[0][i:i + 1].contiguous(), dev[1], dev[2], dev[3]))
-        assert torch.equal(got[i:i + 1], solo), i
+        solo = _sub_call(ci, dev, [i])
+        if kernel_changes and i < 8:
+            assert_parity(solo.cpu().numpy(), ref[i:i + 1], f"solo {i}")
+        else:
+            assert torch.equal(got[i:i + 1], solo), i
+
+
+DRAFT_CASES = [
+    # n_q, n_kv, D, int8 V, ring, drafts per slot, forced chunk
+    (16, 8, 256, False, 0, 4, 0),      # 2 heads x 4 drafts = 8 columns
+    (16, 8, 128, True, 1, 8, 0),       # 2 x 8 = 16 columns, ring storage
+    (16, 8, 256, False, 0, 5, 250),    # 10 columns; members end in different chunks
+    (8, 8, 128, False, 0, 8, 0),       # 1 head x 8 drafts
+    (16, 4, 512, False, 0, 2, 0),      # 4 heads x 2 drafts
+    (16, 4, 256, True, 1, 4, 7),       # 4 x 4 = 16 columns, tiny chunks, ring
+    (16, 2, 256, False, 0, 2, 0),      # 8 heads x 2 drafts (8 heads per kv head: pairs)
+    (16, 8, 256, False, 0, 16, 0),     # 16 drafts: two groups of 8
+]
+
+
+@pytest.mark.parametrize("case", DRAFT_CASES, ids=[f"d{i}" for i in range(len(DRAFT_CASES))])
+def test_matrix_core_draft_groups(case):
+    """Draft queries of a speculative-verify step as matrix-core columns (drafts x heads): each
+    K and V row is read once for the whole group, each draft masked at its own position."""
+    nq, nkv, d, i8, ring, nd, chunk = case
+    cap = 2048
+    base = (1999, 3100) if ring else (1999, 1500)
+    sid = tuple(s for s in range(2) for _ in range(nd)) + (2,)
+    pos = tuple(base[s] + t for s in range(2) for t in range(nd)) + (40,)
+    ci = make_cache_inputs(3, cap, ring, sid, pos, nq, nkv, d, i8, seed_base=9700 + DRAFT_CASES.index(case))
+    dev = to_device(ci)
+    got = run_gpu_cache(ci, 0, chunk=chunk, dev_tensors=dev)
+    ref = run_oracle_cache(ci, 0)
+    _report(f"draft group {case}", assert_parity(got.cpu().numpy(), ref, f"{case}"))
+    for s in range(3):
+        rows = [i for i in range(len(sid)) if sid[i] == s]
+        assert torch.equal(got[rows], _sub_call(ci, dev, rows, chunk=chunk)), f"slot {s}"
 
 
 def test_draft_queries_with_forced_chunks_and_windows():
