@@ -197,14 +197,16 @@ def test_append_rejects_collisions_and_bad_bits():
 # ---------------------------------------------------------------- cache attention over codebook V
 
 def _exact_codebook_cache(r, n_slots, n_kv, cap, d):
-    """Codes, norms and a table whose decoded values are exact fp16 numbers: levels k/8 and
-    norms sqrt(B) * 2^-e, so a V element is (k/8) * 2^-e (sqrt(B) exact: B = 64 or 256)."""
+    """Codes, norms and a 4-bit table whose decoded values are exact fp16 numbers: levels k/8 and
+    norms sqrt(B) * 2^-e, so a V element is (k/8) * 2^-e (sqrt(B) exact: B = 64 or 256).  The
+    stored bytes carry random high bits, which a 4-bit read must ignore."""
     B = min(d, 256)
     cb = (np.arange(16, dtype=np.float32) - 7.5) / 8
-    codes = r.integers(0, 16, n_slots * n_kv * cap * d).astype(np.uint8)
+    low = r.integers(0, 16, n_slots * n_kv * cap * d)
+    codes = (low + 16 * r.integers(0, 16, low.size)).astype(np.uint8)
     e = r.integers(0, 3, n_slots * n_kv * cap * d // B)
     norms = (math.sqrt(B) * 2.0 ** -e).astype(np.float32)
-    vals = (cb.astype(np.float64)[codes].reshape(-1, B) * (norms.astype(np.float64) / math.sqrt(B))[:, None])
+    vals = (cb.astype(np.float64)[low].reshape(-1, B) * (norms.astype(np.float64) / math.sqrt(B))[:, None])
     v16 = vals.reshape(-1).astype(np.float16)
     assert np.array_equal(v16.astype(np.float64), vals.reshape(-1))
     return cb, codes, norms, v16
