@@ -195,3 +195,30 @@ def test_draft_queries_with_forced_chunks_and_windows():
         got = run_gpu_cache(ci, W, chunk=chunk).cpu().numpy()
         ref = run_oracle_cache(ci, W)
         _report(f"drafts W={W} chunk={chunk}", assert_parity(got, ref, f"W={W} chunk={chunk}"))
+
+
+@pytest.mark.parametrize("merge_mode", [0, 2])
+def test_mixed_kernels_across_launch_groups(merge_mode):
+    """20 slots: even slots verify 4 drafts (a matrix-core group at 2 heads per kv head), odd
+    slots decode one token (lane kernel); 50 table entries span two launch groups of each
+    kernel's own.  Every row matches the oracle, and each slot's rows equal a call with that
+    slot's queries alone, bitwise, with the combine kernel or the in-kernel merge."""
+    sid, pos = [], []
+    for s in range(20):
+        n = 4 if s % 2 == 0 else 1
+        base = 300 + 37 * s
+        sid += [s] * n
+        pos += [base + t for t in range(n)]
+    ci = make_cache_inputs(20, 1024, 0, tuple(sid), tuple(pos), 16, 8, 128, True, seed_base=9800 + merge_mode)
+    dev = to_device(ci)
+    got = run_gpu_cache(ci, 0, dev_tensors=dev, merge_mode=merge_mode)
+    ref = run_oracle_cache(ci, 0)
+    _report(f"mixed kernels merge_mode={merge_mode}", assert_parity(got.cpu().numpy(), ref, "mixed"))
+    for s in (0, 1, 18, 19):
+        rows = [i for i in range(len(sid)) if sid[i] == s]
+        one = CacheInputs(ci.q[rows].clone(), ci.k, ci.v, ci.v_scales, tuple(sid[i] for i in rows),
+                          tuple(pos[i] for i in rows), ci.n_cache_slots, ci.capacity, ci.ring, ci.n_q_heads,
+                          ci.n_kv_heads, ci.head_dim, ci.scale)
+        alone = run_gpu_cache(one, 0, dev_tensors=(dev[0][rows].contiguous(), dev[1], dev[2], dev[3]),
+                              merge_mode=merge_mode)
+        assert torch.equal(got[rows], alone), f"slot {s}"
