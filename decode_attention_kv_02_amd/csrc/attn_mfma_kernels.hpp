@@ -1,5 +1,7 @@
-// attn_mfma_kernels.hpp -- gfx950 partial kernel for GQA groups of 8 or 16
-// query heads per workgroup, on the matrix cores.
+// attn_mfma_kernels.hpp -- gfx950 partial kernel for up to 16 (query, head)
+// columns per workgroup, on the matrix cores: 8 or 16 query heads of one kv
+// head, or every head of the kv head for each of a slot's draft queries
+// (a speculative-verify step).
 //
 // Same operation and partial format as attn_partial_kernel (one chunk of one
 // (slot, kv head): out = O / S, or O and (M, S) for the log-sum-exp merge;
