@@ -176,6 +176,14 @@ GQA_SHAPES = (
 )
 
 
+def partial_kernel_name(G: int, head_dim: int, drafts: int = 1) -> str:
+    """The partial kernel the library's automatic choice (planner.hpp) runs: the matrix cores at a
+    multiple of 8 query heads per kv head, or for a slot's drafts x heads filling 8 columns."""
+    if head_dim >= 128 and (G % 8 == 0 or drafts * G >= 8):
+        return "attn_partial_mfma_kernel"
+    return "attn_partial_kernel"
+
+
 def gqa_sweep(only: str = "") -> int:
     import numpy as np
     import torch
@@ -241,8 +249,7 @@ def gqa_sweep(only: str = "") -> int:
             res[key + "_us"] = round(us, 2)
             res[key + "_hbm_frac"] = round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
             del graph
-        # the library's automatic choice (planner.hpp, mfma_preferred): matrix cores wherever they apply
-        res["automatic"] = "matrix" if ((nq // nkv) % 8 == 0 and d >= 128) else "lanes"
+        res["automatic"] = "matrix" if partial_kernel_name(nq // nkv, d) == "attn_partial_mfma_kernel" else "lanes"
         print(json.dumps(res), flush=True)
         del q, k, out
         torch.cuda.empty_cache()
@@ -281,9 +288,10 @@ def main(argv=None) -> int:
 
     by_name = {w.name: w for w in WORKLOADS}
     cb_by_name = {w.name: w for w in CODEBOOK_WORKLOADS}
-    if args.workload not in by_name and args.workload not in cb_by_name:
-        print(f"unknown workload {args.workload}; choose from {sorted(by_name) + sorted(cb_by_name)}",
-              file=sys.stderr)
+    cache_by_name = {w.name: w for w in CACHE_WORKLOADS}
+    if args.workload not in by_name and args.workload not in cb_by_name and args.workload not in cache_by_name:
+        print(f"unknown workload {args.workload}; choose from "
+              f"{sorted(by_name) + sorted(cb_by_name) + sorted(cache_by_name)}", file=sys.stderr)
         return 2
 
     def upload(inp):
@@ -315,6 +323,24 @@ def main(argv=None) -> int:
 
         def step(ev0=None, ev1=None):
             call(inp, tens, out, window, ev0, ev1)
+    elif args.workload in cache_by_name:
+        cfg = cache_by_name[args.workload]
+        window = cfg.window
+        print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+        inp = cache_workload_inputs(cfg)
+        tens = upload(inp)
+        out = torch.empty((inp.n_queries, inp.n_q_heads, inp.head_dim), dtype=torch.float32, device=dev)
+        nbytes = cache_kv_bytes(cfg)[0]
+        v_format = "int8 codes, fp16 scale per 32 dims" if inp.v_scales is not None else "fp16"
+        c_sid = np.asarray(inp.slot_ids, dtype=np.int32)
+        c_pos = np.asarray(inp.positions, dtype=np.int32)
+
+        def step(ev0=None, ev1=None):
+            binding.attn_decode_cache(*tens, c_sid, c_pos, inp.n_queries, inp.n_cache_slots, inp.capacity,
+                                      inp.ring, window, out, inp.n_q_heads, inp.n_kv_heads, inp.head_dim,
+                                      inp.scale, stream=stream, chunk=args.chunk,
+                                      ev_partial_begin=ev0.cuda_event if ev0 is not None else None,
+                                      ev_partial_end=ev1.cuda_event if ev1 is not None else None)
     else:
         cfg = cb_by_name[args.workload]
         window = cfg.window
@@ -386,6 +412,13 @@ def main(argv=None) -> int:
     assert torch.isfinite(out).all().item(), "non-finite output"
 
     traffic = read_traffic(cfg.name, window)
+    if args.workload in cache_by_name:
+        shape = {"n_queries": inp.n_queries, "slot_ids": list(inp.slot_ids), "positions": list(inp.positions),
+                 "n_cache_slots": inp.n_cache_slots, "capacity": inp.capacity, "ring": inp.ring}
+        drafts = max(inp.slot_ids.count(s_) for s_ in set(inp.slot_ids))
+    else:
+        shape = {"n_slots": inp.n_slots, "seq_lens": list(inp.seq_lens)}
+        drafts = 1
     result = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -401,8 +434,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {
             "workload": cfg.name,
-            "n_slots": inp.n_slots,
-            "seq_lens": list(inp.seq_lens),
+            **shape,
             "n_q_heads": inp.n_q_heads,
             "n_kv_heads": inp.n_kv_heads,
             "head_dim": inp.head_dim,
@@ -416,7 +448,7 @@ def main(argv=None) -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_partial_kernel",
+            "kernel": partial_kernel_name(inp.n_q_heads // inp.n_kv_heads, inp.head_dim, drafts),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
