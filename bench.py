@@ -56,6 +56,7 @@ import time
 HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_kv_02_amd", "csrc", "attn_decode_kernels.hpp")
+MFMA_KERNEL_SRC = os.path.join(ROOT, "decode_attention_kv_02_amd", "csrc", "attn_mfma_kernels.hpp")
 TRAFFIC_SUMMARY_DIR = os.path.join(ROOT, "profiles")
 METRIC = "decode-attention effective KV GB/s (% of HBM peak) + µs/call per config"
 HEADLINE = "hybrid_int8v_8x32768"
@@ -101,13 +102,15 @@ def cache_kv_bytes(cfg) -> tuple:
     return read, unique
 
 
-def kernel_source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as fh:
+def kernel_source_digest(kernel: str = "attn_partial_kernel") -> str:
+    """First 16 hex digits of the sha256 of the partial kernel's source header."""
+    with open(MFMA_KERNEL_SRC if kernel == "attn_partial_mfma_kernel" else KERNEL_SRC, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def read_traffic(workload: str, window: int):
-    """HBM bytes per partial-kernel launch from the committed PMC summary, or None."""
+def read_traffic(workload: str, window: int, kernel: str = "attn_partial_kernel"):
+    """HBM bytes per partial-kernel launch from the committed PMC summary, or None when there is
+    none or it was taken from another version of the kernel's source."""
     path = os.path.join(TRAFFIC_SUMMARY_DIR, f"traffic_{workload}_w{window}.txt")
     if not os.path.exists(path):
         return None
@@ -116,7 +119,7 @@ def read_traffic(workload: str, window: int):
         m = re.match(r"^\s*([a-z0-9_]+)\s*:\s*(\S+)", line)
         if m:
             vals[m.group(1)] = m.group(2)
-    if vals.get("kernel_source_sha256_16") != kernel_source_digest():
+    if vals.get("kernel_source_sha256_16") != kernel_source_digest(kernel):
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))
@@ -411,7 +414,6 @@ def main(argv=None) -> int:
     achieved = nbytes / partial_avg_s / 1e9
     assert torch.isfinite(out).all().item(), "non-finite output"
 
-    traffic = read_traffic(cfg.name, window)
     if args.workload in cache_by_name:
         shape = {"n_queries": inp.n_queries, "slot_ids": list(inp.slot_ids), "positions": list(inp.positions),
                  "n_cache_slots": inp.n_cache_slots, "capacity": inp.capacity, "ring": inp.ring}
@@ -419,6 +421,8 @@ def main(argv=None) -> int:
     else:
         shape = {"n_slots": inp.n_slots, "seq_lens": list(inp.seq_lens)}
         drafts = 1
+    kernel = partial_kernel_name(inp.n_q_heads // inp.n_kv_heads, inp.head_dim, drafts)
+    traffic = read_traffic(cfg.name, window, kernel)
     result = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -448,7 +452,7 @@ def main(argv=None) -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": partial_kernel_name(inp.n_q_heads // inp.n_kv_heads, inp.head_dim, drafts),
+            "kernel": kernel,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
