@@ -262,9 +262,8 @@ def gqa_sweep(only: str = "") -> int:
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by slot, KV head or sequence chunk across GPUs by design, "
-              "but no multi-GPU run exists)", file=sys.stderr)
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the path would shard "
+              "by slot, KV head or sequence chunk across GPUs, but no multi-GPU run exists)", file=sys.stderr)
         return 2
 
     if args.calibrate_copy:

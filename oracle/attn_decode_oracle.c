@@ -32,8 +32,8 @@
  * V dequantisation (block-int8 regime): a V element is int8 code times the
  * fp16 scale of its block of 32 consecutive dims along head_dim.  The oracle
  * reads the stored codes and scales and never re-quantises.  The block size
- * and scale type are this build's V format (the pages' own hybrid V is a
- * codebook format; see the reading recorded in the design notes).
+ * and scale type are the library's int8 V format (the pages' own hybrid V is
+ * the codebook format, handled by the codebook functions further below).
  *
  * Cache layout (packed ragged slots): slot s's K occupies n_kv * L_s * D
  * elements starting at element offset sum_{t<s} n_kv * L_t * D, laid out
@@ -437,7 +437,7 @@ int oracle_fwht_undo_f64(const double *x, const float *signs, double *y, int64_t
 /* ------------------------------------------------------------------------
  * KV append: the step before the path.  Each new token's K is stored as fp16
  * and its V as fp16 or as symmetric int8 codes in blocks of 32 dims with one
- * fp16 scale (this build's V format), into the cache row of its (slot,
+ * fp16 scale (the library's int8 V format), into the cache row of its (slot,
  * position): row p for linear storage, row p mod capacity for a ring
  * (mlx-native flash_attn_vec_hybrid.metal, batched kernels: physical row of a
  * position; hf2q gemma4 batched_body.rs, the attention phase's KV encode:
