@@ -156,15 +156,16 @@ def test_large_and_rising_logits(d, nq, nkv, i8):
         _report(f"rising logits D={d} path {path}", assert_parity(got, ref, f"path {path}"))
 
 
-@pytest.mark.parametrize("d,nq,nkv,bits", [(256, 16, 2, 5), (128, 64, 4, 6), (512, 32, 2, 6)])
-def test_matrix_core_codebook_bits(d, nq, nkv, bits):
+@pytest.mark.parametrize("d,nq,nkv,bits,W", [(256, 16, 2, 5, 0), (128, 64, 4, 6, 0), (512, 32, 2, 6, 0),
+                                              (256, 16, 2, 8, 700), (512, 16, 2, 5, 1500)])
+def test_matrix_core_codebook_bits(d, nq, nkv, bits, W):
     seq = (2100, 700, 0)
     ci = make_codebook_inputs(seq, nq, nkv, d, bits, 7900 + d + bits)
     dv = torch.device("cuda:0")
     q, k, vc, vn, cb = (t.to(dv) for t in (ci.q, ci.k, ci.v_codes, ci.v_norms, ci.codebook))
     ref = oracle_attn_decode_cb(ci.q.numpy(), ci.k.numpy(), ci.v_codes.numpy(), ci.v_norms.numpy(),
-                                ci.codebook.numpy(), bits, seq, 0, nq, nkv, d, ci.scale)
+                                ci.codebook.numpy(), bits, seq, W, nq, nkv, d, ci.scale)
     out = torch.full((len(seq), nq, d), float("nan"), dtype=torch.float32, device=dv)
-    binding.attn_decode_cb(q, k, vc, vn, cb, bits, seq, 0, out, len(seq), nq, nkv, d, ci.scale, path=2)
+    binding.attn_decode_cb(q, k, vc, vn, cb, bits, seq, W, out, len(seq), nq, nkv, d, ci.scale, path=2)
     torch.cuda.synchronize()
-    _report(f"codebook {bits}-bit D={d} G={nq // nkv}", assert_parity(out.cpu().numpy(), ref, "codebook"))
+    _report(f"codebook {bits}-bit D={d} G={nq // nkv} W={W}", assert_parity(out.cpu().numpy(), ref, "codebook"))
