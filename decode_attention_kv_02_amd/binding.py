@@ -138,6 +138,13 @@ class _HostInts:
     """A host int32 array for the C ABI; numpy int32 arrays are passed without a copy."""
 
     def __init__(self, values):
+        if (isinstance(values, np.ndarray) and values.dtype == np.int32 and values.ndim == 1 and values.size
+                and values.flags.c_contiguous):
+            # the common case (a decode loop passing its own int32 array): no conversion
+            self.arr = values
+            self.n = int(values.size)
+            self._as_parameter_ = ctypes.c_void_p(values.__array_interface__["data"][0])
+            return
         if isinstance(values, torch.Tensor):
             values = values.detach().cpu().numpy()
         arr = np.ascontiguousarray(np.asarray(values, dtype=np.int32).reshape(-1))
@@ -154,13 +161,21 @@ def _seq_array(seq_lens):
     return h, h.n
 
 
+def _cuda_index(t, name: str) -> int:
+    """Device index of a CUDA tensor; ValueError for anything else."""
+    d = t.get_device() if isinstance(t, torch.Tensor) else -1
+    if d < 0:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    return d
+
+
 def _dev_ptr(t, name: str, dtype, numel: int, device_index: int):
     """Device pointer of a tensor after the marshalling checks (None -> NULL)."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if t.device.type != "cuda" or t.device.index != device_index:
+    if t.get_device() != device_index:        # -1 for host tensors
         raise ValueError(f"{name} must be on cuda:{device_index}, got {t.device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -181,9 +196,7 @@ def _marshal(q, k_cache, v_cache, v_scales, seq_lens, out, n_slots, n_q_heads, n
     if n and int(seq_arr.arr[:n].min()) < 0:
         # the library rejects this too; checked here because sizes below depend on it
         raise AttnDecodeError(ATTN_DECODE_EINVAL, "seq_lens must be >= 0")
-    dev = out.device.index if isinstance(out, torch.Tensor) and out.device.type == "cuda" else None
-    if dev is None:
-        raise ValueError("out must be a CUDA tensor")
+    dev = _cuda_index(out, "out")
     kv = int(seq_arr.arr[:n].astype(np.int64).sum()) * n_kv_heads * head_dim
     int8 = v_scales is not None
     ptrs = (
@@ -196,8 +209,15 @@ def _marshal(q, k_cache, v_cache, v_scales, seq_lens, out, n_slots, n_q_heads, n
     return seq_arr, n_slots, dev, ptrs
 
 
+# torch's current stream of a device as a raw handle, without building a Stream object (about 2 us
+# per call less); the public route where this accessor does not exist
+_current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(stream, dev: int):
     if stream is None:
+        if _current_raw_stream is not None:
+            return _current_raw_stream(dev)
         return torch.cuda.current_stream(dev).cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
@@ -265,9 +285,7 @@ def attn_decode_cb(q, k_cache, v_codes, v_norms, codebook, codebook_bits: int, s
 def attn_fwht_undo(x, signs, y, stream=None) -> None:
     """y = signs * (H x) / sqrt(D) per row of x (fp32 [..., D]); y may be x."""
     lib = load_library()
-    if not isinstance(y, torch.Tensor) or y.device.type != "cuda":
-        raise ValueError("y must be a CUDA tensor")
-    dev = y.device.index
+    dev = _cuda_index(y, "y")
     d = int(x.shape[-1])
     n_rows = x.numel() // d if d else 0
     px = _dev_ptr(x, "x", torch.float32, n_rows * d, dev)
@@ -291,9 +309,7 @@ def attn_decode_cache(q, k_cache, v_cache, v_scales, slot_ids, positions, n_quer
         n_queries = n
     if n != n_queries or n2 != n_queries:
         raise ValueError("slot_ids / positions do not match n_queries")
-    if not isinstance(out, torch.Tensor) or out.device.type != "cuda":
-        raise ValueError("out must be a CUDA tensor")
-    dev = out.device.index
+    dev = _cuda_index(out, "out")
     kv = int(n_cache_slots) * int(n_kv_heads) * int(capacity) * int(head_dim)
     int8 = v_scales is not None
     pq = _dev_ptr(q, "q", torch.float16, n_queries * n_q_heads * head_dim, dev)
@@ -321,9 +337,7 @@ def attn_kv_append(k_new, v_new, k_cache, v_cache, v_scales, slot_ids, positions
         n_rows = n
     if n != n_rows or n2 != n_rows:
         raise ValueError("slot_ids / positions do not match n_rows")
-    if not isinstance(k_cache, torch.Tensor) or k_cache.device.type != "cuda":
-        raise ValueError("k_cache must be a CUDA tensor")
-    dev = k_cache.device.index
+    dev = _cuda_index(k_cache, "k_cache")
     kv = int(n_cache_slots) * int(n_kv_heads) * int(capacity) * int(head_dim)
     int8 = v_scales is not None
     pkn = _dev_ptr(k_new, "k_new", torch.float32, n_rows * n_kv_heads * head_dim, dev)
@@ -362,9 +376,7 @@ def attn_decode_cache_cb(q, k_cache, v_codes, v_norms, codebook, codebook_bits: 
     like the cache); out is in the rotated basis (see attn_fwht_undo)."""
     lib = load_library()
     sid, pos, n_queries = _cache_rows(slot_ids, positions, n_queries)
-    if not isinstance(out, torch.Tensor) or out.device.type != "cuda":
-        raise ValueError("out must be a CUDA tensor")
-    dev = out.device.index
+    dev = _cuda_index(out, "out")
     kv = int(n_cache_slots) * int(n_kv_heads) * int(capacity) * int(head_dim)
     pq = _dev_ptr(q, "q", torch.float16, n_queries * n_q_heads * head_dim, dev)
     pk = _dev_ptr(k_cache, "k_cache", torch.float16, kv, dev)
@@ -387,9 +399,7 @@ def attn_kv_append_cb(k_new, v_new, k_cache, v_codes, v_norms, signs, codebook, 
     nearest level of ``codebook``, fp32 norms per min(D, 256) dims) into the cache."""
     lib = load_library()
     sid, pos, n_rows = _cache_rows(slot_ids, positions, n_rows)
-    if not isinstance(k_cache, torch.Tensor) or k_cache.device.type != "cuda":
-        raise ValueError("k_cache must be a CUDA tensor")
-    dev = k_cache.device.index
+    dev = _cuda_index(k_cache, "k_cache")
     kv = int(n_cache_slots) * int(n_kv_heads) * int(capacity) * int(head_dim)
     pkn = _dev_ptr(k_new, "k_new", torch.float32, n_rows * n_kv_heads * head_dim, dev)
     pvn = _dev_ptr(v_new, "v_new", torch.float32, n_rows * n_kv_heads * head_dim, dev)

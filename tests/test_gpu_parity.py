@@ -209,3 +209,12 @@ def test_binding_rejects_wrong_dtype_on_gpu():
     out = torch.empty((1, 2, 64), dtype=torch.float16, device=q.device)
     with pytest.raises(TypeError):
         binding.attn_decode(q, k, v, None, (10,), 0, out, 1, 2, 1, 64, inp.scale)
+
+
+def test_default_stream_is_torchs_current_stream():
+    """The binding's default stream handle is torch's current stream, also inside a stream context."""
+    assert binding._stream_handle(None, 0) == torch.cuda.current_stream(0).cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert binding._stream_handle(None, 0) == s.cuda_stream == torch.cuda.current_stream(0).cuda_stream
+    assert binding._stream_handle(None, 0) == torch.cuda.current_stream(0).cuda_stream
