@@ -143,6 +143,8 @@ def parse_args(argv=None):
                     help="only time the lane and the matrix-core partial kernels on groups of 8 and 16 "
                          "query heads per kv head (graph-replayed calls, one JSON line per shape)")
     ap.add_argument("--only", default="", help="with --gqa-sweep: comma-separated shape names to run")
+    ap.add_argument("--torch-reductions", action="store_true",
+                    help="time torch's own sum / amax reading 1-4 GiB (a reference streaming read) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), to scale "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -159,6 +161,43 @@ def calibrate_copy(nbytes: int) -> int:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "copies": 5}), flush=True)
+    return 0
+
+
+def torch_reductions() -> int:
+    """GB/s of torch's own reductions reading 1, 2 and 4 GiB once (sum and amax over fp16 and fp32),
+    10 calls captured into a graph and replayed: a streaming read written by someone else, for
+    comparison with the partial kernel's rate."""
+    import torch
+    dev = torch.device("cuda:0")
+    for gib in (1, 2, 4):
+        for dtype in (torch.float16, torch.float32):
+            x = torch.ones((gib << 30) // torch.tensor([], dtype=dtype).element_size(), dtype=dtype, device=dev)
+            for name, fn in (("sum", lambda: x.sum()), ("amax", lambda: x.amax())):
+                side = torch.cuda.Stream(device=dev)
+                side.wait_stream(torch.cuda.current_stream(dev))
+                with torch.cuda.stream(side):
+                    fn()
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=side):
+                    for _ in range(10):
+                        fn()
+                torch.cuda.synchronize()
+                samples = []
+                for _ in range(5):
+                    t0 = time.perf_counter()
+                    graph.replay()
+                    torch.cuda.synchronize()
+                    samples.append((time.perf_counter() - t0) / 10)
+                s_per = statistics.median(samples)
+                gbs = (gib << 30) / s_per / 1e9
+                print(json.dumps({"read": f"{name} {str(dtype).replace('torch.', '')}", "bytes": gib << 30,
+                                  "us_per_call": round(s_per * 1e6, 2), "gbs": round(gbs, 1),
+                                  "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
+                del graph
+            del x
+            torch.cuda.empty_cache()
     return 0
 
 
@@ -268,6 +307,8 @@ def main(argv=None) -> int:
 
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy)
+    if args.torch_reductions:
+        return torch_reductions()
     if args.gqa_sweep:
         return gqa_sweep(args.only)
 
