@@ -1,0 +1,132 @@
+"""Bench presets at their full sizes, in the launch configuration bench.py times, checked on
+sampled output rows against the CPU fp64 oracle (which computes rows one by one):
+
+* the D = 512 global layer with 8-bit codebook V (16 q / 2 kv heads, 8 x 32768): the
+  matrix-core kernel, plus the undo of the rotation;
+* speculative verify (4 slots x 4 drafts over a 32768-row cache): matrix-core draft groups;
+* the codebook serving step (append each slot's token, attend, undo) over 8 x 32768.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_kv_02_amd import binding
+from decode_attention_kv_02_amd.workloads import (CACHE_WORKLOADS, CODEBOOK_WORKLOADS, SERVE_STEP_WORKLOADS,
+                                                   cache_workload_inputs, codebook_workload_inputs,
+                                                   serve_step_inputs)
+from oracle import (oracle_attn_decode_cache, oracle_attn_decode_cache_cb, oracle_attn_decode_cb,
+                    oracle_fwht_undo, oracle_kv_append_cb)
+
+from gpu_util import assert_parity
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(msg):
+    print(f"[presets] {msg}", flush=True)
+
+
+def test_global_d512_codebook_preset_sampled_rows():
+    cfg = next(c for c in CODEBOOK_WORKLOADS if c.head_dim == 512)
+    ci = codebook_workload_inputs(cfg)
+    _say(f"{cfg.name}: generated")
+    q, k, vc, vn, cb, sg = (t.to(DEV) for t in (ci.q, ci.k, ci.v_codes, ci.v_norms, ci.codebook, ci.signs))
+    out = torch.full((ci.n_slots, ci.n_q_heads, ci.head_dim), float("nan"), dtype=torch.float32, device=DEV)
+    binding.attn_decode_cb(q, k, vc, vn, cb, ci.codebook_bits, ci.seq_lens, cfg.window, out, ci.n_slots,
+                           ci.n_q_heads, ci.n_kv_heads, ci.head_dim, ci.scale)
+    rot = out.clone()
+    binding.attn_fwht_undo(out, sg, out)
+    torch.cuda.synchronize()
+    rows = [s * ci.n_q_heads + h for s in range(ci.n_slots) for h in (0, 7, 8, 15)]
+    ref = oracle_attn_decode_cb(ci.q.numpy(), ci.k.numpy(), ci.v_codes.numpy(), ci.v_norms.numpy(),
+                                ci.codebook.numpy(), ci.codebook_bits, ci.seq_lens, cfg.window, ci.n_q_heads,
+                                ci.n_kv_heads, ci.head_dim, ci.scale, rows=rows)
+    got_rot = rot.cpu().numpy().reshape(-1, ci.head_dim)[rows]
+    err = assert_parity(got_rot, ref, "rotated basis")
+    _say(f"{cfg.name}: rotated max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}")
+    got = out.cpu().numpy().reshape(-1, ci.head_dim)[rows]
+    err = assert_parity(got, oracle_fwht_undo(ref, ci.signs.numpy()), "undone")
+    _say(f"{cfg.name}: undone max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}")
+
+
+def test_verify_preset_sampled_rows():
+    cfg = next(c for c in CACHE_WORKLOADS if c.name.startswith("verify"))
+    ci = cache_workload_inputs(cfg)
+    _say(f"{cfg.name}: generated")
+    q, k, v = ci.q.to(DEV), ci.k.to(DEV), ci.v.to(DEV)
+    vs = None if ci.v_scales is None else ci.v_scales.to(DEV)
+    out = torch.full((ci.n_queries, ci.n_q_heads, ci.head_dim), float("nan"), dtype=torch.float32, device=DEV)
+    binding.attn_decode_cache(q, k, v, vs, ci.slot_ids, ci.positions, ci.n_queries, ci.n_cache_slots, ci.capacity,
+                              ci.ring, cfg.window, out, ci.n_q_heads, ci.n_kv_heads, ci.head_dim, ci.scale)
+    torch.cuda.synchronize()
+    rows = [i * ci.n_q_heads + h for i in range(ci.n_queries) for h in (0, 5, 15)]
+    ref = oracle_attn_decode_cache(ci.q.numpy(), ci.k.numpy(), ci.v.numpy(),
+                                   None if ci.v_scales is None else ci.v_scales.numpy(), ci.slot_ids, ci.positions,
+                                   ci.n_cache_slots, ci.capacity, ci.ring, cfg.window, ci.n_q_heads, ci.n_kv_heads,
+                                   ci.head_dim, ci.scale, rows=rows)
+    err = assert_parity(out.cpu().numpy().reshape(-1, ci.head_dim)[rows], ref, cfg.name)
+    _say(f"{cfg.name}: max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}")
+
+
+def test_serving_step_preset_sampled_rows():
+    """Append (fp16 K, codebook V) then attend and undo, on the bench's 8 x 32768 preset.  The codes
+    the GPU writes are checked against the oracle's fp64 decision (a code may differ only where
+    the normalised coordinate lies within 2e-4 of a level midpoint); the outputs, which weigh the
+    new token like any other, against the oracle over the oracle's own cache."""
+    cfg = SERVE_STEP_WORKLOADS[0]
+    ci, kn, vn = serve_step_inputs(cfg)
+    _say(f"{cfg.name}: generated")
+    B = min(ci.head_dim, 256)
+    k_d, vc_d, nm_d = ci.k.to(DEV), ci.v_codes.to(DEV), ci.v_norms.to(DEV)
+    q, cb, sg = ci.q.to(DEV), ci.codebook.to(DEV), ci.signs.to(DEV)
+    out = torch.full((ci.n_queries, ci.n_q_heads, ci.head_dim), float("nan"), dtype=torch.float32, device=DEV)
+    binding.attn_kv_append_cb(kn.to(DEV), vn.to(DEV), k_d, vc_d, nm_d, sg, cb, ci.codebook_bits, ci.slot_ids,
+                              ci.positions, ci.n_queries, ci.n_cache_slots, ci.capacity, ci.ring, ci.n_kv_heads,
+                              ci.head_dim)
+    binding.attn_decode_cache_cb(q, k_d, vc_d, nm_d, cb, ci.codebook_bits, ci.slot_ids, ci.positions, ci.n_queries,
+                                 ci.n_cache_slots, ci.capacity, ci.ring, 0, out, ci.n_q_heads, ci.n_kv_heads,
+                                 ci.head_dim, ci.scale)
+    binding.attn_fwht_undo(out, sg, out)
+    torch.cuda.synchronize()
+    k_h, c_h, n_h, u = oracle_kv_append_cb(kn.numpy(), vn.numpy(), ci.signs.numpy(), ci.codebook.numpy(),
+                                           ci.codebook_bits, ci.k.numpy(), ci.v_codes.numpy(), ci.v_norms.numpy(),
+                                           ci.slot_ids, ci.positions, ci.n_cache_slots, ci.capacity, ci.ring,
+                                           ci.n_kv_heads, ci.head_dim)
+    # the appended rows: K exact, codes by the midpoint rule, norms to 5e-5
+    cap, d = ci.capacity, ci.head_dim
+    gk, gc, gn = k_d.cpu().numpy(), vc_d.cpu().numpy(), nm_d.cpu().numpy()
+    cbd = ci.codebook.numpy().astype(np.float64)
+    n_diff = 0
+    for i, (s, p) in enumerate(zip(ci.slot_ids, ci.positions)):
+        for h in range(ci.n_kv_heads):
+            row = (s * ci.n_kv_heads + h) * cap + (p % cap if ci.ring else p)
+            sl = slice(row * d, (row + 1) * d)
+            assert np.array_equal(gk[sl].view(np.uint16), k_h[sl].view(np.uint16))
+            g_codes, r_codes = gc[sl].astype(np.int64), c_h[sl].astype(np.int64)
+            diff = g_codes != r_codes
+            if diff.any():
+                assert np.all(np.abs(g_codes[diff] - r_codes[diff]) == 1)
+                mid = (cbd[np.minimum(g_codes[diff], r_codes[diff])] + cbd[np.maximum(g_codes[diff], r_codes[diff])]) / 2
+                assert np.abs(u[i, h][diff] - mid).max() <= 2e-4
+                n_diff += int(diff.sum())
+            nsl = slice(row * (d // B), (row + 1) * (d // B))
+            assert np.allclose(gn[nsl], n_h[nsl], rtol=5e-5, atol=0)
+    rows = [i * ci.n_q_heads + h for i in range(ci.n_queries) for h in (0, 9, 15)]
+    ref = oracle_fwht_undo(oracle_attn_decode_cache_cb(ci.q.numpy(), k_h, c_h, n_h, ci.codebook.numpy(),
+                                                       ci.codebook_bits, ci.slot_ids, ci.positions,
+                                                       ci.n_cache_slots, cap, ci.ring, 0, ci.n_q_heads,
+                                                       ci.n_kv_heads, d, ci.scale, rows=rows), ci.signs.numpy())
+    err = assert_parity(out.cpu().numpy().reshape(-1, d)[rows], ref, cfg.name)
+    _say(f"{cfg.name}: codes at a midpoint {n_diff}; max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}")
