@@ -4,7 +4,9 @@ sampled output rows against the CPU fp64 oracle (which computes rows one by one)
 * the D = 512 global layer with 8-bit codebook V (16 q / 2 kv heads, 8 x 32768): the
   matrix-core kernel, plus the undo of the rotation;
 * speculative verify (4 slots x 4 drafts over a 32768-row cache): matrix-core draft groups;
-* the codebook serving step (append each slot's token, attend, undo) over 8 x 32768.
+* the codebook serving steps (append each slot's token, attend, undo) over 8 x 32768 and on
+  8 rings of 1024 rows;
+* the KV appends (one decode step for 8 slots; 4096 tokens into one slot), bit for bit.
 """
 import math
 
@@ -13,11 +15,11 @@ import pytest
 import torch
 
 from decode_attention_kv_02_amd import binding
-from decode_attention_kv_02_amd.workloads import (CACHE_WORKLOADS, CODEBOOK_WORKLOADS, SERVE_STEP_WORKLOADS,
-                                                   cache_workload_inputs, codebook_workload_inputs,
-                                                   serve_step_inputs)
+from decode_attention_kv_02_amd.workloads import (APPEND_WORKLOADS, CACHE_WORKLOADS, CODEBOOK_WORKLOADS,
+                                                   SERVE_STEP_WORKLOADS, append_new_rows, cache_workload_inputs,
+                                                   codebook_workload_inputs, serve_step_inputs)
 from oracle import (oracle_attn_decode_cache, oracle_attn_decode_cache_cb, oracle_attn_decode_cb,
-                    oracle_fwht_undo, oracle_kv_append_cb)
+                    oracle_fwht_undo, oracle_kv_append, oracle_kv_append_cb)
 
 from gpu_util import assert_parity
 
@@ -80,12 +82,12 @@ def test_verify_preset_sampled_rows():
     _say(f"{cfg.name}: max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}")
 
 
-def test_serving_step_preset_sampled_rows():
-    """Append (fp16 K, codebook V) then attend and undo, on the bench's 8 x 32768 preset.  The codes
-    the GPU writes are checked against the oracle's fp64 decision (a code may differ only where
-    the normalised coordinate lies within 2e-4 of a level midpoint); the outputs, which weigh the
-    new token like any other, against the oracle over the oracle's own cache."""
-    cfg = SERVE_STEP_WORKLOADS[0]
+@pytest.mark.parametrize("cfg", SERVE_STEP_WORKLOADS, ids=[c.name for c in SERVE_STEP_WORKLOADS])
+def test_serving_step_preset_sampled_rows(cfg):
+    """Append (fp16 K, codebook V) then attend and undo, on the bench's serving-step presets.  The
+    codes the GPU writes are checked against the oracle's fp64 decision (a code may differ only
+    where the normalised coordinate lies within 2e-4 of a level midpoint); the outputs, which weigh
+    the new token like any other, against the oracle over the oracle's own cache."""
     ci, kn, vn = serve_step_inputs(cfg)
     _say(f"{cfg.name}: generated")
     B = min(ci.head_dim, 256)
@@ -130,3 +132,27 @@ def test_serving_step_preset_sampled_rows():
                                                        ci.n_kv_heads, d, ci.scale, rows=rows), ci.signs.numpy())
     err = assert_parity(out.cpu().numpy().reshape(-1, d)[rows], ref, cfg.name)
     _say(f"{cfg.name}: codes at a midpoint {n_diff}; max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}")
+
+
+@pytest.mark.parametrize("cfg", APPEND_WORKLOADS, ids=[c.name for c in APPEND_WORKLOADS])
+def test_append_preset_bit_exact(cfg):
+    d = cfg.head_dim
+    el = cfg.n_cache_slots * cfg.n_kv_heads * cfg.capacity * d
+    kc = torch.zeros(el, dtype=torch.float16, device=DEV)
+    vc = torch.zeros(el, dtype=torch.int8 if cfg.v_int8 else torch.float16, device=DEV)
+    sc = torch.zeros(el // 32, dtype=torch.float16, device=DEV) if cfg.v_int8 else None
+    kn, vn = append_new_rows(cfg)
+    binding.attn_kv_append(kn.to(DEV), vn.to(DEV), kc, vc, sc, cfg.slot_ids, cfg.positions, cfg.n_rows,
+                           cfg.n_cache_slots, cfg.capacity, cfg.ring, cfg.n_kv_heads, d)
+    torch.cuda.synchronize()
+    rk, rv, rs = oracle_kv_append(kn.numpy(), vn.numpy(), np.zeros(el, np.float16),
+                                  np.zeros(el, np.int8 if cfg.v_int8 else np.float16),
+                                  np.zeros(el // 32, np.float16) if cfg.v_int8 else None, cfg.slot_ids,
+                                  cfg.positions, cfg.n_cache_slots, cfg.capacity, cfg.ring, cfg.n_kv_heads, d)
+    assert np.array_equal(kc.cpu().numpy().view(np.uint16), rk.view(np.uint16)), "K"
+    if cfg.v_int8:
+        assert np.array_equal(vc.cpu().numpy(), rv), "V codes"
+        assert np.array_equal(sc.cpu().numpy().view(np.uint16), rs.view(np.uint16)), "V scales"
+    else:
+        assert np.array_equal(vc.cpu().numpy().view(np.uint16), rv.view(np.uint16)), "V"
+    _say(f"{cfg.name}: bit-exact")
