@@ -218,7 +218,7 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     const int32_t path = opts ? opts->path : 0;
 
     CallPlan plan;
-    std::string err = make_plan(spans, n_q, n_kv, D, chunk, merge_mode, plan, path);
+    std::string err = make_plan(spans, n_q, n_kv, D, chunk, merge_mode, plan, path, vsrc.format != kVF16);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
 
     bool any_mfma = false, any_lanes = false;
@@ -260,7 +260,8 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     args.G = plan.G;
     args.scale_log2 = (float)scale_log2;
 
-    auto fill = [&](const LaunchGroup &lg) {
+    // combine: search keys are the entries' first combine rows, else their first work items
+    auto fill = [&](const LaunchGroup &lg, bool combine) {
         const KernelShape &ks = lg.mfma ? plan.matrix : plan.lanes;
         args.n_sub = ks.n_sub;
         args.fuse_limit = lg.mfma ? 1 : plan.fuse_limit;
@@ -287,6 +288,7 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
             sd.ring_base = sp.ring_base;
             sd.group_n = (int16_t)sp.group_n;
             sd.lead_off = (int16_t)(i - lead_pos);
+            args.key[i] = combine ? sd.comb_begin : sd.item_begin;
             if (sp.group_n > 0) item += n_kv * ks.n_sub * sp.n_chunks;
             if (sp.n_chunks > 1 && !sp.fused) comb += n_q;
         }
@@ -298,7 +300,7 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipEventRecord: ") + hipGetErrorString(e));
     }
     for (const LaunchGroup &lg : plan.groups) {
-        fill(lg);
+        fill(lg, false);
         hipLaunchKernelGGL(lg.mfma ? pk_mfma : pk_lanes, dim3((unsigned)lg.items), dim3(kThreads), 0, stream, args);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
@@ -309,7 +311,7 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     }
     for (const LaunchGroup &lg : plan.groups) {
         if (lg.combine_rows == 0) continue;
-        fill(lg);
+        fill(lg, true);
         hipLaunchKernelGGL(ck, dim3((unsigned)(lg.combine_rows * (D / kCombineDims))), dim3(kThreads), 0, stream, args);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("combine kernel launch: ") + hipGetErrorString(e));
@@ -666,7 +668,7 @@ extern "C" int attn_decode_plan(const int32_t *seq_lens, int32_t n_slots, int32_
     CallPlan plan;
     std::vector<QuerySpan> spans;
     spans_packed(seq_lens, n_slots, window, n_kv_heads, spans);
-    err = make_plan(spans, n_q_heads, n_kv_heads, head_dim, chunk, kMergeAuto, plan);
+    err = make_plan(spans, n_q_heads, n_kv_heads, head_dim, chunk, kMergeAuto, plan, kPathAuto, v_int8 != 0);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
     for (int32_t s = 0; s < n_slots; ++s) {
         if (chunk_keys) chunk_keys[s] = plan.slots[s].chunk;

@@ -29,6 +29,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "planner.hpp"  // kFusedMaxChunks, shared with the host planner
@@ -67,7 +68,19 @@ enum VFormat : int {
     kVCB = 2,    // byte indices into a codebook, one fp32 norm per block of min(D, 256) dims
 };
 
-struct LaunchArgs {
+// The kernel arguments.  A workgroup cannot start its loads before it has found
+// its query: it reads the table size and searches the keys, each read a scalar
+// load that waits for the previous one, and the scalar cache is empty when a
+// kernel starts.  So those reads sit together at the front (the first 64-byte
+// line holds the sizes and the first 12 keys; a search over up to 12 entries
+// misses once), and every query descriptor fills exactly one line.
+struct alignas(64) LaunchArgs {
+    int32_t n_slots;        // slots in this launch (table entries, longest chunks first)
+    int32_t n_items;        // partial-kernel workgroups of this launch
+    int32_t n_sub;          // G / GB
+    int32_t G;              // query heads per kv head
+    int32_t key[kMaxSlotsPerLaunch];  // per entry, non-decreasing: its first work item (partial
+                                      // kernels) or its first combine row (combine kernel)
     const uint16_t *q;      // fp16 [n_slots_total][n_q][D]
     const uint16_t *k;      // fp16 packed cache
     const void *v;          // fp16, int8 or codebook-index cache
@@ -77,18 +90,14 @@ struct LaunchArgs {
     float *ws_o;            // partial O rows [part_rows][D]
     float *ws_ml;           // partial (M, S) [part_rows][2]
     uint32_t *counters;     // arrival counters of in-kernel merges, zero between calls
-    int32_t n_slots;        // slots in this launch (table entries, longest chunks first)
     int32_t cb_mask;        // codebook V: 2^bits - 1 (the index bits that are used)
     int32_t n_q;
-    int32_t G;              // query heads per kv head
-    int32_t n_sub;          // G / GB
     float scale_log2;       // scale * log2(e)
-    int32_t n_items;
     int32_t fuse_limit;     // slots with 2..fuse_limit chunks merge inside the partial kernel
     float cb_scale;         // codebook V: 1 / sqrt(min(D, 256))
-    int32_t pad0;
-    SlotDesc slot[48];
+    alignas(64) SlotDesc slot[kMaxSlotsPerLaunch];
 };
+static_assert(offsetof(LaunchArgs, key) == 16 && offsetof(LaunchArgs, slot) % 64 == 0, "argument layout");
 
 // ---------------------------------------------------------------- helpers
 
@@ -316,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     static_assert(kThreads == 256, "one thread per codebook table entry");
 
     const int item = xcd_item(blockIdx.x, args.n_items, args.n_sub);
-    int si = upper_index(args.n_slots, item, [&](int i) { return args.slot[i].item_begin; });
+    int si = upper_index(args.n_slots, item, [&](int i) { return args.key[i]; });
     si -= args.slot[si].lead_off;
     const SlotDesc sd = args.slot[si];   // group leader: the longest query of the group
     const int local = item - sd.item_begin;
@@ -647,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const LaunchArgs
 
     const int row = blockIdx.x / SLICES;
     const int slice = blockIdx.x - row * SLICES;
-    const int si = upper_index(args.n_slots, row, [&](int i) { return args.slot[i].comb_begin; });
+    const int si = upper_index(args.n_slots, row, [&](int i) { return args.key[i]; });
     const SlotDesc sd = args.slot[si];
     const int h = row - sd.comb_begin;
     const int nc = sd.n_chunks;

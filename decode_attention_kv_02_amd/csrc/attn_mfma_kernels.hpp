@@ -28,8 +28,15 @@
 //    accumulators cover every dim once.  Each V load reads 4 keys x 16 EV
 //    contiguous bytes, whole cache lines, and V is dequantised to fp32 in
 //    registers (exact for fp16, int8 and codebook), never staged in LDS.
+//  * At head_dim 512 with one-byte V (int8, codebook) two sibling workgroups
+//    share each chunk: both compute its
+//    scores and softmax (bitwise the same), each accumulates half the output
+//    dims.  That halves the accumulators and V buffers, which lets two waves
+//    share a SIMD; the second read of the K rows is served by the XCD's L2
+//    (siblings get neighbouring workgroup ids on one XCD).
 //  * Accumulator o[b EV + e] lane l component r holds head l%16, dim
-//    BW b + 4 EV (l/16) + EV r + e (BW = 16 EV dims per load).
+//    DH p + BW b + 4 EV (l/16) + EV r + e (BW = 16 EV dims per load, DH the
+//    dims of one workgroup, p its part).
 //
 // Lane layouts (checked on gfx950 with one-wave probes): 16x16x32 f16:
 // A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]; 16x16x4 f32: A[l%16][l/16],
@@ -52,14 +59,23 @@ constexpr float kLazyMax = 8.f; // log2 headroom of the softmax reference before
 template <int D, int VF>
 struct MfmaGeometry {
     static_assert(D >= 128 && D <= 512, "head_dim 128..512");
+    static constexpr int DS = mfma_dim_split(D, VF != kVF16);            // workgroups sharing a chunk's keys
+    static constexpr int DH = D / DS;                                    // output dims of one workgroup
     static constexpr int KS = D / 32;                                    // QK steps = 16-byte K loads per lane
     static constexpr int EV = (VF == kVF16) ? 8 : (D >= 256 ? 16 : 8);   // V elements per lane per load
     static constexpr int BW = 16 * EV;                                   // dims covered by one load
-    static constexpr int NB = D / BW;                                    // loads per key step
+    static constexpr int NB = DH / BW;                                   // loads per key step
     static constexpr int VBYTES = EV * (VF == kVF16 ? 2 : 1);            // 16, or 8 (byte V at D = 128)
-    static constexpr int NO = NB * EV;                                   // f32x4 accumulators = D / 16
-    static_assert(NO * 16 == D, "accumulators cover every dim once");
+    static constexpr int NO = NB * EV;                                   // f32x4 accumulators = DH / 16
+    static_assert(NO * 16 == DH, "accumulators cover every dim of the workgroup's part once");
     static_assert(VF != kVCB || BW == (D < 256 ? D : 256), "one codebook norm block per load");
+    // Workgroups per CU the register allocation must allow.  Two (two waves per SIMD) for the
+    // split head_dim 512 kernels, which need the bound to fit, and for codebook V at 256, where
+    // it measured faster (4 x 32768, 16 q / 2 kv heads: 46.8 -> 45.5 us).  Elsewhere the
+    // compiler's own allocation: it already allows two waves at 256 and measured as fast or
+    // faster (int8 V, 32 q / 2 kv heads: 35.5 us against 37.1 with the bound); whole fp16 rows
+    // at 512 need more than half the register file (one wave per SIMD).
+    static constexpr int MIN_WG = ((D == 512 && DS == 2) || (D == 256 && VF == kVCB)) ? 2 : 1;
 };
 
 template <int D, int VF>
@@ -76,26 +92,28 @@ struct MVTile {
 __device__ __forceinline__ half8_t as_h8(const uint4 &u) { return __builtin_bit_cast(half8_t, u); }
 
 template <int D, int VF>
-__global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const LaunchArgs args) {
+__global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_partial_mfma_kernel(const LaunchArgs args) {
     using Geo = MfmaGeometry<D, VF>;
     constexpr int KS = Geo::KS, EV = Geo::EV, BW = Geo::BW, NB = Geo::NB, NO = Geo::NO;
+    constexpr int DS = Geo::DS, DH = Geo::DH;
     constexpr int CB_B = D < 256 ? D : 256;   // codebook norm block
     static_assert(kThreads == 256, "one thread per codebook table entry");
 
     const int item = xcd_item(blockIdx.x, args.n_items, args.n_sub);
-    int si = upper_index(args.n_slots, item, [&](int i) { return args.slot[i].item_begin; });
+    int si = upper_index(args.n_slots, item, [&](int i) { return args.key[i]; });
     si -= args.slot[si].lead_off;         // the query group's leader: its longest query
     const SlotDesc sd = args.slot[si];
     const int n_mem = sd.group_n;         // queries of the group (1 when alone); table entries si..
     const int local = item - sd.item_begin;
-    const int sub = local % args.n_sub;
+    const int sub = local % args.n_sub;                 // head block sub / DS, dims part sub % DS
     const int t = local / args.n_sub;
     const int c = t % sd.n_chunks;
     const int kvh = t / sd.n_chunks;
     const int cbeg = sd.lo + c * sd.chunk;
     const int cend = min(cbeg + sd.chunk, sd.L);
-    const int GB = args.G / args.n_sub;                 // heads per query of this block
-    const int h0 = kvh * args.G + sub * GB;             // first head of the block (in the slot)
+    const int GB = args.G / (args.n_sub / DS);          // heads per query of this block
+    const int h0 = kvh * args.G + (sub / DS) * GB;      // first head of the block (in the slot)
+    const int dpart = DH * (sub % DS);                  // first output dim of this workgroup
     const int64_t rowbase = sd.kv_row0 + (int64_t)kvh * sd.kv_stride;
 
     const int tid = threadIdx.x;
@@ -167,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const Launc
             const int64_t row = row_of(kb + 4 * g + i);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const int d0 = BW * b + EV * c16;
+                const int d0 = dpart + BW * b + EV * c16;
                 if constexpr (VF == kVF16) {
                     f.v[i][b] = load_stream16((const uint16_t *)args.v + row * D + d0);
                 } else {
@@ -334,12 +352,12 @@ __global__ __launch_bounds__(kThreads) void attn_partial_mfma_kernel(const Launc
     float *op;
     float scale_out = 1.f;
     if (m_nchunks == 1) {
-        op = args.out + qrow * D;
+        op = args.out + qrow * D + dpart;
         scale_out = (L == 0.f) ? 0.f : 1.f / L;
     } else {
         const int64_t prow = m_part + (int64_t)(h0 + hh) * m_nchunks + c;
-        op = args.ws_o + prow * D;
-        if (g == 0) {
+        op = args.ws_o + prow * D + dpart;
+        if (g == 0 && dpart == 0) {   // (M, S) are the same in every dims part
             args.ws_ml[prow * 2 + 0] = M;
             args.ws_ml[prow * 2 + 1] = L;
         }

@@ -65,8 +65,20 @@ struct SlotPlan {
     bool mfma = false;      // computed by the matrix-core partial kernel
 };
 
+// The matrix-core kernel at head_dim 512 with a one-byte V format (int8 or
+// codebook) splits each chunk's output dims between two sibling workgroups.
+// Each computes the chunk's scores and softmax (from the same K rows, which
+// the second reads from its XCD's L2) and accumulates its own D / 2 dims.
+// Half the accumulators and V buffers leave room for two waves per SIMD
+// instead of one, which hides the per-element decode: measured on MI355X
+// (4 x 32768, 16 q / 2 kv heads, codebook V) 105.7 -> 92.2 us.  With fp16 V
+// the loads already set the pace and the second K read costs more than the
+// second wave gains (103.2 -> 130.1 us), so fp16 stays whole.
+constexpr int mfma_dim_split(int head_dim, bool byte_v) { return head_dim == 512 && byte_v ? 2 : 1; }
+
 // How one partial kernel splits the work: query heads per workgroup (GB, dividing G),
-// G / GB workgroups per (query group, kv head, chunk), queries per workgroup (QB).
+// n_sub workgroups per (query group, kv head, chunk): G / GB head blocks, times the
+// matrix-core kernel's dim split; queries per workgroup (QB).
 struct KernelShape {
     int GB = 1;
     int n_sub = 1;
@@ -294,7 +306,7 @@ constexpr int kMfmaGroupMinCols = 8;  // draft groups this wide go to the matrix
 // Builds the plan from the query spans; returns "" on success or an error message.
 inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, int32_t n_kv,
                              int32_t head_dim, int32_t chunk, int32_t merge_mode, CallPlan &plan,
-                             int32_t path = kPathAuto) {
+                             int32_t path = kPathAuto, bool byte_v = false) {
     plan = CallPlan();
     const int32_t n_slots = (int32_t)spans.size();
     plan.G = n_q / n_kv;
@@ -309,11 +321,11 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
     int mfma_qb_max = 1;
     if (plan.mfma) {
         plan.matrix.GB = G % 16 == 0 ? 16 : 8;
-        plan.matrix.n_sub = G / plan.matrix.GB;
+        plan.matrix.n_sub = G / plan.matrix.GB * mfma_dim_split(head_dim, byte_v);
         mfma_qb_max = kMfmaColumns / plan.matrix.GB;
     } else if (path == kPathAuto && head_dim >= 128 && G <= kMfmaColumns / 2) {
         plan.matrix.GB = G;             // draft groups: every head of the kv head, for each draft
-        plan.matrix.n_sub = 1;
+        plan.matrix.n_sub = mfma_dim_split(head_dim, byte_v);
         mfma_qb_max = kMfmaColumns / G;
     }
     // the matrix-core kernel always merges in the combine kernel

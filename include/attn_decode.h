@@ -289,7 +289,8 @@ int attn_kv_append_cb(const float *k_new, const float *v_new, void *k_cache, voi
  * GPU).  For the given shapes it writes, per slot, the KV positions per chunk
  * and the number of chunks (arrays of n_slots, may be NULL), the workspace
  * bytes the call needs and the number of partial-kernel workgroups it
- * launches (may be NULL).  v_int8 != 0 selects the int8 V format.
+ * launches (may be NULL).  v_int8 != 0 selects the int8 V format (the
+ * codebook format, also one byte per element, plans the same).
  * Returns 0 or ATTN_DECODE_EINVAL for shapes attn_decode would reject.
  */
 int attn_decode_plan(const int32_t *seq_lens, int32_t n_slots, int32_t window,

@@ -132,7 +132,8 @@ def test_matrix_core_path_is_rejected_where_it_does_not_apply():
     assert_parity(ok, run_oracle(inp, 0), "auto at head_dim 64")
 
 
-@pytest.mark.parametrize("d,nq,nkv,i8", [(128, 16, 2, False), (256, 32, 2, True), (512, 16, 2, False)])
+@pytest.mark.parametrize("d,nq,nkv,i8", [(128, 16, 2, False), (256, 32, 2, True), (512, 16, 2, False),
+                                         (512, 16, 2, True)])
 def test_large_and_rising_logits(d, nq, nkv, i8):
     """Logits of several hundred, and for head 0 a ramp rising by about 64 (natural log) over
     each slot, so the running maximum moves at almost every tile: the softmax reference of the
