@@ -31,7 +31,10 @@ One JSON line is printed.  Besides the contract fields it carries
     another buffer before every call, minus the time of those reads alone) and
     graph (20 calls captured into one HIP graph and replayed: the GPU time per
     call without the Python and launch cost on the host, as a decode loop that
-    captures its step sees it),
+    captures its step sees it) and flushed events (50 reps of the 1 GiB read
+    followed by one call between two events on its stream: median, p10, p90),
+    with the CPU fp64 oracle over all query rows of the preset on all cores
+    (and on one core for the three smallest presets),
     plus the codebook-V presets (``attn_decode_cb`` followed by ``attn_fwht_undo``
     in place; bytes = fp16 K, one index byte per V element and the fp32 norms),
     the fixed-capacity cache presets (``attn_decode_cache``: a
@@ -216,6 +219,25 @@ GQA_SHAPES = (
     ("g16_d256_int8_4x16384", (16384,) * 4, 32, 2, 256, "int8"),
     ("g16_d128_fp16_8x8192", (8192,) * 8, 64, 4, 128, "fp16"),
 )
+
+
+def oracle_per_config(inp, W: int, one_thread: bool) -> dict:
+    """The CPU fp64 oracle over every query row of a preset, one pass: µs per call and KV GB/s on
+    all of this host's cores (`oracle_*`) and, when asked, on one core (`oracle_1thread_*`)."""
+    from oracle import oracle_attn_decode
+    threads = len(os.sched_getaffinity(0))
+    rows = list(range(inp.n_slots * inp.n_q_heads))
+    nb = kv_bytes(inp.seq_lens, W, inp.n_kv_heads, inp.head_dim, inp.v_int8)
+    sn = None if inp.v_scales is None else inp.v_scales.numpy()
+    res = {"oracle_threads": threads}
+    for key, t in (("oracle", threads),) + ((("oracle_1thread", 1),) if one_thread else ()):
+        t0 = time.perf_counter()
+        oracle_attn_decode(inp.q.numpy(), inp.k.numpy(), inp.v.numpy(), sn, inp.seq_lens, W, inp.n_q_heads,
+                           inp.n_kv_heads, inp.head_dim, inp.scale, rows=rows, threads=t)
+        dt = time.perf_counter() - t0
+        res[key + "_us_per_call"] = round(dt * 1e6, 1)
+        res[key + "_gbs"] = round(nb / dt / 1e9, 3)
+    return res
 
 
 def partial_kernel_name(G: int, head_dim: int, drafts: int = 1) -> str:
@@ -508,14 +530,20 @@ def main(argv=None) -> int:
     if not args.quick:
         flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         per = []
-        for w in WORKLOADS:
+        for wi, w in enumerate(WORKLOADS):
             if w.name != cfg.name or args.workload not in by_name:
                 print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
                 pin = workload_inputs(w)
                 ptens = upload(pin)
-                del pin.k, pin.v
             else:
                 pin, ptens = inp, tens
+            orc = {}
+            if not args.no_cpu_baseline:
+                # the three smallest presets also on one core; the larger ones on all cores only
+                orc = {W: oracle_per_config(pin, W, wi <= 2) for W in w.windows}
+                print(f"[bench] {w.name}: oracle {orc}", file=sys.stderr, flush=True)
+            if pin is not inp:
+                del pin.k, pin.v
             pout = torch.empty((pin.n_slots, pin.n_q_heads, pin.head_dim), dtype=torch.float32, device=dev)
             for W in w.windows:
                 nb = kv_bytes(pin.seq_lens, W, pin.n_kv_heads, pin.head_dim, pin.v_int8)
@@ -551,8 +579,24 @@ def main(argv=None) -> int:
                     torch.cuda.synchronize()
                     pk.append(c0.elapsed_time(c1) * 1e3)
                 g_us = graph_us_per_call(lambda st: call(pin, ptens, pout, W, st=st))
+                # 50 reps of: a 1 GiB flush read, then one whole call (plan upload, partial and
+                # combine kernels) between two events on the call's stream
+                pairs = [(new_event(), new_event()) for _ in range(50)]
+                torch.cuda.synchronize()
+                for e0, e1 in pairs:
+                    flush.sum()
+                    e0.record(stream)
+                    call(pin, ptens, pout, W)
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                ev = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
+                ev_med, ev_p10, ev_p90 = statistics.median(ev), ev[len(ev) // 10], ev[(9 * len(ev)) // 10]
                 per.append({
                     "workload": w.name, "window": W, "kv_bytes": nb,
+                    "cold_event_us": {"median": round(ev_med, 2), "p10": round(ev_p10, 2),
+                                      "p90": round(ev_p90, 2), "reps": len(ev)},
+                    "cold_event_hbm_frac": round(nb / (ev_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    **orc.get(W, {}),
                     "warm_us_per_call": round(warm, 2),
                     "warm_gbs": round(nb / (warm * 1e-6) / 1e9, 1),
                     "warm_hbm_frac": round(nb / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -566,7 +610,8 @@ def main(argv=None) -> int:
                     "graph_hbm_frac": round(nb / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 })
                 print(f"[bench] {w.name} W={W}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), "
-                      f"cold {cold:.2f} us ({per[-1]['cold_gbs']} GB/s), graph {g_us:.2f} us",
+                      f"cold {cold:.2f} us ({per[-1]['cold_gbs']} GB/s), graph {g_us:.2f} us, "
+                      f"flushed events median {ev_med:.2f} (p10 {ev_p10:.2f}, p90 {ev_p90:.2f}) us",
                       file=sys.stderr, flush=True)
             if w.name != cfg.name or args.workload not in by_name:
                 del ptens
