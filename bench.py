@@ -32,7 +32,8 @@ One JSON line is printed.  Besides the contract fields it carries
     graph (20 calls captured into one HIP graph and replayed: the GPU time per
     call without the Python and launch cost on the host, as a decode loop that
     captures its step sees it) and flushed events (50 reps of the 1 GiB read
-    followed by one call between two events on its stream: median, p10, p90),
+    followed by one call between two events on its stream: median, p10, p90,
+    and the median of the same pairs with nothing between them),
     with the CPU fp64 oracle over all query rows of the preset on all cores
     (and on one core for the three smallest presets),
     plus the codebook-V presets (``attn_decode_cb`` followed by ``attn_fwht_undo``
@@ -209,6 +210,7 @@ def torch_reductions() -> int:
 GQA_SHAPES = (
     ("g8_d512_fp16_4x32768", (32768,) * 4, 16, 2, 512, "fp16"),
     ("g8_d512_codebook_4x32768", (32768,) * 4, 16, 2, 512, "codebook"),
+    ("g8_d512_int8_4x32768", (32768,) * 4, 16, 2, 512, "int8"),
     ("g8_d256_fp16_4x32768", (32768,) * 4, 16, 2, 256, "fp16"),
     ("g8_d256_codebook_4x32768", (32768,) * 4, 16, 2, 256, "codebook"),
     ("g8_d128_fp16_8x8192", (8192,) * 8, 64, 8, 128, "fp16"),
@@ -529,6 +531,15 @@ def main(argv=None) -> int:
     # ---- every preset: cold (flushed) and warm
     if not args.quick:
         flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        # the same flushed event pairs with nothing between them: what the pair itself adds
+        empty = [(new_event(), new_event()) for _ in range(50)]
+        torch.cuda.synchronize()
+        for e0, e1 in empty:
+            flush.sum()
+            e0.record(stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        empty_pair_us = statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in empty)
         per = []
         for wi, w in enumerate(WORKLOADS):
             if w.name != cfg.name or args.workload not in by_name:
@@ -594,7 +605,8 @@ def main(argv=None) -> int:
                 per.append({
                     "workload": w.name, "window": W, "kv_bytes": nb,
                     "cold_event_us": {"median": round(ev_med, 2), "p10": round(ev_p10, 2),
-                                      "p90": round(ev_p90, 2), "reps": len(ev)},
+                                      "p90": round(ev_p90, 2), "reps": len(ev),
+                                      "empty_pair_median": round(empty_pair_us, 2)},
                     "cold_event_hbm_frac": round(nb / (ev_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     **orc.get(W, {}),
                     "warm_us_per_call": round(warm, 2),
