@@ -17,7 +17,8 @@ each slot's attended range, read once:
 
 One JSON line is printed.  Besides the contract fields it carries
   * ``roofline``: the partial kernel's algorithmic bytes / its average launch
-    duration against the 8 TB/s HBM peak.  The duration comes from HIP event
+    duration against the 8 TB/s HBM peak (and, secondary, against a 1 GiB
+    device copy timed on the same GPU, read plus written bytes).  The duration comes from HIP event
     pairs that the library records around the partial-kernel launch, on the
     call's stream, on every ``--event-every``-th step of the timed region (an
     event between two kernels leaves the GPU idle for several microseconds, so
@@ -166,6 +167,26 @@ def calibrate_copy(nbytes: int) -> int:
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "copies": 5}), flush=True)
     return 0
+
+
+def measured_copy_gbs(dev, nbytes: int = 1 << 30, reps: int = 20) -> float:
+    """Bytes moved per second (read + written) by a plain device-to-device copy of `nbytes`,
+    back to back on the current stream: the on-box bandwidth a streaming kernel can be set
+    against, beside the published peak."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / dt / 1e9
 
 
 def torch_reductions() -> int:
@@ -527,6 +548,10 @@ def main(argv=None) -> int:
             "algorithmic_bytes_per_launch": nbytes,
         },
     }
+    # secondary: the same achieved rate against a copy measured on this GPU (read + write bytes)
+    copy_gbs = measured_copy_gbs(dev)
+    result["roofline"]["measured_copy_gbs"] = round(copy_gbs, 1)
+    result["roofline"]["frac_of_measured_copy"] = round(achieved / copy_gbs, 4)
 
     # ---- every preset: cold (flushed) and warm
     if not args.quick:
