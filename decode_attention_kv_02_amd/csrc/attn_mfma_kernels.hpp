@@ -51,6 +51,7 @@
 namespace attn_decode_impl {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaKeys = 16;   // keys per tile (the MFMA M / N size)
@@ -90,6 +91,16 @@ struct MVTile {
 };
 
 __device__ __forceinline__ half8_t as_h8(const uint4 &u) { return __builtin_bit_cast(half8_t, u); }
+
+// Four fp32 values as fp16 pairs: hi = fp16(x), lo = fp16(x - hi); hi + lo carries about 22 bits.
+__device__ __forceinline__ void split_f16(const float (&x)[4], half4_t &hi, half4_t &lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const _Float16 h = (_Float16)x[i];
+        hi[i] = h;
+        lo[i] = (_Float16)(x[i] - (float)h);
+    }
+}
 
 template <int D, int VF>
 __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_partial_mfma_kernel(const LaunchArgs args) {
@@ -161,7 +172,12 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
         }
     }
 
-    __shared__ float s_cb[VF == kVCB ? 256 : 1];   // codebook V: level[i & mask] / sqrt(B)
+    // Codebook V up to head_dim 256 takes the fp16 products of P.V (below), with each table
+    // entry level[i & mask] / sqrt(B) as two fp16 terms (hi in the low half, lo in the high).
+    // The split head_dim 512 kernel keeps the fp32 products and an fp32 table: within its two-wave
+    // register budget the fp16 form spills more and measured slower (91.7 -> 94.3 us, 4 x 32768).
+    constexpr bool CB16 = VF == kVCB && D <= 256;
+    __shared__ uint32_t s_cb[VF == kVCB ? 256 : 1];   // bits of the fp16 pair, or of the fp32 level
     __shared__ float s_m[kWaves][16], s_l[kWaves][16];
     __shared__ f32x4_t s_o[NO][64];                // one wave's accumulators, for the final merge
 
@@ -254,34 +270,111 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
         }
         l += psum;
 
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        if constexpr (VF == kVF16) {
+            // fp16 V on v_mfma_f32_16x16x16_f16: one product covers the tile's 16 keys.  A is
+            // V^T: lane l supplies A[l%16][4(l/16) + j], keys 4(l/16) + j, which are exactly its
+            // loads j = 0..3, so element e of those four loads is its A operand for instruction e.
+            // B is P^T straight from the S^T accumulator (keys 4(l/16) + j of head l%16), as two
+            // fp16 terms, hi + lo, which carry about 22 bits of each weight; the products are
+            // exact and the accumulation fp32.
+            half4_t ph, pl;
+            split_f16(p, ph, pl);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                float x[EV];
-                const uint32_t wd[4] = {vt.v[i][b].x, vt.v[i][b].y, vt.v[i][b].z, vt.v[i][b].w};
-                if constexpr (VF == kVF16) {
+                const half8_t v0 = as_h8(vt.v[0][b]), v1 = as_h8(vt.v[1][b]);
+                const half8_t v2 = as_h8(vt.v[2][b]), v3 = as_h8(vt.v[3][b]);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        x[2 * q] = h2f((uint16_t)(wd[q] & 0xFFFF));
-                        x[2 * q + 1] = h2f((uint16_t)(wd[q] >> 16));
+                for (int e = 0; e < EV; ++e) {
+                    const half4_t a = {v0[e], v1[e], v2[e], v3[e]};
+                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, ph, o[b * EV + e], 0, 0, 0);
+                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pl, o[b * EV + e], 0, 0, 0);
+                }
+            }
+        } else if constexpr (CB16) {
+            // Codebook V on the same products.  The table gives each level as hi + lo (about 22
+            // bits); the block norm scales P, which is split the same way.  x p = xh ph + xh pl +
+            // xl ph, leaving out xl pl (about 2^-22 of the product).
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float pn[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pn[j] = p[j] * vt.side[j][b];
+                half4_t ph, pl;
+                split_f16(pn, ph, pl);
+#pragma unroll
+                for (int e = 0; e < EV; ++e) {
+                    uint32_t t[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint4 &u = vt.v[j][b];
+                        const uint32_t wd = (e / 4 == 0) ? u.x : (e / 4 == 1) ? u.y : (e / 4 == 2) ? u.z : u.w;
+                        t[j] = s_cb[(wd >> (8 * (e % 4))) & 0xFF];
                     }
-                } else {
+                    // low halves (hi terms) of keys 0..3, then high halves (lo terms)
+                    const uint2 ah = make_uint2(__builtin_amdgcn_perm(t[1], t[0], 0x05040100u),
+                                                __builtin_amdgcn_perm(t[3], t[2], 0x05040100u));
+                    const uint2 al = make_uint2(__builtin_amdgcn_perm(t[1], t[0], 0x07060302u),
+                                                __builtin_amdgcn_perm(t[3], t[2], 0x07060302u));
+                    const half4_t xh = __builtin_bit_cast(half4_t, ah), xl = __builtin_bit_cast(half4_t, al);
+                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, ph, o[b * EV + e], 0, 0, 0);
+                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, pl, o[b * EV + e], 0, 0, 0);
+                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(xl, ph, o[b * EV + e], 0, 0, 0);
+                }
+            }
+        } else if constexpr (VF == kVI8 && D <= 256) {
+            // int8 V on the same products, exactly: the block scale is an fp16 value and the code
+            // a small integer, so hi = fp16(code scale) and lo = fma(code, scale, -hi) (the
+            // residual, exact in fp16) sum to code scale exactly.  Keys 0, 1 and 2, 3 of the lane
+            // go through packed fp16 arithmetic side by side, already in the A operand's order.
+            half4_t ph, pl;
+            split_f16(p, ph, pl);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const half2_t s01 = {(_Float16)vt.side[0][b], (_Float16)vt.side[1][b]};
+                const half2_t s23 = {(_Float16)vt.side[2][b], (_Float16)vt.side[3][b]};
+#pragma unroll
+                for (int e = 0; e < EV; ++e) {
+                    _Float16 c[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint4 &u = vt.v[j][b];
+                        const uint32_t wd = (e / 4 == 0) ? u.x : (e / 4 == 1) ? u.y : (e / 4 == 2) ? u.z : u.w;
+                        c[j] = (_Float16)(int)(int8_t)(wd >> (8 * (e % 4)));
+                    }
+                    const half2_t c01 = {c[0], c[1]}, c23 = {c[2], c[3]};
+                    const half2_t h01 = c01 * s01, h23 = c23 * s23;
+                    const half2_t l01 = __builtin_elementwise_fma(c01, s01, -h01);
+                    const half2_t l23 = __builtin_elementwise_fma(c23, s23, -h23);
+                    const half4_t xh = {h01[0], h01[1], h23[0], h23[1]};
+                    const half4_t xl = {l01[0], l01[1], l23[0], l23[1]};
+                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, ph, o[b * EV + e], 0, 0, 0);
+                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, pl, o[b * EV + e], 0, 0, 0);
+                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(xl, ph, o[b * EV + e], 0, 0, 0);
+                }
+            }
+        } else {
+            // head_dim 512 with one-byte V: V^T P^T on v_mfma_f32_16x16x4_f32, four key steps.
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    float x[EV];
+                    const uint32_t wd[4] = {vt.v[i][b].x, vt.v[i][b].y, vt.v[i][b].z, vt.v[i][b].w};
 #pragma unroll
                     for (int e = 0; e < EV; ++e) {
                         const uint32_t code = (wd[e / 4] >> (8 * (e % 4))) & 0xFF;
                         if constexpr (VF == kVI8) x[e] = (float)(int8_t)code * vt.side[i][b];
-                        else x[e] = s_cb[code];
+                        else x[e] = __builtin_bit_cast(float, s_cb[code]);
                     }
-                }
-                // Codebook V: the 16 rows (dims) of these instructions lie in one norm block
-                // (BW = min(D, 256) dims), so the norm belongs to the key alone, the k index:
-                // it scales P, the B operand, once per load instead of every element.
-                float pb = p[i];
-                if constexpr (VF == kVCB) pb *= vt.side[i][b];
+                    // Codebook V: the 16 rows (dims) of these instructions lie in one norm block
+                    // (BW = min(D, 256) dims), so the norm belongs to the key alone, the k index:
+                    // it scales P, the B operand, once per load instead of every element.
+                    float pb = p[i];
+                    if constexpr (VF == kVCB) pb *= vt.side[i][b];
 #pragma unroll
-                for (int e = 0; e < EV; ++e)
-                    o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], pb, o[b * EV + e], 0, 0, 0);
+                    for (int e = 0; e < EV; ++e)
+                        o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], pb, o[b * EV + e], 0, 0, 0);
+                }
             }
         }
     };
@@ -294,7 +387,12 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
         load_k(cbeg + tl * kMfmaKeys, kt);
         load_v(cbeg + tl * kMfmaKeys, va);
     }
-    if constexpr (VF == kVCB) s_cb[tid] = args.codebook[tid & args.cb_mask] * args.cb_scale;
+    if constexpr (VF == kVCB) {
+        const float x = args.codebook[tid & args.cb_mask] * args.cb_scale;
+        const _Float16 h = (_Float16)x, lo = (_Float16)(x - (float)h);
+        s_cb[tid] = CB16 ? (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16)
+                         : __builtin_bit_cast(uint32_t, x);
+    }
     if constexpr (VF == kVCB || QLDS) __syncthreads();
     // K: one buffer, refilled as soon as the QK steps have read it; V: two buffers.
     for (; tl < ntiles; tl += 2 * kWaves) {
