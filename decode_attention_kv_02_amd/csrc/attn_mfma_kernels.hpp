@@ -17,17 +17,22 @@
 //  * S^T (16 keys x 16 heads) = K q^T on v_mfma_f32_16x16x32_f16: A = K rows
 //    (key l%16, 8 dims per lane per step, one 16-byte load), B = q.  fp16
 //    products are exact, the accumulation fp32.
-//  * O^T (dims x heads) += V^T P^T on v_mfma_f32_16x16x4_f32, with both
-//    operands straight from registers.  B = P from the S^T accumulator: lane l
-//    holds keys 4(l/16) + i of head l%16, exactly the B operand (k = l/16) of
-//    step i.  A = V: in step i lane l loads key 4(l/16) + i, EV consecutive
-//    dims starting at EV (l%16) (16 bytes), and feeds element e of that load
-//    to instruction e as A[row l%16][k l/16].  Row l%16 of instruction e is
-//    then dim EV (l%16) + e, the same for every lane with that l%16, and k is
-//    the key, so each instruction is an exact 16-dims x 4-keys product; the
-//    accumulators cover every dim once.  Each V load reads 4 keys x 16 EV
-//    contiguous bytes, whole cache lines, and V is dequantised to fp32 in
-//    registers (exact for fp16, int8 and codebook), never staged in LDS.
+//  * O^T (dims x heads) += V^T P^T with both operands straight from
+//    registers.  Lane l loads keys 4(l/16) + j, j = 0..3, each EV consecutive
+//    dims starting at EV (l%16) (16 bytes); the S^T accumulator gives it P of
+//    the same four keys for head l%16.  Instruction e takes element e of the
+//    loads, so its row l%16 is dim EV (l%16) + e, the same for every lane with
+//    that l%16, and the accumulators cover every dim once.  Each V load reads
+//    4 keys x 16 EV contiguous bytes, whole cache lines; V is never staged in
+//    LDS.
+//    - On v_mfma_f32_16x16x16_f16 (fp16 V; int8 and codebook V up to head_dim
+//      256) A[l%16][4(l/16) + j] is element e of load j, so one product covers
+//      the 16 keys.  P and V enter as fp16 pairs hi + lo that carry about 22
+//      bits (int8 code x scale exactly), the products are exact and the
+//      accumulation fp32.
+//    - On v_mfma_f32_16x16x4_f32 (int8 and codebook V at head_dim 512, whose
+//      two-wave register budget the fp16 form overruns) step j takes load j as
+//      A[l%16][l/16] and P as B[l/16][l%16], with V dequantised to fp32.
 //  * At head_dim 512 with one-byte V (int8, codebook) two sibling workgroups
 //    share each chunk: both compute its
 //    scores and softmax (bitwise the same), each accumulates half the output
@@ -39,8 +44,9 @@
 //    dims of one workgroup, p its part).
 //
 // Lane layouts (checked on gfx950 with one-wave probes): 16x16x32 f16:
-// A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]; 16x16x4 f32: A[l%16][l/16],
-// B[l/16][l%16]; both C[4(l/16)+i][l%16].
+// A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]; 16x16x16 f16: A[l%16][4(l/16)+e],
+// B[4(l/16)+e][l%16]; 16x16x4 f32: A[l%16][l/16], B[l/16][l%16]; all three
+// C[4(l/16)+i][l%16].
 #pragma once
 
 #include <hip/hip_runtime.h>
