@@ -263,10 +263,12 @@ def oracle_per_config(inp, W: int, one_thread: bool) -> dict:
     return res
 
 
-def partial_kernel_name(G: int, head_dim: int, drafts: int = 1) -> str:
+def partial_kernel_name(G: int, head_dim: int, drafts: int = 1, byte_v: bool = False) -> str:
     """The partial kernel the library's automatic choice (planner.hpp) runs: the matrix cores at a
-    multiple of 8 query heads per kv head, or for a slot's drafts x heads filling 8 columns."""
-    if head_dim >= 128 and (G % 8 == 0 or drafts * G >= 8):
+    multiple of 8 query heads per kv head, or for a slot's drafts x heads filling 4 columns (8 at
+    head_dim 512 with one-byte V)."""
+    min_cols = 8 if (head_dim == 512 and byte_v) else 4
+    if head_dim >= 128 and (G % 8 == 0 or drafts * G >= min_cols):
         return "attn_partial_mfma_kernel"
     return "attn_partial_kernel"
 
@@ -336,7 +338,8 @@ def gqa_sweep(only: str = "") -> int:
             res[key + "_us"] = round(us, 2)
             res[key + "_hbm_frac"] = round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
             del graph
-        res["automatic"] = "matrix" if partial_kernel_name(nq // nkv, d) == "attn_partial_mfma_kernel" else "lanes"
+        res["automatic"] = ("matrix" if partial_kernel_name(nq // nkv, d, byte_v=fmt != "fp16") ==
+                            "attn_partial_mfma_kernel" else "lanes")
         print(json.dumps(res), flush=True)
         del q, k, out
         torch.cuda.empty_cache()
@@ -506,7 +509,7 @@ def main(argv=None) -> int:
     else:
         shape = {"n_slots": inp.n_slots, "seq_lens": list(inp.seq_lens)}
         drafts = 1
-    kernel = partial_kernel_name(inp.n_q_heads // inp.n_kv_heads, inp.head_dim, drafts)
+    kernel = partial_kernel_name(inp.n_q_heads // inp.n_kv_heads, inp.head_dim, drafts, byte_v=v_format != "fp16")
     traffic = read_traffic(cfg.name, window, kernel)
     result = {
         "metric": METRIC,

@@ -287,13 +287,14 @@ inline int heads_per_workgroup(int G) {
 // workgroup.  It applies to a whole call at a multiple of 8 query heads per kv
 // head and head_dim >= 128, where it measured faster than the lane kernel on
 // every shape (graph-replayed, fp16 / int8 / codebook V, head_dim 128..512:
-// 1.3x at 8 heads and 512, up to 2.5x at 16 heads and 128).  With fewer heads
-// per kv head, the draft queries of one slot (a speculative-verify step) that
-// the lane kernel would group go to the matrix cores as one workgroup when
-// they fill at least 8 columns (drafts x heads; e.g. 4 drafts at 2 heads per
-// kv head), so each K and V byte is read once for all of them; the lane
-// kernel holds at most 4 rows.  Which kernel a query gets depends only on the
-// queries of its own slot, so a batched call equals per-slot calls bitwise.
+// 1.2x at 8 heads and 512, up to 2.7x at 16 heads and 128).  With fewer heads
+// per kv head, the draft queries of one slot (a speculative-verify step), or
+// one query alone, go to the matrix cores as one workgroup when they fill at
+// least mfma_group_min_cols columns (drafts x heads: 4, e.g. 2 drafts at 2
+// heads per kv head or one query with 4; 8 at head_dim 512 with one-byte V),
+// so each K and V byte is read once for all of them; the lane kernel holds at
+// most 4 rows.  Which kernel a query gets depends only on the queries of its
+// own slot, so a batched call equals per-slot calls bitwise.
 // kPathLanes forces the lane kernel everywhere, kPathMatrix the matrix cores
 // (where they apply to the whole call).
 enum KernelPath { kPathAuto = 0, kPathLanes = 1, kPathMatrix = 2 };
@@ -301,7 +302,14 @@ enum KernelPath { kPathAuto = 0, kPathLanes = 1, kPathMatrix = 2 };
 inline bool mfma_applies(int G, int head_dim) { return G % 8 == 0 && head_dim >= 128; }
 inline bool mfma_preferred(int G, int head_dim) { return mfma_applies(G, head_dim); }
 constexpr int kMfmaColumns = 16;      // (query, head) columns of one matrix-core workgroup
-constexpr int kMfmaGroupMinCols = 8;  // draft groups this wide go to the matrix cores
+// Query groups (a slot's drafts x heads, or one query's heads) at least this many columns wide
+// go to the matrix cores.  Four wherever that kernel takes the fp16 products; measured against the
+// lanes (graph-replayed): one query with 4 heads per kv head at head_dim 128, 8 x 8192, 53.4 ->
+// 46.3 us, codebook V at 256 146.1 -> 136.7 us, fp16 at 256 and 512 within 1%; 3 drafts x 2 heads
+// over 4 x 32768 329.0 -> 171.4 us (the lanes' groups hold at most 4 rows, so 6 rows took two
+// reads of the cache).  Eight at head_dim 512 with one-byte V, whose split kernel keeps the fp32
+// products: one int8 query with 4 heads ran 143.3 us on the lanes against 198.2 there.
+inline int mfma_group_min_cols(int head_dim, bool byte_v) { return head_dim == 512 && byte_v ? 8 : 4; }
 
 // Builds the plan from the query spans; returns "" on success or an error message.
 inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, int32_t n_kv,
@@ -403,6 +411,7 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
         }
     };
     std::vector<int32_t> lane_q;   // queries left to the lane kernel, in candidate order
+    const int min_cols = mfma_group_min_cols(head_dim, byte_v);
     for (size_t i = 0; i < idx.size();) {
         size_t j = i + 1;
         while (j < idx.size() && same_rows(idx[i], idx[j])) ++j;
@@ -410,16 +419,16 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
         if (plan.mfma) {
             for (int32_t q : run) set_chunks(plan.slots[q]);
             if (mfma_qb_max > 1) group_run(run, mfma_qb_max, 2, plan.matrix.QB, nullptr);
-        } else if (mfma_qb_max > 1 && (int64_t)run.size() * G >= kMfmaGroupMinCols) {
-            // draft groups for the matrix cores: chunks by their rule; what does not fill
-            // 8 columns goes back to the lane kernel
+        } else if (mfma_qb_max > 1 && (int64_t)run.size() * G >= min_cols) {
+            // query groups for the matrix cores: chunks by their rule; what does not fill
+            // min_cols columns goes back to the lane kernel (a query that fills them alone stays)
             for (int32_t q : run) {
                 plan.slots[q].mfma = true;
                 set_chunks(plan.slots[q]);
             }
             std::vector<int32_t> back;
-            const int min_q = (kMfmaGroupMinCols + G - 1) / G;
-            group_run(run, mfma_qb_max, min_q, plan.matrix.QB, &back);
+            const int min_q = (min_cols + G - 1) / G;
+            group_run(run, mfma_qb_max, min_q, plan.matrix.QB, min_q > 1 ? &back : nullptr);
             for (int32_t q : back) {
                 plan.slots[q].mfma = false;
                 lane_q.push_back(q);

@@ -57,13 +57,13 @@ def assert_parity(got, ref, what=""):
     return max_abs, rel
 
 
-def run_gpu_cache(ci, window, chunk=0, dev_tensors=None, merge_mode=0):
+def run_gpu_cache(ci, window, chunk=0, dev_tensors=None, merge_mode=0, path=0):
     q, k, v, vs = dev_tensors if dev_tensors is not None else to_device(ci)
     out = torch.full((ci.n_queries, ci.n_q_heads, ci.head_dim), float("nan"), dtype=torch.float32,
                      device=q.device)
     binding.attn_decode_cache(q, k, v, vs, ci.slot_ids, ci.positions, ci.n_queries, ci.n_cache_slots,
                               ci.capacity, ci.ring, window, out, ci.n_q_heads, ci.n_kv_heads,
-                              ci.head_dim, ci.scale, chunk=chunk, merge_mode=merge_mode)
+                              ci.head_dim, ci.scale, chunk=chunk, merge_mode=merge_mode, path=path)
     torch.cuda.synchronize()
     return out
 

@@ -87,6 +87,18 @@ def test_forced_chunk_is_used_and_still_bounded():
     assert p["n_chunks"][0] <= 4096
 
 
+def test_one_query_with_four_heads_per_kv_head_goes_to_the_matrix_cores():
+    # 4 (query, head) columns are enough for the matrix cores wherever they take fp16 products:
+    # their chunk rule gives 512 positions at 4096, the lanes' 64.  Two heads per kv head (the
+    # configs) stay on the lanes, and so does head_dim 512 with one-byte V (its kernel needs 8).
+    assert binding.attn_decode_plan([4096], 0, 32, 8, 128)["chunk"] == [512]
+    assert binding.attn_decode_plan([4096], 0, 32, 8, 256, v_int8=True)["chunk"] == [512]
+    assert binding.attn_decode_plan([4096], 0, 32, 8, 512)["chunk"] == [512]
+    assert binding.attn_decode_plan([4096], 0, 32, 8, 512, v_int8=True)["chunk"] == [64]
+    assert binding.attn_decode_plan([4096], 0, 16, 8, 256)["chunk"] == [64]
+    assert binding.attn_decode_plan([4096], 0, 32, 8, 64)["chunk"] == [64]   # head_dim 64: lanes only
+
+
 def test_gqa_blocks_multiply_workgroups_for_large_groups():
     # lane kernel: G = 3 as three single heads; G = 8 at head_dim 64 as two blocks of 4
     assert binding.attn_decode_plan([640], 0, 6, 2, 128)["partial_workgroups"] == 2 * 3 * 10

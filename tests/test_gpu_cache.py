@@ -61,16 +61,21 @@ def test_ring_chunks_across_the_wrap(chunk):
     _report(f"ring chunk {chunk}", assert_parity(got, ref, f"chunk={chunk}"))
 
 
-def test_queries_are_bitwise_independent():
+def test_slots_are_bitwise_independent():
+    """Queries of several slots in one call, interleaved: each slot's rows equal a call with that
+    slot's queries alone, bitwise (a query's kernel depends only on its own slot's queries), and
+    each query alone matches the oracle (alone it may take the other partial kernel: here each
+    slot's queries fill 4 or 6 matrix-core columns together, 2 alone)."""
     sid, pos = (1, 0, 1, 1, 0), (4000, 100, 4001, 1, 4095)
     ci = make_cache_inputs(2, 4096, 1, sid, pos, 16, 8, 256, True, seed_base=9200)
     dev = to_device(ci)
     batched = run_gpu_cache(ci, 0, dev_tensors=dev)
+    ref = run_oracle_cache(ci, 0)
+    for s_ in (0, 1):
+        rows = [i for i in range(len(sid)) if sid[i] == s_]
+        assert torch.equal(batched[rows], _sub_call(ci, dev, rows)), s_
     for i in range(len(sid)):
-        one = CacheInputs(ci.q[i:i + 1].clone(), ci.k, ci.v, ci.v_scales, (sid[i],), (pos[i],), ci.n_cache_slots,
-                       ci.capacity, ci.ring, ci.n_q_heads, ci.n_kv_heads, ci.head_dim, ci.scale)
-        solo = run_gpu_cache(one, 0, dev_tensors=(dev[0][i:i + 1].contiguous(), dev[1], dev[2], dev[3]))
-        assert torch.equal(batched[i:i + 1], solo), i
+        assert_parity(_sub_call(ci, dev, [i]).cpu().numpy(), ref[i:i + 1], f"query {i} alone")
 
 
 @pytest.mark.parametrize("i8", [False, True])
@@ -118,21 +123,23 @@ def test_sliding_window_ring_at_serving_shape():
     _report("ring 8 x 1024", assert_parity(got, ref, "ring serving shape"))
 
 
-def _sub_call(ci, dev, rows, W=0, chunk=0):
+def _sub_call(ci, dev, rows, W=0, chunk=0, path=0):
     """The queries `rows` of a cache call on their own."""
     one = CacheInputs(ci.q[rows].clone(), ci.k, ci.v, ci.v_scales, tuple(ci.slot_ids[i] for i in rows),
                       tuple(ci.positions[i] for i in rows), ci.n_cache_slots, ci.capacity, ci.ring, ci.n_q_heads,
                       ci.n_kv_heads, ci.head_dim, ci.scale)
-    return run_gpu_cache(one, W, chunk=chunk, dev_tensors=(dev[0][rows].contiguous(), dev[1], dev[2], dev[3]))
+    return run_gpu_cache(one, W, chunk=chunk, dev_tensors=(dev[0][rows].contiguous(), dev[1], dev[2], dev[3]),
+                         path=path)
 
 
 @pytest.mark.parametrize("nq,nkv,i8", [(16, 8, False), (8, 8, True), (4, 4, False), (16, 2, True)])
 def test_draft_queries_share_a_workgroup_and_match_solo(nq, nkv, i8):
-    # 4 consecutive draft positions per slot.  G = 1 groups all four on the lanes; G = 2 makes
-    # 8 (draft, head) columns, a matrix-core workgroup; G = 8 is on the matrix cores anyway and
-    # groups pairs.  Every query equals the oracle; each slot's rows equal a call with that
-    # slot's queries alone bitwise (a query's kernel depends only on its own slot's queries),
-    # and a single query's call too where grouping does not change its kernel.
+    # 4 consecutive draft positions per slot.  G = 1 makes 4 (draft, head) columns and G = 2
+    # makes 8, a matrix-core workgroup either way (a single query needs 4 heads for that); G = 8
+    # is on the matrix cores anyway and groups pairs.  Every query equals the oracle; each
+    # slot's rows equal a call with that slot's queries alone bitwise (a query's kernel depends
+    # only on its own slot's queries), and a single query's call too where grouping does not
+    # change its kernel.  The same with the lane kernel forced, which groups up to 4 rows.
     sid = (0, 0, 0, 0, 1, 1, 1, 1, 2)
     pos = (3000, 3001, 3002, 3003, 700, 701, 702, 703, 50)
     G = nq // nkv
@@ -144,13 +151,18 @@ def test_draft_queries_share_a_workgroup_and_match_solo(nq, nkv, i8):
     for rows in ([0, 1, 2, 3], [4, 5, 6, 7], [8]):
         per_slot = _sub_call(ci, dev, rows)
         assert torch.equal(got[rows], per_slot), rows
-    kernel_changes = G < 8 and 4 * G >= 8      # the four drafts fill 8 matrix-core columns
+    kernel_changes = G < 4      # the four drafts fill 4 matrix-core columns, a lone query does not
     for i in range(len(sid)):
         solo = _sub_call(ci, dev, [i])
         if kernel_changes and i < 8:
             assert_parity(solo.cpu().numpy(), ref[i:i + 1], f"solo {i}")
         else:
             assert torch.equal(got[i:i + 1], solo), i
+    if G % 8:
+        lanes = run_gpu_cache(ci, 0, dev_tensors=dev, path=1)
+        _report(f"drafts G={G} lanes", assert_parity(lanes.cpu().numpy(), ref, "drafts on the lanes"))
+        for rows in ([0, 1, 2, 3], [4, 5, 6, 7], [8]):
+            assert torch.equal(lanes[rows], _sub_call(ci, dev, rows, path=1)), rows
 
 
 DRAFT_CASES = [
