@@ -17,36 +17,24 @@
 //  * S^T (16 keys x 16 heads) = K q^T on v_mfma_f32_16x16x32_f16: A = K rows
 //    (key l%16, 8 dims per lane per step, one 16-byte load), B = q.  fp16
 //    products are exact, the accumulation fp32.
-//  * O^T (dims x heads) += V^T P^T with both operands straight from
-//    registers.  Lane l loads keys 4(l/16) + j, j = 0..3, each EV consecutive
-//    dims starting at EV (l%16) (16 bytes); the S^T accumulator gives it P of
-//    the same four keys for head l%16.  Instruction e takes element e of the
-//    loads, so its row l%16 is dim EV (l%16) + e, the same for every lane with
-//    that l%16, and the accumulators cover every dim once.  Each V load reads
-//    4 keys x 16 EV contiguous bytes, whole cache lines; V is never staged in
-//    LDS.
-//    - On v_mfma_f32_16x16x16_f16 (fp16 V; int8 and codebook V up to head_dim
-//      256) A[l%16][4(l/16) + j] is element e of load j, so one product covers
-//      the 16 keys.  P and V enter as fp16 pairs hi + lo that carry about 22
-//      bits (int8 code x scale exactly), the products are exact and the
-//      accumulation fp32.
-//    - On v_mfma_f32_16x16x4_f32 (int8 and codebook V at head_dim 512, whose
-//      two-wave register budget the fp16 form overruns) step j takes load j as
-//      A[l%16][l/16] and P as B[l/16][l%16], with V dequantised to fp32.
-//  * At head_dim 512 with one-byte V (int8, codebook) two sibling workgroups
-//    share each chunk: both compute its
-//    scores and softmax (bitwise the same), each accumulates half the output
-//    dims.  That halves the accumulators and V buffers, which lets two waves
-//    share a SIMD; the second read of the K rows is served by the XCD's L2
-//    (siblings get neighbouring workgroup ids on one XCD).
+//  * O^T (dims x heads) += V^T P^T on v_mfma_f32_16x16x16_f16, with both
+//    operands straight from registers.  Lane l loads keys 4(l/16) + j,
+//    j = 0..3, each EV consecutive dims starting at EV (l%16) (16 bytes); the
+//    S^T accumulator gives it P of the same four keys for head l%16, which is
+//    the B operand B[4(l/16) + j][l%16].  The A operand A[l%16][4(l/16) + j]
+//    is then element e of load j, so instruction e covers the tile's 16 keys
+//    for dims EV (l%16) + e: the same for every lane with that l%16, and the
+//    accumulators cover every dim once.  Each V load reads 4 keys x 16 EV
+//    contiguous bytes, whole cache lines; V is never staged in LDS.  P and V
+//    enter as fp16 pairs hi + lo that carry about 22 bits (fp16 V as it is,
+//    int8 code x scale exactly), the products are exact and the accumulation
+//    fp32.
 //  * Accumulator o[b EV + e] lane l component r holds head l%16, dim
-//    DH p + BW b + 4 EV (l/16) + EV r + e (BW = 16 EV dims per load, DH the
-//    dims of one workgroup, p its part).
+//    BW b + 4 EV (l/16) + EV r + e (BW = 16 EV dims per load).
 //
 // Lane layouts (checked on gfx950 with one-wave probes): 16x16x32 f16:
 // A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]; 16x16x16 f16: A[l%16][4(l/16)+e],
-// B[4(l/16)+e][l%16]; 16x16x4 f32: A[l%16][l/16], B[l/16][l%16]; all three
-// C[4(l/16)+i][l%16].
+// B[4(l/16)+e][l%16]; both C[4(l/16)+i][l%16].
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -66,23 +54,19 @@ constexpr float kLazyMax = 8.f; // log2 headroom of the softmax reference before
 template <int D, int VF>
 struct MfmaGeometry {
     static_assert(D >= 128 && D <= 512, "head_dim 128..512");
-    static constexpr int DS = mfma_dim_split(D, VF != kVF16);            // workgroups sharing a chunk's keys
-    static constexpr int DH = D / DS;                                    // output dims of one workgroup
     static constexpr int KS = D / 32;                                    // QK steps = 16-byte K loads per lane
     static constexpr int EV = (VF == kVF16) ? 8 : (D >= 256 ? 16 : 8);   // V elements per lane per load
     static constexpr int BW = 16 * EV;                                   // dims covered by one load
-    static constexpr int NB = DH / BW;                                   // loads per key step
+    static constexpr int NB = D / BW;                                    // loads per key step
     static constexpr int VBYTES = EV * (VF == kVF16 ? 2 : 1);            // 16, or 8 (byte V at D = 128)
-    static constexpr int NO = NB * EV;                                   // f32x4 accumulators = DH / 16
-    static_assert(NO * 16 == DH, "accumulators cover every dim of the workgroup's part once");
+    static constexpr int NO = NB * EV;                                   // f32x4 accumulators = D / 16
+    static_assert(NO * 16 == D, "accumulators cover every dim once");
     static_assert(VF != kVCB || BW == (D < 256 ? D : 256), "one codebook norm block per load");
-    // Workgroups per CU the register allocation must allow.  Two (two waves per SIMD) for the
-    // split head_dim 512 kernels, which need the bound to fit, and for codebook V at 256, where
-    // it measured faster (4 x 32768, 16 q / 2 kv heads: 46.8 -> 45.5 us).  Elsewhere the
-    // compiler's own allocation: it already allows two waves at 256 and measured as fast or
-    // faster (int8 V, 32 q / 2 kv heads: 35.5 us against 37.1 with the bound); whole fp16 rows
-    // at 512 need more than half the register file (one wave per SIMD).
-    static constexpr int MIN_WG = ((D == 512 && DS == 2) || (D == 256 && VF == kVCB)) ? 2 : 1;
+    // Workgroups per CU the register allocation must allow: two (two waves per SIMD) for codebook
+    // V at 256, where the bound measured faster (4 x 32768, 16 q / 2 kv heads: 46.8 -> 45.5 us);
+    // elsewhere the compiler's own allocation, which allows two waves at 256 and one at 512
+    // (accumulators, K and V buffers need more than half the register file there).
+    static constexpr int MIN_WG = (D == 256 && VF == kVCB) ? 2 : 1;
 };
 
 template <int D, int VF>
@@ -112,7 +96,6 @@ template <int D, int VF>
 __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_partial_mfma_kernel(const LaunchArgs args) {
     using Geo = MfmaGeometry<D, VF>;
     constexpr int KS = Geo::KS, EV = Geo::EV, BW = Geo::BW, NB = Geo::NB, NO = Geo::NO;
-    constexpr int DS = Geo::DS, DH = Geo::DH;
     constexpr int CB_B = D < 256 ? D : 256;   // codebook norm block
     static_assert(kThreads == 256, "one thread per codebook table entry");
 
@@ -122,15 +105,14 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     const SlotDesc sd = args.slot[si];
     const int n_mem = sd.group_n;         // queries of the group (1 when alone); table entries si..
     const int local = item - sd.item_begin;
-    const int sub = local % args.n_sub;                 // head block sub / DS, dims part sub % DS
+    const int sub = local % args.n_sub;
     const int t = local / args.n_sub;
     const int c = t % sd.n_chunks;
     const int kvh = t / sd.n_chunks;
     const int cbeg = sd.lo + c * sd.chunk;
     const int cend = min(cbeg + sd.chunk, sd.L);
-    const int GB = args.G / (args.n_sub / DS);          // heads per query of this block
-    const int h0 = kvh * args.G + (sub / DS) * GB;      // first head of the block (in the slot)
-    const int dpart = DH * (sub % DS);                  // first output dim of this workgroup
+    const int GB = args.G / args.n_sub;                 // heads per query of this block
+    const int h0 = kvh * args.G + sub * GB;             // first head of the block (in the slot)
     const int64_t rowbase = sd.kv_row0 + (int64_t)kvh * sd.kv_stride;
 
     const int tid = threadIdx.x;
@@ -178,12 +160,8 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
         }
     }
 
-    // Codebook V up to head_dim 256 takes the fp16 products of P.V (below), with each table
-    // entry level[i & mask] / sqrt(B) as two fp16 terms (hi in the low half, lo in the high).
-    // The split head_dim 512 kernel keeps the fp32 products and an fp32 table: within its two-wave
-    // register budget the fp16 form spills more and measured slower (91.7 -> 94.3 us, 4 x 32768).
-    constexpr bool CB16 = VF == kVCB && D <= 256;
-    __shared__ uint32_t s_cb[VF == kVCB ? 256 : 1];   // bits of the fp16 pair, or of the fp32 level
+    // codebook V: level[i & mask] / sqrt(B) as two fp16 terms, hi in the low half, lo in the high
+    __shared__ uint32_t s_cb[VF == kVCB ? 256 : 1];
     __shared__ float s_m[kWaves][16], s_l[kWaves][16];
     __shared__ f32x4_t s_o[NO][64];                // one wave's accumulators, for the final merge
 
@@ -207,7 +185,7 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
             const int64_t row = row_of(kb + 4 * g + i);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const int d0 = dpart + BW * b + EV * c16;
+                const int d0 = BW * b + EV * c16;
                 if constexpr (VF == kVF16) {
                     f.v[i][b] = load_stream16((const uint16_t *)args.v + row * D + d0);
                 } else {
@@ -296,10 +274,12 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
                     o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pl, o[b * EV + e], 0, 0, 0);
                 }
             }
-        } else if constexpr (CB16) {
+        } else if constexpr (VF == kVCB) {
             // Codebook V on the same products.  The table gives each level as hi + lo (about 22
-            // bits); the block norm scales P, which is split the same way.  x p = xh ph + xh pl +
-            // xl ph, leaving out xl pl (about 2^-22 of the product).
+            // bits).  The 16 dims of one instruction lie in one norm block (min(D, 256) dims, one
+            // load), so the norm belongs to the key alone and scales P once per load, which is
+            // then split the same way.  x p = xh ph + xh pl + xl ph, leaving out xl pl (about
+            // 2^-22 of the product).
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 float pn[4];
@@ -327,7 +307,7 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
                     o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(xl, ph, o[b * EV + e], 0, 0, 0);
                 }
             }
-        } else if constexpr (VF == kVI8 && D <= 256) {
+        } else {
             // int8 V on the same products, exactly: the block scale is an fp16 value and the code
             // a small integer, so hi = fp16(code scale) and lo = fma(code, scale, -hi) (the
             // residual, exact in fp16) sum to code scale exactly.  Keys 0, 1 and 2, 3 of the lane
@@ -358,30 +338,6 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
                     o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(xl, ph, o[b * EV + e], 0, 0, 0);
                 }
             }
-        } else {
-            // head_dim 512 with one-byte V: V^T P^T on v_mfma_f32_16x16x4_f32, four key steps.
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    float x[EV];
-                    const uint32_t wd[4] = {vt.v[i][b].x, vt.v[i][b].y, vt.v[i][b].z, vt.v[i][b].w};
-#pragma unroll
-                    for (int e = 0; e < EV; ++e) {
-                        const uint32_t code = (wd[e / 4] >> (8 * (e % 4))) & 0xFF;
-                        if constexpr (VF == kVI8) x[e] = (float)(int8_t)code * vt.side[i][b];
-                        else x[e] = __builtin_bit_cast(float, s_cb[code]);
-                    }
-                    // Codebook V: the 16 rows (dims) of these instructions lie in one norm block
-                    // (BW = min(D, 256) dims), so the norm belongs to the key alone, the k index:
-                    // it scales P, the B operand, once per load instead of every element.
-                    float pb = p[i];
-                    if constexpr (VF == kVCB) pb *= vt.side[i][b];
-#pragma unroll
-                    for (int e = 0; e < EV; ++e)
-                        o[b * EV + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], pb, o[b * EV + e], 0, 0, 0);
-                }
-            }
         }
     };
 
@@ -396,8 +352,7 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     if constexpr (VF == kVCB) {
         const float x = args.codebook[tid & args.cb_mask] * args.cb_scale;
         const _Float16 h = (_Float16)x, lo = (_Float16)(x - (float)h);
-        s_cb[tid] = CB16 ? (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16)
-                         : __builtin_bit_cast(uint32_t, x);
+        s_cb[tid] = (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
     }
     if constexpr (VF == kVCB || QLDS) __syncthreads();
     // K: one buffer, refilled as soon as the QK steps have read it; V: two buffers.
@@ -456,12 +411,12 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     float *op;
     float scale_out = 1.f;
     if (m_nchunks == 1) {
-        op = args.out + qrow * D + dpart;
+        op = args.out + qrow * D;
         scale_out = (L == 0.f) ? 0.f : 1.f / L;
     } else {
         const int64_t prow = m_part + (int64_t)(h0 + hh) * m_nchunks + c;
-        op = args.ws_o + prow * D + dpart;
-        if (g == 0 && dpart == 0) {   // (M, S) are the same in every dims part
+        op = args.ws_o + prow * D;
+        if (g == 0) {
             args.ws_ml[prow * 2 + 0] = M;
             args.ws_ml[prow * 2 + 1] = L;
         }

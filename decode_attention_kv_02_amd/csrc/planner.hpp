@@ -65,20 +65,9 @@ struct SlotPlan {
     bool mfma = false;      // computed by the matrix-core partial kernel
 };
 
-// The matrix-core kernel at head_dim 512 with a one-byte V format (int8 or
-// codebook) splits each chunk's output dims between two sibling workgroups.
-// Each computes the chunk's scores and softmax (from the same K rows, which
-// the second reads from its XCD's L2) and accumulates its own D / 2 dims.
-// Half the accumulators and V buffers leave room for two waves per SIMD
-// instead of one, which hides the per-element decode: measured on MI355X
-// (4 x 32768, 16 q / 2 kv heads, codebook V) 105.7 -> 92.2 us.  With fp16 V
-// the loads already set the pace and the second K read costs more than the
-// second wave gains (103.2 -> 130.1 us), so fp16 stays whole.
-constexpr int mfma_dim_split(int head_dim, bool byte_v) { return head_dim == 512 && byte_v ? 2 : 1; }
 
 // How one partial kernel splits the work: query heads per workgroup (GB, dividing G),
-// n_sub workgroups per (query group, kv head, chunk): G / GB head blocks, times the
-// matrix-core kernel's dim split; queries per workgroup (QB).
+// G / GB workgroups per (query group, kv head, chunk), queries per workgroup (QB).
 struct KernelShape {
     int GB = 1;
     int n_sub = 1;
@@ -307,8 +296,9 @@ constexpr int kMfmaColumns = 16;      // (query, head) columns of one matrix-cor
 // lanes (graph-replayed): one query with 4 heads per kv head at head_dim 128, 8 x 8192, 53.4 ->
 // 46.3 us, codebook V at 256 146.1 -> 136.7 us, fp16 at 256 and 512 within 1%; 3 drafts x 2 heads
 // over 4 x 32768 329.0 -> 171.4 us (the lanes' groups hold at most 4 rows, so 6 rows took two
-// reads of the cache).  Eight at head_dim 512 with one-byte V, whose split kernel keeps the fp32
-// products: one int8 query with 4 heads ran 143.3 us on the lanes against 198.2 there.
+// reads of the cache).  Eight at head_dim 512 with one-byte V, where the matrix-core kernel runs
+// one wave per SIMD: one int8 query with 4 heads (8 x 32768) ran 143 us on the lanes against 164
+// there.
 inline int mfma_group_min_cols(int head_dim, bool byte_v) { return head_dim == 512 && byte_v ? 8 : 4; }
 
 // Builds the plan from the query spans; returns "" on success or an error message.
@@ -329,11 +319,11 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
     int mfma_qb_max = 1;
     if (plan.mfma) {
         plan.matrix.GB = G % 16 == 0 ? 16 : 8;
-        plan.matrix.n_sub = G / plan.matrix.GB * mfma_dim_split(head_dim, byte_v);
+        plan.matrix.n_sub = G / plan.matrix.GB;
         mfma_qb_max = kMfmaColumns / plan.matrix.GB;
     } else if (path == kPathAuto && head_dim >= 128 && G <= kMfmaColumns / 2) {
         plan.matrix.GB = G;             // draft groups: every head of the kv head, for each draft
-        plan.matrix.n_sub = mfma_dim_split(head_dim, byte_v);
+        plan.matrix.n_sub = 1;
         mfma_qb_max = kMfmaColumns / G;
     }
     // the matrix-core kernel always merges in the combine kernel

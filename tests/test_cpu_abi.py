@@ -108,8 +108,7 @@ def test_gqa_blocks_multiply_workgroups_for_large_groups():
     assert binding.attn_decode_plan([640], 0, 16, 2, 128)["partial_workgroups"] == 2 * 1 * 2
     assert binding.attn_decode_plan([640], 0, 64, 2, 128)["partial_workgroups"] == 2 * 2 * 2
     assert binding.attn_decode_plan([640], 0, 64, 2, 512)["partial_workgroups"] == 2 * 2 * 2
-    # with one-byte V at head_dim 512 each chunk's output dims are split between two workgroups
-    assert binding.attn_decode_plan([640], 0, 64, 2, 512, v_int8=True)["partial_workgroups"] == 2 * 2 * 2 * 2
+    assert binding.attn_decode_plan([640], 0, 64, 2, 512, v_int8=True)["partial_workgroups"] == 2 * 2 * 2
     assert binding.attn_decode_plan([640], 0, 64, 2, 256, v_int8=True)["partial_workgroups"] == 2 * 2 * 2
     assert binding.attn_decode_plan([640], 0, 48, 2, 256)["partial_workgroups"] == 2 * 3 * 2
     p = binding.attn_decode_plan([8192, 16384, 32768, 131072], 0, 16, 2, 256)

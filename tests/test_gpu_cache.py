@@ -175,7 +175,7 @@ DRAFT_CASES = [
     (16, 4, 256, True, 1, 4, 7),       # 4 x 4 = 16 columns, tiny chunks, ring
     (16, 2, 256, False, 0, 2, 0),      # 8 heads x 2 drafts (8 heads per kv head: pairs)
     (16, 8, 256, False, 0, 16, 0),     # 16 drafts: two groups of 8
-    (16, 4, 512, True, 1, 2, 0),       # one-byte V at 512: each group's dims split over two workgroups
+    (16, 4, 512, True, 1, 2, 0),       # one-byte V at 512, where a group needs 8 columns
 ]
 
 
