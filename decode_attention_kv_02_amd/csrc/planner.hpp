@@ -276,7 +276,7 @@ inline int heads_per_workgroup(int G) {
 // workgroup.  It applies to a whole call at a multiple of 8 query heads per kv
 // head and head_dim >= 128, where it measured faster than the lane kernel on
 // every shape (graph-replayed, fp16 / int8 / codebook V, head_dim 128..512:
-// 1.2x at 8 heads and 512, up to 2.7x at 16 heads and 128).  With fewer heads
+// 1.46x at 8 heads and 512, up to 2.7x at 16 heads and 128).  With fewer heads
 // per kv head, the draft queries of one slot (a speculative-verify step), or
 // one query alone, go to the matrix cores as one workgroup when they fill at
 // least mfma_group_min_cols columns (drafts x heads: 4, e.g. 2 drafts at 2
