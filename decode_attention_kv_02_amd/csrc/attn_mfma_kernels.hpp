@@ -160,7 +160,10 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
         }
     }
 
-    // codebook V: level[i & mask] / sqrt(B) as two fp16 terms, hi in the low half, lo in the high
+    // codebook V: 2^6 level[i & mask] / sqrt(B) as two fp16 terms, hi in the low half, lo in the
+    // high.  The 2^6 is taken back from the block norm that scales P (below).  With p <= 2^8 the
+    // pair p norm / 2^6 stays finite in fp16 for norms below 16376, and normal for weights
+    // p >= 2^-8 / norm; the table stays finite for levels below 8192.
     __shared__ uint32_t s_cb[VF == kVCB ? 256 : 1];
     __shared__ float s_m[kWaves][16], s_l[kWaves][16];
     __shared__ f32x4_t s_o[NO][64];                // one wave's accumulators, for the final merge
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
             for (int b = 0; b < NB; ++b) {
                 float pn[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pn[j] = p[j] * vt.side[j][b];
+                for (int j = 0; j < 4; ++j) pn[j] = p[j] * (vt.side[j][b] * (1.f / 64.f));
                 half4_t ph, pl;
                 split_f16(pn, ph, pl);
 #pragma unroll
@@ -310,7 +313,8 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
         } else {
             // int8 V on the same products, exactly: the block scale is an fp16 value and the code
             // a small integer, so hi = fp16(code scale) and lo = fma(code, scale, -hi) (the
-            // residual, exact in fp16) sum to code scale exactly.  Keys 0, 1 and 2, 3 of the lane
+            // residual, exact in fp16) sum to code scale exactly, for |code scale| up to 65504
+            // (V within fp16's range).  Keys 0, 1 and 2, 3 of the lane
             // go through packed fp16 arithmetic side by side, already in the A operand's order.
             half4_t ph, pl;
             split_f16(p, ph, pl);
@@ -350,7 +354,7 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
         load_v(cbeg + tl * kMfmaKeys, va);
     }
     if constexpr (VF == kVCB) {
-        const float x = args.codebook[tid & args.cb_mask] * args.cb_scale;
+        const float x = args.codebook[tid & args.cb_mask] * args.cb_scale * 64.f;
         const _Float16 h = (_Float16)x, lo = (_Float16)(x - (float)h);
         s_cb[tid] = (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
     }

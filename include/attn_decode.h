@@ -17,7 +17,9 @@
  *
  * The K cache is fp16.  The V cache is fp16, or ("hybrid" regime) symmetric
  * int8 codes in blocks of 32 consecutive dims along head_dim with one fp16
- * scale per block: V = code * scale, exact in fp32.
+ * scale per block: V = code * scale, exact in fp32.  Int8 values must lie
+ * within fp16's range (|code * scale| <= 65504): the matrix-core kernel
+ * carries them as exact pairs of fp16 values.
  *
  * Memory layout (all device memory unless stated otherwise, caller-owned):
  *   q        fp16  [n_slots][n_q_heads][head_dim], 16-byte aligned
@@ -184,6 +186,12 @@ int attn_decode_cache(const void *q, const void *k_cache, const void *v_cache,
  *             k_cache; 4-byte aligned
  *   codebook  fp32 [2^codebook_bits] levels, device memory; 4-byte aligned
  *   codebook_bits  1..8 (the pages use 5, 6 and 8)
+ * The matrix-core kernel carries levels and norm-scaled weights as pairs of
+ * fp16 values: levels must stay below 8192 in magnitude and block norms
+ * below 16376 (V of rms below about 1000 at 256 dims per block).  Below a
+ * norm of about 4 the weights of the less likely keys lose relative
+ * precision gradually (measured relative-L2 3e-4 at norm 0.01, under 1e-5
+ * from norm 1.6 up).
  * Everything else (q, k_cache, seq_lens, window, out, head_dim, asynchrony,
  * workspace, determinism, errors) is as for attn_decode; opts may be NULL.
  * out must not overlap v_norms or the codebook either.
