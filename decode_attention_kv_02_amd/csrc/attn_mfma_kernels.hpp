@@ -1,7 +1,7 @@
 // attn_mfma_kernels.hpp -- gfx950 partial kernel for up to 16 (query, head)
 // columns per workgroup, on the matrix cores: 8 or 16 query heads of one kv
-// head, or every head of the kv head for each of a slot's draft queries
-// (a speculative-verify step).
+// head, every head of the kv head for each of a slot's draft queries (a
+// speculative-verify step), or the 4 to 7 heads of one query.
 //
 // Same operation and partial format as attn_partial_kernel (one chunk of one
 // (slot, kv head): out = O / S, or O and (M, S) for the log-sum-exp merge;
@@ -121,8 +121,9 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     const int c16 = lane & 15;   // MFMA row / column of the lane
     const int g = lane >> 4;     // lane group
     // Column c16 is head h0 + c16 % GB of the group's query c16 / GB: GB = 8 or 16 heads of one
-    // query, or, for the draft queries of a speculative-verify step, every head of the kv head
-    // for each of up to 16 / GB drafts.  Each query masks the positions past its own end.
+    // query, or every head of the kv head (GB = G < 8) for each of up to 16 / GB queries of one
+    // slot (drafts of a speculative-verify step, or one query alone).  Each query masks the
+    // positions past its own end; columns past the group's queries compute and are not written.
     const int mem = c16 / GB;
     const bool head_ok = mem < n_mem;
     const int mi = si + (head_ok ? mem : 0);
