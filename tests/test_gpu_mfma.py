@@ -170,3 +170,39 @@ def test_matrix_core_codebook_bits(d, nq, nkv, bits, W):
     binding.attn_decode_cb(q, k, vc, vn, cb, bits, seq, W, out, len(seq), nq, nkv, d, ci.scale, path=2)
     torch.cuda.synchronize()
     _report(f"codebook {bits}-bit D={d} G={nq // nkv} W={W}", assert_parity(out.cpu().numpy(), ref, "codebook"))
+
+
+SMALL_G_CASES = [
+    # seq_lens, n_q, n_kv, D, V: one query with 4 to 7 heads per kv head goes to the matrix cores
+    # by itself (4 columns are enough where that kernel takes fp16 products)
+    ((3000, 1, 700), 32, 8, 128, "fp16"),
+    ((2500, 40), 24, 4, 256, "int8"),       # 6 heads
+    ((1800, 33), 20, 4, 512, "fp16"),       # 5 heads
+    ((999,), 28, 4, 256, "fp16"),           # 7 heads
+    ((2100, 700), 32, 8, 256, "codebook"),  # 4 heads
+]
+
+
+@pytest.mark.parametrize("case", SMALL_G_CASES, ids=[f"g{i}" for i in range(len(SMALL_G_CASES))])
+def test_one_query_with_four_to_seven_heads_on_the_matrix_cores(case):
+    seq, nq, nkv, d, fmt = case
+    # the matrix-core chunk rule (at least 512 positions) tells the planner's choice from the lanes' (64)
+    assert binding.attn_decode_plan(list(seq), 0, nq, nkv, d, v_int8=fmt != "fp16")["chunk"][0] == 512
+    dv = torch.device("cuda:0")
+    if fmt == "codebook":
+        ci = make_codebook_inputs(seq, nq, nkv, d, 8, 8100 + d)
+        ref = oracle_attn_decode_cb(ci.q.numpy(), ci.k.numpy(), ci.v_codes.numpy(), ci.v_norms.numpy(),
+                                    ci.codebook.numpy(), 8, seq, 0, nq, nkv, d, ci.scale)
+        q, k, vc, vn, cb = (t.to(dv) for t in (ci.q, ci.k, ci.v_codes, ci.v_norms, ci.codebook))
+        for path in (0, 1):
+            out = torch.full((len(seq), nq, d), float("nan"), dtype=torch.float32, device=dv)
+            binding.attn_decode_cb(q, k, vc, vn, cb, 8, seq, 0, out, len(seq), nq, nkv, d, ci.scale, path=path)
+            torch.cuda.synchronize()
+            _report(f"{case} path {path}", assert_parity(out.cpu().numpy(), ref, f"path {path}"))
+        return
+    inp = make_inputs(seq, nq, nkv, d, fmt == "int8", seed_base=8200 + d + nq)
+    ref = run_oracle(inp, 0)
+    dev = to_device(inp)
+    for path in (0, 1):
+        _report(f"{case} path {path}", assert_parity(_run(inp, 0, path=path, dev=dev).cpu().numpy(), ref,
+                                                     f"path {path}"))
