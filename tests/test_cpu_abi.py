@@ -9,6 +9,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 from decode_attention_kv_02_amd import binding
@@ -76,6 +77,54 @@ def test_plan_of_a_slot_does_not_depend_on_its_batch():
         solo = binding.attn_decode_plan([L], 0, 16, 8, 256)
         assert solo["chunk"][0] == batched["chunk"][i]
         assert solo["n_chunks"][0] == batched["n_chunks"][i]
+
+
+def _expected_kernel_split(G, d, byte_v, empty):
+    """(matrix cores?, workgroups per chunk) of one single-query slot, by the rule the planner
+    states: the matrix cores at a multiple of 8 heads per kv head (blocks of 16, else 8), or at 4
+    or more heads (8 at head_dim 512 with one-byte V) as one block for a slot with something to
+    attend; head_dim >= 128 either way; else the lanes in blocks of 4, 2 or 1 heads."""
+    if d >= 128 and G % 8 == 0:
+        return True, G // (16 if G % 16 == 0 else 8)
+    if d >= 128 and G <= 8 and G >= (8 if (d == 512 and byte_v) else 4) and not empty:
+        return True, 1
+    gb = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+    return False, G // gb
+
+
+def test_random_plans_keep_their_invariants():
+    """Seeded random shapes through the host planner: the chunks of every slot tile its attended
+    range, a slot's plan is the same alone and in the batch, and the workgroup and workspace
+    counts follow the kernel choice."""
+    rng = np.random.default_rng(2024)
+    for _ in range(300):
+        n_kv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 16, 32]))
+        d = int(rng.choice([64, 128, 256, 512]))
+        byte_v = bool(rng.integers(0, 2))
+        n = int(rng.integers(1, 9))
+        seq = [int(x) for x in rng.choice([0, 1, 17, 64, 1000, 4096, 4097, 20000, 131072], n)]
+        seq = [L if rng.random() < 0.5 else int(rng.integers(0, 70000)) for L in seq]
+        W = 0 if rng.random() < 0.6 else int(rng.integers(1, 5000))
+        p = binding.attn_decode_plan(seq, W, n_kv * G, n_kv, d, v_int8=byte_v)
+        items, rows = 0, 0
+        for i, L in enumerate(seq):
+            c, nc = p["chunk"][i], p["n_chunks"][i]
+            span = L - _lo(L, W)
+            mfma, n_sub = _expected_kernel_split(G, d, byte_v, span == 0)
+            assert 1 <= nc <= 4096
+            if span == 0:
+                assert nc == 1
+            else:
+                assert 1 <= c and (nc - 1) * c < span <= nc * c, (seq, W, i)
+            solo = binding.attn_decode_plan([L], W, n_kv * G, n_kv, d, v_int8=byte_v)
+            assert (solo["chunk"][0], solo["n_chunks"][0]) == (c, nc), (seq, W, i)
+            items += n_kv * n_sub * nc
+            rows += n_kv * G * nc if nc > 1 else 0
+            if mfma and span > 0 and nc > 1:
+                assert c % 64 == 0 and c >= 512 or c >= span, (G, d, byte_v, L, c)
+        assert p["partial_workgroups"] == items, (G, d, byte_v, seq, W)
+        assert p["workspace_bytes"] == rows * (d + 2) * 4
 
 
 def test_forced_chunk_is_used_and_still_bounded():
