@@ -33,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "attn_decode_cb",
     "attn_decode_ex",
     "attn_decode_plan",
+    "attn_decode_cache_plan",
     "attn_decode_last_error",
     "attn_decode_release",
     "attn_fwht_undo",
@@ -121,6 +122,11 @@ def load_library():
             ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p]
+        lib.attn_decode_cache_plan.restype = ctypes.c_int
+        lib.attn_decode_cache_plan.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.attn_decode_last_error.restype = ctypes.c_char_p
         lib.attn_decode_last_error.argtypes = []
         lib.attn_decode_release.restype = ctypes.c_int
@@ -464,6 +470,37 @@ def attn_decode_plan(seq_lens, window: int, n_q_heads: int, n_kv_heads: int, hea
         _raise(lib, rc)
     return {"chunk": ck[:n].tolist(), "n_chunks": nc[:n].tolist(), "workspace_bytes": ws.value,
             "partial_workgroups": items.value}
+
+
+_V_FORMATS = {"fp16": 0, "int8": 1, "codebook": 2}
+
+
+def attn_decode_cache_plan(slot_ids, positions, n_cache_slots: int, capacity: int, ring: int, window: int,
+                           n_q_heads: int, n_kv_heads: int, head_dim: int, v_format: str = "fp16",
+                           chunk: int = 0) -> dict:
+    """The host planner alone for a cache call (no GPU needed): per query its chunk, chunk count,
+    partial kernel ("lanes" or "matrix") and query-group leader."""
+    lib = load_library()
+    if v_format not in _V_FORMATS:
+        raise ValueError(f"v_format must be one of {sorted(_V_FORMATS)}")
+    sid, n = _seq_array(slot_ids)
+    pos, n2 = _seq_array(positions)
+    if n != n2:
+        raise ValueError("slot_ids / positions differ in length")
+    ck, nc, kern, lead = (np.zeros(max(n, 1), dtype=np.int32) for _ in range(4))
+    ws = ctypes.c_int64(0)
+    items = ctypes.c_int64(0)
+    rc = lib.attn_decode_cache_plan(sid, pos, n,
+                                    int(n_cache_slots), int(capacity), int(ring), int(window), int(n_q_heads),
+                                    int(n_kv_heads), int(head_dim), _V_FORMATS[v_format], int(chunk),
+                                    ck.ctypes.data_as(ctypes.c_void_p), nc.ctypes.data_as(ctypes.c_void_p),
+                                    kern.ctypes.data_as(ctypes.c_void_p), lead.ctypes.data_as(ctypes.c_void_p),
+                                    ctypes.byref(ws), ctypes.byref(items))
+    if rc != ATTN_DECODE_OK:
+        _raise(lib, rc)
+    return {"chunk": ck[:n].tolist(), "n_chunks": nc[:n].tolist(),
+            "kernel": ["matrix" if k else "lanes" for k in kern[:n]], "group_leader": lead[:n].tolist(),
+            "workspace_bytes": ws.value, "partial_workgroups": items.value}
 
 
 def attn_decode_release() -> None:

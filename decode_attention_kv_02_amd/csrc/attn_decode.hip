@@ -679,6 +679,36 @@ extern "C" int attn_decode_plan(const int32_t *seq_lens, int32_t n_slots, int32_
     return ATTN_DECODE_OK;
 }
 
+extern "C" int attn_decode_cache_plan(const int32_t *slot_ids, const int32_t *positions, int32_t n_queries,
+                                      int32_t n_cache_slots, int32_t capacity, int32_t ring, int32_t window,
+                                      int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t v_format,
+                                      int32_t chunk, int32_t *chunk_keys, int32_t *n_chunks, int32_t *kernel,
+                                      int32_t *group_leader, int64_t *workspace_bytes,
+                                      int64_t *n_partial_workgroups) {
+    g_last_error.clear();
+    if (v_format < kVF16 || v_format > kVCB)
+        return fail(ATTN_DECODE_EINVAL, "v_format must be 0 (fp16), 1 (int8) or 2 (codebook)");
+    if (n_cache_slots < 0) return fail(ATTN_DECODE_EINVAL, "n_cache_slots must be >= 0");
+    std::string err = check_common(n_q_heads, n_kv_heads, head_dim, v_format == kVI8, window, chunk, 0);
+    if (err.empty()) err = check_cache(slot_ids, positions, n_queries, n_cache_slots, capacity, ring);
+    if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
+    CallPlan plan;
+    std::vector<QuerySpan> spans;
+    spans_cache(slot_ids, positions, n_queries, capacity, ring, window, n_kv_heads, spans);
+    err = make_plan(spans, n_q_heads, n_kv_heads, head_dim, chunk, kMergeAuto, plan, kPathAuto, v_format != kVF16);
+    if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
+    for (int32_t i = 0; i < n_queries; ++i) {
+        const SlotPlan &sp = plan.slots[i];
+        if (chunk_keys) chunk_keys[i] = sp.chunk;
+        if (n_chunks) n_chunks[i] = sp.n_chunks;
+        if (kernel) kernel[i] = sp.mfma ? 1 : 0;
+        if (group_leader) group_leader[i] = sp.group_n > 0 ? i : sp.leader;
+    }
+    if (workspace_bytes) *workspace_bytes = plan.workspace_bytes;
+    if (n_partial_workgroups) *n_partial_workgroups = plan.total_items;
+    return ATTN_DECODE_OK;
+}
+
 extern "C" const char *attn_decode_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" int attn_decode_release(void) {

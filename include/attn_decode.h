@@ -307,6 +307,25 @@ int attn_decode_plan(const int32_t *seq_lens, int32_t n_slots, int32_t window,
                      int32_t *n_chunks, int64_t *workspace_bytes,
                      int64_t *n_partial_workgroups);
 
+/*
+ * attn_decode_cache_plan -- the host planner alone for the query rows of an
+ * attn_decode_cache / attn_decode_cache_cb call (no HIP call, usable without a
+ * GPU).  Arguments are those of the call (slot_ids and positions are host
+ * arrays of n_queries) plus v_format: 0 fp16 V, 1 int8 V, 2 codebook V.  Per
+ * query it writes the KV positions per chunk, the number of chunks, the partial
+ * kernel that computes it (0 the lane kernel, 1 the matrix-core kernel) and the
+ * leader of its query group (its own index when it leads a group or is alone):
+ * arrays of n_queries, each may be NULL.  It also writes the workspace bytes
+ * and the number of partial-kernel workgroups (may be NULL).  Returns 0 or
+ * ATTN_DECODE_EINVAL for shapes attn_decode_cache would reject.
+ */
+int attn_decode_cache_plan(const int32_t *slot_ids, const int32_t *positions, int32_t n_queries,
+                           int32_t n_cache_slots, int32_t capacity, int32_t ring, int32_t window,
+                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t v_format,
+                           int32_t chunk, int32_t *chunk_keys, int32_t *n_chunks, int32_t *kernel,
+                           int32_t *group_leader, int64_t *workspace_bytes,
+                           int64_t *n_partial_workgroups);
+
 /* Message describing the last non-zero return on this host thread ("" if none). */
 const char *attn_decode_last_error(void);
 

@@ -290,3 +290,75 @@ def test_cache_codebook_attention_rejects_before_any_gpu_work(kw, frag):
     rc, msg = _cache_cb(**kw)
     assert rc == binding.ATTN_DECODE_EINVAL
     assert frag in msg, msg
+
+
+# ------------------------------------------------------------------ planner, cache calls
+
+def test_cache_plan_groups_drafts_by_columns():
+    """Which kernel a cache call's queries get and how they are grouped: a slot's drafts that
+    fill 4 (query, head) columns share one matrix-core workgroup (8 at head_dim 512 with one-byte
+    V), led by the longest; fewer go to the lanes, whose groups hold up to 4 rows."""
+    cp = binding.attn_decode_cache_plan
+    # the verify preset: 4 slots x 4 drafts x 2 heads = 8 columns per slot
+    p = cp([s for s in range(4) for _ in range(4)], [32764, 32765, 32766, 32767] * 4, 4, 32768, 0, 0, 16, 8, 256)
+    assert p["kernel"] == ["matrix"] * 16
+    assert p["group_leader"] == [3] * 4 + [7] * 4 + [11] * 4 + [15] * 4
+    assert p["partial_workgroups"] == 4 * 8 * 32          # one read per (slot, kv head, chunk)
+    # 3 drafts x 2 heads = 6 columns: one matrix-core group (on the lanes' 4-row groups: two reads)
+    p = cp([0, 0, 0], [3000, 3001, 3002], 1, 4096, 0, 0, 16, 8, 256)
+    assert p["kernel"] == ["matrix"] * 3 and p["group_leader"] == [2, 2, 2]
+    # 2 drafts x 1 head = 2 columns: a 2-row lane group
+    p = cp([0, 0], [3000, 3001], 1, 4096, 0, 0, 8, 8, 256)
+    assert p["kernel"] == ["lanes"] * 2 and p["group_leader"] == [1, 1]
+    # one query with 4 heads per kv head: the matrix cores, except at 512 with one-byte V
+    assert cp([0], [3000], 1, 4096, 0, 0, 16, 4, 512)["kernel"] == ["matrix"]
+    assert cp([0], [3000], 1, 4096, 0, 0, 16, 4, 512, "int8")["kernel"] == ["lanes"]
+    assert cp([0], [3000], 1, 4096, 0, 0, 16, 4, 512, "codebook")["kernel"] == ["lanes"]
+    assert cp([0, 0], [3000, 3001], 1, 4096, 0, 0, 16, 4, 512, "int8")["kernel"] == ["matrix"] * 2
+    # queries of different slots never share a workgroup; two heads alone stay on the lanes
+    p = cp([0, 1], [100, 100], 2, 4096, 0, 0, 16, 8, 256)
+    assert p["kernel"] == ["lanes"] * 2 and p["group_leader"] == [0, 1]
+    # drafts that start their window at different positions do not group
+    p = cp([0, 0], [3000, 3001], 1, 4096, 0, 1000, 16, 8, 256)
+    assert p["group_leader"] == [0, 1]
+
+
+def test_cache_plan_of_a_slot_does_not_depend_on_the_other_slots():
+    """Seeded random batches of draft queries over a ring or linear cache: every slot's queries
+    get the same chunks, kernels and groups in the batch as in a call of their own."""
+    rng = np.random.default_rng(7)
+    cp = binding.attn_decode_cache_plan
+    for _ in range(200):
+        n_kv = int(rng.choice([1, 2, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 8]))
+        d = int(rng.choice([64, 128, 256, 512]))
+        fmt = str(rng.choice(["fp16", "int8", "codebook"]))
+        cap = int(rng.choice([512, 4096, 40000]))
+        ring = int(rng.integers(0, 2))
+        W = 0 if rng.random() < 0.7 else int(rng.integers(1, 3000))
+        n_cs = int(rng.integers(1, 5))
+        sid, pos = [], []
+        for s_ in range(n_cs):
+            nd = int(rng.integers(0, 6))
+            start = int(rng.integers(0, cap * (3 if ring else 1) - 8))
+            sid += [s_] * nd
+            pos += [start + t for t in range(nd)]
+        if not sid:
+            continue
+        p = cp(sid, pos, n_cs, cap, ring, W, n_kv * G, n_kv, d, fmt)
+        for s_ in set(sid):
+            rows = [i for i in range(len(sid)) if sid[i] == s_]
+            alone = cp([sid[i] for i in rows], [pos[i] for i in rows], n_cs, cap, ring, W, n_kv * G, n_kv, d, fmt)
+            for k in ("chunk", "n_chunks", "kernel"):
+                assert [p[k][i] for i in rows] == alone[k], (k, sid, pos, s_)
+            # the same groups: leaders map to the same positions within the slot's rows
+            assert [rows.index(p["group_leader"][i]) for i in rows] == alone["group_leader"]
+
+
+def test_cache_plan_rejects_bad_arguments():
+    with pytest.raises(ValueError, match="v_format"):
+        binding.attn_decode_cache_plan([0], [1], 1, 16, 0, 0, 2, 1, 64, "int4")
+    with pytest.raises(binding.AttnDecodeError, match="slot_ids"):
+        binding.attn_decode_cache_plan([3], [1], 2, 16, 0, 0, 2, 1, 64)
+    with pytest.raises(binding.AttnDecodeError, match="capacity"):
+        binding.attn_decode_cache_plan([0], [16], 1, 16, 0, 0, 2, 1, 64)
