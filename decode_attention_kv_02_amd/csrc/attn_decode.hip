@@ -519,19 +519,37 @@ int run_append(const float *k_new, const float *v_new, void *k_cache, const Appe
     args.inv_sqrt_d = (float)(1.0 / std::sqrt((double)D));
     args.n_kv = n_kv;
     args.capacity = capacity;
-    for (int32_t r0 = 0; r0 < n_rows; r0 += kAppendMaxRows) {
-        const int32_t nr = std::min<int32_t>(kAppendMaxRows, n_rows - r0);
-        args.n_rows = nr;
+    // Rows go out as runs (consecutive cache rows of one slot), up to kAppendMaxRuns runs and
+    // kAppendMaxLaunchRows rows per launch.
+    constexpr int32_t kAppendMaxLaunchRows = 1 << 20;
+    auto cache_row = [&](int32_t i) {
+        const int32_t p = positions[i];
+        return (int64_t)slot_ids[i] * n_kv * capacity + (ring ? p % capacity : p);
+    };
+    int32_t r0 = 0;
+    while (r0 < n_rows) {
         args.row0 = r0;
-        for (int32_t i = 0; i < nr; ++i) {
-            const int32_t p = positions[r0 + i];
-            const int64_t phys = ring ? p % capacity : p;
-            args.cache_row[i] = (int64_t)slot_ids[r0 + i] * n_kv * capacity + phys;
+        int32_t nr = 0, runs = 0;
+        int64_t next = -1;   // cache row that would continue the current run
+        while (r0 + nr < n_rows && nr < kAppendMaxLaunchRows) {
+            const int64_t cr = cache_row(r0 + nr);
+            const bool same_run = runs > 0 && cr == next && slot_ids[r0 + nr] == slot_ids[r0 + nr - 1];
+            if (!same_run) {
+                if (runs == kAppendMaxRuns) break;
+                args.run[runs].cache_row0 = cr;
+                args.run[runs].row_begin = nr;
+                ++runs;
+            }
+            next = cr + 1;
+            ++nr;
         }
+        args.n_rows = nr;
+        args.n_runs = runs;
         const int64_t units = (int64_t)nr * n_kv;
         hipLaunchKernelGGL(fn, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, args);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("append kernel launch: ") + hipGetErrorString(e));
+        r0 += nr;
     }
     return ATTN_DECODE_OK;
 }

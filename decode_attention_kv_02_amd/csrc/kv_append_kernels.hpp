@@ -34,7 +34,16 @@
 
 namespace attn_decode_impl {
 
-constexpr int kAppendMaxRows = 480;   // rows per launch (row table passed by value, < 4 KiB)
+// New rows reach the kernel as runs: rows of one slot whose cache rows follow one another
+// (consecutive positions, no ring wrap).  A decode step is one run per slot; appending a
+// prompt's rows to one slot is one run, two across a ring wrap.
+constexpr int kAppendMaxRuns = 240;   // runs per launch (run table passed by value, < 4 KiB)
+
+struct AppendRun {
+    int64_t cache_row0;   // (slot * n_kv) * capacity + physical row of the run's first row
+    int32_t row_begin;    // the run's first row, counted from the launch's first row
+    int32_t pad;
+};
 
 struct AppendArgs {
     const float *k_new;        // [n_rows][n_kv][D]
@@ -51,7 +60,9 @@ struct AppendArgs {
     int32_t n_kv;
     int32_t capacity;
     int32_t row0;              // index of the launch's first row in k_new / v_new
-    int64_t cache_row[kAppendMaxRows];  // (slot * n_kv) * capacity + physical row, per new row
+    int32_t n_runs;            // runs in this launch (run i covers rows [row_begin_i, row_begin_i+1))
+    int32_t pad0;
+    AppendRun run[kAppendMaxRuns];
 };
 
 __device__ __forceinline__ float lane_max_xor(float x, int mask) {
@@ -147,8 +158,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs args) {
     const int lane = threadIdx.x & 63;
     const int r = unit / args.n_kv;
     const int h = unit - r * args.n_kv;
+    int lo = 0, hi = args.n_runs - 1;   // the run holding row r: largest row_begin <= r
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (args.run[mid].row_begin <= r) lo = mid; else hi = mid - 1;
+    }
     const int64_t src = ((int64_t)(args.row0 + r) * args.n_kv + h) * D + lane * E;
-    const int64_t dst_row = args.cache_row[r] + (int64_t)h * args.capacity;
+    const int64_t dst_row = args.run[lo].cache_row0 + (r - args.run[lo].row_begin) + (int64_t)h * args.capacity;
 
     float kx[E], vx[E];
     load_f32<E>(args.k_new + src, kx);
