@@ -836,10 +836,10 @@ def main(argv=None) -> int:
             a_sid = np.asarray(aw.slot_ids, dtype=np.int32)
             a_pos = np.asarray(aw.positions, dtype=np.int32)
 
-            def append_call():
+            def append_call(st=None):
                 binding.attn_kv_append(kn, vn, kc, vc, sc, a_sid, a_pos, aw.n_rows,
                                        aw.n_cache_slots, aw.capacity, aw.ring, aw.n_kv_heads, d,
-                                       stream=stream)
+                                       stream=st or stream)
 
             def per_call_us(fn, n):
                 torch.cuda.synchronize()
@@ -853,13 +853,18 @@ def main(argv=None) -> int:
                 append_call()
             nb = n_el * 8 + n_el * (2 + (1 + 2 / 32 if aw.v_int8 else 2))
             warm = statistics.median(per_call_us(append_call, args.reps) for _ in range(3))
+            g_us = graph_us_per_call(lambda st: append_call(st=st))
             per.append({
                 "workload": aw.name, "window": 0, "bytes": int(nb),
                 "warm_us_per_call": round(warm, 2),
                 "warm_gbs": round(nb / (warm * 1e-6) / 1e9, 1),
                 "warm_hbm_frac": round(nb / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "graph_us_per_call": round(g_us, 2),
+                "graph_gbs": round(nb / (g_us * 1e-6) / 1e9, 1),
+                "graph_hbm_frac": round(nb / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             })
-            print(f"[bench] {aw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s)", file=sys.stderr, flush=True)
+            print(f"[bench] {aw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), graph {g_us:.2f} us "
+                  f"({per[-1]['graph_gbs']} GB/s)", file=sys.stderr, flush=True)
             del kc, vc, sc, kn, vn
             torch.cuda.empty_cache()
         result["per_config"] = per

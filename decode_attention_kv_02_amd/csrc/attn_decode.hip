@@ -457,13 +457,25 @@ int run_append(const float *k_new, const float *v_new, void *k_cache, const Appe
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
     if (n_rows == 0) return ATTN_DECODE_OK;
 
-    // every new row must land on its own cache row
-    std::vector<std::pair<int32_t, int32_t>> dst(n_rows);
-    for (int32_t i = 0; i < n_rows; ++i)
-        dst[i] = std::make_pair(slot_ids[i], ring ? positions[i] % capacity : positions[i]);
-    std::sort(dst.begin(), dst.end());
-    for (int32_t i = 1; i < n_rows; ++i)
-        if (dst[i] == dst[i - 1]) return fail(ATTN_DECODE_EINVAL, "two new rows land on the same cache row");
+    // every new row must land on its own cache row: rows in increasing (slot, cache row) order
+    // (a prompt, or one token for each of several slots) pass in one pass; any other order is sorted
+    auto dst_of = [&](int32_t i) {
+        return std::make_pair(slot_ids[i], ring ? positions[i] % capacity : positions[i]);
+    };
+    bool increasing = true;
+    if (ring) {
+        for (int32_t i = 1; i < n_rows && increasing; ++i) increasing = dst_of(i - 1) < dst_of(i);
+    } else {   // linear storage: the row is the position
+        for (int32_t i = 1; i < n_rows; ++i)
+            increasing &= slot_ids[i - 1] < slot_ids[i] || (slot_ids[i - 1] == slot_ids[i] && positions[i - 1] < positions[i]);
+    }
+    if (!increasing) {
+        std::vector<std::pair<int32_t, int32_t>> dst(n_rows);
+        for (int32_t i = 0; i < n_rows; ++i) dst[i] = dst_of(i);
+        std::sort(dst.begin(), dst.end());
+        for (int32_t i = 1; i < n_rows; ++i)
+            if (dst[i] == dst[i - 1]) return fail(ATTN_DECODE_EINVAL, "two new rows land on the same cache row");
+    }
 
     const uint64_t rows = (uint64_t)n_cache_slots * (uint64_t)n_kv * (uint64_t)capacity;
     const uint64_t kv_elems = rows * (uint64_t)D;

@@ -258,6 +258,10 @@ def _append_cb(**kw):
     (dict(cb=NM), "signs / codebook overlaps"),
     (dict(n=KC + 8), "overlap"),
     (dict(sid=[0, 0], pos=[1, 5], ring=1), "same cache row"),
+    (dict(sid=[0, 0], pos=[2, 2]), "same cache row"),
+    (dict(sid=[0, 0, 0], pos=[1, 3, 1]), "same cache row"),
+    (dict(sid=[1, 0, 1], pos=[3, 1, 3], slots=2), "same cache row"),
+    (dict(sid=[0, 0, 0], pos=[0, 1, 4], ring=1), "same cache row"),
     (dict(pos=[4]), "capacity"),
 ])
 def test_codebook_append_rejects_before_any_gpu_work(kw, frag):
