@@ -129,19 +129,31 @@ inline int64_t target_chunks(int64_t n) {
     return 16;
 }
 
-// Above 4096 positions a chunk also carries at least 64 KiB of fp16 K and V per
-// kv head (65536 / head_dim positions): slots that long usually come in
+// Above 4096 positions a chunk also carries at least 256 KiB of fp16 K and V
+// per kv head (65536 / head_dim positions): slots that long usually come in
 // batches, where fine chunks leave each workgroup too little work for its
 // fixed cost.  Measured with forced chunks (lane kernel, graph-replayed):
 // 8 x 8192 at head_dim 128 with 4 heads per kv head 83.5 us at 128 positions,
 // 54.9 at 512; at head_dim 64 68.9 -> 36.0 us (1024); 8 x 8192 int8 V at 256
 // 82.2 -> 73.4 us (256), while a lone 8192 slot moves by 0.3-2 us.  Lone
 // slots of 4096 or less (1 x 4096: 12.0 us at 64 positions, 14.4 at 256)
-// keep the fine split.
+// keep the fine split, down to 64 KiB of K and V per chunk and kv head
+// (64 positions at head_dim 256, 128 at 128, 256 at 64).  Below that floor
+// batches lose to the workgroups' fixed cost: at head_dim 128, 16 x 2048 took
+// 38.3 us in 64-position chunks and 29.6 in 128-position ones, 8 x 4096 37.6
+// and 29.8; at head_dim 64 16 x 2048 took 22.0 us and 18.0 in 256-position
+// chunks.  A lone 2048 slot moves by +0.1 / +0.3 us there, a lone 4096 slot
+// gains 0.6-0.9 us.
 constexpr int64_t kLongSlot = 4096;
-constexpr int64_t kMinChunkKVBytes = 65536;   // fp16 K + V bytes per kv head: chunk * 2 * head_dim * 2
+// floors of fp16 K + V bytes per chunk and kv head (chunk * 2 * head_dim * 2)
+constexpr int64_t kMinLongChunkKVBytes = 262144;   // slots of more than kLongSlot positions
+constexpr int64_t kMinShortChunkKVBytes = 65536;   // the others
 
-inline int64_t min_chunk_long(int32_t head_dim) { return kMinChunkKVBytes / (4 * (int64_t)head_dim) * 4; }
+inline int64_t min_chunk_long(int32_t head_dim) { return kMinLongChunkKVBytes / (4 * (int64_t)head_dim); }
+inline int64_t min_chunk_short(int32_t head_dim) {
+    const int64_t c = kMinShortChunkKVBytes / (4 * (int64_t)head_dim);
+    return (c + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
+}
 
 // A slot whose fp16 K and V rows of one kv head fit in this many bytes is not
 // split: one workgroup streams it in about the time of the first-load latency,
@@ -176,6 +188,7 @@ inline int64_t chunk_for(int64_t n, int32_t head_dim, int32_t forced, bool mfma 
         c = ceil_div(c, kChunkQuantum) * kChunkQuantum;
         if (c < kChunkMin) c = kChunkMin;
         if (n > kLongSlot && c < min_chunk_long(head_dim)) c = min_chunk_long(head_dim);
+        if (n <= kLongSlot && c < min_chunk_short(head_dim)) c = min_chunk_short(head_dim);
         if (c > kChunkMax) c = kChunkMax;
     }
     const int64_t floor_c = ceil_div(n, kMaxChunks);

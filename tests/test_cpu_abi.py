@@ -145,13 +145,27 @@ def test_one_query_with_four_heads_per_kv_head_goes_to_the_matrix_cores():
     assert binding.attn_decode_plan([4096], 0, 32, 8, 512)["chunk"] == [512]
     assert binding.attn_decode_plan([4096], 0, 32, 8, 512, v_int8=True)["chunk"] == [64]
     assert binding.attn_decode_plan([4096], 0, 16, 8, 256)["chunk"] == [64]
-    assert binding.attn_decode_plan([4096], 0, 32, 8, 64)["chunk"] == [64]   # head_dim 64: lanes only
+    assert binding.attn_decode_plan([4096], 0, 32, 8, 64)["chunk"] == [256]   # head_dim 64: lanes only
+
+
+@pytest.mark.parametrize("D,floor", [(64, 256), (128, 128), (256, 64), (512, 64)])
+def test_lane_chunks_of_short_slots_carry_at_least_64_kib(D, floor):
+    # a split slot of at most 4096 positions: 64-position chunks where they hold 64 KiB of
+    # fp16 K and V per kv head, else the floor that does; slots whose K and V fit 128 KiB
+    # stay whole
+    whole = 131072 // (4 * D)
+    for L in (whole + 1, 1000, 2048, 3000, 4096):
+        c = binding.attn_decode_plan([L], 0, 16, 8, D)["chunk"][0]
+        assert c == min(max(64, floor), L), (D, L, c)
+        assert c * 4 * D >= 65536 or c == L
+    assert binding.attn_decode_plan([whole], 0, 16, 8, D)["n_chunks"] == [1]
 
 
 def test_gqa_blocks_multiply_workgroups_for_large_groups():
     # lane kernel: G = 3 as three single heads; G = 8 at head_dim 64 as two blocks of 4
-    assert binding.attn_decode_plan([640], 0, 6, 2, 128)["partial_workgroups"] == 2 * 3 * 10
-    assert binding.attn_decode_plan([2560], 0, 16, 2, 64)["partial_workgroups"] == 2 * 2 * 40
+    # (chunks of 128 positions at head_dim 128, 256 at 64)
+    assert binding.attn_decode_plan([640], 0, 6, 2, 128)["partial_workgroups"] == 2 * 3 * 5
+    assert binding.attn_decode_plan([2560], 0, 16, 2, 64)["partial_workgroups"] == 2 * 2 * 10
     # matrix-core kernel, automatic for 8k heads per kv head at head_dim >= 128: blocks of 16, else 8,
     # and chunks of at least 512 positions (640 -> 2 chunks)
     assert binding.attn_decode_plan([640], 0, 16, 2, 128)["partial_workgroups"] == 2 * 1 * 2
