@@ -83,6 +83,8 @@ EDGE = [
     ((63, 64, 65, 4095, 4096, 4097), 16, 8, 256, False, 0),
     ((5000, 3000, 1), 32, 2, 256, True, 0),     # G = 16: four head blocks per chunk
     ((9000, 700), 16, 2, 512, False, 0),        # G = 8 at D = 512
+    ((4096, 1000, 513, 512), 8, 8, 64, True, 0),   # 256-position chunks at D = 64, ragged tails
+    ((4096, 3001, 257), 16, 8, 128, False, 0),     # 128-position chunks at D = 128
 ]
 
 
