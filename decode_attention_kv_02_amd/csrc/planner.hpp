@@ -118,13 +118,15 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // get long chunks, because every workgroup pays a fixed cost (first-load
 // latency, the lane/wave merge, a partial row per head) and the combine reads
 // one partial row per chunk.  Measured on MI355X with forced chunk sizes
-// (warm, back-to-back calls): 1 x 4096 and a 1024-position window run fastest
-// at 64 positions per chunk, 1 x 131072 at 2048, 8 x 32768 int8-V at 2048
-// (1024 is 2% slower there but twice as fast for a lone 32768 slot, so 32768
-// gets 1024).  The pages make the same trade (tessl nn.rs DecodeChunk: grid
-// parallelism against the number of partials the reduce pass combines).
+// (warm, back-to-back calls): a 1024-position window runs fastest at 64
+// positions per chunk, 1 x 131072 at 2048, 8 x 32768 int8-V at 2048 (1024 is
+// 2% slower there but twice as fast for a lone 32768 slot, so 32768 gets
+// 1024).  1 x 4096 at D = 256 takes 128 (graph-replayed, alternating on one
+// box: 11.97 -> 11.46 us against 64, 8 x 4096 51.7 -> 49.6 us; another box
+// measured the single slot 3% slower).  The pages make the same trade (tessl
+// nn.rs DecodeChunk: grid parallelism against the number of partials the
+// reduce pass combines).
 inline int64_t target_chunks(int64_t n) {
-    if (n <= 4096) return 64;
     if (n <= 65536) return 32;
     return 16;
 }
@@ -136,8 +138,8 @@ inline int64_t target_chunks(int64_t n) {
 // 8 x 8192 at head_dim 128 with 4 heads per kv head 83.5 us at 128 positions,
 // 54.9 at 512; at head_dim 64 68.9 -> 36.0 us (1024); 8 x 8192 int8 V at 256
 // 82.2 -> 73.4 us (256), while a lone 8192 slot moves by 0.3-2 us.  Lone
-// slots of 4096 or less (1 x 4096: 12.0 us at 64 positions, 14.4 at 256)
-// keep the fine split, down to 64 KiB of K and V per chunk and kv head
+// slots of 4096 or less (1 x 4096: 11.5 us at 128 positions, 14.4 at 256)
+// keep a finer split, down to 64 KiB of K and V per chunk and kv head
 // (64 positions at head_dim 256, 128 at 128, 256 at 64).  Below that floor
 // batches lose to the workgroups' fixed cost: at head_dim 128, 16 x 2048 took
 // 38.3 us in 64-position chunks and 29.6 in 128-position ones, 8 x 4096 37.6

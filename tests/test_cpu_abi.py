@@ -138,25 +138,26 @@ def test_forced_chunk_is_used_and_still_bounded():
 
 def test_one_query_with_four_heads_per_kv_head_goes_to_the_matrix_cores():
     # 4 (query, head) columns are enough for the matrix cores wherever they take fp16 products:
-    # their chunk rule gives 512 positions at 4096, the lanes' 64.  Two heads per kv head (the
+    # their chunk rule gives 512 positions at 4096, the lanes' 128 (256 at head_dim 64).  Two heads per kv head (the
     # configs) stay on the lanes, and so does head_dim 512 with one-byte V (its kernel needs 8).
     assert binding.attn_decode_plan([4096], 0, 32, 8, 128)["chunk"] == [512]
     assert binding.attn_decode_plan([4096], 0, 32, 8, 256, v_int8=True)["chunk"] == [512]
     assert binding.attn_decode_plan([4096], 0, 32, 8, 512)["chunk"] == [512]
-    assert binding.attn_decode_plan([4096], 0, 32, 8, 512, v_int8=True)["chunk"] == [64]
-    assert binding.attn_decode_plan([4096], 0, 16, 8, 256)["chunk"] == [64]
+    assert binding.attn_decode_plan([4096], 0, 32, 8, 512, v_int8=True)["chunk"] == [128]
+    assert binding.attn_decode_plan([4096], 0, 16, 8, 256)["chunk"] == [128]
     assert binding.attn_decode_plan([4096], 0, 32, 8, 64)["chunk"] == [256]   # head_dim 64: lanes only
 
 
 @pytest.mark.parametrize("D,floor", [(64, 256), (128, 128), (256, 64), (512, 64)])
 def test_lane_chunks_of_short_slots_carry_at_least_64_kib(D, floor):
-    # a split slot of at most 4096 positions: 64-position chunks where they hold 64 KiB of
-    # fp16 K and V per kv head, else the floor that does; slots whose K and V fit 128 KiB
+    # a split slot of at most 4096 positions: about 32 chunks in multiples of 64 positions,
+    # but no chunk under 64 KiB of fp16 K and V per kv head; slots whose K and V fit 128 KiB
     # stay whole
     whole = 131072 // (4 * D)
     for L in (whole + 1, 1000, 2048, 3000, 4096):
         c = binding.attn_decode_plan([L], 0, 16, 8, D)["chunk"][0]
-        assert c == min(max(64, floor), L), (D, L, c)
+        by_count = -(-(-(-L // 32)) // 64) * 64
+        assert c == min(max(by_count, floor), L), (D, L, c)
         assert c * 4 * D >= 65536 or c == L
     assert binding.attn_decode_plan([whole], 0, 16, 8, D)["n_chunks"] == [1]
 
