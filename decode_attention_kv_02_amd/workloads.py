@@ -277,6 +277,73 @@ def append_new_rows(cfg: AppendWorkloadConfig) -> Tuple[torch.Tensor, torch.Tens
 CB_BLOCK = 256
 
 
+# The codebooks the pages' hybrid V uses: mlx-native 0.21.1 flash_attn_vec_hybrid.metal prints
+# three fixed tables of N(0, 1) levels, CODEBOOK_HB_5BIT, _6BIT and _8BIT, which its codebook
+# dequant (dequant_hb_single, dequant_hb_float4) indexes with the low 5 or 6 bits of a byte, or
+# the whole byte at 8 bits.  Transcribed here level by level, as float32 literals, in table order.
+PAGE_CODEBOOKS = {
+    5: (
+        -3.2606790, -2.6910589, -2.3176743, -2.0286608, -1.7871646, -1.5761599, -1.3862739, -1.2117410,
+        -1.0487242, -0.8945114, -0.7470884, -0.6048936, -0.4666676, -0.3313550, -0.1980377, -0.0658849,
+        0.0658849, 0.1980377, 0.3313550, 0.4666676, 0.6048936, 0.7470884, 0.8945114, 1.0487242,
+        1.2117410, 1.3862739, 1.5761599, 1.7871646, 2.0286608, 2.3176743, 2.6910589, 3.2606790,
+    ),
+    6: (
+        -3.6996161, -3.1907215, -2.8640626, -2.6161277, -2.4129324, -2.2388464, -2.0853192, -1.9471373,
+        -1.8208742, -1.7041502, -1.5952401, -1.4928497, -1.3959804, -1.3038428, -1.2157998, -1.1313277,
+        -1.0499889, -0.9714118, -0.8952766, -0.8213046, -0.7492492, -0.6788902, -0.6100285, -0.5424819,
+        -0.4760822, -0.4106724, -0.3461048, -0.2822386, -0.2189392, -0.1560761, -0.0935225, -0.0311537,
+        0.0311537, 0.0935225, 0.1560761, 0.2189392, 0.2822386, 0.3461048, 0.4106724, 0.4760822,
+        0.5424819, 0.6100285, 0.6788902, 0.7492492, 0.8213046, 0.8952766, 0.9714118, 1.0499889,
+        1.1313277, 1.2157998, 1.3038428, 1.3959804, 1.4928497, 1.5952401, 1.7041502, 1.8208742,
+        1.9471373, 2.0853192, 2.2388464, 2.4129324, 2.6161277, 2.8640626, 3.1907215, 3.6996161,
+    ),
+    8: (
+        -5.0652659, -4.6836997, -4.4467193, -4.2715508, -4.1311907, -4.0132856, -3.9111092, -3.8205780,
+        -3.7390194, -3.6645851, -3.5959415, -3.5320936, -3.4722785, -3.4158977, -3.3624729, -3.3116156,
+        -3.2630056, -3.2163758, -3.1715011, -3.1281899, -3.0862780, -3.0456229, -3.0061011, -2.9676040,
+        -2.9300362, -2.8933131, -2.8573596, -2.8221086, -2.7874999, -2.7534795, -2.7199985, -2.6870129,
+        -2.6544825, -2.6223710, -2.5906452, -2.5592748, -2.5282321, -2.4974918, -2.4670306, -2.4368270,
+        -2.4068614, -2.3771157, -2.3475732, -2.3182184, -2.2890372, -2.2600165, -2.2311440, -2.2024086,
+        -2.1737998, -2.1453081, -2.1169245, -2.0886408, -2.0604493, -2.0323430, -2.0043154, -1.9763603,
+        -1.9484722, -1.9206458, -1.8928763, -1.8651592, -1.8374904, -1.8098662, -1.7822828, -1.7547372,
+        -1.7272261, -1.6997469, -1.6722970, -1.6448739, -1.6174755, -1.5900996, -1.5627445, -1.5354084,
+        -1.5080897, -1.4807869, -1.4534986, -1.4262237, -1.3989610, -1.3717093, -1.3444678, -1.3172356,
+        -1.2900118, -1.2627956, -1.2355865, -1.2083838, -1.1811868, -1.1539951, -1.1268081, -1.0996255,
+        -1.0724469, -1.0452718, -1.0180999, -0.9909310, -0.9637647, -0.9366008, -0.9094390, -0.8822793,
+        -0.8551212, -0.8279648, -0.8008098, -0.7736561, -0.7465035, -0.7193520, -0.6922014, -0.6650517,
+        -0.6379027, -0.6107544, -0.5836067, -0.5564596, -0.5293129, -0.5021667, -0.4750208, -0.4478753,
+        -0.4207301, -0.3935852, -0.3664405, -0.3392960, -0.3121517, -0.2850076, -0.2578636, -0.2307198,
+        -0.2035761, -0.1764324, -0.1492888, -0.1221453, -0.0950019, -0.0678584, -0.0407151, -0.0135717,
+        0.0135717, 0.0407151, 0.0678584, 0.0950019, 0.1221453, 0.1492888, 0.1764324, 0.2035761,
+        0.2307198, 0.2578636, 0.2850076, 0.3121517, 0.3392960, 0.3664405, 0.3935852, 0.4207301,
+        0.4478753, 0.4750208, 0.5021667, 0.5293129, 0.5564596, 0.5836067, 0.6107544, 0.6379027,
+        0.6650517, 0.6922014, 0.7193520, 0.7465035, 0.7736561, 0.8008098, 0.8279648, 0.8551212,
+        0.8822793, 0.9094390, 0.9366008, 0.9637647, 0.9909310, 1.0180999, 1.0452718, 1.0724469,
+        1.0996255, 1.1268081, 1.1539951, 1.1811868, 1.2083838, 1.2355865, 1.2627956, 1.2900118,
+        1.3172356, 1.3444678, 1.3717093, 1.3989610, 1.4262237, 1.4534986, 1.4807869, 1.5080897,
+        1.5354084, 1.5627445, 1.5900996, 1.6174755, 1.6448739, 1.6722970, 1.6997469, 1.7272261,
+        1.7547372, 1.7822828, 1.8098662, 1.8374904, 1.8651592, 1.8928763, 1.9206458, 1.9484722,
+        1.9763603, 2.0043154, 2.0323430, 2.0604493, 2.0886408, 2.1169245, 2.1453081, 2.1737998,
+        2.2024086, 2.2311440, 2.2600165, 2.2890372, 2.3182184, 2.3475732, 2.3771157, 2.4068614,
+        2.4368270, 2.4670306, 2.4974918, 2.5282321, 2.5592748, 2.5906452, 2.6223710, 2.6544825,
+        2.6870129, 2.7199985, 2.7534795, 2.7874999, 2.8221086, 2.8573596, 2.8933131, 2.9300362,
+        2.9676040, 3.0061011, 3.0456229, 3.0862780, 3.1281899, 3.1715011, 3.2163758, 3.2630056,
+        3.3116156, 3.3624729, 3.4158977, 3.4722785, 3.5320936, 3.5959415, 3.6645851, 3.7390194,
+        3.8205780, 3.9111092, 4.0132856, 4.1311907, 4.2715508, 4.4467193, 4.6836997, 5.0652659,
+    ),
+}
+
+
+def codebook_levels(bits: int) -> torch.Tensor:
+    """The V codebook (float32, ascending) that the presets and tests use for ``bits``: the
+    pages' printed table at 5, 6 and 8 bits (PAGE_CODEBOOKS); at other widths, which the pages
+    do not use, this build's own Lloyd iteration (lloyd_max_gaussian)."""
+    if int(bits) in PAGE_CODEBOOKS:
+        return torch.tensor(PAGE_CODEBOOKS[int(bits)], dtype=torch.float32)
+    return lloyd_max_gaussian(bits)
+
+
 @functools.lru_cache(maxsize=None)
 def _lloyd_levels(bits: int, iters: int) -> Tuple[float, ...]:
     import numpy as np
@@ -291,7 +358,8 @@ def _lloyd_levels(bits: int, iters: int) -> Tuple[float, ...]:
 
 
 def lloyd_max_gaussian(bits: int, iters: int = 2000) -> torch.Tensor:
-    """Lloyd-Max quantiser levels for N(0, 1) with 2**bits levels (float32, ascending).
+    """This build's own Lloyd-Max levels for N(0, 1) with 2**bits levels (float32, ascending),
+    an alternative to the pages' printed tables and the levels of the widths they do not print.
 
     Lloyd's iteration from the quantile midpoints: cell boundaries at the
     midpoints of neighbouring levels, each level moved to the conditional mean
@@ -375,7 +443,7 @@ def make_codebook_inputs(seq_lens: Sequence[int], n_q_heads: int, n_kv_heads: in
     if direct and keep_plain:
         raise ValueError("direct draws no plain V")
     base = make_inputs(seq_lens, n_q_heads, n_kv_heads, head_dim, False, seed_base)
-    cb = lloyd_max_gaussian(bits)
+    cb = codebook_levels(bits)
     signs = make_signs(head_dim, seed_base + 7)
     gv = torch.Generator("cpu").manual_seed(seed_base + 3)
     B = min(head_dim, CB_BLOCK)

@@ -24,7 +24,7 @@ import pytest
 import torch
 
 from decode_attention_kv_02_amd import binding
-from decode_attention_kv_02_amd.workloads import lloyd_max_gaussian, make_cache_codebook_inputs, make_signs
+from decode_attention_kv_02_amd.workloads import codebook_levels, make_cache_codebook_inputs, make_signs
 from oracle import oracle_attn_decode_cache_cb, oracle_codebook_encode, oracle_fwht_undo, oracle_kv_append_cb
 
 from gpu_util import assert_parity
@@ -105,7 +105,7 @@ def test_codebook_append_matches_oracle(d, bits, ring):
     vn = (r.standard_normal((n_rows, n_kv, d)) * 3).astype(np.float32)
     vn[3, 1] = 0.0                                      # a zero row: code 0, norm 0
     s = make_signs(d, 9100 + d).numpy()
-    cb = lloyd_max_gaussian(bits).numpy()
+    cb = codebook_levels(bits).numpy()
     total = n_slots * n_kv * cap * d
     k0 = r.standard_normal(total).astype(np.float16)
     c0 = r.integers(0, 256, total).astype(np.uint8)
@@ -227,7 +227,7 @@ def test_serving_loop_append_attend_undo(d, bits, nq, nkv):
     B = min(d, 256)
     r = np.random.default_rng(9500 + d)
     s = make_signs(d, 9600 + d).numpy()
-    cb = lloyd_max_gaussian(bits).numpy()
+    cb = codebook_levels(bits).numpy()
     total = ns * nkv * cap * d
     k_host = np.zeros(total, np.float16)
     c_host = np.zeros(total, np.uint8)

@@ -28,7 +28,7 @@ import numpy as np
 import pytest
 import scipy.linalg
 
-from decode_attention_kv_02_amd.workloads import lloyd_max_gaussian, make_signs
+from decode_attention_kv_02_amd.workloads import codebook_levels, make_signs
 from oracle import (oracle_attn_decode_cache, oracle_attn_decode_cache_cb, oracle_attn_decode_cb,
                     oracle_codebook_encode, oracle_fwht_undo, oracle_kv_append, oracle_kv_append_cb)
 
@@ -67,7 +67,7 @@ def test_encode_matches_scipy_hadamard_and_argmin(d, bits):
     r = _rng(100 + d)
     v = r.standard_normal((20, d)).astype(np.float32)
     s = _signs(d, 200 + d)
-    cb = lloyd_max_gaussian(bits).numpy()
+    cb = codebook_levels(bits).numpy()
     codes, norms, u = oracle_codebook_encode(v, s, cb, bits)
     y = (scipy.linalg.hadamard(d).astype(np.float64) @ (s[:, None] * v.T.astype(np.float64))).T / math.sqrt(d)
     B = min(d, 256)
@@ -85,7 +85,7 @@ def test_power_of_two_scale_changes_norms_only():
     r = _rng(7)
     v = r.standard_normal((16, d)).astype(np.float32)
     s = _signs(d, 8)
-    cb = lloyd_max_gaussian(8).numpy()
+    cb = codebook_levels(8).numpy()
     c1, n1, u1 = oracle_codebook_encode(v, s, cb, 8)
     c4, n4, u4 = oracle_codebook_encode(v * 4, s, cb, 8)
     assert np.array_equal(c1, c4)
@@ -122,7 +122,7 @@ def test_decode_and_undo_give_v_back_to_the_quantiser_distortion(bits, d, bound)
     r = _rng(300 + bits)
     v = r.standard_normal((64, d)).astype(np.float32)
     s = _signs(d, 301)
-    cb = lloyd_max_gaussian(bits).numpy()
+    cb = codebook_levels(bits).numpy()
     codes, norms, _ = oracle_codebook_encode(v, s, cb, bits)
     back = oracle_fwht_undo(_decode(codes, norms, cb), s)
     err = np.linalg.norm(back - v) / np.linalg.norm(v)
@@ -161,7 +161,7 @@ def test_append_places_each_row_and_touches_nothing_else(ring, d):
     kn = r.standard_normal((4, n_kv, d)).astype(np.float32)
     vn_ = r.standard_normal((4, n_kv, d)).astype(np.float32)
     s = _signs(d, 401)
-    cb = lloyd_max_gaussian(bits).numpy()
+    cb = codebook_levels(bits).numpy()
     kc, vc, nm = _empty_cache(n_slots, n_kv, cap, d)
     k2, v2, n2, u = oracle_kv_append_cb(kn, vn_, s, cb, bits, kc, vc, nm, sid, pos, n_slots, cap, ring, n_kv, d)
     # K exactly as the (pinned) fp16 append writes it
@@ -235,7 +235,7 @@ def test_cache_codebook_equals_packed_codebook_on_the_same_rows(d):
     n_kv, nq, cap = 2, 8, 40
     B = min(d, 256)
     seq = [40, 13, 1]
-    cb = lloyd_max_gaussian(8).numpy()
+    cb = codebook_levels(8).numpy()
     codes = r.integers(0, 256, 3 * n_kv * cap * d).astype(np.uint8)
     norms = r.uniform(0.5, 20, 3 * n_kv * cap * d // B).astype(np.float32)
     k = (r.standard_normal(3 * n_kv * cap * d) * 0.5).astype(np.float16)
