@@ -123,9 +123,9 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // 2% slower there but twice as fast for a lone 32768 slot, so 32768 gets
 // 1024).  1 x 4096 at D = 256 takes 128 (graph-replayed, alternating on one
 // box: 11.97 -> 11.46 us against 64, 8 x 4096 51.7 -> 49.6 us; another box
-// measured the single slot 3% slower).  The pages make the same trade (tessl
-// nn.rs DecodeChunk: grid parallelism against the number of partials the
-// reduce pass combines).
+// measured the single slot 3% slower).  The pages weigh the same two costs
+// when they pick a chunk (tessl nn.rs, the DecodeChunk table): more chunks give
+// more workgroups, but leave more partial rows for the merge to read.
 inline int64_t target_chunks(int64_t n) {
     if (n <= 65536) return 32;
     return 16;

@@ -14,16 +14,16 @@
  *
  *   for each slot s, query head h, dim d:
  *     G    = n_q / n_kv,  kvh = floor(h / G)
- *          (mlx-native flash_attn_vec_hybrid.metal, flash_attn_vec_hybrid_impl:
- *           "GQA: map query head to KV head")
+ *          (mlx-native flash_attn_vec_hybrid.metal, flash_attn_vec_hybrid_impl,
+ *           the GQA head mapping: consecutive query heads share a KV head)
  *     lo   = (W > 0 && L_s > W) ? L_s - W : 0,  hi = L_s
  *          (same kernel, the sliding-window start; tessl nn.rs,
  *           flash_attn_decode: window 0 selects the global rule)
  *     x_j  = scale * sum_d q[s,h,d] * K[s,kvh,j,d]          for j in [lo, hi)
- *          (same kernel, "Q * K^T" block: the dot is formed first and the
+ *          (same kernel, its QK block: the dot is formed first and the
  *           scale is applied to the finished dot)
  *     out  = sum_j exp(x_j - m) V[s,kvh,j,:] / sum_j exp(x_j - m),  m = max x_j
- *          (same kernel, "Online softmax" and the final 1/S normalisation;
+ *          (same kernel, its online-softmax block and the final 1/S normalisation;
  *           an empty range writes zeros because S == 0 gives inv_S = 0)
  *
  * The softmax is evaluated in two exact passes (max, then weights) rather than
