@@ -1,5 +1,5 @@
-"""Bench presets at their full sizes, in the launch configuration bench.py times, checked on
-sampled output rows against the CPU fp64 oracle (which computes rows one by one):
+"""Bench presets at their full sizes, in the launch configuration bench.py times, checked over
+their whole output tensors against the CPU fp64 oracle (every row, on all host cores):
 
 * the D = 512 global layer with 8-bit codebook V (16 q / 2 kv heads, 8 x 32768): the
   matrix-core kernel, plus the undo of the rotation;
@@ -40,7 +40,7 @@ def _say(msg):
     print(f"[presets] {msg}", flush=True)
 
 
-def test_global_d512_codebook_preset_sampled_rows():
+def test_global_d512_codebook_preset_full_output():
     cfg = next(c for c in CODEBOOK_WORKLOADS if c.head_dim == 512)
     ci = codebook_workload_inputs(cfg)
     _say(f"{cfg.name}: generated")
@@ -51,19 +51,19 @@ def test_global_d512_codebook_preset_sampled_rows():
     rot = out.clone()
     binding.attn_fwht_undo(out, sg, out)
     torch.cuda.synchronize()
-    rows = [s * ci.n_q_heads + h for s in range(ci.n_slots) for h in (0, 7, 8, 15)]
     ref = oracle_attn_decode_cb(ci.q.numpy(), ci.k.numpy(), ci.v_codes.numpy(), ci.v_norms.numpy(),
                                 ci.codebook.numpy(), ci.codebook_bits, ci.seq_lens, cfg.window, ci.n_q_heads,
-                                ci.n_kv_heads, ci.head_dim, ci.scale, rows=rows)
-    got_rot = rot.cpu().numpy().reshape(-1, ci.head_dim)[rows]
+                                ci.n_kv_heads, ci.head_dim, ci.scale).reshape(-1, ci.head_dim)
+    got_rot = rot.cpu().numpy().reshape(-1, ci.head_dim)
+    assert got_rot.shape == ref.shape == (ci.n_slots * ci.n_q_heads, ci.head_dim)
     err = assert_parity(got_rot, ref, "rotated basis")
-    _say(f"{cfg.name}: rotated max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}")
-    got = out.cpu().numpy().reshape(-1, ci.head_dim)[rows]
+    _say(f"{cfg.name}: rotated max-abs {err[0]:.3e} rel-L2 {err[1]:.3e} (all {ref.shape[0]} rows)")
+    got = out.cpu().numpy().reshape(-1, ci.head_dim)
     err = assert_parity(got, oracle_fwht_undo(ref, ci.signs.numpy()), "undone")
     _say(f"{cfg.name}: undone max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}")
 
 
-def test_verify_preset_sampled_rows():
+def test_verify_preset_full_output():
     cfg = next(c for c in CACHE_WORKLOADS if c.name.startswith("verify"))
     ci = cache_workload_inputs(cfg)
     _say(f"{cfg.name}: generated")
@@ -73,17 +73,18 @@ def test_verify_preset_sampled_rows():
     binding.attn_decode_cache(q, k, v, vs, ci.slot_ids, ci.positions, ci.n_queries, ci.n_cache_slots, ci.capacity,
                               ci.ring, cfg.window, out, ci.n_q_heads, ci.n_kv_heads, ci.head_dim, ci.scale)
     torch.cuda.synchronize()
-    rows = [i * ci.n_q_heads + h for i in range(ci.n_queries) for h in (0, 5, 15)]
     ref = oracle_attn_decode_cache(ci.q.numpy(), ci.k.numpy(), ci.v.numpy(),
                                    None if ci.v_scales is None else ci.v_scales.numpy(), ci.slot_ids, ci.positions,
                                    ci.n_cache_slots, ci.capacity, ci.ring, cfg.window, ci.n_q_heads, ci.n_kv_heads,
-                                   ci.head_dim, ci.scale, rows=rows)
-    err = assert_parity(out.cpu().numpy().reshape(-1, ci.head_dim)[rows], ref, cfg.name)
-    _say(f"{cfg.name}: max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}")
+                                   ci.head_dim, ci.scale)
+    got = out.cpu().numpy()
+    assert got.shape == ref.shape
+    err = assert_parity(got, ref, cfg.name)
+    _say(f"{cfg.name}: max-abs {err[0]:.3e} rel-L2 {err[1]:.3e} (all {ci.n_queries * ci.n_q_heads} rows)")
 
 
 @pytest.mark.parametrize("cfg", SERVE_STEP_WORKLOADS, ids=[c.name for c in SERVE_STEP_WORKLOADS])
-def test_serving_step_preset_sampled_rows(cfg):
+def test_serving_step_preset_full_output(cfg):
     """Append (fp16 K, codebook V) then attend and undo, on the bench's serving-step presets.  The
     codes the GPU writes are checked against the oracle's fp64 decision (a code may differ only
     where the normalised coordinate lies within 2e-4 of a level midpoint); the outputs, which weigh
@@ -125,12 +126,14 @@ def test_serving_step_preset_sampled_rows(cfg):
                 n_diff += int(diff.sum())
             nsl = slice(row * (d // B), (row + 1) * (d // B))
             assert np.allclose(gn[nsl], n_h[nsl], rtol=5e-5, atol=0)
-    rows = [i * ci.n_q_heads + h for i in range(ci.n_queries) for h in (0, 9, 15)]
     ref = oracle_fwht_undo(oracle_attn_decode_cache_cb(ci.q.numpy(), k_h, c_h, n_h, ci.codebook.numpy(),
                                                        ci.codebook_bits, ci.slot_ids, ci.positions,
                                                        ci.n_cache_slots, cap, ci.ring, 0, ci.n_q_heads,
-                                                       ci.n_kv_heads, d, ci.scale, rows=rows), ci.signs.numpy())
-    err = assert_parity(out.cpu().numpy().reshape(-1, d)[rows], ref, cfg.name)
+                                                       ci.n_kv_heads, d, ci.scale).reshape(-1, d),
+                           ci.signs.numpy())
+    got = out.cpu().numpy().reshape(-1, d)
+    assert got.shape == ref.shape == (ci.n_queries * ci.n_q_heads, d)
+    err = assert_parity(got, ref, cfg.name)
     _say(f"{cfg.name}: codes at a midpoint {n_diff}; max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}")
 
 
