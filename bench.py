@@ -144,6 +144,10 @@ def parse_args(argv=None):
     ap.add_argument("--event-every", type=int, default=8,
                     help="time the partial kernel with HIP events on every N-th timed step")
     ap.add_argument("--chunk", type=int, default=0, help="forced chunk size (tuning only)")
+    ap.add_argument("--merge-mode", type=int, default=0, choices=(0, 1, 2),
+                    help="merge of split slots: 0 automatic, 1 combine kernel, 2 single launch")
+    ap.add_argument("--window", type=int, default=-1,
+                    help="attention window of the timed workload (default: the workload's first window)")
     ap.add_argument("--gqa-sweep", action="store_true",
                     help="only time the lane and the matrix-core partial kernels on groups of 8 and 16 "
                          "query heads per kv head (graph-replayed calls, one JSON line per shape)")
@@ -398,13 +402,13 @@ def main(argv=None) -> int:
         q, k, v, vs = tens
         binding.attn_decode_ex(q, k, v, vs, inp.seq_lens, W, out, inp.n_slots, inp.n_q_heads,
                                inp.n_kv_heads, inp.head_dim, inp.scale, stream=st or stream,
-                               chunk=args.chunk,
+                               chunk=args.chunk, merge_mode=args.merge_mode,
                                ev_partial_begin=ev0.cuda_event if ev0 is not None else None,
                                ev_partial_end=ev1.cuda_event if ev1 is not None else None)
 
     if args.workload in by_name:
         cfg = by_name[args.workload]
-        window = cfg.windows[0]
+        window = cfg.windows[0] if args.window < 0 else args.window
         print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
         inp = workload_inputs(cfg)
         tens = upload(inp)
@@ -537,6 +541,7 @@ def main(argv=None) -> int:
             "us_per_call": round(ms_per_step * 1e3, 2),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "chunk_override": args.chunk,
+            "merge_mode": args.merge_mode,
         },
         "roofline": {
             "bound": "hbm",

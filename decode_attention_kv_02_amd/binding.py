@@ -249,7 +249,7 @@ def attn_decode_ex(q, k_cache, v_cache, v_scales, seq_lens, window: int, out,
                    ev_partial_begin: Optional[int] = None, ev_partial_end: Optional[int] = None,
                    path: int = 0) -> None:
     """attn_decode with a forced chunk size, a merge mode (0 automatic, 1 combine kernel,
-    2 in-kernel merge), raw hipEvent_t handles around the partial kernel, and/or a forced
+    2 single launch), raw hipEvent_t handles around the partial kernel, and/or a forced
     partial kernel (path: 0 automatic, 1 lanes, 2 matrix cores)."""
     lib = load_library()
     seq_arr, n_slots, dev, (pq, pk, pv, ps, po) = _marshal(

@@ -31,7 +31,7 @@ using namespace attn_decode_impl;
 static_assert(ATTN_DECODE_MAX_SLOTS_PER_LAUNCH == kMaxSlotsPerLaunch, "slot table size");
 static_assert(ATTN_DECODE_MAX_CHUNKS == kMaxChunks, "chunk bound");
 static_assert(kCombineMaxChunks >= kMaxChunks, "combine LDS holds every chunk weight");
-static_assert(kFusedMaxChunks <= kMaxChunks, "in-kernel merge bound");
+static_assert(kSingleLaunchMaxChunks <= kMaxChunks, "single-launch merge bound");
 static_assert(sizeof(LaunchArgs) <= 4096, "kernel arguments stay within 4 KiB");
 static_assert(sizeof(AppendArgs) <= 4096, "kernel arguments stay within 4 KiB");
 
@@ -49,59 +49,58 @@ int fail(int code, const std::string &msg) {
 struct Workspace {
     void *ptr = nullptr;
     size_t bytes = 0;
-    int64_t counter_cap = 0;   // counters at the front; zero between calls
+    int64_t flag_bytes = 0;   // the flagged-pair region at the front; all zero between calls
 };
 
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void *>, Workspace> g_ws;  // keyed by (device, stream)
+// Buffers a workspace outgrew, per device.  They stay allocated until
+// attn_decode_release: a HIP graph captured earlier, work still queued, or
+// another host thread may still hold their address.
+std::vector<std::pair<int, void *>> g_retired;
 
-// Returns the counters (all zero) and the partials area of the (device, stream)
-// workspace, growing it when the call needs more of either.
-int acquire_workspace(int device, hipStream_t stream, int64_t n_counters, int64_t data_bytes,
-                      uint32_t **counters, float **data) {
-    *counters = nullptr;
+// Returns the flagged-pair region (all zero) and the plain partials area of the
+// (device, stream) workspace, growing it when the call needs more of either.
+// Growing allocates a new buffer, clears its flagged region with a fill kernel
+// (no memset node), and retires the old buffer without freeing it, so it never
+// waits for the stream.
+int acquire_workspace(int device, hipStream_t stream, int64_t flag_bytes, int64_t data_bytes,
+                      uint64_t **flags, float **data) {
+    *flags = nullptr;
     *data = nullptr;
-    if (n_counters == 0 && data_bytes == 0) return ATTN_DECODE_OK;
+    if (flag_bytes == 0 && data_bytes == 0) return ATTN_DECODE_OK;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &ws = g_ws[std::make_pair(device, (void *)stream)];
-    const int64_t have_data = (int64_t)ws.bytes - counter_region_bytes(ws.counter_cap);
-    if (ws.ptr == nullptr || ws.counter_cap < n_counters || have_data < data_bytes) {
-        if (ws.ptr != nullptr) {
-            // earlier work of this stream may still use the old buffer
-            hipError_t e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
-            e = hipFree(ws.ptr);
-            ws.ptr = nullptr;
-            ws.bytes = 0;
-            ws.counter_cap = 0;
-            if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipFree: ") + hipGetErrorString(e));
-        }
-        const int64_t cap = std::max<int64_t>(n_counters + n_counters / 4, 4096);
-        int64_t want = data_bytes + data_bytes / 4;
+    const int64_t have_data = (int64_t)ws.bytes - ws.flag_bytes;
+    if (ws.ptr == nullptr || ws.flag_bytes < flag_bytes || have_data < data_bytes) {
+        int64_t fb = std::max<int64_t>(flag_bytes + flag_bytes / 4, ws.flag_bytes);
+        fb = (fb + 0xFFFF) & ~int64_t(0xFFFF);
+        int64_t want = std::max<int64_t>(data_bytes + data_bytes / 4, have_data);
         want = (want + 0xFFFF) & ~int64_t(0xFFFF);
-        const size_t bytes = (size_t)(counter_region_bytes(cap) + want);
+        const size_t bytes = (size_t)(fb + want);
         void *p = nullptr;
         hipError_t e = hipMalloc(&p, bytes);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             return fail(ATTN_DECODE_ENOMEM, "workspace hipMalloc of " + std::to_string(bytes) + " bytes: " + hipGetErrorString(e));
         }
-        // counters start at zero (a fill kernel, no memset node); every call
-        // leaves the counters it used at zero again
-        const int64_t words = counter_region_bytes(cap) / 4;
-        hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
-                           static_cast<uint32_t *>(p), words, 0u);
-        e = hipGetLastError();
-        if (e != hipSuccess) {
-            (void)hipFree(p);
-            return fail(ATTN_DECODE_EHIP, std::string("counter fill launch: ") + hipGetErrorString(e));
+        if (fb > 0) {
+            const int64_t words = fb / 4;
+            hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                               static_cast<uint32_t *>(p), words, 0u);
+            e = hipGetLastError();
+            if (e != hipSuccess) {
+                (void)hipFree(p);
+                return fail(ATTN_DECODE_EHIP, std::string("flag region fill launch: ") + hipGetErrorString(e));
+            }
         }
+        if (ws.ptr != nullptr) g_retired.push_back(std::make_pair(device, ws.ptr));
         ws.ptr = p;
         ws.bytes = bytes;
-        ws.counter_cap = cap;
+        ws.flag_bytes = fb;
     }
-    *counters = static_cast<uint32_t *>(ws.ptr);
-    *data = reinterpret_cast<float *>(static_cast<char *>(ws.ptr) + counter_region_bytes(ws.counter_cap));
+    *flags = static_cast<uint64_t *>(ws.ptr);
+    *data = reinterpret_cast<float *>(static_cast<char *>(ws.ptr) + ws.flag_bytes);
     return ATTN_DECODE_OK;
 }
 
@@ -234,10 +233,10 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
-    uint32_t *counters = nullptr;
+    uint64_t *flags = nullptr;
     float *ws_o = nullptr;
     const int64_t data_bytes = plan.part_rows * (int64_t)(D + 2) * (int64_t)sizeof(float);
-    int rc = acquire_workspace(device, stream, plan.n_counters, data_bytes, &counters, &ws_o);
+    const int rc = acquire_workspace(device, stream, flag_region_bytes(plan.flag_rows, D), data_bytes, &flags, &ws_o);
     if (rc != ATTN_DECODE_OK) return rc;
     float *ws_ml = ws_o ? ws_o + plan.part_rows * D : nullptr;
 
@@ -255,18 +254,18 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     args.out = out;
     args.ws_o = ws_o;
     args.ws_ml = ws_ml;
-    args.counters = counters;
+    args.flags = flags;
     args.n_q = n_q;
     args.G = plan.G;
     args.scale_log2 = (float)scale_log2;
 
-    // combine: search keys are the entries' first combine rows, else their first work items
+    // Search keys: the entries' first work items (partial kernels) or first combine rows
+    // (combine kernel); tkey, the first rows among a single-launch grid's merge workgroups.
     auto fill = [&](const LaunchGroup &lg, bool combine) {
         const KernelShape &ks = lg.mfma ? plan.matrix : plan.lanes;
         args.n_sub = ks.n_sub;
-        args.fuse_limit = lg.mfma ? 1 : plan.fuse_limit;
         args.n_slots = (int32_t)lg.slots.size();
-        int32_t item = 0, comb = 0;
+        int32_t item = 0, comb = 0, tail = 0;
         int32_t lead_pos = 0;
         for (size_t i = 0; i < lg.slots.size(); ++i) {
             const int32_t s = lg.slots[i];
@@ -280,17 +279,18 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
             sd.chunk = sp.chunk;
             sd.n_chunks = sp.n_chunks;
             sd.item_begin = sp.group_n > 0 ? item : args.slot[lead_pos].item_begin;
-            sd.comb_begin = comb;
-            sd.cnt_base = sp.cnt_base;
+            sd.comb_begin = sp.fused ? tail : comb;
+            sd.flag_row0 = sp.fused ? sp.flag_row0 : -1;
             sd.slot_idx = s;
             sd.kv_stride = sp.kv_stride;
             sd.ring_cap = sp.ring_cap;
             sd.ring_base = sp.ring_base;
             sd.group_n = (int16_t)sp.group_n;
             sd.lead_off = (int16_t)(i - lead_pos);
-            args.key[i] = combine ? sd.comb_begin : sd.item_begin;
+            args.key[i] = combine ? comb : sd.item_begin;
+            args.tkey[i] = tail;
             if (sp.group_n > 0) item += n_kv * ks.n_sub * sp.n_chunks;
-            if (sp.n_chunks > 1 && !sp.fused) comb += n_q;
+            if (sp.n_chunks > 1) (sp.fused ? tail : comb) += n_q;
         }
         args.n_items = item;
     };
@@ -301,7 +301,8 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     }
     for (const LaunchGroup &lg : plan.groups) {
         fill(lg, false);
-        hipLaunchKernelGGL(lg.mfma ? pk_mfma : pk_lanes, dim3((unsigned)lg.items), dim3(kThreads), 0, stream, args);
+        const int64_t grid = lg.items + lg.tail_rows * (D / kCombineDims);   // partial, then merge workgroups
+        hipLaunchKernelGGL(lg.mfma ? pk_mfma : pk_lanes, dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
     }
@@ -747,17 +748,23 @@ extern "C" int attn_decode_release(void) {
     int rc = ATTN_DECODE_OK;
     int cur = 0;
     const bool have_cur = hipGetDevice(&cur) == hipSuccess;
-    for (auto &kv : g_ws) {
-        Workspace &ws = kv.second;
-        if (ws.ptr == nullptr) continue;
-        hipError_t e = hipSetDevice(kv.first.first);
-        if (e == hipSuccess) e = hipDeviceSynchronize();
-        if (e == hipSuccess) e = hipFree(ws.ptr);
+    std::vector<std::pair<int, void *>> bufs = g_retired;
+    for (auto &kv : g_ws)
+        if (kv.second.ptr != nullptr) bufs.push_back(std::make_pair(kv.first.first, kv.second.ptr));
+    std::sort(bufs.begin(), bufs.end());
+    int synced = -1;
+    for (const auto &b : bufs) {
+        hipError_t e = hipSuccess;
+        if (b.first != synced) {   // every device that owns a buffer, once
+            e = hipSetDevice(b.first);
+            if (e == hipSuccess) e = hipDeviceSynchronize();
+            synced = b.first;
+        }
+        if (e == hipSuccess) e = hipFree(b.second);
         if (e != hipSuccess) rc = fail(ATTN_DECODE_EHIP, std::string("release: ") + hipGetErrorString(e));
-        ws.ptr = nullptr;
-        ws.bytes = 0;
     }
     g_ws.clear();
+    g_retired.clear();
     if (have_cur) (void)hipSetDevice(cur);
     return rc;
 }

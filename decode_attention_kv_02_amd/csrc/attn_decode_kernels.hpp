@@ -20,9 +20,12 @@
 //    4 waves through LDS.  A slot with one chunk writes out = O / S directly
 //    (S == 0, an empty slot, writes zeros); otherwise O and (M, S) go to the
 //    workspace.
-//  * attn_combine_kernel: one workgroup per (slot, query head) whose slot has
-//    several chunks: M* = max_c M_c, S* = sum_c S_c 2^(M_c - M*),
-//    out = sum_c O_c 2^(M_c - M*) / S*.
+//  * the log-sum-exp merge of a split slot's chunks, per (slot, query head,
+//    64-dim slice): M* = max_c M_c, S* = sum_c S_c 2^(M_c - M*),
+//    out = sum_c O_c 2^(M_c - M*) / S*.  Either in attn_combine_kernel, a
+//    second launch, or (single-launch merge) in extra workgroups at the end of
+//    the partial kernel's own grid, which read the chunks' partials as
+//    self-validating flagged pairs (tail_merge).
 //
 // The logits are kept in the log2 domain (scale * log2 e folded into the
 // scale), so every exponential is one v_exp_f32; exp(x - m) = 2^((x - m) log2 e).
@@ -32,7 +35,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "planner.hpp"  // kFusedMaxChunks, shared with the host planner
+#include "planner.hpp"  // kMaxSlotsPerLaunch, shared with the host planner
 
 namespace attn_decode_impl {
 
@@ -44,14 +47,16 @@ constexpr int kThreads = 64 * kWaves;
 // One query row of a launch (a decode slot, or one query of a cache call).
 struct SlotDesc {
     int64_t kv_row0;    // row of (slot, kv head 0, position-row 0) in the K / V arrays
-    int64_t part_row0;  // first partial row of the query, -1 when it has one chunk
+    int64_t part_row0;  // first plain partial row of the query, -1 when it has none
     int32_t L;          // one past the last attended position
     int32_t lo;         // first attended position
     int32_t chunk;      // positions per chunk
     int32_t n_chunks;   // chunks of the query
     int32_t item_begin; // first partial workgroup of the query in this launch
-    int32_t comb_begin; // first combine-kernel row of the query in this launch
-    int32_t cnt_base;   // first arrival counter of the query (in-kernel merge)
+    int32_t comb_begin; // first merge row of the query in this launch (combine kernel, or the
+                        // merge workgroups at the end of a single-launch grid)
+    int32_t flag_row0;  // first flagged partial row of the query when its chunks are merged in
+                        // the partial kernel's launch (single-launch merge), else -1
     int32_t slot_idx;   // index of the query row in the call (q / out rows)
     int32_t kv_stride;  // rows between consecutive kv heads
     int32_t ring_cap;   // ring capacity, INT32_MAX when rows do not wrap
@@ -81,6 +86,8 @@ struct alignas(64) LaunchArgs {
     int32_t G;              // query heads per kv head
     int32_t key[kMaxSlotsPerLaunch];  // per entry, non-decreasing: its first work item (partial
                                       // kernels) or its first combine row (combine kernel)
+    int32_t tkey[kMaxSlotsPerLaunch]; // partial kernels, per entry, non-decreasing: its first row
+                                      // among the merge workgroups at the end of the grid
     const uint16_t *q;      // fp16 [n_slots_total][n_q][D]
     const uint16_t *k;      // fp16 packed cache
     const void *v;          // fp16, int8 or codebook-index cache
@@ -89,11 +96,10 @@ struct alignas(64) LaunchArgs {
     float *out;             // fp32 [n_slots_total][n_q][D]
     float *ws_o;            // partial O rows [part_rows][D]
     float *ws_ml;           // partial (M, S) [part_rows][2]
-    uint32_t *counters;     // arrival counters of in-kernel merges, zero between calls
+    uint64_t *flags;        // flagged partial rows of single-launch merges, zero between calls
     int32_t cb_mask;        // codebook V: 2^bits - 1 (the index bits that are used)
     int32_t n_q;
     float scale_log2;       // scale * log2(e)
-    int32_t fuse_limit;     // slots with 2..fuse_limit chunks merge inside the partial kernel
     float cb_scale;         // codebook V: 1 / sqrt(min(D, 256))
     alignas(64) SlotDesc slot[kMaxSlotsPerLaunch];
 };
@@ -178,93 +184,321 @@ __device__ __forceinline__ int xcd_item(int b, int n_items, int n_sub) {
 
 // ---------------------------------------------------------------- chunk merge
 
-// Log-sum-exp merge of the nc chunk partials of GB consecutive query heads
-// (h0 .. h0+GB-1 of the slot whose partial rows start at part_row0) into
-// out_rows ([GB][D] fp32), by one 256-thread workgroup:
-//   M* = max_c M_c,  w_c = 2^(M_c - M*),  S* = sum_c w_c S_c,
-//   out = sum_c w_c O_c / S*   (S* == 0 gives zeros).
-// The chunks are visited in a fixed order, so the result does not depend on
-// which workgroup runs the merge.
-template <int D, int GB>
-__device__ __forceinline__ void merge_chunks(const LaunchArgs &args, int64_t part_row0, int nc, int h0,
-                                             float *out_rows) {
-    constexpr int COLS = GB * D / 4;                            // float4 columns of the GB rows
-    constexpr int CG = COLS >= kThreads ? 1 : kThreads / COLS;  // chunk groups
-    __shared__ float s_wt[GB][kFusedMaxChunks];
-    __shared__ float s_lsum[GB];
-    __shared__ float4 s_acc[CG > 1 ? CG : 1][CG > 1 ? COLS : 1];
+constexpr int kCombineMaxChunks = 4096;
+// Dims of one output row merged by one merge workgroup.
+constexpr int kCombineDims = 64;
+// Partial rows each merge thread loads before the chunk weights are known.
+constexpr int kCombinePreload = 4;
+
+// LDS of one merge workgroup that merges up to NC chunks.
+template <int NC>
+struct MergeSmem {
+    float w[NC];                                         // chunk weights 2^(M_c - M*)
+    float4 acc[kThreads / (kCombineDims / 4)][kCombineDims / 4];
+    float red[kWaves];
+};
+
+// Log-sum-exp merge of the sd.n_chunks partials of query head h (of the query
+// whose descriptor is sd) for the 64 output dims of `slice`, by one 256-thread
+// workgroup:  M* = max_c M_c,  w_c = 2^(M_c - M*),  S* = sum_c w_c S_c,
+// out = sum_c w_c O_c / S*  (S* == 0 gives zeros).  16 groups of 16 threads
+// split the chunks; each thread owns 4 dims (16-byte loads of the partial rows,
+// coalesced over the 16 threads).  The first loads of the partial rows are
+// issued together with the loads of the chunk statistics, so the merge costs
+// about one memory round trip; the 16 group sums are added in LDS in a fixed
+// order, so the result does not depend on which kernel runs the merge.
+template <int D, int NC>
+__device__ __forceinline__ void merge_slice(const LaunchArgs &args, const SlotDesc &sd, int h, int slice,
+                                            MergeSmem<NC> &sm) {
+    constexpr int TPR = kCombineDims / 4;       // threads per chunk row of the slice
+    constexpr int CG = kThreads / TPR;          // chunk groups
+    const int nc = sd.n_chunks;
+    const int64_t base = sd.part_row0 + (int64_t)h * nc;
+    const int64_t slot_g = sd.slot_idx;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
-    const int lane = tid & 63;
+    const int cg = tid / TPR;
+    const int j = tid - cg * TPR;
+    const int d0 = slice * kCombineDims + 4 * j;
+    const float *src = args.ws_o + base * D + d0;
+    const float *ml = args.ws_ml + base * 2;
 
-    if (w < GB) {   // wave g prepares the chunk weights of head g
-        const float *ml = args.ws_ml + (part_row0 + (int64_t)(h0 + w) * nc) * 2;
-        float mx = -INFINITY;
-        for (int cc = lane; cc < nc; cc += 64) mx = fmaxf(mx, ml[2 * cc]);
-        mx = wave_max(mx);
-        const float ms = (mx == -INFINITY) ? 0.f : mx;
-        float ls = 0.f;
-        for (int cc = lane; cc < nc; cc += 64) {
-            const float wc = fast_exp2(ml[2 * cc] - ms);
-            s_wt[w][cc] = wc;
-            ls += wc * ml[2 * cc + 1];
+    // partial rows of this thread's first chunks (independent of the weights)
+    float4 pre[kCombinePreload];
+#pragma unroll
+    for (int u = 0; u < kCombinePreload; ++u) {
+        const int c = cg + u * CG;
+        pre[u] = c < nc ? *(const float4 *)(src + (int64_t)c * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    // M* over chunks
+    float mx = -INFINITY;
+    for (int c = tid; c < nc; c += kThreads) mx = fmaxf(mx, ml[2 * c]);
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) sm.red[w] = mx;
+    __syncthreads();
+    mx = sm.red[0];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, sm.red[ww]);
+    const float ms = (mx == -INFINITY) ? 0.f : mx;
+    __syncthreads();
+
+    // chunk weights 2^(M_c - M*) and S*
+    float ls = 0.f;
+    for (int c = tid; c < nc; c += kThreads) {
+        const float wc = fast_exp2(ml[2 * c] - ms);
+        sm.w[c] = wc;
+        ls += wc * ml[2 * c + 1];
+    }
+    ls = wave_sum(ls);
+    if ((tid & 63) == 0) sm.red[w] = ls;
+    __syncthreads();
+    float lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) lsum += sm.red[ww];
+
+    // weighted sum of the partial O rows over this thread's chunks, in chunk order
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kCombinePreload; ++u) {
+        const int c = cg + u * CG;
+        if (c < nc) {
+            const float wc = sm.w[c];
+            acc.x = fmaf(wc, pre[u].x, acc.x);
+            acc.y = fmaf(wc, pre[u].y, acc.y);
+            acc.z = fmaf(wc, pre[u].z, acc.z);
+            acc.w = fmaf(wc, pre[u].w, acc.w);
         }
-        ls = wave_sum(ls);
-        if (lane == 0) s_lsum[w] = ls;
+    }
+    int c = cg + kCombinePreload * CG;
+    for (; c + 3 * CG < nc; c += 4 * CG) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *(const float4 *)(src + (int64_t)(c + u * CG) * D);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float wc = sm.w[c + u * CG];
+            acc.x = fmaf(wc, v[u].x, acc.x);
+            acc.y = fmaf(wc, v[u].y, acc.y);
+            acc.z = fmaf(wc, v[u].z, acc.z);
+            acc.w = fmaf(wc, v[u].w, acc.w);
+        }
+    }
+    for (; c < nc; c += CG) {
+        const float4 v = *(const float4 *)(src + (int64_t)c * D);
+        const float wc = sm.w[c];
+        acc.x = fmaf(wc, v.x, acc.x);
+        acc.y = fmaf(wc, v.y, acc.y);
+        acc.z = fmaf(wc, v.z, acc.z);
+        acc.w = fmaf(wc, v.w, acc.w);
+    }
+    sm.acc[cg][j] = acc;
+    __syncthreads();
+    if (tid < TPR) {
+        float4 t = sm.acc[0][tid];
+#pragma unroll
+        for (int g = 1; g < CG; ++g) {
+            const float4 u = sm.acc[g][tid];
+            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+        }
+        float4 r;
+        r.x = (lsum == 0.f) ? 0.f : t.x / lsum;
+        r.y = (lsum == 0.f) ? 0.f : t.y / lsum;
+        r.z = (lsum == 0.f) ? 0.f : t.z / lsum;
+        r.w = (lsum == 0.f) ? 0.f : t.w / lsum;
+        *(float4 *)(args.out + (slot_g * args.n_q + h) * D + slice * kCombineDims + 4 * tid) = r;
+    }
+}
+
+// Single-launch merge.  The workgroups past the n_items partial workgroups of a
+// launch each merge one (query head, 64-dim slice) of a split query, in the
+// same launch, as soon as every chunk of it has been written.
+//
+// Publication needs no wait.  A fused query's partial workgroup writes each
+// value as one 8-byte pair {value bits, 1} with an agent-scope store (on
+// gfx942/gfx950 such stores go through to the memory side of the per-XCD L2
+// caches); for every 64-dim slice it writes the pairs of M and S, then the 64
+// value pairs.  An aligned 8-byte access is single-copy atomic, so a pair whose
+// flag reads 1 holds the value that came with that flag: each pair validates
+// itself, whatever order the stores arrive in (the protocol of RCCL's "LL"
+// transfers).  The workgroup ends without waiting for any of it.
+//
+// One thread of the merge workgroup first polls a single pair, the M of the
+// last chunk (the last of the query's chunks to be dispatched), with a sleep
+// between polls, so that the merge workgroups, which may be resident long
+// before their chunks finish, load almost nothing while they wait.  Then the
+// workgroup reads every pair it needs, reloads, all at once, those whose flag
+// is not yet 1, and after using a pair writes zeros back over it.  Each pair is
+// written by exactly one partial workgroup and read and cleared by exactly one
+// merge workgroup of the same call, so every call leaves the region all zero,
+// as the next call requires.  (Two designs with an arrival counter per
+// (query, kv head) measured far slower: each chunk waiting for its stores to
+// complete before counting itself, and each chunk counting itself without
+// waiting, the pairs still carrying the data.)
+//
+// Workgroups are dispatched in increasing id order on each XCD, and every merge
+// workgroup has a larger id than every partial workgroup, so each partial
+// workgroup is resident or finished before any merge workgroup on its XCD can
+// hold a slot: every awaited pair arrives.  The polls are still bounded
+// (kTailMaxPolls per thread, about a second); a merge that gives up writes NaN,
+// so a failure shows instead of hanging the GPU.
+constexpr int kTailMaxPolls = 1 << 20;
+
+__device__ __forceinline__ void store_pair(uint64_t *p, float v) {
+    __hip_atomic_store(p, (uint64_t)__builtin_bit_cast(uint32_t, v) | (uint64_t(1) << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t load_pair(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void clear_pair(uint64_t *p) {
+    __hip_atomic_store(p, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float pair_value(uint64_t x) { return __builtin_bit_cast(float, (uint32_t)x); }
+__device__ __forceinline__ bool pair_ready(uint64_t x) { return (uint32_t)(x >> 32) == 1u; }
+
+// The merge of one (query head, 64-dim slice) from flagged pairs: the arithmetic
+// of merge_slice, in the same order, so both merges give the same bits.
+template <int D>
+__device__ __forceinline__ void tail_merge(const LaunchArgs &args) {
+    constexpr int SLICES = D / kCombineDims;
+    constexpr int TPR = kCombineDims / 4;       // threads per chunk row of the slice
+    constexpr int CG = kThreads / TPR;          // chunk groups
+    constexpr int64_t ROW = (int64_t)SLICES * kFlagPairsPerSlice;   // pairs per partial row
+    static_assert(kCombineDims == kMergeSliceDims, "one merge slice per flagged block");
+    static_assert(kSingleLaunchMaxChunks <= kThreads, "one thread per chunk's statistics");
+    __shared__ MergeSmem<kSingleLaunchMaxChunks> sm;
+    __shared__ int s_bad;
+    const int jt = (int)blockIdx.x - args.n_items;
+    const int row = jt / SLICES;
+    const int slice = jt - row * SLICES;
+    const int si = upper_index(args.n_slots, row, [&](int i) { return args.tkey[i]; });
+    const SlotDesc sd = args.slot[si];
+    const int h = row - sd.comb_begin;
+    const int nc = sd.n_chunks;
+    uint64_t *blk = args.flags + ((int64_t)sd.flag_row0 + (int64_t)h * nc) * ROW + slice * kFlagPairsPerSlice;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int cg = tid / TPR;
+    const int j = tid - cg * TPR;
+    int polls = 0;
+    if (tid == 0) {
+        s_bad = 0;
+        const uint64_t *p = blk + (int64_t)(nc - 1) * ROW;   // the last chunk's M
+        while (!pair_ready(load_pair(p)) && polls < kTailMaxPolls) {
+            __builtin_amdgcn_s_sleep(16);
+            ++polls;
+        }
+        polls = 0;
     }
     __syncthreads();
 
-    for (int col0 = 0; col0 < COLS; col0 += (CG > 1 ? COLS : kThreads)) {
-        const int t = tid % (CG > 1 ? COLS : kThreads);
-        const int cg = CG > 1 ? tid / COLS : 0;
-        const int col = col0 + t;
-        const int g = col / (D / 4);
-        const int d0 = (col - g * (D / 4)) * 4;
-        const float *src = args.ws_o + (part_row0 + (int64_t)(h0 + g) * nc) * D + d0;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        int cc = cg;
-        for (; cc + 3 * CG < nc; cc += 4 * CG) {
-            float4 v[4];
+    // chunk statistics: thread c reads chunk c's (M, S), reloading until both have arrived
+    float mc = -INFINITY, sc = 0.f;
+    if (tid < nc) {
+        uint64_t *p = blk + (int64_t)tid * ROW;
+        uint64_t a = load_pair(p), b = load_pair(p + 1);
+        while (!(pair_ready(a) && pair_ready(b)) && polls < kTailMaxPolls) {
+            __builtin_amdgcn_s_sleep(2);
+            if (!pair_ready(a)) a = load_pair(p);
+            if (!pair_ready(b)) b = load_pair(p + 1);
+            ++polls;
+        }
+        if (!(pair_ready(a) && pair_ready(b))) s_bad = 1;
+        mc = pair_value(a);
+        sc = pair_value(b);
+        clear_pair(p);
+        clear_pair(p + 1);
+    }
+    float mx = wave_max(mc);
+    if ((tid & 63) == 0) sm.red[w] = mx;
+    __syncthreads();
+    mx = sm.red[0];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = *(const float4 *)(src + (int64_t)(cc + u * CG) * D);
+    for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, sm.red[ww]);
+    const float ms = (mx == -INFINITY) ? 0.f : mx;
+    __syncthreads();
+    float ls = 0.f;
+    if (tid < nc) {
+        const float wc = fast_exp2(mc - ms);
+        sm.w[tid] = wc;
+        ls = wc * sc;
+    }
+    ls = wave_sum(ls);
+    if ((tid & 63) == 0) sm.red[w] = ls;
+    __syncthreads();
+    float lsum = 0.f;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float wc = s_wt[g][cc + u * CG];
-                acc.x = fmaf(wc, v[u].x, acc.x);
-                acc.y = fmaf(wc, v[u].y, acc.y);
-                acc.z = fmaf(wc, v[u].z, acc.z);
-                acc.w = fmaf(wc, v[u].w, acc.w);
+    for (int ww = 0; ww < kWaves; ++ww) lsum += sm.red[ww];
+
+    // this thread's 4 dims over its chunks cg, cg + CG, ... in chunk order, kCombinePreload
+    // chunks per batch; pairs not yet in are reloaded, all at once
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool bad = false;
+    for (int c0 = cg; c0 < nc; c0 += kCombinePreload * CG) {
+        uint64_t x[kCombinePreload][4];
+#pragma unroll
+        for (int u = 0; u < kCombinePreload; ++u) {
+            const int c = c0 + u * CG;
+            const uint64_t *p = blk + (int64_t)c * ROW + 2 + 4 * j;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[u][e] = c < nc ? load_pair(p + e) : uint64_t(0);
+        }
+        for (;;) {
+            bool all = true;
+#pragma unroll
+            for (int u = 0; u < kCombinePreload; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) all &= (c0 + u * CG >= nc) || pair_ready(x[u][e]);
+            if (all || polls >= kTailMaxPolls) break;
+            __builtin_amdgcn_s_sleep(2);
+            ++polls;
+#pragma unroll
+            for (int u = 0; u < kCombinePreload; ++u) {
+                const int c = c0 + u * CG;
+                const uint64_t *p = blk + (int64_t)c * ROW + 2 + 4 * j;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c < nc && !pair_ready(x[u][e])) x[u][e] = load_pair(p + e);
             }
         }
-        for (; cc < nc; cc += CG) {
-            const float4 v = *(const float4 *)(src + (int64_t)cc * D);
-            const float wc = s_wt[g][cc];
-            acc.x = fmaf(wc, v.x, acc.x);
-            acc.y = fmaf(wc, v.y, acc.y);
-            acc.z = fmaf(wc, v.z, acc.z);
-            acc.w = fmaf(wc, v.w, acc.w);
-        }
-        if constexpr (CG > 1) {
-            s_acc[cg][t] = acc;
-            __syncthreads();
-            if (tid < COLS) {
-                acc = s_acc[0][tid];
 #pragma unroll
-                for (int k = 1; k < CG; ++k) {
-                    const float4 u = s_acc[k][tid];
-                    acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
-                }
+        for (int u = 0; u < kCombinePreload; ++u) {
+            const int c = c0 + u * CG;
+            if (c >= nc) continue;
+            uint64_t *p = blk + (int64_t)c * ROW + 2 + 4 * j;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bad |= !pair_ready(x[u][e]);
+                clear_pair(p + e);
             }
+            const float wc = sm.w[c];
+            acc.x = fmaf(wc, pair_value(x[u][0]), acc.x);
+            acc.y = fmaf(wc, pair_value(x[u][1]), acc.y);
+            acc.z = fmaf(wc, pair_value(x[u][2]), acc.z);
+            acc.w = fmaf(wc, pair_value(x[u][3]), acc.w);
         }
-        if (CG == 1 || tid < COLS) {
-            const float ls = s_lsum[g];
-            float4 r;
-            r.x = (ls == 0.f) ? 0.f : acc.x / ls;
-            r.y = (ls == 0.f) ? 0.f : acc.y / ls;
-            r.z = (ls == 0.f) ? 0.f : acc.z / ls;
-            r.w = (ls == 0.f) ? 0.f : acc.w / ls;
-            *(float4 *)(out_rows + g * D + d0) = r;
+    }
+    if (bad) s_bad = 1;
+    sm.acc[cg][j] = acc;
+    __syncthreads();
+    if (tid < TPR) {
+        float4 t = sm.acc[0][tid];
+#pragma unroll
+        for (int g = 1; g < CG; ++g) {
+            const float4 u = sm.acc[g][tid];
+            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
         }
+        float4 r;
+        r.x = (lsum == 0.f) ? 0.f : t.x / lsum;
+        r.y = (lsum == 0.f) ? 0.f : t.y / lsum;
+        r.z = (lsum == 0.f) ? 0.f : t.z / lsum;
+        r.w = (lsum == 0.f) ? 0.f : t.w / lsum;
+        if (s_bad) r = make_float4(NAN, NAN, NAN, NAN);
+        *(float4 *)(args.out + ((int64_t)sd.slot_idx * args.n_q + h) * D + slice * kCombineDims + 4 * tid) = r;
     }
 }
 
@@ -324,6 +558,10 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     constexpr int CB_B = D < 256 ? D : 256;             // codebook norm block
     static_assert(kThreads == 256, "one thread per codebook table entry");
 
+    if ((int)blockIdx.x >= args.n_items) {   // a merge workgroup of a single-launch call
+        tail_merge<D>(args);
+        return;
+    }
     const int item = xcd_item(blockIdx.x, args.n_items, args.n_sub);
     int si = upper_index(args.n_slots, item, [&](int i) { return args.key[i]; });
     si -= args.slot[si].lead_off;
@@ -336,7 +574,6 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     const int cbeg = sd.lo + c * sd.chunk;
     const int cend = min(cbeg + sd.chunk, sd.L);
     const int h0 = kvh * args.G + sub * GB;            // first query head of the block (in the slot)
-    const int64_t slot_g = sd.slot_idx;
     const int64_t rowbase = sd.kv_row0 + (int64_t)kvh * sd.kv_stride;
     const int n_mem = QB == 1 ? 1 : (int)sd.group_n;
 
@@ -566,8 +803,9 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     }
     __syncthreads();
 
-    // the leader decides the in-kernel merge; groups (QB > 1) always use the combine kernel
-    const bool fused = QB == 1 && sd.n_chunks > 1 && sd.n_chunks <= args.fuse_limit;
+    // A query merged in this launch (flag_row0 >= 0: not in a query group, several chunks)
+    // writes its partials as flagged pairs and is done (tail_merge).
+    const bool publish = sd.flag_row0 >= 0;
     for (int idx = tid; idx < NR * D; idx += kThreads) {
         const int g = idx / D;
         const int d = idx - g * D;
@@ -588,173 +826,39 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
         }
         if (mb.n_chunks == 1) {
             args.out[qrow[g] * D + d] = (lsum == 0.f) ? 0.f : acc / lsum;
+        } else if (publish) {
+            constexpr int SL = D / kMergeSliceDims;
+            const int64_t r = (int64_t)mb.flag_row0 + (int64_t)(h0 + g % GB) * mb.n_chunks + c;
+            uint64_t *blk = args.flags + (r * SL + d / kMergeSliceDims) * kFlagPairsPerSlice;
+            store_pair(blk + 2 + (d % kMergeSliceDims), acc);
+            if (d % kMergeSliceDims == 0) {
+                store_pair(blk, mx);
+                store_pair(blk + 1, lsum);
+            }
         } else {
             const int64_t prow = mb.part_row0 + (int64_t)(h0 + g % GB) * mb.n_chunks + c;
-            if (fused) {
-                // agent-scope stores (sc1): coherent across XCDs without an L2 write-back
-                __hip_atomic_store(args.ws_o + prow * D + d, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (d == 0) {
-                    __hip_atomic_store(args.ws_ml + prow * 2 + 0, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(args.ws_ml + prow * 2 + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            } else {
-                args.ws_o[prow * D + d] = acc;
-                if (d == 0) {
-                    args.ws_ml[prow * 2 + 0] = mx;
-                    args.ws_ml[prow * 2 + 1] = lsum;
-                }
+            args.ws_o[prow * D + d] = acc;
+            if (d == 0) {
+                args.ws_ml[prow * 2 + 0] = mx;
+                args.ws_ml[prow * 2 + 1] = lsum;
             }
         }
     }
-    if constexpr (QB != 1) return;
-    if (!fused) return;
-
-    // ---- in-kernel merge: the last chunk of this (slot, kv head, head block) to finish merges all
-    // Every wave waits until its partial stores have completed (they are
-    // agent-scope stores, so completion means visible to every XCD), then one
-    // thread takes a ticket.  The workgroup holding the last ticket acquires at
-    // agent scope and reads every chunk's partial back.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    __shared__ int s_last;
-    uint32_t *counter = args.counters + sd.cnt_base + kvh * args.n_sub + sub;
-    if (tid == 0)
-        s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                 (uint32_t)(sd.n_chunks - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    merge_chunks<D, GB>(args, sd.part_row0, sd.n_chunks, h0, args.out + (slot_g * args.n_q + h0) * D);
-    // the counter is zero again for the next call on this stream
-    if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- combine kernel
 
-constexpr int kCombineMaxChunks = 4096;
-
-
-// Dims of one output row merged by one combine workgroup.
-constexpr int kCombineDims = 64;
-// Partial rows each combine thread loads before the chunk weights are known.
-constexpr int kCombinePreload = 4;
-
-// One workgroup per (slot, query head, 64-dim slice).  16 groups of 16
-// threads split the chunks; each thread owns 4 dims (16-byte loads of the
-// partial rows, coalesced over the 16 threads).  The first loads of the
-// partial rows are issued together with the loads of the chunk statistics,
-// so the merge costs about one memory round trip; the 16 group sums are added
-// in LDS in a fixed order.
+// One workgroup per (query, query head, 64-dim slice) of a query with several
+// chunks, after the partial kernel has finished.
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(const LaunchArgs args) {
     constexpr int SLICES = D / kCombineDims;
-    constexpr int TPR = kCombineDims / 4;       // threads per chunk row of the slice
-    constexpr int CG = kThreads / TPR;          // chunk groups
-    __shared__ float s_w[kCombineMaxChunks];
-    __shared__ float4 s_acc[CG][TPR];
-    __shared__ float s_red[kWaves];
-
+    __shared__ MergeSmem<kCombineMaxChunks> sm;
     const int row = blockIdx.x / SLICES;
     const int slice = blockIdx.x - row * SLICES;
     const int si = upper_index(args.n_slots, row, [&](int i) { return args.key[i]; });
     const SlotDesc sd = args.slot[si];
-    const int h = row - sd.comb_begin;
-    const int nc = sd.n_chunks;
-    const int64_t base = sd.part_row0 + (int64_t)h * nc;
-    const int64_t slot_g = sd.slot_idx;
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int cg = tid / TPR;
-    const int j = tid - cg * TPR;
-    const int d0 = slice * kCombineDims + 4 * j;
-    const float *src = args.ws_o + base * D + d0;
-    const float *ml = args.ws_ml + base * 2;
-
-    // partial rows of this thread's first chunks (independent of the weights)
-    float4 pre[kCombinePreload];
-#pragma unroll
-    for (int u = 0; u < kCombinePreload; ++u) {
-        const int c = cg + u * CG;
-        pre[u] = c < nc ? *(const float4 *)(src + (int64_t)c * D) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
-    // M* over chunks
-    float mx = -INFINITY;
-    for (int c = tid; c < nc; c += kThreads) mx = fmaxf(mx, ml[2 * c]);
-    mx = wave_max(mx);
-    if ((tid & 63) == 0) s_red[w] = mx;
-    __syncthreads();
-    mx = s_red[0];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, s_red[ww]);
-    const float ms = (mx == -INFINITY) ? 0.f : mx;
-    __syncthreads();
-
-    // chunk weights 2^(M_c - M*) and S*
-    float ls = 0.f;
-    for (int c = tid; c < nc; c += kThreads) {
-        const float wc = fast_exp2(ml[2 * c] - ms);
-        s_w[c] = wc;
-        ls += wc * ml[2 * c + 1];
-    }
-    ls = wave_sum(ls);
-    if ((tid & 63) == 0) s_red[w] = ls;
-    __syncthreads();
-    float lsum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) lsum += s_red[ww];
-
-    // weighted sum of the partial O rows over this thread's chunks, in chunk order
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int u = 0; u < kCombinePreload; ++u) {
-        const int c = cg + u * CG;
-        if (c < nc) {
-            const float wc = s_w[c];
-            acc.x = fmaf(wc, pre[u].x, acc.x);
-            acc.y = fmaf(wc, pre[u].y, acc.y);
-            acc.z = fmaf(wc, pre[u].z, acc.z);
-            acc.w = fmaf(wc, pre[u].w, acc.w);
-        }
-    }
-    int c = cg + kCombinePreload * CG;
-    for (; c + 3 * CG < nc; c += 4 * CG) {
-        float4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *(const float4 *)(src + (int64_t)(c + u * CG) * D);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float wc = s_w[c + u * CG];
-            acc.x = fmaf(wc, v[u].x, acc.x);
-            acc.y = fmaf(wc, v[u].y, acc.y);
-            acc.z = fmaf(wc, v[u].z, acc.z);
-            acc.w = fmaf(wc, v[u].w, acc.w);
-        }
-    }
-    for (; c < nc; c += CG) {
-        const float4 v = *(const float4 *)(src + (int64_t)c * D);
-        const float wc = s_w[c];
-        acc.x = fmaf(wc, v.x, acc.x);
-        acc.y = fmaf(wc, v.y, acc.y);
-        acc.z = fmaf(wc, v.z, acc.z);
-        acc.w = fmaf(wc, v.w, acc.w);
-    }
-    s_acc[cg][j] = acc;
-    __syncthreads();
-    if (tid < TPR) {
-        float4 t = s_acc[0][tid];
-#pragma unroll
-        for (int g = 1; g < CG; ++g) {
-            const float4 u = s_acc[g][tid];
-            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-        }
-        float4 r;
-        r.x = (lsum == 0.f) ? 0.f : t.x / lsum;
-        r.y = (lsum == 0.f) ? 0.f : t.y / lsum;
-        r.z = (lsum == 0.f) ? 0.f : t.z / lsum;
-        r.w = (lsum == 0.f) ? 0.f : t.w / lsum;
-        *(float4 *)(args.out + (slot_g * args.n_q + h) * D + slice * kCombineDims + 4 * tid) = r;
-    }
+    merge_slice<D, kCombineMaxChunks>(args, sd, row - sd.comb_begin, slice, sm);
 }
 
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t value) {

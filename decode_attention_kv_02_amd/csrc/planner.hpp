@@ -57,8 +57,8 @@ struct SlotPlan {
     int32_t n_chunks = 1;   // >= 1 (an empty slot has one empty chunk)
     int64_t kv_row0 = 0;    // row of (slot, kv head 0, position-row 0)
     int64_t part_row0 = -1; // first partial row when n_chunks > 1, else -1
-    bool fused = false;     // 2..fuse_limit chunks: merged inside the partial kernel
-    int32_t cnt_base = 0;   // first arrival counter when fused
+    bool fused = false;     // merged by the partial kernel's own launch (single-launch merge)
+    int32_t flag_row0 = -1; // fused: first of its partial rows in the flagged region, else -1
     int32_t group_n = 1;    // on a group leader: queries of its group; 0 on a follower
     int32_t leader = -1;    // on a follower: the leader's index
     std::vector<int32_t> members;   // on a leader: followers in table order
@@ -77,7 +77,9 @@ struct KernelShape {
 struct LaunchGroup {
     std::vector<int32_t> slots;        // slot indices, in work-list order
     int64_t items = 0;                 // partial-kernel workgroups
-    int64_t combine_rows = 0;          // combine-kernel workgroups
+    int64_t combine_rows = 0;          // query heads merged by the combine kernel
+    int64_t tail_rows = 0;             // query heads merged by merge workgroups at the end of the
+                                       // partial kernel's grid (head_dim / 64 workgroups each)
     bool mfma = false;                 // which partial kernel computes this launch
 };
 
@@ -88,26 +90,31 @@ struct CallPlan {
     KernelShape matrix;  // the matrix-core kernel's: GB 8 or 16, or GB = G for draft groups
     std::vector<SlotPlan> slots;
     std::vector<LaunchGroup> groups;
-    int64_t part_rows = 0;         // partial rows (each head_dim floats + 2 stats)
-    int64_t n_counters = 0;        // arrival counters (one per kv head and head block of fused slots)
-    int fuse_limit = 1;            // largest chunk count merged inside the partial kernel
-    int64_t workspace_bytes = 0;   // counter region (256-byte aligned) + partial rows
+    int64_t part_rows = 0;         // plain partial rows (each head_dim floats + 2 stats)
+    int64_t flag_rows = 0;         // partial rows of fused queries, as flagged pairs
+    int fuse_limit = 1;            // largest chunk count merged in the partial kernel's launch
+    int64_t workspace_bytes = 0;   // flagged region (256-byte aligned) + plain partial rows
     int64_t total_items = 0;
 };
 
-// With the in-kernel merge, slots split into at most this many chunks are
-// merged by the last of their workgroups to finish (its LDS holds one weight
-// per chunk); longer slots still go to the combine kernel.
-constexpr int kFusedMaxChunks = 256;
+// With the single-launch merge, lane-kernel queries split into at most this many
+// chunks (the merge workgroup's LDS holds one weight per chunk) that are not part
+// of a query group are merged by workgroups at the end of the partial kernel's
+// own grid; the others still go to the combine kernel.
+constexpr int kSingleLaunchMaxChunks = 256;
 
-// kMergeAuto currently selects the combine kernel: on MI355X the in-kernel
-// merge measured slower on every preset (each workgroup must wait for its
-// write-through partial stores before it may take a ticket, and the last one
-// merges alone), e.g. 276 vs 252 us for 8 x 32768 int8-V slots.
+// kMergeAuto currently selects the combine kernel.
 enum MergeMode { kMergeAuto = 0, kMergeCombineKernel = 1, kMergeInKernel = 2 };
 
-// Counters sit at the front of the workspace in a 256-byte aligned region.
-inline int64_t counter_region_bytes(int64_t n_counters) { return (n_counters * 4 + 255) / 256 * 256; }
+// A fused query's partial rows are written as 8-byte pairs {value bits, 1}: per
+// 64-dim slice of a row, the pair of M, the pair of S, then 64 value pairs.  The
+// pairs sit at the front of the workspace in a 256-byte aligned region that is
+// all zero between calls (each call clears the pairs it wrote).
+constexpr int kMergeSliceDims = 64;
+constexpr int kFlagPairsPerSlice = kMergeSliceDims + 2;
+inline int64_t flag_region_bytes(int64_t flag_rows, int32_t head_dim) {
+    return (flag_rows * (head_dim / kMergeSliceDims) * kFlagPairsPerSlice * 8 + 255) / 256 * 256;
+}
 
 inline bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
@@ -330,7 +337,7 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
     const int G = plan.G;
     plan.lanes.GB = heads_per_workgroup(G);
     plan.lanes.n_sub = G / plan.lanes.GB;
-    const int lane_qb_max = merge_mode == kMergeInKernel ? 1 : GROUP_ROWS / plan.lanes.GB;
+    const int lane_qb_max = GROUP_ROWS / plan.lanes.GB;
     int mfma_qb_max = 1;
     if (plan.mfma) {
         plan.matrix.GB = G % 16 == 0 ? 16 : 8;
@@ -342,7 +349,7 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
         mfma_qb_max = kMfmaColumns / G;
     }
     // the matrix-core kernel always merges in the combine kernel
-    plan.fuse_limit = merge_mode == kMergeInKernel ? kFusedMaxChunks : 1;
+    plan.fuse_limit = merge_mode == kMergeInKernel ? kSingleLaunchMaxChunks : 1;
     plan.slots.resize(n_slots);
     for (int32_t s = 0; s < n_slots; ++s) {
         SlotPlan &sp = plan.slots[s];
@@ -370,7 +377,7 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
     // Query groups: queries of one slot with the same attended start and chunk
     // size (draft tokens of a speculative-verify step) share one workgroup, so
     // their K and V rows are read once: on the lane kernel up to 4 / GB of
-    // them (not with the in-kernel merge), on the matrix cores up to 16 / GB.
+    // them, on the matrix cores up to 16 / GB.
     // Candidates are the non-empty queries with the same rows and start,
     // longest first (a group's leader is its longest query).
     std::vector<int32_t> idx;
@@ -462,22 +469,25 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
         }
     }
 
-    // partial rows and, for the lane kernel's in-kernel merge, arrival counters
-    int64_t part = 0;
+    // partial rows: plain rows for the combine kernel, flagged pairs for the single-launch merge
+    int64_t part = 0, flagged = 0;
     for (int32_t s = 0; s < n_slots; ++s) {
         SlotPlan &sp = plan.slots[s];
         if (sp.n_chunks <= 1) continue;
-        sp.part_row0 = part;
-        part += (int64_t)n_q * sp.n_chunks;
-        sp.fused = !sp.mfma && sp.n_chunks <= plan.fuse_limit;
+        const bool grouped = sp.leader >= 0 || sp.group_n > 1;
+        sp.fused = !sp.mfma && !grouped && sp.n_chunks <= plan.fuse_limit;
         if (sp.fused) {
-            if (plan.n_counters + (int64_t)n_kv * plan.lanes.n_sub > INT32_MAX) return "too many split slots";
-            sp.cnt_base = (int32_t)plan.n_counters;
-            plan.n_counters += (int64_t)n_kv * plan.lanes.n_sub;
+            if (flagged + (int64_t)n_q * sp.n_chunks > INT32_MAX) return "too many split slots";
+            sp.flag_row0 = (int32_t)flagged;
+            flagged += (int64_t)n_q * sp.n_chunks;
+        } else {
+            sp.part_row0 = part;
+            part += (int64_t)n_q * sp.n_chunks;
         }
     }
     plan.part_rows = part;
-    plan.workspace_bytes = counter_region_bytes(plan.n_counters) +
+    plan.flag_rows = flagged;
+    plan.workspace_bytes = flag_region_bytes(flagged, head_dim) +
                            part * (int64_t)(head_dim + 2) * (int64_t)sizeof(float);
 
     // Work-list order: longest chunks first (ties by slot index), so the
@@ -499,10 +509,11 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
     for (int32_t s : order) {
         const SlotPlan &sp = plan.slots[s];
         const int n_sub = sp.mfma ? plan.matrix.n_sub : plan.lanes.n_sub;
-        const int64_t items = (int64_t)n_kv * n_sub * sp.n_chunks;
+        // a fused query's merge workgroups count against the launch's workgroups
+        const int64_t items = (int64_t)n_kv * n_sub * sp.n_chunks + (sp.fused ? (int64_t)n_q * (head_dim / 64) : 0);
         if (items > kMaxItemsPerLaunch) return "too many workgroups for one slot (n_kv_heads too large)";
         const int entries = sp.group_n;
-        const bool full = (int)g.slots.size() + entries > kMaxSlotsPerLaunch || g.items + items > kMaxItemsPerLaunch ||
+        const bool full = (int)g.slots.size() + entries > kMaxSlotsPerLaunch || g.items + g.tail_rows * (head_dim / 64) + items > kMaxItemsPerLaunch ||
                           (!g.slots.empty() && g.mfma != sp.mfma);
         if (full) {
             plan.groups.push_back(g);
@@ -511,10 +522,10 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
         g.mfma = sp.mfma;
         g.slots.push_back(s);
         for (int32_t f : sp.members) g.slots.push_back(f);
-        g.items += items;
-        if (sp.n_chunks > 1 && !sp.fused) g.combine_rows += n_q;
+        g.items += (int64_t)n_kv * n_sub * sp.n_chunks;
+        if (sp.n_chunks > 1) (sp.fused ? g.tail_rows : g.combine_rows) += n_q;
         for (int32_t f : sp.members)
-            if (plan.slots[f].n_chunks > 1 && !plan.slots[f].fused) g.combine_rows += n_q;
+            if (plan.slots[f].n_chunks > 1) g.combine_rows += n_q;   // group members are never fused
     }
     if (!g.slots.empty()) plan.groups.push_back(g);
     for (const LaunchGroup &lg : plan.groups) plan.total_items += lg.items;

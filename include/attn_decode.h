@@ -43,14 +43,20 @@
  * must stay alive and unmodified until the work completes.
  *
  * Workspace: the library keeps one growable buffer per (device, stream): a
- * block of arrival counters used by the in-kernel merge mode (zeroed by a fill
- * kernel when the buffer is allocated; every call returns the counters it
- * uses to zero) followed by the per-chunk partials, which are never zeroed
- * (every partial a merge reads was written by the same call).  Allocating or growing it calls hipMalloc
- * and synchronises that stream once, so a call that needs a bigger workspace
- * cannot be captured into a HIP graph; a call that fits the existing one only
- * enqueues kernels.  Calls on different streams use different buffers; calls
- * on the same stream are ordered by it.  attn_decode_release frees them.
+ * region of flagged partials used by the single-launch merge mode (zeroed by
+ * a fill kernel when the buffer is allocated; every call clears the flags it
+ * sets) followed by the per-chunk partials of the combine kernel, which are
+ * never zeroed (every partial a merge reads was written by the same call).  A call that
+ * needs more than the stream's buffer holds calls hipMalloc for a larger one
+ * (so it should not be the call that is captured into a HIP graph: size the
+ * workspace with one eager call of the largest shape first); a call that fits
+ * only enqueues kernels.  The buffer a workspace outgrows is not freed: it
+ * stays allocated until attn_decode_release, so a graph captured on it, work
+ * still queued on it, or another host thread calling on the same stream keep
+ * a valid buffer.  Calls on different streams use different buffers; calls on
+ * the same stream are ordered by it.  attn_decode_release frees every buffer,
+ * current and outgrown, after synchronising each device that owns one: a
+ * graph captured before it must not be replayed after it.
  *
  * Determinism: the KV split of a slot depends only on that slot's own
  * attended length, head_dim, the V format and the chunk override, so a
@@ -106,16 +112,17 @@ typedef struct attn_decode_options {
     int32_t chunk;
     /* How a slot split over several chunks is merged: 0 = automatic (today
      * the combine kernel, the faster of the two on MI355X), 1 = the separate
-     * combine kernel, 2 = in-kernel: slots with at most 256 chunks are merged
-     * inside the partial kernel by the last workgroup of each (slot, KV head)
-     * to finish (one launch per call), longer ones by the combine kernel.
-     * Results of the modes differ only in rounding; within one mode batched
-     * equals per-slot bitwise. */
+     * combine kernel, 2 = single launch: the lane kernel's queries with at
+     * most 256 chunks that are not part of a query group are merged by extra
+     * workgroups at the end of the partial kernel's own grid (one launch per
+     * call where every split query qualifies), the others by the combine
+     * kernel.  Both merges run the same arithmetic in the same order, so the
+     * modes give bitwise the same results. */
     int32_t merge_mode;
     /* hipEvent_t handles (as void*) recorded on the stream immediately before
      * the first partial-kernel launch and immediately after the last one, or
      * NULL.  They bracket the partial (KV-streaming) kernels, including the
-     * in-kernel merges, and exclude the combine kernel. */
+     * merges of a single-launch call, and exclude the combine kernel. */
     void *ev_partial_begin;
     void *ev_partial_end;
     /* Which partial kernel computes the call: 0 = automatic (the matrix-core
@@ -329,8 +336,11 @@ int attn_decode_cache_plan(const int32_t *slot_ids, const int32_t *positions, in
 /* Message describing the last non-zero return on this host thread ("" if none). */
 const char *attn_decode_last_error(void);
 
-/* Free every workspace the library holds, after synchronising each device
- * that owns one.  Later calls allocate again.  Returns 0 or ATTN_DECODE_EHIP. */
+/* Free every workspace the library holds (the current buffer of each
+ * (device, stream) and every buffer a workspace outgrew), after synchronising
+ * each device that owns one.  HIP graphs captured before this call hold the
+ * freed addresses and must not be replayed after it.  Later calls allocate
+ * again.  Returns 0 or ATTN_DECODE_EHIP. */
 int attn_decode_release(void);
 
 #ifdef __cplusplus

@@ -27,9 +27,12 @@ def _need_gpu():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("merge_mode", [1, 2])
 @pytest.mark.parametrize("case", [((256,), 1, 1, 64, False, 0), ((4096, 1000), 16, 8, 256, True, 0),
                                   ((20000,), 16, 8, 256, False, 1024)], ids=["tiny", "split", "window"])
-def test_graph_replay_matches_eager(case):
+def test_graph_replay_matches_eager(case, merge_mode):
+    """Both merge modes; the single-launch merge's arrival counters must be back at zero after
+    every replay, or the next replay would merge before its chunks are written."""
     seq, nq, nkv, d, i8, W = case
     inp = make_inputs(seq, nq, nkv, d, i8, seed_base=8800)
     dev = torch.device("cuda:0")
@@ -40,7 +43,8 @@ def test_graph_replay_matches_eager(case):
     seq_a = np.asarray(seq, dtype=np.int32)
 
     def call():
-        binding.attn_decode_ex(q, k, v, vs, seq_a, W, out, inp.n_slots, nq, nkv, d, inp.scale, stream=side)
+        binding.attn_decode_ex(q, k, v, vs, seq_a, W, out, inp.n_slots, nq, nkv, d, inp.scale, stream=side,
+                               merge_mode=merge_mode)
 
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -132,3 +136,57 @@ def test_graph_of_codebook_serving_step():
         torch.cuda.synchronize()
         for got, want, name in zip((out, k, vc, vn), eager, ("out", "k", "codes", "norms")):
             assert torch.equal(got, want), f"replay {i}: {name}"
+
+
+def test_graph_replays_after_the_workspace_grows():
+    """A graph captured while the stream's workspace was small keeps working after a larger eager
+    call on the same stream has grown the workspace: the outgrown buffer, whose address the graph
+    holds, stays allocated (it is freed only by attn_decode_release)."""
+    dev = torch.device("cuda:0")
+    small = make_inputs((3000, 700), 16, 8, 256, True, seed_base=8900)
+    big = make_inputs((30000, 20000, 9000), 16, 8, 256, False, seed_base=8901)
+    side = torch.cuda.Stream()
+
+    def tensors(inp):
+        return (inp.q.to(dev), inp.k.to(dev), inp.v.to(dev),
+                None if inp.v_scales is None else inp.v_scales.to(dev))
+
+    ts, tb = tensors(small), tensors(big)
+    out_s = torch.full((small.n_slots, 16, 256), float("nan"), dtype=torch.float32, device=dev)
+    out_b = torch.full((big.n_slots, 16, 256), float("nan"), dtype=torch.float32, device=dev)
+    seq_s = np.asarray(small.seq_lens, dtype=np.int32)
+    seq_b = np.asarray(big.seq_lens, dtype=np.int32)
+
+    def call_small():
+        binding.attn_decode_ex(*ts, seq_s, 0, out_s, small.n_slots, 16, 8, 256, small.scale, stream=side)
+
+    def call_big():
+        binding.attn_decode_ex(*tb, seq_b, 0, out_b, big.n_slots, 16, 8, 256, big.scale, stream=side)
+
+    ws_s = binding.attn_decode_plan(small.seq_lens, 0, 16, 8, 256, v_int8=True)["workspace_bytes"]
+    ws_b = binding.attn_decode_plan(big.seq_lens, 0, 16, 8, 256, v_int8=False)["workspace_bytes"]
+    assert ws_b > 2 * ws_s, (ws_s, ws_b)   # the big call must outgrow what the small one allocated
+
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call_small()                # eager: sizes the stream's workspace for the small call only
+    torch.cuda.synchronize()
+    eager_s = out_s.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call_small()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        call_big()                  # grows the workspace: a new buffer, the old one retired
+    torch.cuda.synchronize()
+    eager_b = out_b.clone()
+    for i in range(4):
+        out_s.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_s, eager_s), f"replay {i}"
+        with torch.cuda.stream(side):
+            call_big()              # eager work on the grown workspace between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out_b, eager_b), f"eager call after replay {i}"
