@@ -32,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "attn_decode_cache_cb",
     "attn_decode_cb",
     "attn_decode_ex",
+    "attn_decode_noalloc",
     "attn_decode_plan",
     "attn_decode_cache_plan",
     "attn_decode_last_error",
@@ -85,6 +86,8 @@ def load_library():
         lib.attn_decode.argtypes = common
         lib.attn_decode_ex.restype = ctypes.c_int
         lib.attn_decode_ex.argtypes = common + [ctypes.POINTER(_Options)]
+        lib.attn_decode_noalloc.restype = ctypes.c_int
+        lib.attn_decode_noalloc.argtypes = common + [ctypes.POINTER(_Options)]
         lib.attn_decode_cache.restype = ctypes.c_int
         lib.attn_decode_cache.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -258,6 +261,24 @@ def attn_decode_ex(q, k_cache, v_cache, v_scales, seq_lens, window: int, out,
     rc = lib.attn_decode_ex(pq, pk, pv, ps, seq_arr, int(window), po, int(n_slots), int(n_q_heads),
                             int(n_kv_heads), int(head_dim), float(scale), _stream_handle(stream, dev),
                             ctypes.byref(opts))
+    if rc != ATTN_DECODE_OK:
+        _raise(lib, rc)
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, v_scales, seq_lens, window: int, out,
+                        n_slots: Optional[int], n_q_heads: int, n_kv_heads: int, head_dim: int,
+                        scale: float, stream=None, chunk: int = 0, merge_mode: int = 0,
+                        ev_partial_begin: Optional[int] = None, ev_partial_end: Optional[int] = None,
+                        path: int = 0) -> None:
+    """attn_decode_ex whose partials go to the library's fixed device scratch (no allocation;
+    calls that overlap in time on one GPU race)."""
+    lib = load_library()
+    seq_arr, n_slots, dev, (pq, pk, pv, ps, po) = _marshal(
+        q, k_cache, v_cache, v_scales, seq_lens, out, n_slots, n_q_heads, n_kv_heads, head_dim)
+    opts = _Options(int(chunk), int(merge_mode), ev_partial_begin or None, ev_partial_end or None, int(path))
+    rc = lib.attn_decode_noalloc(pq, pk, pv, ps, seq_arr, int(window), po, int(n_slots), int(n_q_heads),
+                                 int(n_kv_heads), int(head_dim), float(scale), _stream_handle(stream, dev),
+                                 ctypes.byref(opts))
     if rc != ATTN_DECODE_OK:
         _raise(lib, rc)
 

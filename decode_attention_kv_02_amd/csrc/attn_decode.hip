@@ -104,6 +104,35 @@ int acquire_workspace(int device, hipStream_t stream, int64_t flag_bytes, int64_
     return ATTN_DECODE_OK;
 }
 
+// ------------------------------------------------------------ no-allocation scratch
+
+// The partials of attn_decode_noalloc: file-scope device memory of a fixed size,
+// one copy on each GPU the library runs on, held until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is handed to kernels.
+constexpr int64_t kNoAllocScratchBytes = ATTN_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mutex;
+std::map<int, void *> g_scratch_ptr;   // device -> address of its copy of `scratch`
+
+int scratch_on_device(int device, void **ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    auto it = g_scratch_ptr.find(device);
+    if (it != g_scratch_ptr.end()) {
+        *ptr = it->second;
+        return ATTN_DECODE_OK;
+    }
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+        return fail(ATTN_DECODE_EHIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[device] = p;
+    *ptr = p;
+    return ATTN_DECODE_OK;
+}
+
 // ------------------------------------------------------------ kernel tables
 
 typedef void (*partial_fn)(const LaunchArgs);
@@ -209,9 +238,12 @@ struct VSource {
 };
 
 // Everything after the layout-specific checks: plan, workspace, launches.
+// no_alloc: the partials go to this device's `scratch` instead of the stream's
+// workspace, and the call neither allocates nor frees anything.
 int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cache,
            const VSource &vsrc, float *out, int32_t n_q, int32_t n_kv,
-           int32_t D, float scale, void *stream_ptr, const attn_decode_options *opts) {
+           int32_t D, float scale, void *stream_ptr, const attn_decode_options *opts,
+           bool no_alloc = false) {
     const int32_t chunk = opts ? opts->chunk : 0;
     const int32_t merge_mode = opts ? opts->merge_mode : 0;
     const int32_t path = opts ? opts->path : 0;
@@ -219,6 +251,11 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     CallPlan plan;
     std::string err = make_plan(spans, n_q, n_kv, D, chunk, merge_mode, plan, path, vsrc.format != kVF16);
     if (!err.empty()) return fail(ATTN_DECODE_EINVAL, err);
+    if (no_alloc && plan.workspace_bytes > kNoAllocScratchBytes)
+        return fail(ATTN_DECODE_EINVAL, "the call needs " + std::to_string(plan.workspace_bytes) +
+                                            " bytes of partials, more than the " +
+                                            std::to_string(kNoAllocScratchBytes) +
+                                            " bytes of scratch of attn_decode_noalloc");
 
     bool any_mfma = false, any_lanes = false;
     for (const LaunchGroup &lg : plan.groups) (lg.mfma ? any_mfma : any_lanes) = true;
@@ -236,8 +273,16 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     uint64_t *flags = nullptr;
     float *ws_o = nullptr;
     const int64_t data_bytes = plan.part_rows * (int64_t)(D + 2) * (int64_t)sizeof(float);
-    const int rc = acquire_workspace(device, stream, flag_region_bytes(plan.flag_rows, D), data_bytes, &flags, &ws_o);
-    if (rc != ATTN_DECODE_OK) return rc;
+    if (no_alloc) {
+        void *p = nullptr;
+        const int rc = scratch_on_device(device, &p);
+        if (rc != ATTN_DECODE_OK) return rc;
+        ws_o = static_cast<float *>(p);   // plain partials only: this entry point merges in the combine kernel
+    } else {
+        const int rc = acquire_workspace(device, stream, flag_region_bytes(plan.flag_rows, D), data_bytes, &flags,
+                                         &ws_o);
+        if (rc != ATTN_DECODE_OK) return rc;
+    }
     float *ws_ml = ws_o ? ws_o + plan.part_rows * D : nullptr;
 
     const double scale_log2 = (double)scale * 1.4426950408889634074;  // scale * log2(e)
@@ -353,7 +398,8 @@ int check_pointers(const void *q, const void *k_cache, const VSource &vsrc,
 
 int run(const void *q, const void *k_cache, const VSource &vsrc,
         const int32_t *seq_lens, int32_t window, float *out, int32_t n_slots, int32_t n_q,
-        int32_t n_kv, int32_t D, float scale, void *stream_ptr, const attn_decode_options *opts) {
+        int32_t n_kv, int32_t D, float scale, void *stream_ptr, const attn_decode_options *opts,
+        bool no_alloc = false) {
     g_last_error.clear();
     const int32_t chunk = opts ? opts->chunk : 0;
     const int32_t merge_mode = opts ? opts->merge_mode : 0;
@@ -377,7 +423,7 @@ int run(const void *q, const void *k_cache, const VSource &vsrc,
 
     std::vector<QuerySpan> spans;
     spans_packed(seq_lens, n_slots, window, n_kv, spans);
-    return launch(spans, q, k_cache, vsrc, out, n_q, n_kv, D, scale, stream_ptr, opts);
+    return launch(spans, q, k_cache, vsrc, out, n_q, n_kv, D, scale, stream_ptr, opts, no_alloc);
 }
 
 int run_cache(const void *q, const void *k_cache, const VSource &vsrc,
@@ -586,6 +632,19 @@ extern "C" int attn_decode_ex(const void *q, const void *k_cache, const void *v_
                               const attn_decode_options *opts) {
     return run(q, k_cache, VSource::plain_or_int8(v_cache, v_scales), seq_lens, window, out, n_slots, n_q_heads,
                n_kv_heads, head_dim, scale, stream, opts);
+}
+
+extern "C" int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                   const void *v_scales, const int32_t *seq_lens, int32_t window,
+                                   float *out, int32_t n_slots, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, float scale, void *stream,
+                                   const attn_decode_options *opts) {
+    if (opts && opts->merge_mode == kMergeInKernel) {
+        g_last_error.clear();
+        return fail(ATTN_DECODE_EINVAL, "attn_decode_noalloc merges in the combine kernel: merge_mode must be 0 or 1");
+    }
+    return run(q, k_cache, VSource::plain_or_int8(v_cache, v_scales), seq_lens, window, out, n_slots, n_q_heads,
+               n_kv_heads, head_dim, scale, stream, opts, true);
 }
 
 extern "C" int attn_decode_cb(const void *q, const void *k_cache, const void *v_codes,

@@ -142,6 +142,32 @@ int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                    int32_t head_dim, float scale, void *stream,
                    const attn_decode_options *opts);
 
+/* Bytes of device scratch attn_decode_noalloc has for a call's partials. */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+
+/*
+ * attn_decode_noalloc -- attn_decode_ex for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It calls no hipMalloc, hipFree or other allocating
+ * routine.  The per-chunk partials go to a fixed device array of
+ * ATTN_DECODE_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, held
+ * until the process ends) instead of a per-stream workspace; a call whose
+ * partials need more (attn_decode_plan's workspace_bytes) returns
+ * ATTN_DECODE_EINVAL before any GPU work.  Split slots are always merged by
+ * the combine kernel (opts->merge_mode 2 is rejected), so the results equal
+ * attn_decode_ex's bitwise.  Nothing in the array has to start at zero: every
+ * partial a merge reads was written by the same call.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from several host threads without ordering) race and
+ * must not be issued.  Arguments, layout, asynchrony and errors are as for
+ * attn_decode_ex; opts may be NULL.
+ */
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                        const void *v_scales, const int32_t *seq_lens, int32_t window,
+                        float *out, int32_t n_slots, int32_t n_q_heads, int32_t n_kv_heads,
+                        int32_t head_dim, float scale, void *stream,
+                        const attn_decode_options *opts);
+
 /*
  * attn_decode_cache -- decode attention over a fixed-capacity KV cache.
  *
