@@ -736,26 +736,52 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
         }
     };
 
-    // Two register buffers: the loads of the next iteration are in flight
-    // while the current one is computed.
     constexpr int STEP = kWaves * RW;
-    Frag<U> fa, fb;
+    // Register buffers of loads in flight: three where the third keeps the
+    // variant's occupancy (one or two rows up to head_dim 256, one row at 512),
+    // else two.  The rows of each iteration and the order they are consumed in
+    // do not change, so neither do the results.
+    constexpr int NBUF = (NR == 1 || (NR == 2 && D <= 256)) ? 3 : 2;
     int wb = cbeg + w * RW;
-    if (wb < cend) load(wb, fa);
-    if constexpr (VF == kVCB) {
-        s_cb[tid] = args.codebook[tid & args.cb_mask] * args.cb_scale;
-        __syncthreads();
-    }
-    while (wb < cend) {
-        int wn = wb + STEP;
-        if (wn < cend) load(wn, fb);
-        consume(wb, fa);
-        wb = wn;
-        if (wb >= cend) break;
-        wn = wb + STEP;
-        if (wn < cend) load(wn, fa);
-        consume(wb, fb);
-        wb = wn;
+    if constexpr (NBUF == 3) {
+        Frag<U> f0, f1, f2;
+        if (wb < cend) load(wb, f0);
+        if (wb + STEP < cend) load(wb + STEP, f1);
+        if constexpr (VF == kVCB) {
+            s_cb[tid] = args.codebook[tid & args.cb_mask] * args.cb_scale;
+            __syncthreads();
+        }
+        while (wb < cend) {
+            if (wb + 2 * STEP < cend) load(wb + 2 * STEP, f2);
+            consume(wb, f0);
+            wb += STEP;
+            if (wb >= cend) break;
+            if (wb + 2 * STEP < cend) load(wb + 2 * STEP, f0);
+            consume(wb, f1);
+            wb += STEP;
+            if (wb >= cend) break;
+            if (wb + 2 * STEP < cend) load(wb + 2 * STEP, f1);
+            consume(wb, f2);
+            wb += STEP;
+        }
+    } else {
+        Frag<U> fa, fb;
+        if (wb < cend) load(wb, fa);
+        if constexpr (VF == kVCB) {
+            s_cb[tid] = args.codebook[tid & args.cb_mask] * args.cb_scale;
+            __syncthreads();
+        }
+        while (wb < cend) {
+            int wn = wb + STEP;
+            if (wn < cend) load(wn, fb);
+            consume(wb, fa);
+            wb = wn;
+            if (wb >= cend) break;
+            wn = wb + STEP;
+            if (wn < cend) load(wn, fa);
+            consume(wb, fb);
+            wb = wn;
+        }
     }
 
     // ---- merge the P lane groups of the wave (lanes lane ^ off share the dims)
