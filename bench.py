@@ -40,9 +40,9 @@ One JSON line is printed.  Besides the contract fields it carries
     plus the codebook-V presets (``attn_decode_cb`` followed by ``attn_fwht_undo``
     in place; bytes = fp16 K, one index byte per V element and the fp32 norms),
     the fixed-capacity cache presets (``attn_decode_cache``: a
-    sliding-window ring layer and a speculative-verify shape; for the latter
-    ``kv_bytes`` counts what the kernels read, every query its own rows, and
-    ``unique_kv_bytes`` each cache row once), and the KV-append presets
+    sliding-window ring layer and a speculative-verify shape; rates and
+    fractions count ``kv_bytes``, each cache row once, while
+    ``kv_bytes_per_query`` counts every query's own rows), and the KV-append presets
     (``attn_kv_append``; ``bytes`` = fp32 K and V read plus the fp16 K and the
     fp16 or int8 V and scales written).
 """
@@ -108,9 +108,13 @@ def cache_kv_bytes(cfg) -> tuple:
 
 
 def kernel_source_digest(kernel: str = "attn_partial_kernel") -> str:
-    """First 16 hex digits of the sha256 of the partial kernel's source header."""
-    with open(MFMA_KERNEL_SRC if kernel == "attn_partial_mfma_kernel" else KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """First 16 hex digits of the sha256 of the kernels' source headers (the lane kernel's, and the
+    matrix-core kernel's, which includes it), so a summary taken on other kernel code never matches."""
+    h = hashlib.sha256()
+    for path in (KERNEL_SRC, MFMA_KERNEL_SRC):
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload: str, window: int, kernel: str = "attn_partial_kernel"):
@@ -556,10 +560,9 @@ def main(argv=None) -> int:
             "algorithmic_bytes_per_launch": nbytes,
         },
     }
-    # secondary: the same achieved rate against a copy measured on this GPU (read + write bytes)
-    copy_gbs = measured_copy_gbs(dev)
-    result["roofline"]["measured_copy_gbs"] = round(copy_gbs, 1)
-    result["roofline"]["frac_of_measured_copy"] = round(achieved / copy_gbs, 4)
+    # context only, not a ceiling: a plain 1 GiB device copy on this GPU, read plus written bytes
+    # per second (a copy pays for its writes, so a read-only stream can exceed it)
+    result["device_copy_gbs"] = round(measured_copy_gbs(dev), 1)
 
     # ---- every preset: cold (flushed) and warm
     if not args.quick:
@@ -763,16 +766,19 @@ def main(argv=None) -> int:
             cold = statistics.median(per_call_us(flush_then_cache_call, args.reps) -
                                      per_call_us(lambda: flush.sum(), args.reps) for _ in range(5))
             g_us = graph_us_per_call(lambda st: cache_call(st=st))
+            # rates and fractions on the unique bytes (each cache row once, as HBM serves it);
+            # kv_bytes_per_query counts every query's own rows, as if nothing were shared
             per.append({
-                "workload": cw.name, "window": cw.window, "kv_bytes": read_b, "unique_kv_bytes": uniq_b,
+                "workload": cw.name, "window": cw.window, "kv_bytes": uniq_b, "kv_bytes_per_query": read_b,
                 "warm_us_per_call": round(warm, 2),
-                "warm_gbs": round(read_b / (warm * 1e-6) / 1e9, 1),
-                "warm_hbm_frac": round(read_b / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "warm_gbs": round(uniq_b / (warm * 1e-6) / 1e9, 1),
+                "warm_hbm_frac": round(uniq_b / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "cold_us_per_call": round(cold, 2),
-                "cold_gbs": round(read_b / (cold * 1e-6) / 1e9, 1),
-                "cold_hbm_frac": round(read_b / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "cold_gbs": round(uniq_b / (cold * 1e-6) / 1e9, 1),
+                "cold_hbm_frac": round(uniq_b / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "graph_us_per_call": round(g_us, 2),
-                "graph_gbs": round(read_b / (g_us * 1e-6) / 1e9, 1),
+                "graph_gbs": round(uniq_b / (g_us * 1e-6) / 1e9, 1),
+                "graph_hbm_frac": round(uniq_b / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             })
             print(f"[bench] {cw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), cold {cold:.2f} us",
                   file=sys.stderr, flush=True)
