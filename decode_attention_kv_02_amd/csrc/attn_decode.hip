@@ -30,7 +30,6 @@ using namespace attn_decode_impl;
 
 static_assert(ATTN_DECODE_MAX_SLOTS_PER_LAUNCH == kMaxSlotsPerLaunch, "slot table size");
 static_assert(ATTN_DECODE_MAX_CHUNKS == kMaxChunks, "chunk bound");
-static_assert(kCombineMaxChunks >= kMaxChunks, "combine LDS holds every chunk weight");
 static_assert(kSingleLaunchMaxChunks <= kMaxChunks, "single-launch merge bound");
 static_assert(sizeof(LaunchArgs) <= 4096, "kernel arguments stay within 4 KiB");
 static_assert(sizeof(AppendArgs) <= 4096, "kernel arguments stay within 4 KiB");
@@ -346,7 +345,7 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     }
     for (const LaunchGroup &lg : plan.groups) {
         fill(lg, false);
-        const int64_t grid = lg.items + lg.tail_rows * (D / kCombineDims);   // partial, then merge workgroups
+        const int64_t grid = lg.items + lg.tail_rows * merge_groups(D);   // partial, then merge workgroups
         hipLaunchKernelGGL(lg.mfma ? pk_mfma : pk_lanes, dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
@@ -358,7 +357,7 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     for (const LaunchGroup &lg : plan.groups) {
         if (lg.combine_rows == 0) continue;
         fill(lg, true);
-        hipLaunchKernelGGL(ck, dim3((unsigned)(lg.combine_rows * (D / kCombineDims))), dim3(kThreads), 0, stream, args);
+        hipLaunchKernelGGL(ck, dim3((unsigned)(lg.combine_rows * (D / kCombineDims))), dim3(kCombineThreads), 0, stream, args);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("combine kernel launch: ") + hipGetErrorString(e));
     }

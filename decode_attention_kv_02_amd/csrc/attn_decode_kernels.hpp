@@ -184,154 +184,97 @@ __device__ __forceinline__ int xcd_item(int b, int n_items, int n_sub) {
 
 // ---------------------------------------------------------------- chunk merge
 
-constexpr int kCombineMaxChunks = 4096;
-// Dims of one output row merged by one merge workgroup.
+// Dims of one output row merged by one wave: lane l owns dim slice * 64 + l.
 constexpr int kCombineDims = 64;
-// Partial rows each merge thread loads before the chunk weights are known.
-constexpr int kCombinePreload = 4;
+static_assert(kCombineDims == kMergeSliceDims, "one merge slice per flagged block");
+static_assert(kWaves == kMergeSlicesPerGroup, "a merge workgroup of the partial kernel: one slice per wave");
+// Chunks whose partial values a merging wave loads before it uses them.
+constexpr int kMergeBatch = 32;
+// The combine kernel's workgroup: one wave.
+constexpr int kCombineThreads = 64;
 
-// LDS of one merge workgroup that merges up to NC chunks.
-template <int NC>
-struct MergeSmem {
-    float w[NC];                                         // chunk weights 2^(M_c - M*)
-    float4 acc[kThreads / (kCombineDims / 4)][kCombineDims / 4];
-    float red[kWaves];
-};
+// x of lane `lane` (the same for every lane), through the LDS crossbar (no LDS
+// allocation, no SGPR).
+__device__ __forceinline__ float lane_value(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(lane << 2, __builtin_bit_cast(int, x)));
+}
 
 // Log-sum-exp merge of the sd.n_chunks partials of query head h (of the query
-// whose descriptor is sd) for the 64 output dims of `slice`, by one 256-thread
-// workgroup:  M* = max_c M_c,  w_c = 2^(M_c - M*),  S* = sum_c w_c S_c,
-// out = sum_c w_c O_c / S*  (S* == 0 gives zeros).  16 groups of 16 threads
-// split the chunks; each thread owns 4 dims (16-byte loads of the partial rows,
-// coalesced over the 16 threads).  The first loads of the partial rows are
-// issued together with the loads of the chunk statistics, so the merge costs
-// about one memory round trip; the 16 group sums are added in LDS in a fixed
-// order, so the result does not depend on which kernel runs the merge.
-template <int D, int NC>
-__device__ __forceinline__ void merge_slice(const LaunchArgs &args, const SlotDesc &sd, int h, int slice,
-                                            MergeSmem<NC> &sm) {
-    constexpr int TPR = kCombineDims / 4;       // threads per chunk row of the slice
-    constexpr int CG = kThreads / TPR;          // chunk groups
+// whose descriptor is sd) for the 64 output dims of `slice`, by one wave:
+//   M* = max_c M_c;
+//   per block of 64 chunks, lane l takes chunk c0 + l: w = 2^(M_c - M*), and its
+//   share of S* = fmaf(w, S_c, share); then every lane adds w_c O_c[its dim]
+//   for the block's chunks in chunk order (w_c read from lane c - c0);
+//   S* = the wave sum of the shares; out = acc / S* (S* == 0 gives zeros).
+// Each partial row of the slice is one whole-wave load of 256 consecutive
+// bytes.  The first kMergeBatch rows are loaded together with the statistics,
+// so a merge of up to 32 chunks takes one memory round trip, and there is no
+// LDS and no barrier.  tail_merge runs the same arithmetic in the same order.
+template <int D>
+__device__ __forceinline__ void merge_wave(const LaunchArgs &args, const SlotDesc &sd, int h, int slice) {
+    const int lane = threadIdx.x & 63;
     const int nc = sd.n_chunks;
     const int64_t base = sd.part_row0 + (int64_t)h * nc;
-    const int64_t slot_g = sd.slot_idx;
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int cg = tid / TPR;
-    const int j = tid - cg * TPR;
-    const int d0 = slice * kCombineDims + 4 * j;
-    const float *src = args.ws_o + base * D + d0;
-    const float *ml = args.ws_ml + base * 2;
+    const float *src = args.ws_o + base * D + slice * kCombineDims + lane;    // chunk c at src + c * D
+    const float2 *ml = reinterpret_cast<const float2 *>(args.ws_ml) + base;   // chunk c's (M, S)
 
-    // partial rows of this thread's first chunks (independent of the weights)
-    float4 pre[kCombinePreload];
+    // the first batch of partial values (indices past the last chunk re-read it; unused)
+    float o[kMergeBatch];
 #pragma unroll
-    for (int u = 0; u < kCombinePreload; ++u) {
-        const int c = cg + u * CG;
-        pre[u] = c < nc ? *(const float4 *)(src + (int64_t)c * D) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int u = 0; u < kMergeBatch; ++u) o[u] = src[(int64_t)min(u, nc - 1) * D];
+    const float2 st0 = lane < nc ? ml[lane] : make_float2(-INFINITY, 0.f);
 
-    // M* over chunks
-    float mx = -INFINITY;
-    for (int c = tid; c < nc; c += kThreads) mx = fmaxf(mx, ml[2 * c]);
-    mx = wave_max(mx);
-    if ((tid & 63) == 0) sm.red[w] = mx;
-    __syncthreads();
-    mx = sm.red[0];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, sm.red[ww]);
+    float mloc = st0.x;
+    for (int c = lane + 64; c < nc; c += 64) mloc = fmaxf(mloc, ml[c].x);
+    const float mx = wave_max(mloc);
     const float ms = (mx == -INFINITY) ? 0.f : mx;
-    __syncthreads();
 
-    // chunk weights 2^(M_c - M*) and S*
-    float ls = 0.f;
-    for (int c = tid; c < nc; c += kThreads) {
-        const float wc = fast_exp2(ml[2 * c] - ms);
-        sm.w[c] = wc;
-        ls += wc * ml[2 * c + 1];
-    }
-    ls = wave_sum(ls);
-    if ((tid & 63) == 0) sm.red[w] = ls;
-    __syncthreads();
-    float lsum = 0.f;
+    float acc = 0.f, share = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+        const int c = c0 + lane;
+        const float2 st = c0 == 0 ? st0 : (c < nc ? ml[c] : make_float2(-INFINITY, 0.f));
+        const float w = c < nc ? fast_exp2(st.x - ms) : 0.f;
+        share = fmaf(w, st.y, share);
+        for (int b0 = 0; b0 < 64 && c0 + b0 < nc; b0 += kMergeBatch) {
+            if (c0 + b0 > 0) {
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) lsum += sm.red[ww];
-
-    // weighted sum of the partial O rows over this thread's chunks, in chunk order
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int u = 0; u < kMergeBatch; ++u) o[u] = src[(int64_t)min(c0 + b0 + u, nc - 1) * D];
+            }
 #pragma unroll
-    for (int u = 0; u < kCombinePreload; ++u) {
-        const int c = cg + u * CG;
-        if (c < nc) {
-            const float wc = sm.w[c];
-            acc.x = fmaf(wc, pre[u].x, acc.x);
-            acc.y = fmaf(wc, pre[u].y, acc.y);
-            acc.z = fmaf(wc, pre[u].z, acc.z);
-            acc.w = fmaf(wc, pre[u].w, acc.w);
+            for (int u = 0; u < kMergeBatch; ++u)
+                if (c0 + b0 + u < nc) acc = fmaf(lane_value(w, b0 + u), o[u], acc);
         }
     }
-    int c = cg + kCombinePreload * CG;
-    for (; c + 3 * CG < nc; c += 4 * CG) {
-        float4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *(const float4 *)(src + (int64_t)(c + u * CG) * D);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float wc = sm.w[c + u * CG];
-            acc.x = fmaf(wc, v[u].x, acc.x);
-            acc.y = fmaf(wc, v[u].y, acc.y);
-            acc.z = fmaf(wc, v[u].z, acc.z);
-            acc.w = fmaf(wc, v[u].w, acc.w);
-        }
-    }
-    for (; c < nc; c += CG) {
-        const float4 v = *(const float4 *)(src + (int64_t)c * D);
-        const float wc = sm.w[c];
-        acc.x = fmaf(wc, v.x, acc.x);
-        acc.y = fmaf(wc, v.y, acc.y);
-        acc.z = fmaf(wc, v.z, acc.z);
-        acc.w = fmaf(wc, v.w, acc.w);
-    }
-    sm.acc[cg][j] = acc;
-    __syncthreads();
-    if (tid < TPR) {
-        float4 t = sm.acc[0][tid];
-#pragma unroll
-        for (int g = 1; g < CG; ++g) {
-            const float4 u = sm.acc[g][tid];
-            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-        }
-        float4 r;
-        r.x = (lsum == 0.f) ? 0.f : t.x / lsum;
-        r.y = (lsum == 0.f) ? 0.f : t.y / lsum;
-        r.z = (lsum == 0.f) ? 0.f : t.z / lsum;
-        r.w = (lsum == 0.f) ? 0.f : t.w / lsum;
-        *(float4 *)(args.out + (slot_g * args.n_q + h) * D + slice * kCombineDims + 4 * tid) = r;
-    }
+    const float lsum = wave_sum(share);
+    args.out[((int64_t)sd.slot_idx * args.n_q + h) * D + slice * kCombineDims + lane] =
+        (lsum == 0.f) ? 0.f : acc / lsum;
 }
 
 // Single-launch merge.  The workgroups past the n_items partial workgroups of a
-// launch each merge one (query head, 64-dim slice) of a split query, in the
-// same launch, as soon as every chunk of it has been written.
+// launch merge, in the same launch, the split queries' heads, each wave one
+// 64-dim slice of one query head (a workgroup takes up to four slices of a
+// head), as soon as every chunk of it has been written.
 //
 // Publication needs no wait.  A fused query's partial workgroup writes each
 // value as one 8-byte pair {value bits, 1} with an agent-scope store (on
 // gfx942/gfx950 such stores go through to the memory side of the per-XCD L2
-// caches); for every 64-dim slice it writes the pairs of M and S, then the 64
-// value pairs.  An aligned 8-byte access is single-copy atomic, so a pair whose
-// flag reads 1 holds the value that came with that flag: each pair validates
-// itself, whatever order the stores arrive in (the protocol of RCCL's "LL"
-// transfers).  The workgroup ends without waiting for any of it.
+// caches); per 64-dim slice of a partial row, a block of kFlagPairsPerSlice
+// pairs holds the 64 value pairs, then the pairs of M and S.  An aligned 8-byte
+// access is single-copy atomic, so a pair whose flag reads 1 holds the value
+// that came with that flag: each pair validates itself, whatever order the
+// stores arrive in (the protocol of RCCL's "LL" transfers).  The workgroup ends
+// without waiting for any of it.
 //
-// One thread of the merge workgroup first polls a single pair, the M of the
-// last chunk (the last of the query's chunks to be dispatched), with a sleep
-// between polls, so that the merge workgroups, which may be resident long
-// before their chunks finish, load almost nothing while they wait.  Then the
-// workgroup reads every pair it needs, reloads, all at once, those whose flag
-// is not yet 1, and after using a pair writes zeros back over it.  Each pair is
+// Lane 0 of the merging wave first polls a single pair, the M of the last chunk
+// (the last of the query's chunks to be dispatched), with a sleep between
+// polls, so that the merge workgroups, which may be resident long before their
+// chunks finish, load almost nothing while they wait.  Then the wave reads
+// every pair it needs (lane c the statistics of chunk c; one whole-wave load of
+// 512 consecutive bytes per chunk's values), reloads those whose flag is not
+// yet 1, and after using a pair writes zeros back over it.  Each pair is
 // written by exactly one partial workgroup and read and cleared by exactly one
-// merge workgroup of the same call, so every call leaves the region all zero,
-// as the next call requires.  (Two designs with an arrival counter per
+// merging wave of the same call, so every call leaves the region all zero, as
+// the next call requires.  (Two designs with an arrival counter per
 // (query, kv head) measured far slower: each chunk waiting for its stores to
 // complete before counting itself, and each chunk counting itself without
 // waiting, the pairs still carrying the data.)
@@ -340,7 +283,7 @@ __device__ __forceinline__ void merge_slice(const LaunchArgs &args, const SlotDe
 // workgroup has a larger id than every partial workgroup, so each partial
 // workgroup is resident or finished before any merge workgroup on its XCD can
 // hold a slot: every awaited pair arrives.  The polls are still bounded
-// (kTailMaxPolls per thread, about a second); a merge that gives up writes NaN,
+// (kTailMaxPolls per lane, about a second); a merge that gives up writes NaN,
 // so a failure shows instead of hanging the GPU.
 constexpr int kTailMaxPolls = 1 << 20;
 
@@ -360,146 +303,92 @@ __device__ __forceinline__ void clear_pair(uint64_t *p) {
 __device__ __forceinline__ float pair_value(uint64_t x) { return __builtin_bit_cast(float, (uint32_t)x); }
 __device__ __forceinline__ bool pair_ready(uint64_t x) { return (uint32_t)(x >> 32) == 1u; }
 
-// The merge of one (query head, 64-dim slice) from flagged pairs: the arithmetic
-// of merge_slice, in the same order, so both merges give the same bits.
+// The merge of one (query head, 64-dim slice) per wave from flagged pairs: the
+// arithmetic of merge_wave, in the same order, so both merges give the same
+// bits.  At most 64 chunks (lane c holds chunk c's statistics); the values are
+// read kTailBatch chunks at a time.
+constexpr int kTailBatch = 16;
 template <int D>
 __device__ __forceinline__ void tail_merge(const LaunchArgs &args) {
     constexpr int SLICES = D / kCombineDims;
-    constexpr int TPR = kCombineDims / 4;       // threads per chunk row of the slice
-    constexpr int CG = kThreads / TPR;          // chunk groups
-    constexpr int64_t ROW = (int64_t)SLICES * kFlagPairsPerSlice;   // pairs per partial row
-    static_assert(kCombineDims == kMergeSliceDims, "one merge slice per flagged block");
-    static_assert(kSingleLaunchMaxChunks <= kThreads, "one thread per chunk's statistics");
-    __shared__ MergeSmem<kSingleLaunchMaxChunks> sm;
-    __shared__ int s_bad;
+    constexpr int TG = (SLICES + kWaves - 1) / kWaves;                  // merge workgroups per query head
+    constexpr int64_t CS = (int64_t)SLICES * kFlagPairsPerSlice;        // pairs from a chunk's block to the next's
+    static_assert(kSingleLaunchMaxChunks <= 64, "one chunk's statistics per lane");
+    static_assert(kTailBatch <= kMergeBatch && 64 % kTailBatch == 0, "batches of whole chunks");
     const int jt = (int)blockIdx.x - args.n_items;
-    const int row = jt / SLICES;
-    const int slice = jt - row * SLICES;
+    const int row = jt / TG;
+    const int slice = (jt - row * TG) * kWaves + (int)(threadIdx.x >> 6);
+    if (slice >= SLICES) return;   // a wave with no slice of this head
     const int si = upper_index(args.n_slots, row, [&](int i) { return args.tkey[i]; });
     const SlotDesc sd = args.slot[si];
     const int h = row - sd.comb_begin;
     const int nc = sd.n_chunks;
-    uint64_t *blk = args.flags + ((int64_t)sd.flag_row0 + (int64_t)h * nc) * ROW + slice * kFlagPairsPerSlice;
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int cg = tid / TPR;
-    const int j = tid - cg * TPR;
+    const int lane = threadIdx.x & 63;
+    uint64_t *const blk =
+        args.flags + (((int64_t)sd.flag_row0 + (int64_t)h * nc) * SLICES + slice) * kFlagPairsPerSlice;
     int polls = 0;
-    if (tid == 0) {
-        s_bad = 0;
-        const uint64_t *p = blk + (int64_t)(nc - 1) * ROW;   // the last chunk's M
+    bool bad = false;
+    if (lane == 0) {
+        const uint64_t *p = blk + (int64_t)(nc - 1) * CS + kMergeSliceDims;   // the last chunk's M
         while (!pair_ready(load_pair(p)) && polls < kTailMaxPolls) {
             __builtin_amdgcn_s_sleep(16);
             ++polls;
         }
         polls = 0;
     }
-    __syncthreads();
 
-    // chunk statistics: thread c reads chunk c's (M, S), reloading until both have arrived
+    // statistics: lane c holds chunk c's (M, S)
     float mc = -INFINITY, sc = 0.f;
-    if (tid < nc) {
-        uint64_t *p = blk + (int64_t)tid * ROW;
-        uint64_t a = load_pair(p), b = load_pair(p + 1);
-        while (!(pair_ready(a) && pair_ready(b)) && polls < kTailMaxPolls) {
+    if (lane < nc) {
+        uint64_t *p = blk + (int64_t)lane * CS + kMergeSliceDims;
+        uint64_t x = load_pair(p), y = load_pair(p + 1);
+        while (!(pair_ready(x) && pair_ready(y)) && polls < kTailMaxPolls) {
             __builtin_amdgcn_s_sleep(2);
-            if (!pair_ready(a)) a = load_pair(p);
-            if (!pair_ready(b)) b = load_pair(p + 1);
+            if (!pair_ready(x)) x = load_pair(p);
+            if (!pair_ready(y)) y = load_pair(p + 1);
             ++polls;
         }
-        if (!(pair_ready(a) && pair_ready(b))) s_bad = 1;
-        mc = pair_value(a);
-        sc = pair_value(b);
+        bad |= !(pair_ready(x) && pair_ready(y));
+        mc = pair_value(x);
+        sc = pair_value(y);
         clear_pair(p);
         clear_pair(p + 1);
     }
-    float mx = wave_max(mc);
-    if ((tid & 63) == 0) sm.red[w] = mx;
-    __syncthreads();
-    mx = sm.red[0];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) mx = fmaxf(mx, sm.red[ww]);
+    const float mx = wave_max(mc);
     const float ms = (mx == -INFINITY) ? 0.f : mx;
-    __syncthreads();
-    float ls = 0.f;
-    if (tid < nc) {
-        const float wc = fast_exp2(mc - ms);
-        sm.w[tid] = wc;
-        ls = wc * sc;
-    }
-    ls = wave_sum(ls);
-    if ((tid & 63) == 0) sm.red[w] = ls;
-    __syncthreads();
-    float lsum = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) lsum += sm.red[ww];
+    const float w = lane < nc ? fast_exp2(mc - ms) : 0.f;
+    const float share = fmaf(w, sc, 0.f);
 
-    // this thread's 4 dims over its chunks cg, cg + CG, ... in chunk order, kCombinePreload
-    // chunks per batch; pairs not yet in are reloaded, all at once
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    bool bad = false;
-    for (int c0 = cg; c0 < nc; c0 += kCombinePreload * CG) {
-        uint64_t x[kCombinePreload][4];
+    float acc = 0.f;
+    uint64_t *const col = blk + lane;   // this lane's value pair of chunk c: col + c * CS
+    for (int b0 = 0; b0 < nc; b0 += kTailBatch) {
+        uint64_t x[kTailBatch];
 #pragma unroll
-        for (int u = 0; u < kCombinePreload; ++u) {
-            const int c = c0 + u * CG;
-            const uint64_t *p = blk + (int64_t)c * ROW + 2 + 4 * j;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[u][e] = c < nc ? load_pair(p + e) : uint64_t(0);
-        }
+        for (int u = 0; u < kTailBatch; ++u) x[u] = load_pair(col + (int64_t)min(b0 + u, nc - 1) * CS);
         for (;;) {
             bool all = true;
 #pragma unroll
-            for (int u = 0; u < kCombinePreload; ++u)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) all &= (c0 + u * CG >= nc) || pair_ready(x[u][e]);
+            for (int u = 0; u < kTailBatch; ++u) all &= (b0 + u >= nc) || pair_ready(x[u]);
             if (all || polls >= kTailMaxPolls) break;
             __builtin_amdgcn_s_sleep(2);
             ++polls;
 #pragma unroll
-            for (int u = 0; u < kCombinePreload; ++u) {
-                const int c = c0 + u * CG;
-                const uint64_t *p = blk + (int64_t)c * ROW + 2 + 4 * j;
+            for (int u = 0; u < kTailBatch; ++u)
+                if (b0 + u < nc && !pair_ready(x[u])) x[u] = load_pair(col + (int64_t)(b0 + u) * CS);
+        }
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (c < nc && !pair_ready(x[u][e])) x[u][e] = load_pair(p + e);
+        for (int u = 0; u < kTailBatch; ++u) {
+            if (b0 + u < nc) {
+                bad |= !pair_ready(x[u]);
+                acc = fmaf(lane_value(w, b0 + u), pair_value(x[u]), acc);
+                clear_pair(col + (int64_t)(b0 + u) * CS);
             }
         }
-#pragma unroll
-        for (int u = 0; u < kCombinePreload; ++u) {
-            const int c = c0 + u * CG;
-            if (c >= nc) continue;
-            uint64_t *p = blk + (int64_t)c * ROW + 2 + 4 * j;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bad |= !pair_ready(x[u][e]);
-                clear_pair(p + e);
-            }
-            const float wc = sm.w[c];
-            acc.x = fmaf(wc, pair_value(x[u][0]), acc.x);
-            acc.y = fmaf(wc, pair_value(x[u][1]), acc.y);
-            acc.z = fmaf(wc, pair_value(x[u][2]), acc.z);
-            acc.w = fmaf(wc, pair_value(x[u][3]), acc.w);
-        }
     }
-    if (bad) s_bad = 1;
-    sm.acc[cg][j] = acc;
-    __syncthreads();
-    if (tid < TPR) {
-        float4 t = sm.acc[0][tid];
-#pragma unroll
-        for (int g = 1; g < CG; ++g) {
-            const float4 u = sm.acc[g][tid];
-            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-        }
-        float4 r;
-        r.x = (lsum == 0.f) ? 0.f : t.x / lsum;
-        r.y = (lsum == 0.f) ? 0.f : t.y / lsum;
-        r.z = (lsum == 0.f) ? 0.f : t.z / lsum;
-        r.w = (lsum == 0.f) ? 0.f : t.w / lsum;
-        if (s_bad) r = make_float4(NAN, NAN, NAN, NAN);
-        *(float4 *)(args.out + ((int64_t)sd.slot_idx * args.n_q + h) * D + slice * kCombineDims + 4 * tid) = r;
-    }
+    const float lsum = wave_sum(share);
+    float r = (lsum == 0.f) ? 0.f : acc / lsum;
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) r = NAN;
+    args.out[((int64_t)sd.slot_idx * args.n_q + h) * D + slice * kCombineDims + lane] = r;
 }
 
 // ---------------------------------------------------------------- partial kernel
@@ -856,10 +745,10 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
             constexpr int SL = D / kMergeSliceDims;
             const int64_t r = (int64_t)mb.flag_row0 + (int64_t)(h0 + g % GB) * mb.n_chunks + c;
             uint64_t *blk = args.flags + (r * SL + d / kMergeSliceDims) * kFlagPairsPerSlice;
-            store_pair(blk + 2 + (d % kMergeSliceDims), acc);
+            store_pair(blk + (d % kMergeSliceDims), acc);
             if (d % kMergeSliceDims == 0) {
-                store_pair(blk, mx);
-                store_pair(blk + 1, lsum);
+                store_pair(blk + kMergeSliceDims, mx);
+                store_pair(blk + kMergeSliceDims + 1, lsum);
             }
         } else {
             const int64_t prow = mb.part_row0 + (int64_t)(h0 + g % GB) * mb.n_chunks + c;
@@ -874,17 +763,16 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
 
 // ---------------------------------------------------------------- combine kernel
 
-// One workgroup per (query, query head, 64-dim slice) of a query with several
+// One wave per (query, query head, 64-dim slice) of a query with several
 // chunks, after the partial kernel has finished.
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_combine_kernel(const LaunchArgs args) {
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const LaunchArgs args) {
     constexpr int SLICES = D / kCombineDims;
-    __shared__ MergeSmem<kCombineMaxChunks> sm;
     const int row = blockIdx.x / SLICES;
     const int slice = blockIdx.x - row * SLICES;
     const int si = upper_index(args.n_slots, row, [&](int i) { return args.key[i]; });
     const SlotDesc sd = args.slot[si];
-    merge_slice<D, kCombineMaxChunks>(args, sd, row - sd.comb_begin, slice, sm);
+    merge_wave<D>(args, sd, row - sd.comb_begin, slice);
 }
 
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t value) {

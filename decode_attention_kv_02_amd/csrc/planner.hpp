@@ -98,22 +98,30 @@ struct CallPlan {
 };
 
 // With the single-launch merge, lane-kernel queries split into at most this many
-// chunks (the merge workgroup's LDS holds one weight per chunk) that are not part
-// of a query group are merged by workgroups at the end of the partial kernel's
-// own grid; the others still go to the combine kernel.
-constexpr int kSingleLaunchMaxChunks = 256;
+// chunks (a merging wave keeps one chunk's statistics per lane) that are not
+// part of a query group are merged by workgroups at the end of the partial
+// kernel's own grid; the others still go to the combine kernel.
+constexpr int kSingleLaunchMaxChunks = 64;
 
 // kMergeAuto currently selects the combine kernel.
 enum MergeMode { kMergeAuto = 0, kMergeCombineKernel = 1, kMergeInKernel = 2 };
 
 // A fused query's partial rows are written as 8-byte pairs {value bits, 1}: per
-// 64-dim slice of a row, the pair of M, the pair of S, then 64 value pairs.  The
-// pairs sit at the front of the workspace in a 256-byte aligned region that is
-// all zero between calls (each call clears the pairs it wrote).
+// 64-dim slice of a row, a block of 80 pairs (640 bytes, five 128-byte lines)
+// holding the 64 value pairs, the pair of M, the pair of S and 14 unused pairs,
+// so every slice's values start on a 128-byte line.  The pairs sit at the front
+// of the workspace in a 256-byte aligned region that is all zero between calls
+// (each call clears the pairs it wrote).
 constexpr int kMergeSliceDims = 64;
-constexpr int kFlagPairsPerSlice = kMergeSliceDims + 2;
+constexpr int kFlagPairsPerSlice = 80;
 inline int64_t flag_region_bytes(int64_t flag_rows, int32_t head_dim) {
     return (flag_rows * (head_dim / kMergeSliceDims) * kFlagPairsPerSlice * 8 + 255) / 256 * 256;
+}
+// A merge workgroup at the end of a single-launch grid merges up to this many
+// slices of one query head, one per wave.
+constexpr int kMergeSlicesPerGroup = 4;
+inline int64_t merge_groups(int32_t head_dim) {
+    return (head_dim / kMergeSliceDims + kMergeSlicesPerGroup - 1) / kMergeSlicesPerGroup;
 }
 
 inline bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
@@ -510,10 +518,10 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
         const SlotPlan &sp = plan.slots[s];
         const int n_sub = sp.mfma ? plan.matrix.n_sub : plan.lanes.n_sub;
         // a fused query's merge workgroups count against the launch's workgroups
-        const int64_t items = (int64_t)n_kv * n_sub * sp.n_chunks + (sp.fused ? (int64_t)n_q * (head_dim / 64) : 0);
+        const int64_t items = (int64_t)n_kv * n_sub * sp.n_chunks + (sp.fused ? (int64_t)n_q * merge_groups(head_dim) : 0);
         if (items > kMaxItemsPerLaunch) return "too many workgroups for one slot (n_kv_heads too large)";
         const int entries = sp.group_n;
-        const bool full = (int)g.slots.size() + entries > kMaxSlotsPerLaunch || g.items + g.tail_rows * (head_dim / 64) + items > kMaxItemsPerLaunch ||
+        const bool full = (int)g.slots.size() + entries > kMaxSlotsPerLaunch || g.items + g.tail_rows * merge_groups(head_dim) + items > kMaxItemsPerLaunch ||
                           (!g.slots.empty() && g.mfma != sp.mfma);
         if (full) {
             plan.groups.push_back(g);

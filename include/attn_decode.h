@@ -113,7 +113,7 @@ typedef struct attn_decode_options {
     /* How a slot split over several chunks is merged: 0 = automatic (today
      * the combine kernel, the faster of the two on MI355X), 1 = the separate
      * combine kernel, 2 = single launch: the lane kernel's queries with at
-     * most 256 chunks that are not part of a query group are merged by extra
+     * most 64 chunks that are not part of a query group are merged by extra
      * workgroups at the end of the partial kernel's own grid (one launch per
      * call where every split query qualifies), the others by the combine
      * kernel.  Both merges run the same arithmetic in the same order, so the

@@ -31,7 +31,7 @@ def _need_gpu():
 @pytest.mark.parametrize("case", [((256,), 1, 1, 64, False, 0), ((4096, 1000), 16, 8, 256, True, 0),
                                   ((20000,), 16, 8, 256, False, 1024)], ids=["tiny", "split", "window"])
 def test_graph_replay_matches_eager(case, merge_mode):
-    """Both merge modes; the single-launch merge's arrival counters must be back at zero after
+    """Both merge modes; the single-launch merge's flagged pairs must be back at zero after
     every replay, or the next replay would merge before its chunks are written."""
     seq, nq, nkv, d, i8, W = case
     inp = make_inputs(seq, nq, nkv, d, i8, seed_base=8800)

@@ -115,8 +115,8 @@ def test_chunking_changes_only_rounding(chunk, i8, merge_mode):
 
 @pytest.mark.parametrize("D,nq,nkv", [(64, 4, 1), (128, 8, 2), (256, 16, 2), (512, 4, 4), (512, 16, 4)])
 def test_in_kernel_merge_every_geometry(D, nq, nkv):
-    # every (head_dim, heads per workgroup) layout of the in-kernel merge, at 256 chunks
-    inp = make_inputs((256 * 5 + 3, 70), nq, nkv, D, D % 32 == 0 and nq == 16, seed_base=7150 + D + nq)
+    # every (head_dim, heads per workgroup) layout of the in-kernel merge, at its bound of 64 chunks
+    inp = make_inputs((64 * 5, 70), nq, nkv, D, D % 32 == 0 and nq == 16, seed_base=7150 + D + nq)
     ref = run_oracle(inp, 0)
     got = run_gpu(inp, 0, chunk=5, merge_mode=2).cpu().numpy()
     _report(f"merge geometry D={D} G={nq // nkv}", assert_parity(got, ref, f"D={D}"))
@@ -131,7 +131,10 @@ SINGLE_LAUNCH = [
     ((5000, 700), 32, 4, 128, True, 0, 0),              # 8 heads per kv head: two head blocks
     ((3000, 2500), 4, 4, 64, False, 0, 0),
     ((2600, 1300), 8, 2, 512, True, 999, 0),
-    ((256 * 5 + 3, 70), 16, 8, 256, False, 0, 5),        # 257 chunks: over the single-launch bound
+    ((64 * 5, 70), 16, 8, 256, False, 0, 5),             # 64 chunks: at the single-launch bound
+    ((64 * 5 + 3, 70), 16, 8, 256, False, 0, 5),         # 65 chunks: over it (combine kernel)
+    ((40 * 5, 1000, 17), 8, 8, 512, True, 0, 5),         # D = 512: two merge workgroups per head
+    ((33 * 7, 31 * 7), 4, 2, 64, False, 0, 7),           # D = 64: one slice, 33 and 31 chunks
 ]
 
 
@@ -139,7 +142,7 @@ SINGLE_LAUNCH = [
 def test_single_launch_merge_equals_combine_kernel_bitwise(case):
     """The merge workgroups at the end of the partial kernel's grid run the combine kernel's
     arithmetic on the same partials, so both merge modes give the same bits; twice in a row on
-    one stream (the arrival counters return to zero)."""
+    one stream (each call leaves the flagged pairs all zero for the next)."""
     seq, nq, nkv, d, i8, W, chunk = case
     inp = make_inputs(seq, nq, nkv, d, i8, seed_base=7170 + d + nq)
     dev = to_device(inp)
