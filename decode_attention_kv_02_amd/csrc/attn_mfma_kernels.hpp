@@ -31,6 +31,14 @@
 //    fp32.
 //  * Accumulator o[b EV + e] lane l component r holds head l%16, dim
 //    BW b + 4 EV (l/16) + EV r + e (BW = 16 EV dims per load).
+//  * At head_dim 512 with one-byte V a chunk is shared by two sibling
+//    workgroups (mfma_dim_splits): both compute the whole S^T and softmax, the
+//    same values, and each accumulates O for 256 of the dims, which halves the
+//    accumulators and V buffers and lets two waves run per SIMD instead of one
+//    (graph-replayed, 8 x 32768, 16 q / 2 kv heads: codebook V 176.4 -> 166.0 us,
+//    int8 165.7 -> 162.2 us; FETCH_SIZE 1.025 x the algorithmic bytes, the
+//    sibling's K reads are served by the XCD's L2).  A four-way split, three
+//    waves per SIMD, ran 1.8 times slower.
 //
 // Lane layouts (checked on gfx950 with one-wave probes): 16x16x32 f16:
 // A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]; 16x16x16 f16: A[l%16][4(l/16)+e],
@@ -54,19 +62,22 @@ constexpr float kLazyMax = 8.f; // log2 headroom of the softmax reference before
 template <int D, int VF>
 struct MfmaGeometry {
     static_assert(D >= 128 && D <= 512, "head_dim 128..512");
+    static constexpr int DS = mfma_dim_splits(D, VF != kVF16);          // sibling workgroups by output dims
+    static constexpr int DH = D / DS;                                    // output dims of one workgroup
     static constexpr int KS = D / 32;                                    // QK steps = 16-byte K loads per lane
-    static constexpr int EV = (VF == kVF16) ? 8 : (D >= 256 ? 16 : 8);   // V elements per lane per load
+    static constexpr int EV = (VF == kVF16) ? 8 : (DH >= 256 ? 16 : 8);  // V elements per lane per load
     static constexpr int BW = 16 * EV;                                   // dims covered by one load
-    static constexpr int NB = D / BW;                                    // loads per key step
+    static constexpr int NB = DH / BW;                                   // loads per key step
     static constexpr int VBYTES = EV * (VF == kVF16 ? 2 : 1);            // 16, or 8 (byte V at D = 128)
-    static constexpr int NO = NB * EV;                                   // f32x4 accumulators = D / 16
-    static_assert(NO * 16 == D, "accumulators cover every dim once");
-    static_assert(VF != kVCB || BW == (D < 256 ? D : 256), "one codebook norm block per load");
+    static constexpr int NO = NB * EV;                                   // f32x4 accumulators = DH / 16
+    static_assert(NO * 16 == DH, "accumulators cover every dim of the workgroup once");
+    static_assert(VF != kVCB || (D < 256 ? D : 256) % BW == 0, "one codebook norm block per load");
     // Workgroups per CU the register allocation must allow: two (two waves per SIMD) for codebook
-    // V at 256, where the bound measured faster (4 x 32768, 16 q / 2 kv heads: 46.8 -> 45.5 us);
-    // elsewhere the compiler's own allocation, which allows two waves at 256 and one at 512
-    // (accumulators, K and V buffers need more than half the register file there).
-    static constexpr int MIN_WG = (D == 256 && VF == kVCB) ? 2 : 1;
+    // V at 256, where the bound measured faster (4 x 32768, 16 q / 2 kv heads: 46.8 -> 45.5 us),
+    // and for the dim-split workgroups at 512; elsewhere the compiler's own allocation, which
+    // allows two waves at 256 and one for fp16 V at 512 (accumulators, K and V buffers need more
+    // than half the register file there).
+    static constexpr int MIN_WG = ((D == 256 && VF == kVCB) || DS > 1) ? 2 : 1;
 };
 
 template <int D, int VF>
@@ -105,13 +116,16 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     const SlotDesc sd = args.slot[si];
     const int n_mem = sd.group_n;         // queries of the group (1 when alone); table entries si..
     const int local = item - sd.item_begin;
-    const int sub = local % args.n_sub;
+    constexpr int DS = Geo::DS, DH = Geo::DH;
+    const int subx = local % args.n_sub;
+    const int sub = subx / DS;                          // head block
+    const int dhalf = subx - sub * DS;                  // output dims [dhalf DH, dhalf DH + DH)
     const int t = local / args.n_sub;
     const int c = t % sd.n_chunks;
     const int kvh = t / sd.n_chunks;
     const int cbeg = sd.lo + c * sd.chunk;
     const int cend = min(cbeg + sd.chunk, sd.L);
-    const int GB = args.G / args.n_sub;                 // heads per query of this block
+    const int GB = args.G * DS / args.n_sub;            // heads per query of this block
     const int h0 = kvh * args.G + sub * GB;             // first head of the block (in the slot)
     const int64_t rowbase = sd.kv_row0 + (int64_t)kvh * sd.kv_stride;
 
@@ -189,7 +203,7 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
             const int64_t row = row_of(kb + 4 * g + i);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const int d0 = BW * b + EV * c16;
+                const int d0 = dhalf * DH + BW * b + EV * c16;
                 if constexpr (VF == kVF16) {
                     f.v[i][b] = load_stream16((const uint16_t *)args.v + row * D + d0);
                 } else {
@@ -360,6 +374,18 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
         s_cb[tid] = (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
     }
     if constexpr (VF == kVCB || QLDS) __syncthreads();
+    if constexpr (DS == 2) {
+        // Dim-split workgroups run two waves per SIMD: one V buffer, refilled once the PV
+        // products have read it (the other wave covers the wait); K as below.
+        for (; tl < ntiles; tl += kWaves) {
+            f32x4_t acc = qk(kt);
+            const bool more = tl + kWaves < ntiles;
+            if (more) load_k(cbeg + (tl + kWaves) * kMfmaKeys, kt);
+            step(cbeg + tl * kMfmaKeys, acc, va);
+            if (more) load_v(cbeg + (tl + kWaves) * kMfmaKeys, va);
+        }
+        tl = ntiles;
+    }
     // K: one buffer, refilled as soon as the QK steps have read it; V: two buffers.
     for (; tl < ntiles; tl += 2 * kWaves) {
         f32x4_t acc = qk(kt);
@@ -416,12 +442,12 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     float *op;
     float scale_out = 1.f;
     if (m_nchunks == 1) {
-        op = args.out + qrow * D;
+        op = args.out + qrow * D + dhalf * DH;
         scale_out = (L == 0.f) ? 0.f : 1.f / L;
     } else {
         const int64_t prow = m_part + (int64_t)(h0 + hh) * m_nchunks + c;
-        op = args.ws_o + prow * D;
-        if (g == 0) {
+        op = args.ws_o + prow * D + dhalf * DH;
+        if (g == 0 && dhalf == 0) {   // the siblings' (M, S) are the same values
             args.ws_ml[prow * 2 + 0] = M;
             args.ws_ml[prow * 2 + 1] = L;
         }
