@@ -301,6 +301,16 @@ inline int heads_per_workgroup(int G) {
     return 1;
 }
 
+// A lane-kernel call with fewer workgroups than this (fewer than the GPU's 256
+// compute units) takes half the heads per workgroup, down to one: twice the
+// workgroups, the sibling reading the same K and V rows from its XCD's L2.
+// Measured (graph-replayed / flushed events): the 1024-position window of one
+// 131072 slot, 128 -> 256 workgroups, 8.2 -> 7.2 us / 13.5 -> 12.3 us; calls
+// that already fill the chip lose (the ragged 4-slot call 60 -> 81 us, 1 x 4096
+// 11.9 -> 12.5 us).  Each (query, head) row takes the same steps whatever the
+// number of heads per workgroup, so the results do not change.
+constexpr int64_t kSplitHeadsBelowItems = 256;
+
 // Which partial kernel computes a query.  The matrix-core kernel
 // (attn_partial_mfma_kernel) puts up to 16 (query, head) columns in one
 // workgroup.  It applies to a whole call at a multiple of 8 query heads per kv
@@ -340,7 +350,8 @@ constexpr int mfma_dim_splits(int head_dim, bool byte_v) { return head_dim == 51
 // Builds the plan from the query spans; returns "" on success or an error message.
 inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, int32_t n_kv,
                              int32_t head_dim, int32_t chunk, int32_t merge_mode, CallPlan &plan,
-                             int32_t path = kPathAuto, bool byte_v = false) {
+                             int32_t path = kPathAuto, bool byte_v = false, int32_t lanes_gb = 0,
+                             int32_t group_gb = 0) {
     plan = CallPlan();
     const int32_t n_slots = (int32_t)spans.size();
     plan.G = n_q / n_kv;
@@ -349,9 +360,11 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
         return "the matrix-core path needs a multiple of 8 query heads per kv head and head_dim >= 128";
     plan.mfma = path == kPathMatrix || (path == kPathAuto && mfma_preferred(plan.G, head_dim));
     const int G = plan.G;
-    plan.lanes.GB = heads_per_workgroup(G);
+    plan.lanes.GB = lanes_gb > 0 ? lanes_gb : heads_per_workgroup(G);
     plan.lanes.n_sub = G / plan.lanes.GB;
-    const int lane_qb_max = GROUP_ROWS / plan.lanes.GB;
+    // query groups are bounded by the automatic heads per workgroup, so splitting the heads of a
+    // small call (below) changes no group
+    const int lane_qb_max = GROUP_ROWS / (group_gb > 0 ? group_gb : plan.lanes.GB);
     int mfma_qb_max = 1;
     if (plan.mfma) {
         plan.matrix.GB = G % 16 == 0 ? 16 : 8;
@@ -543,6 +556,12 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
     }
     if (!g.slots.empty()) plan.groups.push_back(g);
     for (const LaunchGroup &lg : plan.groups) plan.total_items += lg.items;
+    // a small lane-kernel call without query groups: fewer heads per workgroup, more workgroups
+    bool lanes_only = plan.lanes.QB == 1;
+    for (const SlotPlan &sp : plan.slots) lanes_only = lanes_only && !sp.mfma;
+    if (lanes_only && plan.lanes.GB > 1 && plan.total_items < kSplitHeadsBelowItems)
+        return make_plan(spans, n_q, n_kv, head_dim, chunk, merge_mode, plan, path, byte_v, plan.lanes.GB / 2,
+                         group_gb > 0 ? group_gb : plan.lanes.GB);
     return "";
 }
 

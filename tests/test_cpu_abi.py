@@ -49,6 +49,15 @@ def _lo(L, W):
     return L - W if (W > 0 and L > W) else 0
 
 
+def _lane_items(n_kv, G, chunks):
+    """Workgroups of a lane-kernel call of single queries: blocks of 4, 2 or 1 heads, halved
+    while the call has fewer workgroups than the GPU's 256 compute units."""
+    gb = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+    while gb > 1 and n_kv * (G // gb) * chunks < 256:
+        gb //= 2
+    return n_kv * (G // gb) * chunks
+
+
 @pytest.mark.parametrize("seq,W", [
     ([256], 0), ([4096], 0), ([1024, 8192, 32768, 2000], 0), ([32768] * 8, 0),
     ([131072], 0), ([131072], 1024), ([0, 1, 63, 64, 65, 1000], 0), ([5000, 3], 100),
@@ -64,7 +73,7 @@ def test_plan_chunks_cover_each_attended_range(seq, W):
         else:
             assert 1 <= c <= span
             assert (n - 1) * c < span <= n * c  # chunks tile [lo, L), only the last is short
-    assert p["partial_workgroups"] == sum(p["n_chunks"]) * 8
+    assert p["partial_workgroups"] == _lane_items(8, 2, sum(p["n_chunks"]))
     rows = sum(16 * n for n in p["n_chunks"] if n > 1)
     # the planner query reports the automatic merge mode: combine kernel, no counters
     assert p["workspace_bytes"] == rows * (256 + 2) * 4
@@ -109,7 +118,7 @@ def test_random_plans_keep_their_invariants():
         seq = [L if rng.random() < 0.5 else int(rng.integers(0, 70000)) for L in seq]
         W = 0 if rng.random() < 0.6 else int(rng.integers(1, 5000))
         p = binding.attn_decode_plan(seq, W, n_kv * G, n_kv, d, v_int8=byte_v)
-        items, rows = 0, 0
+        items, rows, lane_chunks, any_matrix = 0, 0, 0, False
         for i, L in enumerate(seq):
             c, nc = p["chunk"][i], p["n_chunks"][i]
             span = L - _lo(L, W)
@@ -122,9 +131,13 @@ def test_random_plans_keep_their_invariants():
             solo = binding.attn_decode_plan([L], W, n_kv * G, n_kv, d, v_int8=byte_v)
             assert (solo["chunk"][0], solo["n_chunks"][0]) == (c, nc), (seq, W, i)
             items += n_kv * n_sub * nc
+            lane_chunks += 0 if mfma else nc
+            any_matrix = any_matrix or mfma
             rows += n_kv * G * nc if nc > 1 else 0
             if mfma and span > 0 and nc > 1:
                 assert c % 64 == 0 and c >= 512 or c >= span, (G, d, byte_v, L, c)
+        if not any_matrix:   # a lane-kernel call: fewer heads per workgroup when it is small
+            items = _lane_items(n_kv, G, lane_chunks)
         assert p["partial_workgroups"] == items, (G, d, byte_v, seq, W)
         assert p["workspace_bytes"] == rows * (d + 2) * 4
 
@@ -166,9 +179,11 @@ def test_lane_chunks_of_short_slots_carry_at_least_64_kib(D, floor):
 
 def test_gqa_blocks_multiply_workgroups_for_large_groups():
     # lane kernel: G = 3 as three single heads; G = 8 at head_dim 64 as two blocks of 4
-    # (chunks of 128 positions at head_dim 128, 256 at 64)
+    # (chunks of 128 positions at head_dim 128, 256 at 64) in a call that fills the GPU, and in
+    # single heads in a call of fewer workgroups than compute units
     assert binding.attn_decode_plan([640], 0, 6, 2, 128)["partial_workgroups"] == 2 * 3 * 5
-    assert binding.attn_decode_plan([2560], 0, 16, 2, 64)["partial_workgroups"] == 2 * 2 * 10
+    assert binding.attn_decode_plan([2560] * 8, 0, 16, 2, 64)["partial_workgroups"] == 8 * 2 * 2 * 10
+    assert binding.attn_decode_plan([2560], 0, 16, 2, 64)["partial_workgroups"] == 2 * 8 * 10
     # matrix-core kernel, automatic for 8k heads per kv head at head_dim >= 128: blocks of 16, else 8,
     # and chunks of at least 512 positions (640 -> 2 chunks)
     assert binding.attn_decode_plan([640], 0, 16, 2, 128)["partial_workgroups"] == 2 * 1 * 2
