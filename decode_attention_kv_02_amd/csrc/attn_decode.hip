@@ -346,7 +346,8 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     for (const LaunchGroup &lg : plan.groups) {
         fill(lg, false);
         const int64_t grid = lg.items + lg.tail_rows * merge_groups(D);   // partial, then merge workgroups
-        hipLaunchKernelGGL(lg.mfma ? pk_mfma : pk_lanes, dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
+        const int threads = lg.mfma ? kThreads * mfma_dim_splits(D) : kThreads;
+        hipLaunchKernelGGL(lg.mfma ? pk_mfma : pk_lanes, dim3((unsigned)grid), dim3(threads), 0, stream, args);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
     }

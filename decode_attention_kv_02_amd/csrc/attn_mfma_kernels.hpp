@@ -31,14 +31,16 @@
 //    fp32.
 //  * Accumulator o[b EV + e] lane l component r holds head l%16, dim
 //    BW b + 4 EV (l/16) + EV r + e (BW = 16 EV dims per load).
-//  * At head_dim 512 with one-byte V a chunk is shared by two sibling
-//    workgroups (mfma_dim_splits): both compute the whole S^T and softmax, the
-//    same values, and each accumulates O for 256 of the dims, which halves the
-//    accumulators and V buffers and lets two waves run per SIMD instead of one
-//    (graph-replayed, 8 x 32768, 16 q / 2 kv heads: codebook V 176.4 -> 166.0 us,
-//    int8 165.7 -> 162.2 us; FETCH_SIZE 1.025 x the algorithmic bytes, the
-//    sibling's K reads are served by the XCD's L2).  A four-way split, three
-//    waves per SIMD, ran 1.8 times slower.
+//  * At head_dim 512 the workgroup has 8 waves in two halves (mfma_dim_splits):
+//    waves w and w + 4 take the same key tiles; each loads K for 256 of the
+//    dims and sums its QK steps, the two halves of S^T are added through LDS
+//    (both waves form lower + upper, the same bits), and each accumulates O
+//    for 256 of the output dims.  Accumulators and V buffers halve, so two
+//    waves run per SIMD instead of one (graph-replayed, 8 x 32768, 16 q / 2 kv
+//    heads: codebook V 176.4 -> 145.3 us, int8 165.7 -> 150.9, fp16
+//    174.0 -> 169.2).  Two sibling workgroups that each computed the whole
+//    QK product measured 166.0 and 162.2 us (their second K read hit L2);
+//    four, 1.8 times slower; a second K buffer spills.
 //
 // Lane layouts (checked on gfx950 with one-wave probes): 16x16x32 f16:
 // A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]; 16x16x16 f16: A[l%16][4(l/16)+e],
@@ -62,27 +64,29 @@ constexpr float kLazyMax = 8.f; // log2 headroom of the softmax reference before
 template <int D, int VF>
 struct MfmaGeometry {
     static_assert(D >= 128 && D <= 512, "head_dim 128..512");
-    static constexpr int DS = mfma_dim_splits(D, VF != kVF16);          // sibling workgroups by output dims
-    static constexpr int DH = D / DS;                                    // output dims of one workgroup
     static constexpr int KS = D / 32;                                    // QK steps = 16-byte K loads per lane
+    static constexpr int DS = mfma_dim_splits(D);                       // waves sharing a key tile, by dims
+    static constexpr int DH = D / DS;                                    // output dims of one wave
+    static constexpr int THREADS = kThreads * DS;                        // DS groups of kWaves waves
+    static constexpr int KW = KS / DS;                                   // QK steps of one wave
     static constexpr int EV = (VF == kVF16) ? 8 : (DH >= 256 ? 16 : 8);  // V elements per lane per load
     static constexpr int BW = 16 * EV;                                   // dims covered by one load
     static constexpr int NB = DH / BW;                                   // loads per key step
     static constexpr int VBYTES = EV * (VF == kVF16 ? 2 : 1);            // 16, or 8 (byte V at D = 128)
     static constexpr int NO = NB * EV;                                   // f32x4 accumulators = DH / 16
-    static_assert(NO * 16 == DH, "accumulators cover every dim of the workgroup once");
+    static_assert(NO * 16 == DH, "accumulators cover every dim of the wave once");
     static_assert(VF != kVCB || (D < 256 ? D : 256) % BW == 0, "one codebook norm block per load");
     // Workgroups per CU the register allocation must allow: two (two waves per SIMD) for codebook
-    // V at 256, where the bound measured faster (4 x 32768, 16 q / 2 kv heads: 46.8 -> 45.5 us),
-    // and for the dim-split workgroups at 512; elsewhere the compiler's own allocation, which
-    // allows two waves at 256 and one for fp16 V at 512 (accumulators, K and V buffers need more
-    // than half the register file there).
-    static constexpr int MIN_WG = ((D == 256 && VF == kVCB) || DS > 1) ? 2 : 1;
+    // V at 256, where the bound measured faster (4 x 32768, 16 q / 2 kv heads: 46.8 -> 45.5 us);
+    // elsewhere the compiler's own allocation, which allows two waves at 256 and one for fp16 V at
+    // 512 (accumulators, K and V buffers need more than half the register file there).  The
+    // 8-wave workgroups of the split run one per CU, two waves per SIMD.
+    static constexpr int MIN_WG = (D == 256 && VF == kVCB) ? 2 : 1;
 };
 
 template <int D, int VF>
 struct MKTile {
-    uint4 k[MfmaGeometry<D, VF>::KS];   // key kb + l%16, dims 32 s + 8 (l/16) + [0, 8)
+    uint4 k[MfmaGeometry<D, VF>::KW];   // key kb + l%16, dims 32 s + 8 (l/16) + [0, 8) of the wave's steps s
 };
 
 template <int D, int VF>
@@ -103,12 +107,17 @@ __device__ __forceinline__ void split_f16(const float (&x)[4], half4_t &hi, half
     }
 }
 
+// Spins of a wave waiting for its partner's half of a QK product (about a tenth of a second); past
+// it the wave goes on with what it has, so a fault shows in the results instead of hanging the GPU.
+constexpr int kPairMaxSpins = 1 << 21;
+
 template <int D, int VF>
-__global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_partial_mfma_kernel(const LaunchArgs args) {
+__global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF>::MIN_WG)) void attn_partial_mfma_kernel(const LaunchArgs args) {
     using Geo = MfmaGeometry<D, VF>;
-    constexpr int KS = Geo::KS, EV = Geo::EV, BW = Geo::BW, NB = Geo::NB, NO = Geo::NO;
+    constexpr int KS = Geo::KS, KW = Geo::KW, EV = Geo::EV, BW = Geo::BW, NB = Geo::NB, NO = Geo::NO;
+    constexpr int DS = Geo::DS, DH = Geo::DH, NT = Geo::THREADS;
     constexpr int CB_B = D < 256 ? D : 256;   // codebook norm block
-    static_assert(kThreads == 256, "one thread per codebook table entry");
+    static_assert(NT >= 256, "one thread per codebook table entry");
 
     const int item = xcd_item(blockIdx.x, args.n_items, args.n_sub);
     int si = upper_index(args.n_slots, item, [&](int i) { return args.key[i]; });
@@ -116,22 +125,21 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     const SlotDesc sd = args.slot[si];
     const int n_mem = sd.group_n;         // queries of the group (1 when alone); table entries si..
     const int local = item - sd.item_begin;
-    constexpr int DS = Geo::DS, DH = Geo::DH;
-    const int subx = local % args.n_sub;
-    const int sub = subx / DS;                          // head block
-    const int dhalf = subx - sub * DS;                  // output dims [dhalf DH, dhalf DH + DH)
+    const int sub = local % args.n_sub;
     const int t = local / args.n_sub;
     const int c = t % sd.n_chunks;
     const int kvh = t / sd.n_chunks;
     const int cbeg = sd.lo + c * sd.chunk;
     const int cend = min(cbeg + sd.chunk, sd.L);
-    const int GB = args.G * DS / args.n_sub;            // heads per query of this block
+    const int GB = args.G / args.n_sub;                 // heads per query of this block
     const int h0 = kvh * args.G + sub * GB;             // first head of the block (in the slot)
     const int64_t rowbase = sd.kv_row0 + (int64_t)kvh * sd.kv_stride;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop control
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar loop control
+    const int w = wv % kWaves;   // the wave's stream of key tiles: w, w + 4, ...
+    const int dh = wv / kWaves;  // with the split, its output dims [dh DH, dh DH + DH) and QK steps [dh KW, dh KW + KW)
     const int c16 = lane & 15;   // MFMA row / column of the lane
     const int g = lane >> 4;     // lane group
     // Column c16 is head h0 + c16 % GB of the group's query c16 / GB: GB = 8 or 16 heads of one
@@ -156,8 +164,8 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     __shared__ uint16_t s_q[QLDS ? 16 * QS : 1];
     half8_t qf[QLDS ? 1 : KS];
     if constexpr (QLDS) {
-        // 4 waves x 64 lanes fill 16 rows of D halves, 16 bytes per thread per pass
-        for (int x = tid * 8; x < 16 * D; x += kThreads * 8) {
+        // the workgroup's threads fill 16 rows of D halves, 16 bytes per thread per pass
+        for (int x = tid * 8; x < 16 * D; x += NT * 8) {
             const int hr = x / D, dd = x % D;   // row hr: column hr's query and head
             uint4 a = make_uint4(0, 0, 0, 0);
             if (hr / GB < n_mem) {
@@ -181,7 +189,13 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     // p >= 2^-8 / norm; the table stays finite for levels below 8192.
     __shared__ uint32_t s_cb[VF == kVCB ? 256 : 1];
     __shared__ float s_m[kWaves][16], s_l[kWaves][16];
-    __shared__ f32x4_t s_o[NO][64];                // one wave's accumulators, for the final merge
+    __shared__ f32x4_t s_o[DS][NO][64];            // one wave's accumulators per dim range, for the final merge
+    // the split: each wave's half of S^T per tile (two tiles in turn) and the count of halves it has posted
+    __shared__ f32x4_t s_x[DS > 1 ? kWaves * DS * 2 : 1][64];
+    __shared__ int s_posted[DS > 1 ? kWaves * DS : 1];
+    if constexpr (DS > 1) {
+        if (tid < kWaves * DS) s_posted[tid] = 0;
+    }
 
     // Cache row of a key of the chunk (keys past its end read its last key; they are masked).
     auto row_of = [&](int key) -> int64_t {
@@ -193,9 +207,9 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     // from consecutive steps; plain (cached) loads let the second half hit in L1, where
     // non-temporal ones measured 3-12% slower.  V reads whole lines and streams.
     auto load_k = [&](int kb, MKTile<D, VF> &f) {
-        const uint16_t *kp = args.k + row_of(kb + c16) * D + 8 * g;
+        const uint16_t *kp = args.k + row_of(kb + c16) * D + 8 * g + 32 * KW * dh;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) f.k[s] = *(const uint4 *)(kp + 32 * s);
+        for (int s = 0; s < KW; ++s) f.k[s] = *(const uint4 *)(kp + 32 * s);
     };
     auto load_v = [&](int kb, MVTile<D, VF> &f) {
 #pragma unroll
@@ -203,7 +217,7 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
             const int64_t row = row_of(kb + 4 * g + i);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const int d0 = dhalf * DH + BW * b + EV * c16;
+                const int d0 = dh * DH + BW * b + EV * c16;
                 if constexpr (VF == kVF16) {
                     f.v[i][b] = load_stream16((const uint16_t *)args.v + row * D + d0);
                 } else {
@@ -229,15 +243,31 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     for (int j = 0; j < NO; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const float sl2 = args.scale_log2;
 
-    // S^T of one tile of 16 keys
+    // S^T of one tile of 16 keys (with the split: this wave's steps, then the sum with the
+    // partner wave's steps through LDS; both waves form lower half + upper half, the same bits)
+    int posted = 0;   // halves this wave has posted
     auto qk = [&](const MKTile<D, VF> &kt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+        for (int s = 0; s < KW; ++s) {
             half8_t qb;
-            if constexpr (QLDS) qb = as_h8(*(const uint4 *)(s_q + c16 * QS + 32 * s + 8 * g));
+            if constexpr (QLDS) qb = as_h8(*(const uint4 *)(s_q + c16 * QS + 32 * (KW * dh + s) + 8 * g));
             else qb = qf[s];
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kt.k[s]), qb, acc, 0, 0, 0);
+        }
+        if constexpr (DS > 1) {
+            const int mine = (w * DS + dh) * 2 + (posted & 1), theirs = (w * DS + (dh ^ 1)) * 2 + (posted & 1);
+            s_x[mine][lane] = acc;
+            ++posted;
+            __hip_atomic_store(&s_posted[w * DS + dh], posted, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            int spins = 0;
+            while (__hip_atomic_load(&s_posted[w * DS + (dh ^ 1)], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
+                       posted && spins < kPairMaxSpins) {
+                __builtin_amdgcn_s_sleep(1);
+                ++spins;
+            }
+            const f32x4_t other = s_x[theirs][lane];
+            acc = dh == 0 ? acc + other : other + acc;
         }
         return acc;
     };
@@ -369,23 +399,13 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
         load_v(cbeg + tl * kMfmaKeys, va);
     }
     if constexpr (VF == kVCB) {
-        const float x = args.codebook[tid & args.cb_mask] * args.cb_scale * 64.f;
-        const _Float16 h = (_Float16)x, lo = (_Float16)(x - (float)h);
-        s_cb[tid] = (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
-    }
-    if constexpr (VF == kVCB || QLDS) __syncthreads();
-    if constexpr (DS == 2) {
-        // Dim-split workgroups run two waves per SIMD: one V buffer, refilled once the PV
-        // products have read it (the other wave covers the wait); K as below.
-        for (; tl < ntiles; tl += kWaves) {
-            f32x4_t acc = qk(kt);
-            const bool more = tl + kWaves < ntiles;
-            if (more) load_k(cbeg + (tl + kWaves) * kMfmaKeys, kt);
-            step(cbeg + tl * kMfmaKeys, acc, va);
-            if (more) load_v(cbeg + (tl + kWaves) * kMfmaKeys, va);
+        if (tid < 256) {
+            const float x = args.codebook[tid & args.cb_mask] * args.cb_scale * 64.f;
+            const _Float16 h = (_Float16)x, lo = (_Float16)(x - (float)h);
+            s_cb[tid] = (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
         }
-        tl = ntiles;
     }
+    if constexpr (VF == kVCB || QLDS || DS > 1) __syncthreads();
     // K: one buffer, refilled as soon as the QK steps have read it; V: two buffers.
     for (; tl < ntiles; tl += 2 * kWaves) {
         f32x4_t acc = qk(kt);
@@ -404,10 +424,11 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
         step(cbeg + (tl + kWaves) * kMfmaKeys, acc, vb);
     }
 
-    // merge the 4 waves: M = max of their maxima, each wave's O and S scaled by 2^(m_w - M)
+    // merge the 4 tile streams: M = max of their maxima, each stream's O and S scaled by 2^(m_w - M)
+    // (with the split both waves of a stream hold the same m and l)
     l += shfl_xor_f32(l, 16);
     l += shfl_xor_f32(l, 32);
-    if (g == 0) {
+    if (g == 0 && dh == 0) {
         s_m[w][c16] = m;
         s_l[w][c16] = l;
     }
@@ -422,14 +443,14 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     const float f = fast_exp2(m - Ms);
 #pragma unroll
     for (int j = 0; j < NO; ++j) o[j] *= f;
-    // ((o3 + o2) + o1) + o0 through one LDS buffer, in a fixed order
+    // ((o3 + o2) + o1) + o0 through one LDS buffer per dim range, in a fixed order
 #pragma unroll
     for (int ww = kWaves - 1; ww >= 1; --ww) {
         if (w == ww) {
 #pragma unroll
             for (int j = 0; j < NO; ++j) {
-                if (ww < kWaves - 1) o[j] += s_o[j][lane];
-                s_o[j][lane] = o[j];
+                if (ww < kWaves - 1) o[j] += s_o[dh][j][lane];
+                s_o[dh][j][lane] = o[j];
             }
         }
         __syncthreads();
@@ -437,17 +458,17 @@ __global__ __launch_bounds__(kThreads, (MfmaGeometry<D, VF>::MIN_WG)) void attn_
     // a group member whose last chunk is before c has nothing here
     if (w != 0 || !head_ok || c >= m_nchunks) return;   // no barriers follow
 #pragma unroll
-    for (int j = 0; j < NO; ++j) o[j] += s_o[j][lane];
+    for (int j = 0; j < NO; ++j) o[j] += s_o[dh][j][lane];
 
     float *op;
     float scale_out = 1.f;
     if (m_nchunks == 1) {
-        op = args.out + qrow * D + dhalf * DH;
+        op = args.out + qrow * D + dh * DH;
         scale_out = (L == 0.f) ? 0.f : 1.f / L;
     } else {
         const int64_t prow = m_part + (int64_t)(h0 + hh) * m_nchunks + c;
-        op = args.ws_o + prow * D + dhalf * DH;
-        if (g == 0 && dhalf == 0) {   // the siblings' (M, S) are the same values
+        op = args.ws_o + prow * D + dh * DH;
+        if (g == 0 && dh == 0) {
             args.ws_ml[prow * 2 + 0] = M;
             args.ws_ml[prow * 2 + 1] = L;
         }

@@ -70,7 +70,7 @@ struct SlotPlan {
 // G / GB workgroups per (query group, kv head, chunk), queries per workgroup (QB).
 struct KernelShape {
     int GB = 1;
-    int n_sub = 1;   // sibling workgroups per chunk: head blocks (G / GB) times the matrix kernel's dim splits
+    int n_sub = 1;   // workgroups per chunk: head blocks, G / GB
     int QB = 1;      // lane kernel: its template parameter (QB * GB <= 4); matrix cores: the largest group
 };
 
@@ -336,16 +336,16 @@ constexpr int kMfmaColumns = 16;      // (query, head) columns of one matrix-cor
 // lanes (graph-replayed): one query with 4 heads per kv head at head_dim 128, 8 x 8192, 53.4 ->
 // 46.3 us, codebook V at 256 146.1 -> 136.7 us, fp16 at 256 and 512 within 1%; 3 drafts x 2 heads
 // over 4 x 32768 329.0 -> 171.4 us (the lanes' groups hold at most 4 rows, so 6 rows took two
-// reads of the cache).  Eight at head_dim 512 with one-byte V, where the matrix-core kernel runs
-// one wave per SIMD: one int8 query with 4 heads (8 x 32768) ran 143 us on the lanes against 164
-// there.
+// reads of the cache).  Eight at head_dim 512 with one-byte V: one query with 4 heads per kv head
+// (8 x 32768, 16 q / 4 kv heads) runs as fast on the lanes (int8 278.9 us against 284.2 on the
+// matrix cores, codebook 283.3 against 279.2; with one wave per SIMD there the matrix cores took
+// 164 us against the lanes' 143 on int8 at 8 heads).
 inline int mfma_group_min_cols(int head_dim, bool byte_v) { return head_dim == 512 && byte_v ? 8 : 4; }
-// Sibling workgroups that share one chunk of the matrix-core kernel by output dims: at head_dim
-// 512 with one-byte V, two, each computing the whole QK product and PV for 256 of the dims, so
-// that the O accumulator and V buffers of a wave halve and two waves fit per SIMD.  The siblings
-// get neighbouring work items (the same XCD, dispatched together), so the second read of the
-// chunk's K rows is served by that XCD's L2.
-constexpr int mfma_dim_splits(int head_dim, bool byte_v) { return head_dim == 512 && byte_v ? 2 : 1; }
+// Waves of a matrix-core workgroup that share each 16-key tile by dims: at head_dim 512, two (an
+// 8-wave workgroup): each wave loads K for 256 of the dims and V for 256 of the output dims, so
+// that its accumulators and V buffers halve and two waves run per SIMD instead of one; the two
+// halves of each QK product are summed through LDS.
+constexpr int mfma_dim_splits(int head_dim) { return head_dim == 512 ? 2 : 1; }
 
 // Builds the plan from the query spans; returns "" on success or an error message.
 inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, int32_t n_kv,
@@ -368,11 +368,11 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
     int mfma_qb_max = 1;
     if (plan.mfma) {
         plan.matrix.GB = G % 16 == 0 ? 16 : 8;
-        plan.matrix.n_sub = G / plan.matrix.GB * mfma_dim_splits(head_dim, byte_v);
+        plan.matrix.n_sub = G / plan.matrix.GB;
         mfma_qb_max = kMfmaColumns / plan.matrix.GB;
     } else if (path == kPathAuto && head_dim >= 128 && G <= kMfmaColumns / 2) {
         plan.matrix.GB = G;             // draft groups: every head of the kv head, for each draft
-        plan.matrix.n_sub = mfma_dim_splits(head_dim, byte_v);
+        plan.matrix.n_sub = 1;
         mfma_qb_max = kMfmaColumns / G;
     }
     // the matrix-core kernel always merges in the combine kernel

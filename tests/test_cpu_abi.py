@@ -92,13 +92,11 @@ def _expected_kernel_split(G, d, byte_v, empty):
     """(matrix cores?, workgroups per chunk) of one single-query slot, by the rule the planner
     states: the matrix cores at a multiple of 8 heads per kv head (blocks of 16, else 8), or at 4
     or more heads (8 at head_dim 512 with one-byte V) as one block for a slot with something to
-    attend; head_dim >= 128 either way; else the lanes in blocks of 4, 2 or 1 heads.  At head_dim
-    512 with one-byte V every matrix-core block is two workgroups, each for half of the dims."""
-    splits = 2 if (d == 512 and byte_v) else 1
+    attend; head_dim >= 128 either way; else the lanes in blocks of 4, 2 or 1 heads."""
     if d >= 128 and G % 8 == 0:
-        return True, G // (16 if G % 16 == 0 else 8) * splits
+        return True, G // (16 if G % 16 == 0 else 8)
     if d >= 128 and G <= 8 and G >= (8 if (d == 512 and byte_v) else 4) and not empty:
-        return True, splits
+        return True, 1
     gb = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
     return False, G // gb
 
@@ -189,8 +187,7 @@ def test_gqa_blocks_multiply_workgroups_for_large_groups():
     assert binding.attn_decode_plan([640], 0, 16, 2, 128)["partial_workgroups"] == 2 * 1 * 2
     assert binding.attn_decode_plan([640], 0, 64, 2, 128)["partial_workgroups"] == 2 * 2 * 2
     assert binding.attn_decode_plan([640], 0, 64, 2, 512)["partial_workgroups"] == 2 * 2 * 2
-    # at head_dim 512 with one-byte V each block is two workgroups, one per half of the dims
-    assert binding.attn_decode_plan([640], 0, 64, 2, 512, v_int8=True)["partial_workgroups"] == 2 * 2 * 2 * 2
+    assert binding.attn_decode_plan([640], 0, 64, 2, 512, v_int8=True)["partial_workgroups"] == 2 * 2 * 2
     assert binding.attn_decode_plan([640], 0, 64, 2, 256, v_int8=True)["partial_workgroups"] == 2 * 2 * 2
     assert binding.attn_decode_plan([640], 0, 48, 2, 256)["partial_workgroups"] == 2 * 3 * 2
     p = binding.attn_decode_plan([8192, 16384, 32768, 131072], 0, 16, 2, 256)
