@@ -240,6 +240,8 @@ GQA_SHAPES = (
     ("g8_d512_fp16_4x32768", (32768,) * 4, 16, 2, 512, "fp16"),
     ("g8_d512_codebook_4x32768", (32768,) * 4, 16, 2, 512, "codebook"),
     ("g8_d512_int8_4x32768", (32768,) * 4, 16, 2, 512, "int8"),
+    ("g8_d512_codebook_8x32768", (32768,) * 8, 16, 2, 512, "codebook"),
+    ("g8_d512_int8_8x32768", (32768,) * 8, 16, 2, 512, "int8"),
     ("g8_d256_fp16_4x32768", (32768,) * 4, 16, 2, 256, "fp16"),
     ("g8_d256_codebook_4x32768", (32768,) * 4, 16, 2, 256, "codebook"),
     ("g8_d128_fp16_8x8192", (8192,) * 8, 64, 8, 128, "fp16"),
