@@ -108,7 +108,8 @@ __device__ __forceinline__ void split_f16(const float (&x)[4], half4_t &hi, half
 }
 
 // Spins of a wave waiting for its partner's half of a QK product (about a tenth of a second); past
-// it the wave goes on with what it has, so a fault shows in the results instead of hanging the GPU.
+// it the wave goes on and the workgroup writes NaN, so a fault shows in the results instead of
+// hanging the GPU.
 constexpr int kPairMaxSpins = 1 << 21;
 
 template <int D, int VF>
@@ -193,8 +194,10 @@ __global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF
     // the split: each wave's half of S^T per tile (two tiles in turn) and the count of halves it has posted
     __shared__ f32x4_t s_x[DS > 1 ? kWaves * DS * 2 : 1][64];
     __shared__ int s_posted[DS > 1 ? kWaves * DS : 1];
+    __shared__ int s_pair_late;   // a wave gave up waiting for its partner
     if constexpr (DS > 1) {
         if (tid < kWaves * DS) s_posted[tid] = 0;
+        if (tid == 0) s_pair_late = 0;
     }
 
     // Cache row of a key of the chunk (keys past its end read its last key; they are masked).
@@ -246,6 +249,7 @@ __global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF
     // S^T of one tile of 16 keys (with the split: this wave's steps, then the sum with the
     // partner wave's steps through LDS; both waves form lower half + upper half, the same bits)
     int posted = 0;   // halves this wave has posted
+    bool late = false;
     auto qk = [&](const MKTile<D, VF> &kt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -266,6 +270,7 @@ __global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF
                 __builtin_amdgcn_s_sleep(1);
                 ++spins;
             }
+            late |= spins >= kPairMaxSpins;
             const f32x4_t other = s_x[theirs][lane];
             acc = dh == 0 ? acc + other : other + acc;
         }
@@ -432,6 +437,9 @@ __global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF
         s_m[w][c16] = m;
         s_l[w][c16] = l;
     }
+    if constexpr (DS > 1) {
+        if (late) s_pair_late = 1;
+    }
     __syncthreads();
     float M = s_m[0][c16];
 #pragma unroll
@@ -462,6 +470,8 @@ __global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF
 
     float *op;
     float scale_out = 1.f;
+    bool failed = false;
+    if constexpr (DS > 1) failed = s_pair_late != 0;
     if (m_nchunks == 1) {
         op = args.out + qrow * D + dh * DH;
         scale_out = (L == 0.f) ? 0.f : 1.f / L;
@@ -469,10 +479,11 @@ __global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF
         const int64_t prow = m_part + (int64_t)(h0 + hh) * m_nchunks + c;
         op = args.ws_o + prow * D + dh * DH;
         if (g == 0 && dh == 0) {
-            args.ws_ml[prow * 2 + 0] = M;
-            args.ws_ml[prow * 2 + 1] = L;
+            args.ws_ml[prow * 2 + 0] = failed ? NAN : M;
+            args.ws_ml[prow * 2 + 1] = failed ? NAN : L;
         }
     }
+    if (failed) scale_out = NAN;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
