@@ -158,12 +158,16 @@ __global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF
     const int cend_col = min(cbeg + sd.chunk, m_L);
 
     // q as the B operand of the QK steps: step s covers dims 32 s + 8 g + [0, 8), like the K loads.
-    // Held in registers up to head_dim 128; above, in LDS (rows padded by 16 bytes so the 16
-    // heads of one read fall in different banks), which leaves the registers to K and V.
-    constexpr bool QLDS = D >= 256;
+    // Each wave holds the KW steps it computes in registers (32 per lane up to 128 dims; at 512
+    // each wave of a pair takes 256 dims), except for fp16 V at head_dim 256, whose accumulators
+    // and V buffers need the registers: there q sits in LDS (rows padded by 16 bytes so the 16
+    // heads of one read fall in different banks) and is read again for every tile.  In registers
+    // it saves those reads (graph-replayed, 8 x 32768 slots, 16 q / 2 kv heads at 512: codebook V
+    // 144.1 -> 140.3 us, one slot 62.3 -> 54.9; int8 and fp16 V and byte V at 256 0.2-2%).
+    constexpr bool QLDS = D >= 256 && DS == 1 && VF == kVF16;
     constexpr int QS = D + 8;                      // LDS row stride of q, in halves
     __shared__ uint16_t s_q[QLDS ? 16 * QS : 1];
-    half8_t qf[QLDS ? 1 : KS];
+    half8_t qf[QLDS ? 1 : KW];
     if constexpr (QLDS) {
         // the workgroup's threads fill 16 rows of D halves, 16 bytes per thread per pass
         for (int x = tid * 8; x < 16 * D; x += NT * 8) {
@@ -177,9 +181,9 @@ __global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF
         }
     } else {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+        for (int s = 0; s < KW; ++s) {
             uint4 a = make_uint4(0, 0, 0, 0);
-            if (head_ok) a = *(const uint4 *)(args.q + qrow * D + 32 * s + 8 * g);
+            if (head_ok) a = *(const uint4 *)(args.q + qrow * D + 32 * (KW * dh + s) + 8 * g);
             qf[s] = as_h8(a);
         }
     }
