@@ -91,7 +91,7 @@ def cache_attended(pos: int, capacity: int, ring: int, window: int) -> int:
 
 
 def cache_kv_bytes(cfg) -> tuple:
-    """(bytes the kernels read: every query reads its own attended rows,
+    """(bytes counted per query: every query's own attended rows, as if nothing were shared,
         unique bytes: each cache row counted once however many queries read it)."""
     d = cfg.head_dim
     per_row = 2 * d + (d + 2 * (d // 32) if cfg.v_int8 else 2 * d)
@@ -431,7 +431,9 @@ def main(argv=None) -> int:
         inp = cache_workload_inputs(cfg)
         tens = upload(inp)
         out = torch.empty((inp.n_queries, inp.n_q_heads, inp.head_dim), dtype=torch.float32, device=dev)
-        nbytes = cache_kv_bytes(cfg)[0]
+        # rates on the unique bytes (each cache row once, as HBM serves it); draft queries of one
+        # slot share their rows, so bytes counted per query would exceed what is read
+        per_query_bytes, nbytes = cache_kv_bytes(cfg)
         v_format = "int8 codes, fp16 scale per 32 dims" if inp.v_scales is not None else "fp16"
         c_sid = np.asarray(inp.slot_ids, dtype=np.int32)
         c_pos = np.asarray(inp.positions, dtype=np.int32)
@@ -514,7 +516,8 @@ def main(argv=None) -> int:
 
     if args.workload in cache_by_name:
         shape = {"n_queries": inp.n_queries, "slot_ids": list(inp.slot_ids), "positions": list(inp.positions),
-                 "n_cache_slots": inp.n_cache_slots, "capacity": inp.capacity, "ring": inp.ring}
+                 "n_cache_slots": inp.n_cache_slots, "capacity": inp.capacity, "ring": inp.ring,
+                 "kv_bytes_per_query": per_query_bytes}
         drafts = max(inp.slot_ids.count(s_) for s_ in set(inp.slot_ids))
     else:
         shape = {"n_slots": inp.n_slots, "seq_lens": list(inp.seq_lens)}
