@@ -17,12 +17,12 @@ each slot's attended range, read once:
 
 One JSON line is printed.  Besides the contract fields it carries
   * ``roofline``: the partial kernel's algorithmic bytes / its average launch
-    duration against the 8 TB/s HBM peak (and, secondary, against a 1 GiB
-    device copy timed on the same GPU, read plus written bytes).  The duration comes from HIP event
-    pairs that the library records around the partial-kernel launch, on the
-    call's stream, on every ``--event-every``-th step of the timed region (an
-    event between two kernels leaves the GPU idle for several microseconds, so
-    they are not recorded on every step).  ``traffic`` comes from the committed
+    duration against the 8 TB/s HBM peak.  The duration comes from HIP event
+    pairs (timing-only events, created with hipEventDisableSystemFence) that the
+    library records around the partial-kernel launch, on the call's stream, on
+    every ``--event-every``-th step of the timed region (an event between two
+    kernels leaves the GPU idle for a few microseconds, so they are not recorded
+    on every step).  ``traffic`` comes from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary when that summary was taken on
     the current kernel source, else null;
   * ``cpu_baseline``: the CPU fp64 oracle timed on a bounded sample of the same
@@ -34,7 +34,9 @@ One JSON line is printed.  Besides the contract fields it carries
     call without the Python and launch cost on the host, as a decode loop that
     captures its step sees it) and flushed events (50 reps of the 1 GiB read
     followed by one call between two events on its stream: median, p10, p90,
-    and the median of the same pairs with nothing between them),
+    and the median of the same pairs with nothing between them; once with
+    default events and once with timing-only ones, which skip the system-scope
+    cache writeback and invalidation a default event performs),
     with the CPU fp64 oracle over all query rows of the preset on all cores
     (and on one core for the three smallest presets),
     plus the codebook-V presets (``attn_decode_cb`` followed by ``attn_fwht_undo``
@@ -44,7 +46,10 @@ One JSON line is printed.  Besides the contract fields it carries
     fractions count ``kv_bytes``, each cache row once, while
     ``kv_bytes_per_query`` counts every query's own rows), and the KV-append presets
     (``attn_kv_append``; ``bytes`` = fp32 K and V read plus the fp16 K and the
-    fp16 or int8 V and scales written).
+    fp16 or int8 V and scales written);
+  * ``device_copy_gbs``: a plain 1 GiB device copy, read plus written bytes per
+    second, timed for about 0.15 s right before the warm-up steps (context, not
+    a ceiling; it also lets the GPU's clocks settle before the timed steps).
 """
 from __future__ import annotations
 
@@ -177,10 +182,15 @@ def calibrate_copy(nbytes: int) -> int:
     return 0
 
 
-def measured_copy_gbs(dev, nbytes: int = 1 << 30, reps: int = 20) -> float:
-    """Bytes moved per second (read + written) by a plain device-to-device copy of `nbytes`,
-    back to back on the current stream: the on-box bandwidth a streaming kernel can be set
-    against, beside the published peak."""
+def measured_copy_gbs(dev, nbytes: int = 1 << 30, seconds: float = 0.15, keep: list = None):
+    """(bytes moved per second, read + written, by a plain device-to-device copy of `nbytes`,
+    back to back on the current stream for about `seconds`; the seconds it ran).  Context for
+    the partial kernel's rate, not a ceiling.  It runs right before the headline's warm-up
+    steps: after an idle spell the GPU takes some 10 ms of streaming to settle (calls 10-40 of
+    a fresh loop ran up to 7% slower than later ones), and this copy is that much streaming
+    work of its own.  With `keep` (a list), the two buffers are appended to it instead of
+    being freed: calls right after a large free ran about 2% slower (measured over 60 calls),
+    so the caller frees them after its timed region."""
     import torch
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -188,13 +198,68 @@ def measured_copy_gbs(dev, nbytes: int = 1 << 30, reps: int = 20) -> float:
         dst.copy_(src)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(reps):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / reps
-    del src, dst
-    torch.cuda.empty_cache()
-    return 2 * nbytes / dt / 1e9
+    reps = 0
+    while True:
+        for _ in range(10):
+            dst.copy_(src)
+        reps += 10
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    if keep is not None:
+        keep.extend((src, dst))
+    else:
+        del src, dst
+        torch.cuda.empty_cache()
+    return 2 * nbytes * reps / el / 1e9, el
+
+
+class TimingEvent:
+    """A hipEvent for timing only, created with hipEventDisableSystemFence: HIP documents that
+    such an event skips the system-scope cache writeback and invalidation that a default event
+    performs when it is recorded, which makes the interval between two of them more precise.
+    Used where the bench times GPU work between events; nothing on the host reads results
+    through them."""
+    _hip = None
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, stream):
+        import ctypes
+        if TimingEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self._c = ctypes
+        self.handle = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.handle), self.FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.record(stream)   # a recorded event, as torch's own new_event() gives
+
+    @property
+    def cuda_event(self) -> int:
+        return self.handle.value
+
+    def record(self, stream):
+        rc = TimingEvent._hip.hipEventRecord(self.handle, self._c.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both complete)."""
+        ms = self._c.c_float()
+        rc = TimingEvent._hip.hipEventElapsedTime(self._c.byref(ms), self.handle, end.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._hip is not None and self.handle:
+            TimingEvent._hip.hipEventDestroy(self.handle)
 
 
 def torch_reductions() -> int:
@@ -464,6 +529,11 @@ def main(argv=None) -> int:
                                    ev_partial_end=ev1.cuda_event if ev1 is not None else None)
             binding.attn_fwht_undo(out, sg, out, stream=stream)
 
+    # context, not a ceiling: a plain 1 GiB device copy on this GPU, read plus written bytes per
+    # second (a copy pays for its writes, so a read-only stream can exceed it); measured here, before
+    # the warm-up steps, so the timed steps do not start on clocks still settling from idle
+    copy_bufs = []
+    copy_gbs, copy_s = measured_copy_gbs(dev, keep=copy_bufs)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -496,7 +566,7 @@ def main(argv=None) -> int:
     # each event between kernels idles the GPU for several microseconds, so
     # recording them on every step would slow the steps being timed.
     sampled = set(range(0, args.steps, max(1, args.event_every)))
-    evs = {i: (new_event(), new_event()) for i in sampled}
+    evs = {i: (TimingEvent(stream), TimingEvent(stream)) for i in sampled}
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
@@ -508,6 +578,8 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    del copy_bufs[:]
+    torch.cuda.empty_cache()
     partial_ms = [e0.elapsed_time(e1) for e0, e1 in evs.values()]
     partial_avg_s = statistics.fmean(partial_ms) * 1e-3
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -565,9 +637,8 @@ def main(argv=None) -> int:
             "algorithmic_bytes_per_launch": nbytes,
         },
     }
-    # context only, not a ceiling: a plain 1 GiB device copy on this GPU, read plus written bytes
-    # per second (a copy pays for its writes, so a read-only stream can exceed it)
-    result["device_copy_gbs"] = round(measured_copy_gbs(dev), 1)
+    result["device_copy_gbs"] = round(copy_gbs, 1)
+    result["device_copy_seconds"] = round(copy_s, 3)
 
     # ---- every preset: cold (flushed) and warm
     if not args.quick:
@@ -581,6 +652,16 @@ def main(argv=None) -> int:
             e1.record(stream)
         torch.cuda.synchronize()
         empty_pair_us = statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in empty)
+        # and with timing-only events (TimingEvent: no system-scope fence when recorded)
+        empty_t = [(TimingEvent(stream), TimingEvent(stream)) for _ in range(50)]
+        torch.cuda.synchronize()
+        for e0, e1 in empty_t:
+            flush.sum()
+            e0.record(stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        empty_pair_t_us = statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in empty_t)
+        del empty_t
         per = []
         for wi, w in enumerate(WORKLOADS):
             if w.name != cfg.name or args.workload not in by_name:
@@ -626,7 +707,7 @@ def main(argv=None) -> int:
                 cold = statistics.median(cold_samples)
                 pk = []
                 for _ in range(5):
-                    c0, c1 = new_event(), new_event()
+                    c0, c1 = TimingEvent(stream), TimingEvent(stream)
                     call(pin, ptens, pout, W, c0, c1)
                     torch.cuda.synchronize()
                     pk.append(c0.elapsed_time(c1) * 1e3)
@@ -643,12 +724,28 @@ def main(argv=None) -> int:
                 torch.cuda.synchronize()
                 ev = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs)
                 ev_med, ev_p10, ev_p90 = statistics.median(ev), ev[len(ev) // 10], ev[(9 * len(ev)) // 10]
+                # the same protocol between timing-only events
+                pairs_t = [(TimingEvent(stream), TimingEvent(stream)) for _ in range(50)]
+                torch.cuda.synchronize()
+                for e0, e1 in pairs_t:
+                    flush.sum()
+                    e0.record(stream)
+                    call(pin, ptens, pout, W)
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                evt = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pairs_t)
+                del pairs_t
+                evt_med = statistics.median(evt)
                 per.append({
                     "workload": w.name, "window": W, "kv_bytes": nb,
                     "cold_event_us": {"median": round(ev_med, 2), "p10": round(ev_p10, 2),
                                       "p90": round(ev_p90, 2), "reps": len(ev),
                                       "empty_pair_median": round(empty_pair_us, 2)},
                     "cold_event_hbm_frac": round(nb / (ev_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "cold_timing_event_us": {"median": round(evt_med, 2), "p10": round(evt[len(evt) // 10], 2),
+                                             "p90": round(evt[(9 * len(evt)) // 10], 2), "reps": len(evt),
+                                             "empty_pair_median": round(empty_pair_t_us, 2)},
+                    "cold_timing_event_hbm_frac": round(nb / (evt_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     **orc.get(W, {}),
                     "warm_us_per_call": round(warm, 2),
                     "warm_gbs": round(nb / (warm * 1e-6) / 1e9, 1),
@@ -664,7 +761,8 @@ def main(argv=None) -> int:
                 })
                 print(f"[bench] {w.name} W={W}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), "
                       f"cold {cold:.2f} us ({per[-1]['cold_gbs']} GB/s), graph {g_us:.2f} us, "
-                      f"flushed events median {ev_med:.2f} (p10 {ev_p10:.2f}, p90 {ev_p90:.2f}) us",
+                      f"flushed events median {ev_med:.2f} (p10 {ev_p10:.2f}, p90 {ev_p90:.2f}) us, "
+                      f"timing-only events {evt_med:.2f} us",
                       file=sys.stderr, flush=True)
             if w.name != cfg.name or args.workload not in by_name:
                 del ptens
@@ -708,7 +806,7 @@ def main(argv=None) -> int:
                                      per_call_us(lambda: flush.sum(), args.reps) for _ in range(5))
             pk = []
             for _ in range(5):
-                c0, c1 = new_event(), new_event()
+                c0, c1 = TimingEvent(stream), TimingEvent(stream)
                 cb_call(c0, c1)
                 torch.cuda.synchronize()
                 pk.append(c0.elapsed_time(c1) * 1e3)
