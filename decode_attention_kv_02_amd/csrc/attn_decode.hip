@@ -173,6 +173,17 @@ partial_fn select_partial(int D, int QB, int GB, int vf) {
     return nullptr;
 }
 
+// The single-buffer lane kernel: head_dim 256, one-byte V, one query per workgroup and one or two
+// heads (the launches single_pass_positions admits).
+partial_fn select_partial_single(int D, int GB, int vf) {
+    static_assert(kWaves * Geometry<256, kVI8>::RW == 64 && kWaves * Geometry<256, kVCB>::RW == 64,
+                  "one iteration of one-byte V at head_dim 256 covers the planner's single_pass_positions");
+    if (D != 256) return nullptr;
+    if (vf == kVI8) return GB == 1 ? attn_partial_single_kernel<256, 1, kVI8> : GB == 2 ? attn_partial_single_kernel<256, 2, kVI8> : nullptr;
+    if (vf == kVCB) return GB == 1 ? attn_partial_single_kernel<256, 1, kVCB> : GB == 2 ? attn_partial_single_kernel<256, 2, kVCB> : nullptr;
+    return nullptr;
+}
+
 template <int D>
 partial_fn mfma_for_format(int vf) {
     switch (vf) {
@@ -256,12 +267,17 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
                                             std::to_string(kNoAllocScratchBytes) +
                                             " bytes of scratch of attn_decode_noalloc");
 
-    bool any_mfma = false, any_lanes = false;
-    for (const LaunchGroup &lg : plan.groups) (lg.mfma ? any_mfma : any_lanes) = true;
+    bool any_mfma = false, any_lanes = false, any_single = false;
+    for (const LaunchGroup &lg : plan.groups) {
+        (lg.mfma ? any_mfma : any_lanes) = true;
+        any_single = any_single || lg.single;
+    }
     const partial_fn pk_mfma = any_mfma ? select_partial_mfma(D, vsrc.format) : nullptr;
     const partial_fn pk_lanes = any_lanes ? select_partial(D, plan.lanes.QB, plan.lanes.GB, vsrc.format) : nullptr;
+    const partial_fn pk_single = any_single ? select_partial_single(D, plan.lanes.GB, vsrc.format) : nullptr;
     const combine_fn ck = select_combine(D);
-    if ((any_mfma && pk_mfma == nullptr) || (any_lanes && pk_lanes == nullptr) || ck == nullptr)
+    if ((any_mfma && pk_mfma == nullptr) || (any_lanes && pk_lanes == nullptr) || (any_single && pk_single == nullptr) ||
+        ck == nullptr)
         return fail(ATTN_DECODE_EINVAL, "no kernel for this shape");
 
     // ---- HIP from here on
@@ -347,7 +363,8 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
         fill(lg, false);
         const int64_t grid = lg.items + lg.tail_rows * merge_groups(D);   // partial, then merge workgroups
         const int threads = lg.mfma ? kThreads * mfma_dim_splits(D) : kThreads;
-        hipLaunchKernelGGL(lg.mfma ? pk_mfma : pk_lanes, dim3((unsigned)grid), dim3(threads), 0, stream, args);
+        hipLaunchKernelGGL(lg.mfma ? pk_mfma : lg.single ? pk_single : pk_lanes, dim3((unsigned)grid), dim3(threads), 0,
+                           stream, args);
         e = hipGetLastError();
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
     }

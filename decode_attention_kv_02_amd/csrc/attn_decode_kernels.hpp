@@ -438,8 +438,13 @@ struct Frag {
 // softmax weight.  The codebook is expanded once per workgroup into a
 // 256-entry LDS table already masked and multiplied by 1/sqrt(B), so an
 // element costs one byte extract and one LDS read.
-template <int D, int QB, int GB, int VF>
-__global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs args) {
+//
+// SINGLE: one register buffer, each iteration's loads issued right before it is
+// consumed, for launches whose every chunk is at most one iteration per wave
+// (attn_partial_single_kernel); the rows, their order and the arithmetic are
+// those of the buffered form.
+template <int D, int QB, int GB, int VF, bool SINGLE>
+__device__ __forceinline__ void partial_lanes(const LaunchArgs &args) {
     using Geo = Geometry<D, VF>;
     constexpr int R = Geo::R, P = Geo::P, U = Geo::U, RW = Geo::RW, HALF = Geo::HALF;
     constexpr int NR = QB * GB;   // rows: (query of the group, head of the block)
@@ -628,11 +633,22 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
     constexpr int STEP = kWaves * RW;
     // Register buffers of loads in flight: three where the third keeps the
     // variant's occupancy (one or two rows up to head_dim 256, one row at 512),
-    // else two.  The rows of each iteration and the order they are consumed in
-    // do not change, so neither do the results.
-    constexpr int NBUF = (NR == 1 || (NR == 2 && D <= 256)) ? 3 : 2;
+    // else two; one in the SINGLE form.  The rows of each iteration and the
+    // order they are consumed in do not change, so neither do the results.
+    constexpr int NBUF = SINGLE ? 1 : (NR == 1 || (NR == 2 && D <= 256)) ? 3 : 2;
     int wb = cbeg + w * RW;
-    if constexpr (NBUF == 3) {
+    if constexpr (NBUF == 1) {
+        Frag<U> f0;
+        if constexpr (VF == kVCB) {
+            s_cb[tid] = args.codebook[tid & args.cb_mask] * args.cb_scale;
+            __syncthreads();
+        }
+        while (wb < cend) {
+            load(wb, f0);
+            consume(wb, f0);
+            wb += STEP;
+        }
+    } else if constexpr (NBUF == 3) {
         Frag<U> f0, f1, f2;
         if (wb < cend) load(wb, f0);
         if (wb + STEP < cend) load(wb + STEP, f1);
@@ -759,6 +775,22 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
             }
         }
     }
+}
+
+template <int D, int QB, int GB, int VF>
+__global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs args) {
+    partial_lanes<D, QB, GB, VF, false>(args);
+}
+
+// The lane kernel for launches of many chunks of at most one iteration per wave
+// (one-byte V at head_dim 256: up to 64 positions, the chunks of slots of up to
+// 2048 positions).  There the buffered form's extra buffers are never filled,
+// and without them the registers allow four waves per SIMD instead of two, so
+// twice the workgroups per CU overlap their fixed start and merge costs.  Same
+// results bit for bit.
+template <int D, int GB, int VF>
+__global__ __launch_bounds__(kThreads, 4) void attn_partial_single_kernel(const LaunchArgs args) {
+    partial_lanes<D, 1, GB, VF, true>(args);
 }
 
 // ---------------------------------------------------------------- combine kernel

@@ -77,6 +77,7 @@ struct KernelShape {
 struct LaunchGroup {
     std::vector<int32_t> slots;        // slot indices, in work-list order
     int64_t items = 0;                 // partial-kernel workgroups
+    bool single = false;               // lane kernel in its single-buffer form (see single_pass_positions)
     int64_t combine_rows = 0;          // query heads merged by the combine kernel
     int64_t tail_rows = 0;             // query heads merged by merge workgroups at the end of the
                                        // partial kernel's grid (head_dim / 64 workgroups each)
@@ -310,6 +311,18 @@ inline int heads_per_workgroup(int G) {
 // 11.9 -> 12.5 us).  Each (query, head) row takes the same steps whatever the
 // number of heads per workgroup, so the results do not change.
 constexpr int64_t kSplitHeadsBelowItems = 256;
+
+// Positions one iteration of the lane kernel's four waves covers with one-byte V at head_dim 256
+// (each wave 16 rows); 0 where the single-buffer form is not built.  A lane-kernel launch whose
+// every chunk fits in one such iteration, with at least kSingleMinItems workgroups, runs the
+// single-buffer form (attn_partial_single_kernel): its workgroups never fill a second buffer, and
+// without the buffers the registers allow four waves per SIMD instead of two.  The arithmetic is
+// the same, so the choice never changes a result.  Measured (graph-replayed, 16 q / 8 kv heads,
+// int8 V): 48 x 2048 150.0 -> 134.8 us, 128 x 1024 209.5 -> 189.9, 16 x 2048 55.4 -> 50.6,
+// 8 x 1024 19.1 -> 17.0; a lone 2048 slot (256 workgroups) 9.3 -> 10.7 us, so small grids keep
+// the buffered form.
+inline int single_pass_positions(int32_t head_dim, bool byte_v) { return head_dim == 256 && byte_v ? 64 : 0; }
+constexpr int64_t kSingleMinItems = 1024;
 
 // Which partial kernel computes a query.  The matrix-core kernel
 // (attn_partial_mfma_kernel) puts up to 16 (query, head) columns in one
@@ -556,6 +569,14 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
     }
     if (!g.slots.empty()) plan.groups.push_back(g);
     for (const LaunchGroup &lg : plan.groups) plan.total_items += lg.items;
+    const int one_pass = single_pass_positions(head_dim, byte_v);
+    for (LaunchGroup &lg : plan.groups) {
+        if (lg.mfma || one_pass == 0 || plan.lanes.QB != 1 || plan.lanes.GB > 2 || lg.items < kSingleMinItems)
+            continue;
+        bool fits = true;
+        for (int32_t s : lg.slots) fits = fits && plan.slots[s].chunk <= one_pass;
+        lg.single = fits;
+    }
     // a small lane-kernel call without query groups: fewer heads per workgroup, more workgroups
     bool lanes_only = plan.lanes.QB == 1;
     for (const SlotPlan &sp : plan.slots) lanes_only = lanes_only && !sp.mfma;
