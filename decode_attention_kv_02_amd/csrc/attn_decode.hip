@@ -31,7 +31,9 @@ using namespace attn_decode_impl;
 static_assert(ATTN_DECODE_MAX_SLOTS_PER_LAUNCH == kMaxSlotsPerLaunch, "slot table size");
 static_assert(ATTN_DECODE_MAX_CHUNKS == kMaxChunks, "chunk bound");
 static_assert(kSingleLaunchMaxChunks <= kMaxChunks, "single-launch merge bound");
-static_assert(sizeof(LaunchArgs) <= 4096, "kernel arguments stay within 4 KiB");
+static_assert(sizeof(LaunchArgsT<kSmallTableSlots>) <= 4096, "the small query table stays within 4 KiB of arguments");
+// the large table: 18.5 KiB of kernel arguments, which ROCm copies whole (checked on MI355X up to 18 KiB)
+static_assert(sizeof(LaunchArgsT<kMaxSlotsPerLaunch>) <= 20 * 1024, "large query table");
 static_assert(sizeof(AppendArgs) <= 4096, "kernel arguments stay within 4 KiB");
 
 namespace {
@@ -133,82 +135,91 @@ int scratch_on_device(int device, void **ptr) {
 }
 
 // ------------------------------------------------------------ kernel tables
+// Every kernel that reads the query table exists for both table capacities NS.
 
-typedef void (*partial_fn)(const LaunchArgs);
-typedef void (*combine_fn)(const LaunchArgs);
+template <int NS> using partial_fn_t = void (*)(const LaunchArgsT<NS>);
+template <int NS> using combine_fn_t = void (*)(const LaunchArgsT<NS>);
 
-template <int D, int VF>
-partial_fn partial_for(int QB, int GB) {
+template <int D, int VF, int NS>
+partial_fn_t<NS> partial_for(int QB, int GB) {
     if (QB == 1) {
         switch (GB) {
-            case 1: return attn_partial_kernel<D, 1, 1, VF>;
-            case 2: return attn_partial_kernel<D, 1, 2, VF>;
-            case 4: return attn_partial_kernel<D, 1, 4, VF>;
+            case 1: return attn_partial_kernel<D, 1, 1, VF, NS>;
+            case 2: return attn_partial_kernel<D, 1, 2, VF, NS>;
+            case 4: return attn_partial_kernel<D, 1, 4, VF, NS>;
         }
     } else if (QB == 2 && GB == 2) {
-        return attn_partial_kernel<D, 2, 2, VF>;
+        return attn_partial_kernel<D, 2, 2, VF, NS>;
     } else if (QB == 4 && GB == 1) {
-        return attn_partial_kernel<D, 4, 1, VF>;
+        return attn_partial_kernel<D, 4, 1, VF, NS>;
     }
     return nullptr;
 }
 
-template <int D>
-partial_fn partial_for_format(int vf, int QB, int GB) {
+template <int D, int NS>
+partial_fn_t<NS> partial_for_format(int vf, int QB, int GB) {
     switch (vf) {
-        case kVF16: return partial_for<D, kVF16>(QB, GB);
-        case kVI8: return partial_for<D, kVI8>(QB, GB);
-        case kVCB: return partial_for<D, kVCB>(QB, GB);
+        case kVF16: return partial_for<D, kVF16, NS>(QB, GB);
+        case kVI8: return partial_for<D, kVI8, NS>(QB, GB);
+        case kVCB: return partial_for<D, kVCB, NS>(QB, GB);
     }
     return nullptr;
 }
 
-partial_fn select_partial(int D, int QB, int GB, int vf) {
+template <int NS>
+partial_fn_t<NS> select_partial(int D, int QB, int GB, int vf) {
     switch (D) {
-        case 64: return partial_for_format<64>(vf, QB, GB);
-        case 128: return partial_for_format<128>(vf, QB, GB);
-        case 256: return partial_for_format<256>(vf, QB, GB);
-        case 512: return partial_for_format<512>(vf, QB, GB);
+        case 64: return partial_for_format<64, NS>(vf, QB, GB);
+        case 128: return partial_for_format<128, NS>(vf, QB, GB);
+        case 256: return partial_for_format<256, NS>(vf, QB, GB);
+        case 512: return partial_for_format<512, NS>(vf, QB, GB);
     }
     return nullptr;
 }
 
 // The single-buffer lane kernel: head_dim 256, one-byte V, one query per workgroup and one or two
 // heads (the launches single_pass_positions admits).
-partial_fn select_partial_single(int D, int GB, int vf) {
-    static_assert(kWaves * Geometry<256, kVI8>::RW == 64 && kWaves * Geometry<256, kVCB>::RW == 64,
-                  "one iteration of one-byte V at head_dim 256 covers the planner's single_pass_positions");
+static_assert(kWaves * Geometry<256, kVI8>::RW == 64 && kWaves * Geometry<256, kVCB>::RW == 64,
+              "one iteration of one-byte V at head_dim 256 covers the planner's single_pass_positions");
+template <int NS>
+partial_fn_t<NS> select_partial_single(int D, int GB, int vf) {
     if (D != 256) return nullptr;
-    if (vf == kVI8) return GB == 1 ? attn_partial_single_kernel<256, 1, kVI8> : GB == 2 ? attn_partial_single_kernel<256, 2, kVI8> : nullptr;
-    if (vf == kVCB) return GB == 1 ? attn_partial_single_kernel<256, 1, kVCB> : GB == 2 ? attn_partial_single_kernel<256, 2, kVCB> : nullptr;
+    if (vf == kVI8)
+        return GB == 1 ? attn_partial_single_kernel<256, 1, kVI8, NS>
+                       : GB == 2 ? attn_partial_single_kernel<256, 2, kVI8, NS> : nullptr;
+    if (vf == kVCB)
+        return GB == 1 ? attn_partial_single_kernel<256, 1, kVCB, NS>
+                       : GB == 2 ? attn_partial_single_kernel<256, 2, kVCB, NS> : nullptr;
     return nullptr;
 }
 
-template <int D>
-partial_fn mfma_for_format(int vf) {
+template <int D, int NS>
+partial_fn_t<NS> mfma_for_format(int vf) {
     switch (vf) {
-        case kVF16: return attn_partial_mfma_kernel<D, kVF16>;
-        case kVI8: return attn_partial_mfma_kernel<D, kVI8>;
-        case kVCB: return attn_partial_mfma_kernel<D, kVCB>;
+        case kVF16: return attn_partial_mfma_kernel<D, kVF16, NS>;
+        case kVI8: return attn_partial_mfma_kernel<D, kVI8, NS>;
+        case kVCB: return attn_partial_mfma_kernel<D, kVCB, NS>;
     }
     return nullptr;
 }
 
-partial_fn select_partial_mfma(int D, int vf) {
+template <int NS>
+partial_fn_t<NS> select_partial_mfma(int D, int vf) {
     switch (D) {
-        case 128: return mfma_for_format<128>(vf);
-        case 256: return mfma_for_format<256>(vf);
-        case 512: return mfma_for_format<512>(vf);
+        case 128: return mfma_for_format<128, NS>(vf);
+        case 256: return mfma_for_format<256, NS>(vf);
+        case 512: return mfma_for_format<512, NS>(vf);
     }
     return nullptr;
 }
 
-combine_fn select_combine(int D) {
+template <int NS>
+combine_fn_t<NS> select_combine(int D) {
     switch (D) {
-        case 64: return attn_combine_kernel<64>;
-        case 128: return attn_combine_kernel<128>;
-        case 256: return attn_combine_kernel<256>;
-        case 512: return attn_combine_kernel<512>;
+        case 64: return attn_combine_kernel<64, NS>;
+        case 128: return attn_combine_kernel<128, NS>;
+        case 256: return attn_combine_kernel<256, NS>;
+        case 512: return attn_combine_kernel<512, NS>;
     }
     return nullptr;
 }
@@ -248,6 +259,118 @@ struct VSource {
 };
 
 // Everything after the layout-specific checks: plan, workspace, launches.
+// What every launch of one call shares.
+struct CallArgs {
+    const void *q = nullptr;
+    const void *k = nullptr;
+    VSource vsrc;
+    float *out = nullptr;
+    float *ws_o = nullptr;
+    float *ws_ml = nullptr;
+    uint64_t *flags = nullptr;
+    int32_t n_q = 0, n_kv = 0, D = 0;
+    float scale_log2 = 0.f;
+};
+
+// A launch group of at most kSmallTableSlots query rows takes the small query table.
+bool small_table(const LaunchGroup &lg) { return (int)lg.slots.size() <= kSmallTableSlots; }
+
+// The kernels of one table capacity that a plan's launch groups of that capacity use.
+template <int NS>
+struct Kernels {
+    partial_fn_t<NS> mfma = nullptr, lanes = nullptr, single = nullptr;
+    combine_fn_t<NS> combine = nullptr;
+};
+
+template <int NS>
+bool pick_kernels(const CallPlan &plan, int D, int vf, Kernels<NS> &k) {
+    const bool small = NS == kSmallTableSlots;
+    bool mfma = false, lanes = false, single = false, combine = false;
+    for (const LaunchGroup &lg : plan.groups) {
+        if (small_table(lg) != small) continue;
+        (lg.mfma ? mfma : lanes) = true;
+        single = single || lg.single;
+        combine = combine || lg.combine_rows > 0;
+    }
+    if (mfma && (k.mfma = select_partial_mfma<NS>(D, vf)) == nullptr) return false;
+    if (lanes && (k.lanes = select_partial<NS>(D, plan.lanes.QB, plan.lanes.GB, vf)) == nullptr) return false;
+    if (single && (k.single = select_partial_single<NS>(D, plan.lanes.GB, vf)) == nullptr) return false;
+    if (combine && (k.combine = select_combine<NS>(D)) == nullptr) return false;
+    return true;
+}
+
+// Fills the query table of one launch group and enqueues its partial kernel, or (combine) its
+// combine kernel.
+template <int NS>
+int enqueue_group(const CallPlan &plan, const LaunchGroup &lg, bool combine, const CallArgs &c,
+                  const Kernels<NS> &kn, hipStream_t stream) {
+    LaunchArgsT<NS> args;
+    std::memset(&args, 0, sizeof(args));
+    args.q = static_cast<const uint16_t *>(c.q);
+    args.k = static_cast<const uint16_t *>(c.k);
+    args.v = c.vsrc.v;
+    args.vs = c.vsrc.side;
+    args.codebook = c.vsrc.codebook;
+    args.cb_mask = c.vsrc.format == kVCB ? (1 << c.vsrc.bits) - 1 : 0;
+    args.cb_scale = (float)(1.0 / std::sqrt((double)(c.D < 256 ? c.D : 256)));
+    args.out = c.out;
+    args.ws_o = c.ws_o;
+    args.ws_ml = c.ws_ml;
+    args.flags = c.flags;
+    args.n_q = c.n_q;
+    args.G = plan.G;
+    args.scale_log2 = c.scale_log2;
+
+    // Search keys: the entries' first work items (partial kernels) or first combine rows
+    // (combine kernel); tkey, the first rows among a single-launch grid's merge workgroups.
+    const KernelShape &ks = lg.mfma ? plan.matrix : plan.lanes;
+    args.n_sub = ks.n_sub;
+    args.n_slots = (int32_t)lg.slots.size();
+    int32_t item = 0, comb = 0, tail = 0;
+    int32_t lead_pos = 0;
+    for (size_t i = 0; i < lg.slots.size(); ++i) {
+        const int32_t s = lg.slots[i];
+        const SlotPlan &sp = plan.slots[s];
+        SlotDesc &sd = args.slot[i];
+        if (sp.group_n > 0) lead_pos = (int32_t)i;   // a leader or an ungrouped query
+        sd.kv_row0 = sp.kv_row0;
+        sd.part_row0 = sp.part_row0;
+        sd.L = sp.L;
+        sd.lo = sp.lo;
+        sd.chunk = sp.chunk;
+        sd.n_chunks = sp.n_chunks;
+        sd.item_begin = sp.group_n > 0 ? item : args.slot[lead_pos].item_begin;
+        sd.comb_begin = sp.fused ? tail : comb;
+        sd.flag_row0 = sp.fused ? sp.flag_row0 : -1;
+        sd.slot_idx = s;
+        sd.kv_stride = sp.kv_stride;
+        sd.ring_cap = sp.ring_cap;
+        sd.ring_base = sp.ring_base;
+        sd.group_n = (int16_t)sp.group_n;
+        sd.lead_off = (int16_t)(i - lead_pos);
+        args.key[i] = combine ? comb : sd.item_begin;
+        args.tkey[i] = tail;
+        if (sp.group_n > 0) item += c.n_kv * ks.n_sub * sp.n_chunks;
+        if (sp.n_chunks > 1) (sp.fused ? tail : comb) += c.n_q;
+    }
+    args.n_items = item;
+
+    if (combine) {
+        hipLaunchKernelGGL(kn.combine, dim3((unsigned)(lg.combine_rows * (c.D / kCombineDims))),
+                           dim3(kCombineThreads), 0, stream, args);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("combine kernel launch: ") + hipGetErrorString(e));
+        return ATTN_DECODE_OK;
+    }
+    const int64_t grid = lg.items + lg.tail_rows * merge_groups(c.D);   // partial, then merge workgroups
+    const int threads = lg.mfma ? kThreads * mfma_dim_splits(c.D) : kThreads;
+    hipLaunchKernelGGL(lg.mfma ? kn.mfma : lg.single ? kn.single : kn.lanes, dim3((unsigned)grid), dim3(threads), 0,
+                       stream, args);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
+    return ATTN_DECODE_OK;
+}
+
 // no_alloc: the partials go to this device's `scratch` instead of the stream's
 // workspace, and the call neither allocates nor frees anything.
 int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cache,
@@ -267,17 +390,9 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
                                             std::to_string(kNoAllocScratchBytes) +
                                             " bytes of scratch of attn_decode_noalloc");
 
-    bool any_mfma = false, any_lanes = false, any_single = false;
-    for (const LaunchGroup &lg : plan.groups) {
-        (lg.mfma ? any_mfma : any_lanes) = true;
-        any_single = any_single || lg.single;
-    }
-    const partial_fn pk_mfma = any_mfma ? select_partial_mfma(D, vsrc.format) : nullptr;
-    const partial_fn pk_lanes = any_lanes ? select_partial(D, plan.lanes.QB, plan.lanes.GB, vsrc.format) : nullptr;
-    const partial_fn pk_single = any_single ? select_partial_single(D, plan.lanes.GB, vsrc.format) : nullptr;
-    const combine_fn ck = select_combine(D);
-    if ((any_mfma && pk_mfma == nullptr) || (any_lanes && pk_lanes == nullptr) || (any_single && pk_single == nullptr) ||
-        ck == nullptr)
+    Kernels<kSmallTableSlots> small;
+    Kernels<kMaxSlotsPerLaunch> large;
+    if (!pick_kernels(plan, D, vsrc.format, small) || !pick_kernels(plan, D, vsrc.format, large))
         return fail(ATTN_DECODE_EINVAL, "no kernel for this shape");
 
     // ---- HIP from here on
@@ -298,75 +413,28 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
                                          &ws_o);
         if (rc != ATTN_DECODE_OK) return rc;
     }
-    float *ws_ml = ws_o ? ws_o + plan.part_rows * D : nullptr;
 
-    const double scale_log2 = (double)scale * 1.4426950408889634074;  // scale * log2(e)
-
-    LaunchArgs args;
-    std::memset(&args, 0, sizeof(args));
-    args.q = static_cast<const uint16_t *>(q);
-    args.k = static_cast<const uint16_t *>(k_cache);
-    args.v = vsrc.v;
-    args.vs = vsrc.side;
-    args.codebook = vsrc.codebook;
-    args.cb_mask = vsrc.format == kVCB ? (1 << vsrc.bits) - 1 : 0;
-    args.cb_scale = (float)(1.0 / std::sqrt((double)(D < 256 ? D : 256)));
-    args.out = out;
-    args.ws_o = ws_o;
-    args.ws_ml = ws_ml;
-    args.flags = flags;
-    args.n_q = n_q;
-    args.G = plan.G;
-    args.scale_log2 = (float)scale_log2;
-
-    // Search keys: the entries' first work items (partial kernels) or first combine rows
-    // (combine kernel); tkey, the first rows among a single-launch grid's merge workgroups.
-    auto fill = [&](const LaunchGroup &lg, bool combine) {
-        const KernelShape &ks = lg.mfma ? plan.matrix : plan.lanes;
-        args.n_sub = ks.n_sub;
-        args.n_slots = (int32_t)lg.slots.size();
-        int32_t item = 0, comb = 0, tail = 0;
-        int32_t lead_pos = 0;
-        for (size_t i = 0; i < lg.slots.size(); ++i) {
-            const int32_t s = lg.slots[i];
-            const SlotPlan &sp = plan.slots[s];
-            SlotDesc &sd = args.slot[i];
-            if (sp.group_n > 0) lead_pos = (int32_t)i;   // a leader or an ungrouped query
-            sd.kv_row0 = sp.kv_row0;
-            sd.part_row0 = sp.part_row0;
-            sd.L = sp.L;
-            sd.lo = sp.lo;
-            sd.chunk = sp.chunk;
-            sd.n_chunks = sp.n_chunks;
-            sd.item_begin = sp.group_n > 0 ? item : args.slot[lead_pos].item_begin;
-            sd.comb_begin = sp.fused ? tail : comb;
-            sd.flag_row0 = sp.fused ? sp.flag_row0 : -1;
-            sd.slot_idx = s;
-            sd.kv_stride = sp.kv_stride;
-            sd.ring_cap = sp.ring_cap;
-            sd.ring_base = sp.ring_base;
-            sd.group_n = (int16_t)sp.group_n;
-            sd.lead_off = (int16_t)(i - lead_pos);
-            args.key[i] = combine ? comb : sd.item_begin;
-            args.tkey[i] = tail;
-            if (sp.group_n > 0) item += n_kv * ks.n_sub * sp.n_chunks;
-            if (sp.n_chunks > 1) (sp.fused ? tail : comb) += n_q;
-        }
-        args.n_items = item;
-    };
+    CallArgs c;
+    c.q = q;
+    c.k = k_cache;
+    c.vsrc = vsrc;
+    c.out = out;
+    c.ws_o = ws_o;
+    c.ws_ml = ws_o ? ws_o + plan.part_rows * D : nullptr;
+    c.flags = flags;
+    c.n_q = n_q;
+    c.n_kv = n_kv;
+    c.D = D;
+    c.scale_log2 = (float)((double)scale * 1.4426950408889634074);   // scale * log2(e)
 
     if (opts && opts->ev_partial_begin) {
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(opts->ev_partial_begin), stream);
         if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("hipEventRecord: ") + hipGetErrorString(e));
     }
     for (const LaunchGroup &lg : plan.groups) {
-        fill(lg, false);
-        const int64_t grid = lg.items + lg.tail_rows * merge_groups(D);   // partial, then merge workgroups
-        const int threads = lg.mfma ? kThreads * mfma_dim_splits(D) : kThreads;
-        hipLaunchKernelGGL(lg.mfma ? pk_mfma : lg.single ? pk_single : pk_lanes, dim3((unsigned)grid), dim3(threads), 0,
-                           stream, args);
-        e = hipGetLastError();
-        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("partial kernel launch: ") + hipGetErrorString(e));
+        const int rc = small_table(lg) ? enqueue_group(plan, lg, false, c, small, stream)
+                                       : enqueue_group(plan, lg, false, c, large, stream);
+        if (rc != ATTN_DECODE_OK) return rc;
     }
     if (opts && opts->ev_partial_end) {
         e = hipEventRecord(reinterpret_cast<hipEvent_t>(opts->ev_partial_end), stream);
@@ -374,10 +442,9 @@ int launch(const std::vector<QuerySpan> &spans, const void *q, const void *k_cac
     }
     for (const LaunchGroup &lg : plan.groups) {
         if (lg.combine_rows == 0) continue;
-        fill(lg, true);
-        hipLaunchKernelGGL(ck, dim3((unsigned)(lg.combine_rows * (D / kCombineDims))), dim3(kCombineThreads), 0, stream, args);
-        e = hipGetLastError();
-        if (e != hipSuccess) return fail(ATTN_DECODE_EHIP, std::string("combine kernel launch: ") + hipGetErrorString(e));
+        const int rc = small_table(lg) ? enqueue_group(plan, lg, true, c, small, stream)
+                                       : enqueue_group(plan, lg, true, c, large, stream);
+        if (rc != ATTN_DECODE_OK) return rc;
     }
     return ATTN_DECODE_OK;
 }

@@ -79,15 +79,19 @@ enum VFormat : int {
 // kernel starts.  So those reads sit together at the front (the first 64-byte
 // line holds the sizes and the first 12 keys; a search over up to 12 entries
 // misses once), and every query descriptor fills exactly one line.
-struct alignas(64) LaunchArgs {
+// NS is the table's capacity: kSmallTableSlots (3.4 KB of arguments) for launches
+// of up to 48 query rows, kMaxSlotsPerLaunch (18.5 KB) for larger ones, so a batch
+// of up to 256 rows is one launch while a small call copies only the small table.
+template <int NS>
+struct alignas(64) LaunchArgsT {
     int32_t n_slots;        // slots in this launch (table entries, longest chunks first)
     int32_t n_items;        // partial-kernel workgroups of this launch
     int32_t n_sub;          // G / GB
     int32_t G;              // query heads per kv head
-    int32_t key[kMaxSlotsPerLaunch];  // per entry, non-decreasing: its first work item (partial
-                                      // kernels) or its first combine row (combine kernel)
-    int32_t tkey[kMaxSlotsPerLaunch]; // partial kernels, per entry, non-decreasing: its first row
-                                      // among the merge workgroups at the end of the grid
+    int32_t key[NS];        // per entry, non-decreasing: its first work item (partial
+                            // kernels) or its first combine row (combine kernel)
+    int32_t tkey[NS];       // partial kernels, per entry, non-decreasing: its first row
+                            // among the merge workgroups at the end of the grid
     const uint16_t *q;      // fp16 [n_slots_total][n_q][D]
     const uint16_t *k;      // fp16 packed cache
     const void *v;          // fp16, int8 or codebook-index cache
@@ -101,9 +105,11 @@ struct alignas(64) LaunchArgs {
     int32_t n_q;
     float scale_log2;       // scale * log2(e)
     float cb_scale;         // codebook V: 1 / sqrt(min(D, 256))
-    alignas(64) SlotDesc slot[kMaxSlotsPerLaunch];
+    alignas(64) SlotDesc slot[NS];
 };
-static_assert(offsetof(LaunchArgs, key) == 16 && offsetof(LaunchArgs, slot) % 64 == 0, "argument layout");
+static_assert(offsetof(LaunchArgsT<kSmallTableSlots>, key) == 16 &&
+              offsetof(LaunchArgsT<kSmallTableSlots>, slot) % 64 == 0 &&
+              offsetof(LaunchArgsT<kMaxSlotsPerLaunch>, slot) % 64 == 0, "argument layout");
 
 // ---------------------------------------------------------------- helpers
 
@@ -210,8 +216,8 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
 // bytes.  The first kMergeBatch rows are loaded together with the statistics,
 // so a merge of up to 32 chunks takes one memory round trip, and there is no
 // LDS and no barrier.  tail_merge runs the same arithmetic in the same order.
-template <int D>
-__device__ __forceinline__ void merge_wave(const LaunchArgs &args, const SlotDesc &sd, int h, int slice) {
+template <int D, class Args>
+__device__ __forceinline__ void merge_wave(const Args &args, const SlotDesc &sd, int h, int slice) {
     const int lane = threadIdx.x & 63;
     const int nc = sd.n_chunks;
     const int64_t base = sd.part_row0 + (int64_t)h * nc;
@@ -308,8 +314,8 @@ __device__ __forceinline__ bool pair_ready(uint64_t x) { return (uint32_t)(x >> 
 // bits.  At most 64 chunks (lane c holds chunk c's statistics); the values are
 // read kTailBatch chunks at a time.
 constexpr int kTailBatch = 16;
-template <int D>
-__device__ __forceinline__ void tail_merge(const LaunchArgs &args) {
+template <int D, class Args>
+__device__ __forceinline__ void tail_merge(const Args &args) {
     constexpr int SLICES = D / kCombineDims;
     constexpr int TG = (SLICES + kWaves - 1) / kWaves;                  // merge workgroups per query head
     constexpr int64_t CS = (int64_t)SLICES * kFlagPairsPerSlice;        // pairs from a chunk's block to the next's
@@ -443,8 +449,8 @@ struct Frag {
 // consumed, for launches whose every chunk is at most one iteration per wave
 // (attn_partial_single_kernel); the rows, their order and the arithmetic are
 // those of the buffered form.
-template <int D, int QB, int GB, int VF, bool SINGLE>
-__device__ __forceinline__ void partial_lanes(const LaunchArgs &args) {
+template <int D, int QB, int GB, int VF, bool SINGLE, class Args>
+__device__ __forceinline__ void partial_lanes(const Args &args) {
     using Geo = Geometry<D, VF>;
     constexpr int R = Geo::R, P = Geo::P, U = Geo::U, RW = Geo::RW, HALF = Geo::HALF;
     constexpr int NR = QB * GB;   // rows: (query of the group, head of the block)
@@ -777,8 +783,8 @@ __device__ __forceinline__ void partial_lanes(const LaunchArgs &args) {
     }
 }
 
-template <int D, int QB, int GB, int VF>
-__global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs args) {
+template <int D, int QB, int GB, int VF, int NS>
+__global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgsT<NS> args) {
     partial_lanes<D, QB, GB, VF, false>(args);
 }
 
@@ -788,8 +794,8 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(const LaunchArgs
 // and without them the registers allow four waves per SIMD instead of two, so
 // twice the workgroups per CU overlap their fixed start and merge costs.  Same
 // results bit for bit.
-template <int D, int GB, int VF>
-__global__ __launch_bounds__(kThreads, 4) void attn_partial_single_kernel(const LaunchArgs args) {
+template <int D, int GB, int VF, int NS>
+__global__ __launch_bounds__(kThreads, 4) void attn_partial_single_kernel(const LaunchArgsT<NS> args) {
     partial_lanes<D, 1, GB, VF, true>(args);
 }
 
@@ -797,8 +803,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_partial_single_kernel(const 
 
 // One wave per (query, query head, 64-dim slice) of a query with several
 // chunks, after the partial kernel has finished.
-template <int D>
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const LaunchArgs args) {
+template <int D, int NS>
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(const LaunchArgsT<NS> args) {
     constexpr int SLICES = D / kCombineDims;
     const int row = blockIdx.x / SLICES;
     const int slice = blockIdx.x - row * SLICES;

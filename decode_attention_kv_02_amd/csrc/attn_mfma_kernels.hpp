@@ -112,8 +112,8 @@ __device__ __forceinline__ void split_f16(const float (&x)[4], half4_t &hi, half
 // hanging the GPU.
 constexpr int kPairMaxSpins = 1 << 21;
 
-template <int D, int VF>
-__global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF>::MIN_WG)) void attn_partial_mfma_kernel(const LaunchArgs args) {
+template <int D, int VF, int NS>
+__global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF>::MIN_WG)) void attn_partial_mfma_kernel(const LaunchArgsT<NS> args) {
     using Geo = MfmaGeometry<D, VF>;
     constexpr int KS = Geo::KS, KW = Geo::KW, EV = Geo::EV, BW = Geo::BW, NB = Geo::NB, NO = Geo::NO;
     constexpr int DS = Geo::DS, DH = Geo::DH, NT = Geo::THREADS;

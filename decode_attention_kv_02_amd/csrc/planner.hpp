@@ -27,7 +27,8 @@
 
 namespace attn_decode_impl {
 
-constexpr int kMaxSlotsPerLaunch = 48;   // query table passed by value in the kernel arguments
+constexpr int kMaxSlotsPerLaunch = 256;  // query table passed by value in the kernel arguments
+constexpr int kSmallTableSlots = 48;     // launches of up to this many query rows take the small table
 constexpr int kMaxChunks = 4096;         // per slot; bounds the combine kernel's LDS weights
 constexpr int kChunkQuantum = 64;        // chunk sizes are multiples of this (one workgroup iteration at D=256)
 constexpr int kChunkMin = 64;

@@ -36,9 +36,11 @@
  *
  * Execution: every entry point that takes a stream is asynchronous on it
  * (a hipStream_t passed as void*; NULL = the null stream of the current
- * device).  A call enqueues one partial kernel per launch group of up to 48
+ * device).  A call enqueues one partial kernel per launch group of up to 256
  * slots (normally one group) and, when some slot is split into several KV
- * chunks, one log-sum-exp combine kernel per such group.  It never
+ * chunks, one log-sum-exp combine kernel per such group.  The slot table goes
+ * to the kernels by value: 3.4 KB of arguments per launch for groups of up to
+ * 48 slots, 18.5 KB for larger ones.  It never
  * synchronises the host and never reads device memory from the host.  Inputs
  * must stay alive and unmodified until the work completes.
  *
@@ -84,7 +86,7 @@ extern "C" {
 
 /* Largest number of query rows (slots, or cache queries) one kernel launch
  * covers; more are split into several launch groups inside one call. */
-#define ATTN_DECODE_MAX_SLOTS_PER_LAUNCH 48
+#define ATTN_DECODE_MAX_SLOTS_PER_LAUNCH 256
 /* Upper bound of KV chunks per slot; the planner widens chunks to stay below. */
 #define ATTN_DECODE_MAX_CHUNKS 4096
 

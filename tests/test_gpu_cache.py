@@ -235,3 +235,15 @@ def test_mixed_kernels_across_launch_groups(merge_mode):
         alone = run_gpu_cache(one, 0, dev_tensors=(dev[0][rows].contiguous(), dev[1], dev[2], dev[3]),
                               merge_mode=merge_mode)
         assert torch.equal(got[rows], alone), f"slot {s}"
+
+
+def test_cache_call_of_many_queries():
+    """130 query rows (two per slot over 65 ring slots, positions before and past the wrap) take the
+    large query table: one launch, against the oracle."""
+    rng = np.random.default_rng(9660)
+    sid = tuple(s for s in range(65) for _ in range(2))
+    pos = tuple(int(x) for x in rng.integers(0, 2000, size=130))
+    ci = make_cache_inputs(65, 256, 1, sid, pos, 8, 4, 128, True, seed_base=9660)
+    got = run_gpu_cache(ci, 0).cpu().numpy()
+    ref = run_oracle_cache(ci, 0)
+    _report("130 cache queries", assert_parity(got, ref, "130 cache queries"))

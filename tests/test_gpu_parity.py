@@ -170,13 +170,27 @@ def test_large_logits_stay_stable():
     _report("large logits", assert_parity(got, ref, "large logits"))
 
 
-def test_many_slots_span_several_launch_groups():
-    rng = np.random.default_rng(7400)
-    seq = tuple(int(x) for x in rng.integers(0, 400, size=150))
-    inp = make_inputs(seq, 4, 2, 128, True, seed_base=7400)
+@pytest.mark.parametrize("n_slots", [49, 150, 300])
+def test_many_slots(n_slots):
+    """Query tables of both capacities: up to 48 rows per launch take the small table, more the
+    large one (up to 256); 300 slots are one launch of 256 and one of 44."""
+    rng = np.random.default_rng(7400 + n_slots)
+    seq = tuple(int(x) for x in rng.integers(0, 400, size=n_slots))
+    inp = make_inputs(seq, 4, 2, 128, True, seed_base=7400 + n_slots)
     got = run_gpu(inp, 0).cpu().numpy()
     ref = run_oracle(inp, 0)
-    _report("150 slots", assert_parity(got, ref, "150 slots"))
+    _report(f"{n_slots} slots", assert_parity(got, ref, f"{n_slots} slots"))
+
+
+def test_many_slots_equal_per_slot_bitwise():
+    """A slot's result does not depend on which table or launch carried it: rows of a 300-slot call
+    (large table, then small) equal the same slots called alone."""
+    rng = np.random.default_rng(7450)
+    seq = tuple(int(x) for x in rng.integers(1, 600, size=300))
+    inp = make_inputs(seq, 16, 8, 256, False, seed_base=7450)
+    batched = run_gpu(inp, 0)
+    for s in (0, 1, 47, 48, 200, 255, 256, 299):
+        assert torch.equal(batched[s:s + 1], run_gpu(_slot_inputs(inp, s), 0)), s
 
 
 # ------------------------------------------------------------------ structural contracts
