@@ -48,7 +48,7 @@ One JSON line is printed.  Besides the contract fields it carries
     (``attn_kv_append``; ``bytes`` = fp32 K and V read plus the fp16 K and the
     fp16 or int8 V and scales written);
   * ``device_copy_gbs``: a plain 1 GiB device copy, read plus written bytes per
-    second, timed for about 0.15 s right before the warm-up steps (context, not
+    second, timed for about 0.3 s right before the warm-up steps (context, not
     a ceiling; it also lets the GPU's clocks settle before the timed steps).
 """
 from __future__ import annotations
@@ -182,7 +182,7 @@ def calibrate_copy(nbytes: int) -> int:
     return 0
 
 
-def measured_copy_gbs(dev, nbytes: int = 1 << 30, seconds: float = 0.15, keep: list = None):
+def measured_copy_gbs(dev, nbytes: int = 1 << 30, seconds: float = 0.3, keep: list = None):
     """(bytes moved per second, read + written, by a plain device-to-device copy of `nbytes`,
     back to back on the current stream for about `seconds`; the seconds it ran).  Context for
     the partial kernel's rate, not a ceiling.  It runs right before the headline's warm-up
