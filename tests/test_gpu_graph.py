@@ -27,9 +27,16 @@ def _need_gpu():
     torch.cuda.synchronize()
 
 
+# 300 short int8 slots at head_dim 256: a launch group of 256 rows (the large query table, 18.5 KB
+# of arguments frozen in the graph node) and one of 44 (the small table), both on the single-buffer
+# lane kernel
+_MANY = tuple(int(x) for x in np.random.default_rng(8850).integers(129, 2049, size=300))
+
+
 @pytest.mark.parametrize("merge_mode", [1, 2])
 @pytest.mark.parametrize("case", [((256,), 1, 1, 64, False, 0), ((4096, 1000), 16, 8, 256, True, 0),
-                                  ((20000,), 16, 8, 256, False, 1024)], ids=["tiny", "split", "window"])
+                                  ((20000,), 16, 8, 256, False, 1024), (_MANY, 16, 8, 256, True, 0)],
+                         ids=["tiny", "split", "window", "many_slots"])
 def test_graph_replay_matches_eager(case, merge_mode):
     """Both merge modes; the single-launch merge's flagged pairs must be back at zero after
     every replay, or the next replay would merge before its chunks are written."""
