@@ -108,3 +108,27 @@ def test_noalloc_takes_the_same_form():
     binding.attn_decode_noalloc(q, k, v, vs, np.asarray(seq, dtype=np.int32), 0, b, len(seq), 16, 8, 256, inp.scale)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_ring_cache_queries_take_the_same_form():
+    """80 queries over 40 ring slots of 2048 rows, positions past the wrap: one large-table launch
+    on the single-buffer form, against the oracle and against each slot's queries alone."""
+    from decode_attention_kv_02_amd.workloads import make_cache_inputs
+    from gpu_util import run_gpu_cache, run_oracle_cache
+    rng = np.random.default_rng(9770)
+    sid = tuple(s for s in range(40) for _ in range(2))
+    pos = tuple(int(x) for x in rng.integers(2048, 9000, size=80))
+    p = binding.attn_decode_cache_plan(sid, pos, 40, 2048, 1, 0, 16, 8, 256, "int8")
+    assert p["partial_workgroups"] >= MIN_ITEMS and max(p["chunk"]) <= ONE_PASS
+    ci = make_cache_inputs(40, 2048, 1, sid, pos, 16, 8, 256, True, seed_base=9770)
+    dev = to_device(ci)
+    got = run_gpu_cache(ci, 0, dev_tensors=dev)
+    _report("ring 80 queries", assert_parity(got.cpu().numpy(), run_oracle_cache(ci, 0), "ring 80 queries"))
+    q, k, v, vs = dev
+    for s in (0, 17, 39):
+        rows = [2 * s, 2 * s + 1]
+        out = torch.full((2, 16, 256), float("nan"), dtype=torch.float32, device=q.device)
+        binding.attn_decode_cache(q[rows].contiguous(), k, v, vs, (s, s), (pos[2 * s], pos[2 * s + 1]), 2, 40,
+                                  2048, 1, 0, out, 16, 8, 256, ci.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out, got[rows]), s
