@@ -843,10 +843,11 @@ def main(argv=None) -> int:
             c_sid = np.asarray(ci.slot_ids, dtype=np.int32)
             c_pos = np.asarray(ci.positions, dtype=np.int32)
 
-            def cache_call(e0=None, e1=None, st=None):
+            def cache_call(e0=None, e1=None, st=None, chunk=0):
                 binding.attn_decode_cache(*ct, c_sid, c_pos, ci.n_queries, ci.n_cache_slots,
                                           ci.capacity, ci.ring, cw.window, cout, ci.n_q_heads,
                                           ci.n_kv_heads, ci.head_dim, ci.scale, stream=st or stream,
+                                          chunk=chunk,
                                           ev_partial_begin=e0.cuda_event if e0 is not None else None,
                                           ev_partial_end=e1.cuda_event if e1 is not None else None)
 
@@ -883,6 +884,14 @@ def main(argv=None) -> int:
                 "graph_gbs": round(uniq_b / (g_us * 1e-6) / 1e9, 1),
                 "graph_hbm_frac": round(uniq_b / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             })
+            if ci.n_queries > 48:
+                # the same batch with the per-call chunk floor (chunk = CHUNK_PER_CALL): longer
+                # chunks for a large batch of short slots, rounding then depending on the batch
+                for _ in range(3):
+                    cache_call(chunk=binding.CHUNK_PER_CALL)
+                g_pc = graph_us_per_call(lambda st: cache_call(st=st, chunk=binding.CHUNK_PER_CALL))
+                per[-1].update({"graph_us_per_call_chunk_per_call": round(g_pc, 2),
+                                "graph_hbm_frac_chunk_per_call": round(uniq_b / (g_pc * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
             print(f"[bench] {cw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), cold {cold:.2f} us",
                   file=sys.stderr, flush=True)
             del ct

@@ -50,6 +50,10 @@ class AttnDecodeError(RuntimeError):
         self.message = message
 
 
+# attn_decode_ex(chunk=CHUNK_PER_CALL): the per-call chunk floor (ATTN_DECODE_CHUNK_PER_CALL)
+CHUNK_PER_CALL = -1
+
+
 class _Options(ctypes.Structure):
     _fields_ = [
         ("chunk", ctypes.c_int32),

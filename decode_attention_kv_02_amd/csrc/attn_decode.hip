@@ -30,6 +30,7 @@ using namespace attn_decode_impl;
 
 static_assert(ATTN_DECODE_MAX_SLOTS_PER_LAUNCH == kMaxSlotsPerLaunch, "slot table size");
 static_assert(ATTN_DECODE_MAX_CHUNKS == kMaxChunks, "chunk bound");
+static_assert(ATTN_DECODE_CHUNK_PER_CALL == kChunkPerCall, "per-call chunk floor");
 static_assert(kSingleLaunchMaxChunks <= kMaxChunks, "single-launch merge bound");
 static_assert(sizeof(LaunchArgsT<kSmallTableSlots>) <= 4096, "the small query table stays within 4 KiB of arguments");
 // the large table: 18.5 KiB of kernel arguments, which ROCm copies whole (checked on MI355X up to 18 KiB)

@@ -215,6 +215,20 @@ inline int64_t chunk_for(int64_t n, int32_t head_dim, int32_t forced, bool mfma 
     return c;
 }
 
+// The chunk option's per-call mode (ATTN_DECODE_CHUNK_PER_CALL): every query's chunk is at least a
+// floor the planner takes from the whole call, so that a large batch of short slots runs about
+// kPerCallItems workgroups of long chunks instead of many short ones.  The floor depends on the
+// batch, so in this mode a slot's result can differ in rounding between a batched call and a call
+// of that slot alone; the default mode keeps them bitwise equal.  Measured (graph-replayed, one
+// launch): 128 ring slots of 2048 rows, int8 V, D = 256, 340 -> 244 us; the 1024 workgroups of
+// 2048-position chunks fill two generations of the int8 lane kernel's residency.
+constexpr int32_t kChunkPerCall = -1;
+constexpr int64_t kPerCallItems = 1024;
+inline int64_t per_call_floor(int64_t positions_x_heads) {
+    int64_t c = ceil_div(ceil_div(positions_x_heads, kPerCallItems), kChunkQuantum) * kChunkQuantum;
+    return c < kChunkMin ? kChunkMin : c > kChunkMax ? kChunkMax : c;
+}
+
 // Shape checks shared by every entry point.  Returns "" when valid.
 inline std::string check_common(int32_t n_q, int32_t n_kv, int32_t head_dim, bool v_int8,
                                 int32_t window, int32_t chunk, int32_t merge_mode) {
@@ -225,7 +239,7 @@ inline std::string check_common(int32_t n_q, int32_t n_kv, int32_t head_dim, boo
     if (!supported_head_dim(head_dim)) return "head_dim must be 64, 128, 256 or 512";
     if (v_int8 && head_dim % kQuantBlock != 0) return "int8 V needs head_dim % 32 == 0";
     if (window < 0) return "window must be >= 0";
-    if (chunk < 0) return "chunk override must be >= 0";
+    if (chunk < 0 && chunk != kChunkPerCall) return "chunk override must be >= 0, or -1 for the per-call floor";
     return "";
 }
 
@@ -404,12 +418,19 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
         sp.ring_base = qs.ring_base;
         sp.mfma = plan.mfma;
     }
+    int64_t call_floor = 0;   // the per-call mode's floor, 0 otherwise
+    if (chunk == kChunkPerCall) {
+        int64_t units = 0;
+        for (int32_t s = 0; s < n_slots; ++s) units += (int64_t)plan.slots[s].n * n_kv;
+        call_floor = per_call_floor(units);
+    }
     auto set_chunks = [&](SlotPlan &sp) {
         if (sp.n == 0) {
             sp.chunk = 0;
             sp.n_chunks = 1;
         } else {
-            const int64_t c = chunk_for(sp.n, head_dim, chunk, sp.mfma);
+            int64_t c = chunk_for(sp.n, head_dim, chunk > 0 ? chunk : 0, sp.mfma);
+            if (c < call_floor) c = call_floor;
             sp.chunk = (int32_t)(c > sp.n ? sp.n : c);
             sp.n_chunks = (int32_t)ceil_div(sp.n, sp.chunk);
         }

@@ -219,6 +219,12 @@ CACHE_WORKLOADS = (
                         "speculative verify: 4 slots x 4 consecutive draft positions over a 32768-row linear cache",
                         4, 32768, 0, tuple(s for s in range(4) for _ in range(4)),
                         tuple(32764 + t for _ in range(4) for t in range(4)), 16, 8, 256, False),
+    # the hybrid regime's bytes (1.64 GB) as a serving batch of 128 sequences on a sliding-window layer:
+    # one query per slot, each attending its ring's 2048 rows (one launch, the large query table)
+    CacheWorkloadConfig(12, "batch128_ring2048_d256_int8",
+                        "serving batch: 128 slots, a 2048-row ring each (int8 V), tokens deep into long contexts",
+                        128, 2048, 1, tuple(range(128)), tuple(4096 + 997 * s for s in range(128)),
+                        16, 8, 256, True),
 )
 
 

@@ -89,6 +89,8 @@ extern "C" {
 #define ATTN_DECODE_MAX_SLOTS_PER_LAUNCH 256
 /* Upper bound of KV chunks per slot; the planner widens chunks to stay below. */
 #define ATTN_DECODE_MAX_CHUNKS 4096
+/* attn_decode_options.chunk value selecting the per-call chunk floor (below). */
+#define ATTN_DECODE_CHUNK_PER_CALL (-1)
 
 /*
  * attn_decode -- decode attention for n_slots slots in one call.
@@ -106,11 +108,17 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
 
 /* Options of attn_decode_ex.  Zero-initialise and set what is needed. */
 typedef struct attn_decode_options {
-    /* KV positions per chunk: 0 = the planner's choice; otherwise a positive
-     * value forcing that chunk size for every slot (still widened to keep at
-     * most ATTN_DECODE_MAX_CHUNKS chunks per slot).  Used by tuning sweeps
-     * and by the chunking-invariance tests (cf. tessl nn.rs,
-     * flash_attn_decode_with_chunk). */
+    /* KV positions per chunk: 0 = the planner's choice, which depends on each
+     * slot's own length only, so a slot gives bitwise the same result batched
+     * or alone; a positive value forces that chunk size for every slot (still
+     * widened to keep at most ATTN_DECODE_MAX_CHUNKS chunks per slot), used by
+     * tuning sweeps and by the chunking-invariance tests (cf. tessl nn.rs,
+     * flash_attn_decode_with_chunk); ATTN_DECODE_CHUNK_PER_CALL = the
+     * planner's choice raised to a floor taken from the whole call (its
+     * attended positions times n_kv_heads over 1024, a multiple of 64 in
+     * [64, 2048]), for throughput on large batches of short slots: results then
+     * depend on the batch in fp32 rounding (they stay deterministic for a
+     * given call).  Other negative values are EINVAL. */
     int32_t chunk;
     /* How a slot split over several chunks is merged: 0 = automatic (today
      * the combine kernel, the faster of the two on MI355X), 1 = the separate

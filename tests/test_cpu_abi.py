@@ -149,6 +149,33 @@ def test_forced_chunk_is_used_and_still_bounded():
     assert p["n_chunks"][0] <= 4096
 
 
+def test_per_call_chunk_floor():
+    """chunk = CHUNK_PER_CALL raises every slot's chunk to ceil(positions x kv heads / 1024), rounded
+    up to a multiple of 64 within [64, 2048]; a chunk the per-slot rule already makes longer stays."""
+    pc = binding.CHUNK_PER_CALL
+    p = binding.attn_decode_plan([2048] * 128, 0, 16, 8, 256, v_int8=True, chunk=pc)
+    assert set(p["chunk"]) == {2048} and set(p["n_chunks"]) == {1}          # 2^21 / 1024 = 2048
+    assert p["partial_workgroups"] == 128 * 8
+    p = binding.attn_decode_plan([2048] * 48, 0, 16, 8, 256, v_int8=True, chunk=pc)
+    assert set(p["chunk"]) == {768} and set(p["n_chunks"]) == {3}           # 786432 / 1024 = 768
+    p = binding.attn_decode_plan([32768] * 8, 0, 16, 8, 256, v_int8=True, chunk=pc)
+    assert set(p["chunk"]) == {2048}
+    # small calls: the floor is at most 64 and the per-slot rule decides
+    for seq in ([4096], [256], [1024, 8192, 32768, 2000]):
+        default = binding.attn_decode_plan(seq, 0, 16, 8, 256)
+        per_call = binding.attn_decode_plan(seq, 0, 16, 8, 256, chunk=pc)
+        units = sum(seq) * 8
+        floor = min(2048, max(64, -(-(-(-units // 1024)) // 64) * 64))
+        for n, c0, c1 in zip(seq, default["chunk"], per_call["chunk"]):
+            assert c1 == min(n, max(c0, floor)), (seq, n, c0, c1, floor)
+    # the floor never exceeds 2048 or the slot
+    p = binding.attn_decode_plan([300, 131072 * 4], 0, 16, 8, 256, chunk=pc)
+    assert p["chunk"] == [300, 2048]
+    with pytest.raises(binding.AttnDecodeError) as ei:
+        binding.attn_decode_plan([4], 0, 2, 1, 64, chunk=-2)
+    assert ei.value.code == binding.ATTN_DECODE_EINVAL
+
+
 def test_one_query_with_four_heads_per_kv_head_goes_to_the_matrix_cores():
     # 4 (query, head) columns are enough for the matrix cores wherever they take fp16 products:
     # their chunk rule gives 512 positions at 4096, the lanes' 128 (256 at head_dim 64).  Two heads per kv head (the

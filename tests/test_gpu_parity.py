@@ -182,6 +182,22 @@ def test_many_slots(n_slots):
     _report(f"{n_slots} slots", assert_parity(got, ref, f"{n_slots} slots"))
 
 
+@pytest.mark.parametrize("case", [
+    ((2048,) * 48, 16, 8, 256, True),          # floor 768: three chunks per slot
+    ((1024, 8192, 32768, 2000), 16, 8, 256, False),
+    ((300,) * 60, 16, 8, 256, False),
+    ((512,) * 64, 32, 4, 128, False),          # matrix cores, eight heads per kv head
+], ids=["int8_48x2048", "ragged", "60x300", "mfma_64x512"])
+def test_per_call_chunk_floor(case):
+    """chunk = CHUNK_PER_CALL: every output against the oracle, and the same call twice bitwise."""
+    seq, nq, nkv, d, i8 = case
+    inp = make_inputs(seq, nq, nkv, d, i8, seed_base=7470 + len(seq))
+    dev = to_device(inp)
+    got = run_gpu(inp, 0, chunk=binding.CHUNK_PER_CALL, dev_tensors=dev)
+    _report(f"per-call floor {len(seq)} slots", assert_parity(got.cpu().numpy(), run_oracle(inp, 0), str(case)))
+    assert torch.equal(got, run_gpu(inp, 0, chunk=binding.CHUNK_PER_CALL, dev_tensors=dev))
+
+
 def test_many_slots_equal_per_slot_bitwise():
     """A slot's result does not depend on which table or launch carried it: rows of a 300-slot call
     (large table, then small) equal the same slots called alone."""

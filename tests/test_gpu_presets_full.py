@@ -63,8 +63,11 @@ def test_global_d512_codebook_preset_full_output():
     _say(f"{cfg.name}: undone max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}")
 
 
-def test_verify_preset_full_output():
-    cfg = next(c for c in CACHE_WORKLOADS if c.name.startswith("verify"))
+@pytest.mark.parametrize("prefix", ["verify", "batch128"])
+def test_cache_preset_full_output(prefix):
+    """The speculative-verify preset and the 128-slot serving batch (one launch on the large query
+    table and the single-buffer lane kernel), every output row against the oracle."""
+    cfg = next(c for c in CACHE_WORKLOADS if c.name.startswith(prefix))
     ci = cache_workload_inputs(cfg)
     _say(f"{cfg.name}: generated")
     q, k, v = ci.q.to(DEV), ci.k.to(DEV), ci.v.to(DEV)
