@@ -258,8 +258,9 @@ class TimingEvent:
         return ms.value
 
     def __del__(self):
-        if TimingEvent._hip is not None and self.handle:
-            TimingEvent._hip.hipEventDestroy(self.handle)
+        hip = type(self)._hip   # the class stays reachable at interpreter exit, its module name may not
+        if hip is not None and self.handle:
+            hip.hipEventDestroy(self.handle)
 
 
 def torch_reductions() -> int:
