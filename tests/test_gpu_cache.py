@@ -247,3 +247,16 @@ def test_cache_call_of_many_queries():
     got = run_gpu_cache(ci, 0).cpu().numpy()
     ref = run_oracle_cache(ci, 0)
     _report("130 cache queries", assert_parity(got, ref, "130 cache queries"))
+
+
+def test_per_call_chunk_floor_on_draft_groups():
+    """The per-call chunk floor on a speculative-verify call (drafts grouped on the matrix cores and
+    on the lanes) and a ring call: every output against the oracle."""
+    for case in ((4, 4096, 0, tuple(s for s in range(4) for _ in range(4)),
+                  tuple(4092 + t for _ in range(4) for t in range(4)), 16, 8, 256, False),
+                 (4, 4096, 0, (0, 0, 1, 1, 2, 2, 3, 3), (4000, 4001) * 4, 4, 2, 128, True),
+                 (8, 1024, 1, tuple(range(8)) * 2, tuple(range(5000, 5016)), 16, 8, 256, True)):
+        nc, cap, ring, sid, pos, nq, nkv, d, i8 = case
+        ci = make_cache_inputs(nc, cap, ring, sid, pos, nq, nkv, d, i8, seed_base=9670 + nq + ring)
+        got = run_gpu_cache(ci, 0, chunk=binding.CHUNK_PER_CALL).cpu().numpy()
+        _report(f"per-call floor {len(sid)} queries", assert_parity(got, run_oracle_cache(ci, 0), str(case[:3])))
