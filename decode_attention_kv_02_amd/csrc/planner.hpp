@@ -216,16 +216,18 @@ inline int64_t chunk_for(int64_t n, int32_t head_dim, int32_t forced, bool mfma 
 }
 
 // The chunk option's per-call mode (ATTN_DECODE_CHUNK_PER_CALL): every query's chunk is at least a
-// floor the planner takes from the whole call, so that a large batch of short slots runs about
-// kPerCallItems workgroups of long chunks instead of many short ones.  The floor depends on the
-// batch, so in this mode a slot's result can differ in rounding between a batched call and a call
-// of that slot alone; the default mode keeps them bitwise equal.  Measured (graph-replayed, one
-// launch): 128 ring slots of 2048 rows, int8 V, D = 256, 340 -> 244 us; the 1024 workgroups of
-// 2048-position chunks fill two generations of the int8 lane kernel's residency.
+// floor the planner takes from the whole call, so that a large batch runs about as many workgroups
+// of long chunks as its kernel keeps resident over one or two generations, instead of many short
+// ones: 1024 on the lane kernel (two or three 4-wave workgroups per CU), 256 on the matrix cores
+// at head_dim 512 (one 8-wave workgroup per CU), 512 on the matrix cores below.  The floor depends
+// on the batch, so in this mode a slot's result can differ in rounding between a batched call and
+// a call of that slot alone; the default mode keeps them bitwise equal.  Measured (graph-replayed):
+// 128 ring slots of 2048 rows, int8 V, D = 256, 340 -> 244 us; 8 x 32768 at D = 512, codebook V,
+// 16 q / 2 kv heads, forced chunks 1024 -> 2048: 145.0 -> 136.8 us, 16 x 32768 283.7 -> 264.6.
 constexpr int32_t kChunkPerCall = -1;
-constexpr int64_t kPerCallItems = 1024;
-inline int64_t per_call_floor(int64_t positions_x_heads) {
-    int64_t c = ceil_div(ceil_div(positions_x_heads, kPerCallItems), kChunkQuantum) * kChunkQuantum;
+inline int64_t per_call_items(bool mfma, int32_t head_dim) { return !mfma ? 1024 : head_dim == 512 ? 256 : 512; }
+inline int64_t per_call_floor(int64_t positions_x_heads, int64_t items) {
+    int64_t c = ceil_div(ceil_div(positions_x_heads, items), kChunkQuantum) * kChunkQuantum;
     return c < kChunkMin ? kChunkMin : c > kChunkMax ? kChunkMax : c;
 }
 
@@ -418,19 +420,19 @@ inline std::string make_plan(const std::vector<QuerySpan> &spans, int32_t n_q, i
         sp.ring_base = qs.ring_base;
         sp.mfma = plan.mfma;
     }
-    int64_t call_floor = 0;   // the per-call mode's floor, 0 otherwise
-    if (chunk == kChunkPerCall) {
-        int64_t units = 0;
-        for (int32_t s = 0; s < n_slots; ++s) units += (int64_t)plan.slots[s].n * n_kv;
-        call_floor = per_call_floor(units);
-    }
+    int64_t call_units = 0;   // the per-call mode: attended positions x kv heads of the call
+    if (chunk == kChunkPerCall)
+        for (int32_t s = 0; s < n_slots; ++s) call_units += (int64_t)plan.slots[s].n * n_kv;
     auto set_chunks = [&](SlotPlan &sp) {
         if (sp.n == 0) {
             sp.chunk = 0;
             sp.n_chunks = 1;
         } else {
             int64_t c = chunk_for(sp.n, head_dim, chunk > 0 ? chunk : 0, sp.mfma);
-            if (c < call_floor) c = call_floor;
+            if (chunk == kChunkPerCall) {
+                const int64_t floor_c = per_call_floor(call_units, per_call_items(sp.mfma, head_dim));
+                if (c < floor_c) c = floor_c;
+            }
             sp.chunk = (int32_t)(c > sp.n ? sp.n : c);
             sp.n_chunks = (int32_t)ceil_div(sp.n, sp.chunk);
         }

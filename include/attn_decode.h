@@ -115,10 +115,12 @@ typedef struct attn_decode_options {
      * tuning sweeps and by the chunking-invariance tests (cf. tessl nn.rs,
      * flash_attn_decode_with_chunk); ATTN_DECODE_CHUNK_PER_CALL = the
      * planner's choice raised to a floor taken from the whole call (its
-     * attended positions times n_kv_heads over 1024, a multiple of 64 in
-     * [64, 2048]), for throughput on large batches of short slots: results then
-     * depend on the batch in fp32 rounding (they stay deterministic for a
-     * given call).  Other negative values are EINVAL. */
+     * attended positions times n_kv_heads over the workgroups the partial
+     * kernel keeps busy: 1024 on the lane kernel, 256 on the matrix cores at
+     * head_dim 512, 512 below; a multiple of 64 in [64, 2048]), for throughput
+     * on large batches: results then depend on the batch in fp32 rounding
+     * (they stay deterministic for a given call).  Other negative values are
+     * EINVAL. */
     int32_t chunk;
     /* How a slot split over several chunks is merged: 0 = automatic (today
      * the combine kernel, the faster of the two on MI355X), 1 = the separate

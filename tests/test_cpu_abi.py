@@ -150,8 +150,9 @@ def test_forced_chunk_is_used_and_still_bounded():
 
 
 def test_per_call_chunk_floor():
-    """chunk = CHUNK_PER_CALL raises every slot's chunk to ceil(positions x kv heads / 1024), rounded
-    up to a multiple of 64 within [64, 2048]; a chunk the per-slot rule already makes longer stays."""
+    """chunk = CHUNK_PER_CALL raises every slot's chunk to ceil(positions x kv heads / W), rounded
+    up to a multiple of 64 within [64, 2048], with W = 1024 on the lane kernel, 256 on the matrix
+    cores at head_dim 512; a chunk the per-slot rule already makes longer stays."""
     pc = binding.CHUNK_PER_CALL
     p = binding.attn_decode_plan([2048] * 128, 0, 16, 8, 256, v_int8=True, chunk=pc)
     assert set(p["chunk"]) == {2048} and set(p["n_chunks"]) == {1}          # 2^21 / 1024 = 2048
@@ -171,6 +172,10 @@ def test_per_call_chunk_floor():
     # the floor never exceeds 2048 or the slot
     p = binding.attn_decode_plan([300, 131072 * 4], 0, 16, 8, 256, chunk=pc)
     assert p["chunk"] == [300, 2048]
+    # the matrix cores at head_dim 512 aim at 256 workgroups (one 8-wave workgroup per CU)
+    assert binding.attn_decode_plan([32768] * 8, 0, 16, 2, 512, v_int8=True, chunk=pc)["chunk"] == [2048] * 8
+    assert binding.attn_decode_plan([16384] * 8, 0, 16, 2, 512, v_int8=True, chunk=pc)["chunk"] == [1024] * 8
+    assert binding.attn_decode_plan([32768] * 4, 0, 16, 2, 512, v_int8=True, chunk=pc)["chunk"] == [1024] * 4
     with pytest.raises(binding.AttnDecodeError) as ei:
         binding.attn_decode_plan([4], 0, 2, 1, 64, chunk=-2)
     assert ei.value.code == binding.ATTN_DECODE_EINVAL

@@ -187,7 +187,8 @@ def test_many_slots(n_slots):
     ((1024, 8192, 32768, 2000), 16, 8, 256, False),
     ((300,) * 60, 16, 8, 256, False),
     ((512,) * 64, 32, 4, 128, False),          # matrix cores, eight heads per kv head
-], ids=["int8_48x2048", "ragged", "60x300", "mfma_64x512"])
+    ((16384,) * 8, 16, 2, 512, True),          # matrix cores at head_dim 512: 1024 instead of 512
+], ids=["int8_48x2048", "ragged", "60x300", "mfma_64x512", "mfma_d512_8x16384"])
 def test_per_call_chunk_floor(case):
     """chunk = CHUNK_PER_CALL: every output against the oracle, and the same call twice bitwise."""
     seq, nq, nkv, d, i8 = case
