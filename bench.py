@@ -779,10 +779,10 @@ def main(argv=None) -> int:
             bout = torch.empty((bi.n_slots, bi.n_q_heads, bi.head_dim), dtype=torch.float32, device=dev)
             b_seq = np.asarray(bi.seq_lens, dtype=np.int32)
 
-            def cb_call(e0=None, e1=None, st=None):
+            def cb_call(e0=None, e1=None, st=None, chunk=0):
                 binding.attn_decode_cb(bq, bk, bvc, bvn, bcb, bi.codebook_bits, b_seq, bw.window, bout,
                                        bi.n_slots, bi.n_q_heads, bi.n_kv_heads, bi.head_dim, bi.scale,
-                                       stream=st or stream,
+                                       stream=st or stream, chunk=chunk,
                                        ev_partial_begin=e0.cuda_event if e0 is not None else None,
                                        ev_partial_end=e1.cuda_event if e1 is not None else None)
                 binding.attn_fwht_undo(bout, bsg, bout, stream=st or stream)
@@ -828,6 +828,18 @@ def main(argv=None) -> int:
                 "graph_us_per_call": round(g_us, 2),
                 "graph_gbs": round(nb / (g_us * 1e-6) / 1e9, 1),
             })
+            # the same step with the per-call chunk floor (chunk = CHUNK_PER_CALL)
+            for _ in range(3):
+                cb_call(chunk=binding.CHUNK_PER_CALL)
+            pk_pc = []
+            for _ in range(5):
+                c0, c1 = TimingEvent(stream), TimingEvent(stream)
+                cb_call(c0, c1, chunk=binding.CHUNK_PER_CALL)
+                torch.cuda.synchronize()
+                pk_pc.append(c0.elapsed_time(c1) * 1e3)
+            g_pc = graph_us_per_call(lambda st: cb_call(st=st, chunk=binding.CHUNK_PER_CALL))
+            per[-1].update({"partial_kernel_us_median_chunk_per_call": round(statistics.median(pk_pc), 2),
+                            "graph_us_per_call_chunk_per_call": round(g_pc, 2)})
             print(f"[bench] {bw.name}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), cold {cold:.2f} us, "
                   f"partial {per[-1]['partial_kernel_gbs']} GB/s", file=sys.stderr, flush=True)
             del bq, bk, bvc, bvn, bcb, bsg, bout
