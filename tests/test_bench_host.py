@@ -23,3 +23,15 @@ def test_traffic_summary_is_read_only_for_the_current_kernel_source(tmp_path, mo
     (tmp_path / "traffic_wl_w0.txt").write_text(body.format("0" * 16))
     assert bench.read_traffic("wl", 0) is None
     assert bench.read_traffic("missing", 0) is None
+
+
+def test_every_committed_profile_is_of_the_current_kernel_source():
+    """Each rocprofv3 summary under profiles/ names the digest of the kernel headers it was
+    taken on; a summary of other kernels describes code that is no longer built."""
+    import glob
+    import os
+    digest = bench.kernel_source_digest()
+    files = sorted(glob.glob(os.path.join(os.path.dirname(os.path.abspath(bench.__file__)), "profiles", "*")))
+    assert files, "no profiles committed"
+    stale = [os.path.basename(f) for f in files if digest not in open(f).read()]
+    assert not stale, f"profiles taken on other kernel sources (current {digest}): {stale}"
