@@ -344,7 +344,7 @@ PAGE_CODEBOOKS = {
 def codebook_levels(bits: int) -> torch.Tensor:
     """The V codebook (float32, ascending) that the presets and tests use for ``bits``: the
     pages' printed table at 5, 6 and 8 bits (PAGE_CODEBOOKS); at other widths, which the pages
-    do not use, this build's own Lloyd iteration (lloyd_max_gaussian)."""
+    do not use, a Lloyd iteration computed here (lloyd_max_gaussian)."""
     if int(bits) in PAGE_CODEBOOKS:
         return torch.tensor(PAGE_CODEBOOKS[int(bits)], dtype=torch.float32)
     return lloyd_max_gaussian(bits)
@@ -364,7 +364,7 @@ def _lloyd_levels(bits: int, iters: int) -> Tuple[float, ...]:
 
 
 def lloyd_max_gaussian(bits: int, iters: int = 2000) -> torch.Tensor:
-    """This build's own Lloyd-Max levels for N(0, 1) with 2**bits levels (float32, ascending),
+    """Lloyd-Max levels for N(0, 1), computed here, with 2**bits levels (float32, ascending),
     an alternative to the pages' printed tables and the levels of the widths they do not print.
 
     Lloyd's iteration from the quantile midpoints: cell boundaries at the

@@ -16,7 +16,7 @@ bits takes its levels from there.
   +-5.0652659.
 * As quantisers of N(0, 1) they are close to Lloyd-Max: the 5-bit table is a
   fixed point of Lloyd's map, and every table's mean-square error lies within
-  1% of this build's own 2000-step Lloyd iteration and well below a uniform
+  1% of a 2000-step Lloyd iteration (lloyd_max_gaussian) and well below a uniform
   quantiser's over the same range.
 """
 import json
