@@ -7,6 +7,7 @@ applies, a forced kernel path; a third of the cases are cache calls (fixed-capac
 positions past the wrap).  The shapes are sized so the oracle finishes each in about a second.
 Every output element is compared with the oracle; for packed calls a slot drawn at random is also
 called alone and must give the same bits (the chunks of a slot depend on its own length only).
+Twelve more cases draw codebook V on the fixed-capacity or ring cache (attn_decode_cache_cb).
 """
 import numpy as np
 import pytest
@@ -133,3 +134,56 @@ def test_random_shape_matches_the_oracle(case):
         _cache(case)
     else:
         _packed(case)
+
+
+def _draw_cb_cache(i):
+    """Codebook V on the fixed-capacity or ring cache (attn_decode_cache_cb)."""
+    r = np.random.default_rng(8300 + i)
+    while True:
+        d = int(r.choice([64, 128, 256, 512]))
+        G = int(r.choice([1, 2, 3, 4, 6, 8, 16]))
+        nkv = int(r.choice([1, 2, 4, 8]))
+        bits = int(r.choice([5, 6, 8]))
+        cap = int(r.choice([300, 1024, 4096]))
+        ring = int(r.integers(0, 2))
+        n_cache = int(r.integers(1, 4))
+        nqu = int(r.integers(1, 6))
+        sid = tuple(int(x) for x in r.integers(0, n_cache, size=nqu))
+        pos = tuple(int(x) for x in r.integers(0, 3 * cap if ring else cap, size=nqu))
+        W = 0 if r.random() < 0.6 else int(r.integers(1, 3000))
+        mm = int(r.choice([0, 1, 2]))
+        path = int(r.choice([0, 1] + ([2] if G % 8 == 0 and d >= 128 else [])))
+        if nqu * cap * G * nkv * d <= WORK_LIMIT and G * nkv <= 64:
+            return dict(d=d, G=G, nkv=nkv, bits=bits, cap=cap, ring=ring, n_cache=n_cache, sid=sid, pos=pos, W=W,
+                        mm=mm, path=path, seed=8300 + i)
+
+
+CB_CACHE_CASES = [_draw_cb_cache(i) for i in range(12)]
+
+
+def _cb_id(c):
+    return (f"cbcache-D{c['d']}-G{c['G']}-kv{c['nkv']}-b{c['bits']}-cap{c['cap']}-r{c['ring']}-W{c['W']}"
+            f"-mm{c['mm']}-p{c['path']}")
+
+
+@pytest.mark.parametrize("case", CB_CACHE_CASES, ids=[_cb_id(c) for c in CB_CACHE_CASES])
+def test_random_codebook_cache_matches_the_oracle(case):
+    from decode_attention_kv_02_amd.workloads import make_cache_codebook_inputs
+    from oracle import oracle_attn_decode_cache_cb
+    c = case
+    d, G, nkv, bits = c["d"], c["G"], c["nkv"], c["bits"]
+    nq = G * nkv
+    print(f"[random] start {_cb_id(c)} sid={c['sid']} pos={c['pos']}", flush=True)
+    ci = make_cache_codebook_inputs(c["n_cache"], c["cap"], c["ring"], c["sid"], c["pos"], nq, nkv, d, bits,
+                                    seed_base=c["seed"])
+    dev = torch.device("cuda:0")
+    q, k, vc, vn, cb = (t.to(dev) for t in (ci.q, ci.k, ci.v_codes, ci.v_norms, ci.codebook))
+    out = torch.full((len(c["sid"]), nq, d), float("nan"), dtype=torch.float32, device=dev)
+    binding.attn_decode_cache_cb(q, k, vc, vn, cb, bits, c["sid"], c["pos"], len(c["sid"]), c["n_cache"], c["cap"],
+                                 c["ring"], c["W"], out, nq, nkv, d, ci.scale, merge_mode=c["mm"], path=c["path"])
+    torch.cuda.synchronize()
+    ref = oracle_attn_decode_cache_cb(ci.q.numpy(), ci.k.numpy(), ci.v_codes.numpy(), ci.v_norms.numpy(),
+                                      ci.codebook.numpy(), bits, c["sid"], c["pos"], c["n_cache"], c["cap"],
+                                      c["ring"], c["W"], nq, nkv, d, ci.scale)
+    err = assert_parity(out.cpu().numpy(), ref, _cb_id(c))
+    print(f"[random] {_cb_id(c)}: max-abs {err[0]:.3e} rel-L2 {err[1]:.3e}", flush=True)
