@@ -38,7 +38,10 @@ One JSON line is printed.  Besides the contract fields it carries
     default events and once with timing-only ones, which skip the system-scope
     cache writeback and invalidation a default event performs),
     with the CPU fp64 oracle over all query rows of the preset on all cores
-    (and on one core for the three smallest presets),
+    (and on one core for the three smallest presets), and the graph figure again
+    with ``chunk = CHUNK_PER_CALL`` (``*_chunk_per_call``: chunks raised to the
+    per-call floor, which gives up the per-slot bitwise contract; small calls keep
+    their chunks),
     plus the codebook-V presets (``attn_decode_cb`` followed by ``attn_fwht_undo``
     in place; bytes = fp16 K, one index byte per V element and the fp32 norms),
     the fixed-capacity cache presets (``attn_decode_cache``: a
@@ -470,11 +473,11 @@ def main(argv=None) -> int:
         e.record(stream)  # materialise the underlying hipEvent_t
         return e
 
-    def call(inp, tens, out, W, ev0=None, ev1=None, st=None):
+    def call(inp, tens, out, W, ev0=None, ev1=None, st=None, chunk=None):
         q, k, v, vs = tens
         binding.attn_decode_ex(q, k, v, vs, inp.seq_lens, W, out, inp.n_slots, inp.n_q_heads,
                                inp.n_kv_heads, inp.head_dim, inp.scale, stream=st or stream,
-                               chunk=args.chunk, merge_mode=args.merge_mode,
+                               chunk=args.chunk if chunk is None else chunk, merge_mode=args.merge_mode,
                                ev_partial_begin=ev0.cuda_event if ev0 is not None else None,
                                ev_partial_end=ev1.cuda_event if ev1 is not None else None)
 
@@ -713,6 +716,10 @@ def main(argv=None) -> int:
                     torch.cuda.synchronize()
                     pk.append(c0.elapsed_time(c1) * 1e3)
                 g_us = graph_us_per_call(lambda st: call(pin, ptens, pout, W, st=st))
+                # the same call with the per-call chunk floor (chunk = CHUNK_PER_CALL; small calls
+                # keep their chunks), context beside the per-slot figures
+                call(pin, ptens, pout, W, chunk=binding.CHUNK_PER_CALL)
+                g_pc = graph_us_per_call(lambda st: call(pin, ptens, pout, W, st=st, chunk=binding.CHUNK_PER_CALL))
                 # 50 reps of: a 1 GiB flush read, then one whole call (plan upload, partial and
                 # combine kernels) between two events on the call's stream
                 pairs = [(new_event(), new_event()) for _ in range(50)]
@@ -759,6 +766,8 @@ def main(argv=None) -> int:
                     "graph_us_per_call": round(g_us, 2),
                     "graph_gbs": round(nb / (g_us * 1e-6) / 1e9, 1),
                     "graph_hbm_frac": round(nb / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "graph_us_per_call_chunk_per_call": round(g_pc, 2),
+                    "graph_hbm_frac_chunk_per_call": round(nb / (g_pc * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 })
                 print(f"[bench] {w.name} W={W}: warm {warm:.2f} us ({per[-1]['warm_gbs']} GB/s), "
                       f"cold {cold:.2f} us ({per[-1]['cold_gbs']} GB/s), graph {g_us:.2f} us, "
