@@ -35,3 +35,9 @@ def test_every_committed_profile_is_of_the_current_kernel_source():
     assert files, "no profiles committed"
     stale = [os.path.basename(f) for f in files if digest not in open(f).read()]
     assert not stale, f"profiles taken on other kernel sources (current {digest}): {stale}"
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work(capsys):
+    for n in (2, 8):
+        assert bench.main(["--gpus", str(n)]) == 2
+        assert f"--gpus {n} is not supported" in capsys.readouterr().err
