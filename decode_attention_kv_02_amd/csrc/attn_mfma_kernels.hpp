@@ -115,7 +115,7 @@ constexpr int kPairMaxSpins = 1 << 21;
 template <int D, int VF, int NS>
 __global__ __launch_bounds__((MfmaGeometry<D, VF>::THREADS), (MfmaGeometry<D, VF>::MIN_WG)) void attn_partial_mfma_kernel(const LaunchArgsT<NS> args) {
     using Geo = MfmaGeometry<D, VF>;
-    constexpr int KS = Geo::KS, KW = Geo::KW, EV = Geo::EV, BW = Geo::BW, NB = Geo::NB, NO = Geo::NO;
+    constexpr int KW = Geo::KW, EV = Geo::EV, BW = Geo::BW, NB = Geo::NB, NO = Geo::NO;
     constexpr int DS = Geo::DS, DH = Geo::DH, NT = Geo::THREADS;
     constexpr int CB_B = D < 256 ? D : 256;   // codebook norm block
     static_assert(NT >= 256, "one thread per codebook table entry");
